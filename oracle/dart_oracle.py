@@ -1,0 +1,366 @@
+"""Plain fp64 CPU oracle for the DART hot path.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke check
+in ``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py`` may import
+this module.  It shares no code, headers, helpers or tables with the HIP
+library; the HIP path never imports it.  Every function is written for a
+reader to check against the pages by eye: loops and numpy primitives (einsum,
+cumsum, exp), fp64 throughout, no blocking or fusion beyond what the
+definition states.
+
+Sources (cited by page and section; the pages print no code):
+
+* [abstract]  DART abstract (aipentium and mlsanity pages): DART keeps the
+  per-chunk state contributions that the Mamba-2 chunked scan produces,
+  decodes token-conditioned keys and values from them, runs state-memory
+  attention (SMA) over them and adds the result to the Mamba-2 output through
+  a gated residual; the cache saving is 75% at S=256, N=128.
+* [pith-core]  Pith review of DART, "Core claim": values read as C_t·ΔH[c],
+  keys as ΔH[c]·E_t, attention over chunk-level pairs, readout added through a
+  zero-initialised scalar gate.
+* [pith-carries]  Pith review, "What carries the argument": ΔH[c] is the
+  N×P contribution of chunk c to the chunk-boundary state (key axis N, value
+  axis P); query Q_t.
+* [pith-maj3]  Pith review, referee major comment 3 (paper §3 Eq. 8): the
+  readouts use the raw ΔH[c], with no inter-chunk decay applied.
+* [pith-eq14]  Pith review, minor comment 1 and circularity check (paper §4
+  Eq. 14): per head the DART cache holds M·N·P values against 2·L·P for a
+  token-level attention layer.
+* [pith-axioms]  Pith review, axiom ledger: SSD writes Mamba-2 as structured
+  causal attention (paper Eq. 4); the chunked scan splits the output into
+  intra-chunk and inter-chunk terms and yields ΔH[c].
+
+Readings where the pages are silent (each one is listed in the design doc):
+* Mamba-2 recurrence h_t = exp(dt_t·A)·h_{t-1} + dt_t·B_t x_tᵀ, y_t = C_tᵀ h_t
+  (zero-order-hold discretisation; D skip, gating and norm are absent).
+* A token in chunk k attends over the completed chunks c < k only; tokens of
+  chunk 0 get a zero SMA readout.
+* Score scale 1/sqrt(N) (N is the key dimension).
+* Gate: y = y_ssd + g·o with g a raw scalar.
+* B, C and Q are shared by groups of H/G consecutive heads; x, E, dt per head.
+
+Layouts (row-major numpy arrays, float64):
+  x, E   [B, L, H, P]      dt [B, L, H]      A [H]
+  Bm, C, Q [B, L, G, N]    ΔH [B, H, M, N, P]   H_in [B, H, M+1, N, P]
+"""
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "group_of_head",
+    "recurrence",
+    "chunk_states",
+    "state_pass",
+    "chunk_output",
+    "sma",
+    "sma_bruteforce",
+    "gated_output",
+    "prefill",
+    "decode_step",
+    "cache_elements",
+    "cache_ratio",
+    "round_bf16",
+]
+
+
+def group_of_head(H, G):
+    """Head h reads the B/C/Q group h // (H // G) (reading: heads grouped
+    contiguously, as in Mamba-2's grouped B/C)."""
+    if G <= 0 or H % G:
+        raise ValueError(f"heads {H} not divisible by groups {G}")
+    return np.arange(H) // (H // G)
+
+
+def _per_head(T, H):
+    """Expand a grouped [B, L, G, N] tensor to [B, L, H, N]."""
+    return np.asarray(T, dtype=np.float64)[:, :, group_of_head(H, T.shape[2]), :]
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# O2 - sequential recurrence (ground truth of the SSM branch)
+# --------------------------------------------------------------------------
+def recurrence(x, dt, A, Bm, C, h0=None, keep_states=False):
+    """Token-by-token Mamba-2 recurrence [pith-core: Mamba-2 reads values
+    from its state as C_t H_t; pith-axioms].
+
+    a_t = exp(dt_t·A_h);  h_t = a_t·h_{t-1} + dt_t·B_t x_tᵀ;  y_t = C_tᵀ h_t.
+    Returns (y [B,L,H,P], h_final [B,H,N,P], states [B,L,H,N,P] or None).
+    """
+    x, dt, A = _f64(x), _f64(dt), _f64(A)
+    Bsz, L, H, P = x.shape
+    Bh, Ch = _per_head(Bm, H), _per_head(C, H)
+    N = Bh.shape[-1]
+    h = np.zeros((Bsz, H, N, P)) if h0 is None else _f64(h0).copy()
+    y = np.empty((Bsz, L, H, P))
+    states = np.empty((Bsz, L, H, N, P)) if keep_states else None
+    for t in range(L):
+        a = np.exp(dt[:, t, :] * A[None, :])                      # [B,H]
+        inp = dt[:, t, :, None, None] * Bh[:, t, :, :, None] * x[:, t, :, None, :]
+        h = a[:, :, None, None] * h + inp
+        y[:, t] = np.einsum("bhn,bhnp->bhp", Ch[:, t], h)
+        if keep_states:
+            states[:, t] = h
+    return y, h, states
+
+
+# --------------------------------------------------------------------------
+# O3 - chunk state contributions ΔH[c]
+# --------------------------------------------------------------------------
+def chunk_states(x, dt, A, Bm, S):
+    """ΔH[c] = Σ_{i in c} exp(A·Σ_{j=i+1}^{end(c)} dt_j)·dt_i·B_i x_iᵀ
+    [pith-carries: contribution of chunk c to the chunk-boundary state;
+    abstract].  The decay from token i to the chunk end is a direct segment
+    sum of the later dt's of the chunk (not a cumsum difference).
+    Returns ΔH [B,H,M,N,P]."""
+    x, dt, A = _f64(x), _f64(dt), _f64(A)
+    Bsz, L, H, P = x.shape
+    if L % S:
+        raise ValueError("L must be a multiple of S")
+    M = L // S
+    Bh = _per_head(Bm, H)
+    N = Bh.shape[-1]
+    dH = np.zeros((Bsz, H, M, N, P))
+    for c in range(M):
+        sl = slice(c * S, (c + 1) * S)
+        dtc = dt[:, sl, :]                                          # [B,S,H]
+        tail = np.zeros_like(dtc)
+        for i in range(S):
+            tail[:, i, :] = dtc[:, i + 1:, :].sum(axis=1)
+        w = np.exp(tail * A[None, None, :]) * dtc                   # [B,S,H]
+        dH[:, :, c] = np.einsum("bsh,bshn,bshp->bhnp", w, Bh[:, sl], x[:, sl])
+    return dH
+
+
+# --------------------------------------------------------------------------
+# O4 - inter-chunk state passing
+# --------------------------------------------------------------------------
+def state_pass(dH, dt, A, S, h0=None):
+    """H_in[0] = h0 (zero by default); H_in[c+1] = exp(A·Σ_{j in c} dt_j)·H_in[c]
+    + ΔH[c]  [pith-axioms: inter-chunk term of the chunked scan].
+    Returns H_in [B,H,M+1,N,P]; H_in[:, :, M] is the final state."""
+    dH, dt, A = _f64(dH), _f64(dt), _f64(A)
+    Bsz, H, M, N, P = dH.shape
+    H_in = np.zeros((Bsz, H, M + 1, N, P))
+    if h0 is not None:
+        H_in[:, :, 0] = _f64(h0)
+    for c in range(M):
+        total = dt[:, c * S:(c + 1) * S, :].sum(axis=1)             # [B,H]
+        decay = np.exp(total * A[None, :])
+        H_in[:, :, c + 1] = decay[:, :, None, None] * H_in[:, :, c] + dH[:, :, c]
+    return H_in
+
+
+# --------------------------------------------------------------------------
+# O5 - native chunk output (quadratic SSD form)
+# --------------------------------------------------------------------------
+def chunk_output(x, dt, A, Bm, C, H_in, S):
+    """y_t = Σ_{j in k, j<=t} (C_t·B_j)·exp(A·Σ_{l=j+1}^{t} dt_l)·dt_j·x_j
+           + exp(A·Σ_{l=kS}^{t} dt_l)·C_tᵀ H_in[k]
+    for token t of chunk k  [pith-axioms: SSD as structured causal attention
+    (paper Eq. 4), split into intra- and inter-chunk terms].
+    Returns y_ssd [B,L,H,P]."""
+    x, dt, A = _f64(x), _f64(dt), _f64(A)
+    Bsz, L, H, P = x.shape
+    M = L // S
+    Bh, Ch = _per_head(Bm, H), _per_head(C, H)
+    y = np.empty((Bsz, L, H, P))
+    causal = np.tril(np.ones((S, S), dtype=bool))                   # j <= t
+    for k in range(M):
+        sl = slice(k * S, (k + 1) * S)
+        dtk = dt[:, sl, :]                                          # [B,S,H]
+        cs = np.cumsum(dtk, axis=1)                                 # Σ_{l=kS}^{t}
+        seg = cs[:, :, None, :] - cs[:, None, :, :]                 # [B,t,j,H] = Σ_{l=j+1}^{t}
+        seg = np.where(causal[None, :, :, None], seg, 0.0)
+        decay = np.where(causal[None, :, :, None], np.exp(seg * A), 0.0)
+        cb = np.einsum("bthn,bjhn->btjh", Ch[:, sl], Bh[:, sl])
+        wts = cb * decay * dtk[:, None, :, :]
+        intra = np.einsum("btjh,bjhp->bthp", wts, x[:, sl])
+        inter = np.einsum("bthn,bhnp->bthp", Ch[:, sl], H_in[:, :, k])
+        y[:, sl] = intra + np.exp(cs * A)[..., None] * inter
+    return y
+
+
+# --------------------------------------------------------------------------
+# O6 - state-memory attention
+# --------------------------------------------------------------------------
+def _softmax(s):
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def sma(Q, E, C, dH, S, tokens=None):
+    """SMA readout o_t for every token (or for the listed token indices)
+    [pith-core; pith-carries; pith-maj3; abstract]:
+
+    for token t of chunk k >= 1 and every completed chunk c < k
+        key    K_{t,c} = ΔH[c]·E_t          (in R^N, value axis contracted)
+        value  V_{t,c} = C_tᵀ·ΔH[c]         (in R^P, same C_t as the SSM)
+        score  s_{t,c} = Q_t·K_{t,c} / sqrt(N)
+        o_t = Σ_c softmax_c(s_{t,c})·V_{t,c};  o_t = 0 for chunk 0.
+    Returns o [B,L,H,P] (rows not listed in ``tokens`` stay zero)."""
+    E, dH = _f64(E), _f64(dH)
+    Bsz, L, H, P = E.shape
+    Qh, Ch = _per_head(Q, H), _per_head(C, H)
+    N = Qh.shape[-1]
+    o = np.zeros((Bsz, L, H, P))
+    t_all = np.arange(L) if tokens is None else np.asarray(tokens)
+    for b in range(Bsz):
+        for h in range(H):
+            for k in range(1, L // S):
+                ts = t_all[(t_all >= k * S) & (t_all < (k + 1) * S)]
+                if ts.size == 0:
+                    continue
+                mem = dH[b, h, :k]                                  # [k,N,P]
+                keys = np.einsum("cnp,tp->tcn", mem, E[b, ts, h])
+                scores = np.einsum("tn,tcn->tc", Qh[b, ts, h], keys) / math.sqrt(N)
+                vals = np.einsum("tn,cnp->tcp", Ch[b, ts, h], mem)
+                o[b, ts, h] = np.einsum("tc,tcp->tp", _softmax(scores), vals)
+    return o
+
+
+def sma_bruteforce(Q, E, C, dH, S):
+    """The same readout as :func:`sma`, one token and one chunk at a time with
+    scalar loops (tiny inputs only)."""
+    E, dH = _f64(E), _f64(dH)
+    Bsz, L, H, P = E.shape
+    Qh, Ch = _per_head(Q, H), _per_head(C, H)
+    N = Qh.shape[-1]
+    o = np.zeros((Bsz, L, H, P))
+    for b in range(Bsz):
+        for h in range(H):
+            for t in range(L):
+                k = t // S
+                if k == 0:
+                    continue
+                scores, vals = [], []
+                for c in range(k):
+                    s = 0.0
+                    for n in range(N):
+                        key_n = 0.0
+                        for p in range(P):
+                            key_n += dH[b, h, c, n, p] * E[b, t, h, p]
+                        s += Qh[b, t, h, n] * key_n
+                    scores.append(s / math.sqrt(N))
+                    v = [sum(Ch[b, t, h, n] * dH[b, h, c, n, p] for n in range(N))
+                         for p in range(P)]
+                    vals.append(v)
+                mx = max(scores)
+                wts = [math.exp(s - mx) for s in scores]
+                tot = sum(wts)
+                for p in range(P):
+                    o[b, t, h, p] = sum(w * v[p] for w, v in zip(wts, vals)) / tot
+    return o
+
+
+# --------------------------------------------------------------------------
+# O7 - gated residual
+# --------------------------------------------------------------------------
+def gated_output(y_ssd, o, g):
+    """y = y_ssd + g·o  [pith-core: readout added through a zero-initialised
+    scalar gate; abstract: gated residual]."""
+    return _f64(y_ssd) + float(g) * _f64(o)
+
+
+def prefill(x, dt, A, Bm, C, Q, E, g, S, h0=None):
+    """The whole prefill path O3 -> O4 -> O5 -> O6 -> O7.
+    Returns a dict with dH, H_in, y_ssd, o, y, h_final."""
+    dH = chunk_states(x, dt, A, Bm, S)
+    H_in = state_pass(dH, dt, A, S, h0)
+    y_ssd = chunk_output(x, dt, A, Bm, C, H_in, S)
+    o = sma(Q, E, C, dH, S)
+    return {"dH": dH, "H_in": H_in, "y_ssd": y_ssd, "o": o,
+            "y": gated_output(y_ssd, o, g), "h_final": H_in[:, :, -1]}
+
+
+# --------------------------------------------------------------------------
+# O8 - single-token decode over the chunk-memory cache
+# --------------------------------------------------------------------------
+def round_bf16(a):
+    """Round fp64 values to the nearest bfloat16 (ties to even), returned as
+    fp64.  Used where the cache is kept in bfloat16."""
+    import torch  # library conversion primitive, CPU only
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)).to(
+        torch.bfloat16).to(torch.float64).numpy()
+
+
+def decode_step(state, x, dt, A, Bm, C, Q, E, g, S, cache_bf16=True):
+    """One new token per sequence [abstract: the length-dependent cache is
+    the set of chunk memories; pith-eq14].
+
+    state: dict with cache [B,H,Mmax,N,P], h [B,H,N,P], dH_cur [B,H,N,P],
+    n_chunks [B] and pos [B] (pos = index of the new token in its chunk).
+    Token inputs: x [B,H,P], dt [B,H], A [H], Bm/C/Q [B,G,N], E [B,H,P].
+
+    1. a = exp(dt·A); h <- a·h + dt·B xᵀ; ΔH_cur <- a·ΔH_cur + dt·B xᵀ;
+       y_ssd = Cᵀ h.
+    2. o = SMA over cache[0 .. n_chunks-1] (same formulas as :func:`sma`).
+    3. y = y_ssd + g·o.
+    4. If the token closes its chunk (pos = S-1): cache[n_chunks] <- ΔH_cur
+       (rounded to bfloat16 when the cache is bfloat16), ΔH_cur <- 0,
+       n_chunks += 1, pos <- 0; otherwise pos += 1.
+    Returns (y [B,H,P], new_state)."""
+    x, dt, A, E = _f64(x), _f64(dt), _f64(A), _f64(E)
+    Bsz, H, P = x.shape
+    gmap = group_of_head(H, Bm.shape[1])
+    Bh, Ch, Qh = _f64(Bm)[:, gmap], _f64(C)[:, gmap], _f64(Q)[:, gmap]
+    N = Bh.shape[-1]
+    cache = _f64(state["cache"]).copy()
+    h = _f64(state["h"]).copy()
+    dHc = _f64(state["dH_cur"]).copy()
+    n_chunks = np.asarray(state["n_chunks"]).astype(np.int64).copy()
+    pos = np.asarray(state["pos"]).astype(np.int64).copy()
+
+    a = np.exp(dt * A[None, :])                                     # [B,H]
+    inp = dt[:, :, None, None] * Bh[:, :, :, None] * x[:, :, None, :]
+    h = a[:, :, None, None] * h + inp
+    dHc = a[:, :, None, None] * dHc + inp
+    y_ssd = np.einsum("bhn,bhnp->bhp", Ch, h)
+
+    o = np.zeros((Bsz, H, P))
+    for b in range(Bsz):
+        k = int(n_chunks[b])
+        if k == 0:
+            continue
+        for hh in range(H):
+            mem = cache[b, hh, :k]                                  # [k,N,P]
+            keys = np.einsum("cnp,p->cn", mem, E[b, hh])
+            scores = keys @ Qh[b, hh] / math.sqrt(N)
+            vals = np.einsum("n,cnp->cp", Ch[b, hh], mem)
+            o[b, hh] = _softmax(scores) @ vals
+    y = y_ssd + float(g) * o
+
+    for b in range(Bsz):
+        if pos[b] == S - 1:
+            k = int(n_chunks[b])
+            cache[b, :, k] = round_bf16(dHc[b]) if cache_bf16 else dHc[b]
+            dHc[b] = 0.0
+            n_chunks[b] = k + 1
+            pos[b] = 0
+        else:
+            pos[b] += 1
+    new_state = {"cache": cache, "h": h, "dH_cur": dHc,
+                 "n_chunks": n_chunks, "pos": pos}
+    return y, new_state
+
+
+# --------------------------------------------------------------------------
+# O9 - cache accounting
+# --------------------------------------------------------------------------
+def cache_elements(L, S, N, P):
+    """Per head: DART keeps one N×P memory per completed chunk, a token-level
+    attention layer keeps a key and a value of size P per token
+    [pith-eq14].  Returns (dart_elements, attention_elements)."""
+    return (L // S) * N * P, 2 * L * P
+
+
+def cache_ratio(L, S, N, P):
+    """DART cache / attention cache, per head [pith-eq14]."""
+    dart, attn = cache_elements(L, S, N, P)
+    return dart / attn

@@ -1,0 +1,363 @@
+"""Pins for the fp64 oracle: checks against facts the pages and the
+mathematics fix, independent of the oracle's own formulas.
+
+Each ``pin_*`` takes the oracle module (so that the mutation test can run the
+same pins against a deliberately broken copy) and raises AssertionError when
+the oracle disagrees.  Inputs are small and seeded; every pin finishes in well
+under a second.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import scipy.signal
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _inputs(seed, B=2, L=24, H=4, G=2, N=3, P=5, dt_const=None, A_zero=False):
+    rng = np.random.default_rng(seed)
+    A = np.zeros(H) if A_zero else -np.exp(rng.uniform(0.0, math.log(16.0), H))
+    if dt_const is None:
+        dt = np.exp(rng.uniform(math.log(1e-2), math.log(3e-1), (B, L, H)))
+    else:
+        dt = np.full((B, L, H), float(dt_const))
+    x = rng.standard_normal((B, L, H, P))
+    Bm = rng.standard_normal((B, L, G, N))
+    C = rng.standard_normal((B, L, G, N))
+    Q = rng.standard_normal((B, L, G, N))
+    E = rng.standard_normal((B, L, H, P))
+    return dict(A=A, dt=dt, x=x, Bm=Bm, C=C, Q=Q, E=E)
+
+
+def _heads(T, H):
+    """Grouped [B, L, G, N] -> per head, heads grouped contiguously."""
+    G = T.shape[2]
+    return np.stack([T[:, :, h // (H // G)] for h in range(H)], axis=2)
+
+
+def _close(a, b, tol=1e-10, what=""):
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    scale = max(1.0, float(np.max(np.abs(b))) if b.size else 1.0)
+    assert err <= tol * scale, f"{what}: max err {err:.3e} (scale {scale:.3e})"
+
+
+# --------------------------------------------------------------- recurrence
+def pin_recurrence_linear_attention(orc):
+    """With A = 0 nothing decays and the SSM is causal linear attention:
+    y_t = Σ_{j<=t} (C_t·B_j)·dt_j·x_j  (SSD duality, Pith review axiom
+    ledger, paper Eq. 4)."""
+    d = _inputs(1, A_zero=True)
+    y, _, _ = orc.recurrence(d["x"], d["dt"], d["A"], d["Bm"], d["C"])
+    Bh, Ch = _heads(d["Bm"], 4), _heads(d["C"], 4)
+    B, L, H, P = d["x"].shape
+    ref = np.zeros_like(y)
+    for b in range(B):
+        for h in range(H):
+            for t in range(L):
+                for j in range(t + 1):
+                    ref[b, t, h] += (Ch[b, t, h] @ Bh[b, j, h]) * d["dt"][b, j, h] * d["x"][b, j, h]
+    _close(y, ref, what="linear-attention closed form")
+
+
+def pin_recurrence_lfilter(orc):
+    """With constant dt the decay a = exp(dt·A) is constant, so every state
+    entry is a first-order IIR filter h_t = a·h_{t-1} + u_t; scipy's lfilter
+    evaluates it independently."""
+    dtc = 0.07
+    d = _inputs(2, dt_const=dtc)
+    _, hfin, states = orc.recurrence(d["x"], d["dt"], d["A"], d["Bm"], d["C"],
+                                     keep_states=True)
+    B, L, H, P = d["x"].shape
+    Bh = _heads(d["Bm"], H)
+    N = Bh.shape[-1]
+    for b in range(B):
+        for h in range(H):
+            a = math.exp(dtc * d["A"][h])
+            for n in range(N):
+                for p in range(P):
+                    u = dtc * Bh[b, :, h, n] * d["x"][b, :, h, p]
+                    ref = scipy.signal.lfilter([1.0], [1.0, -a], u)
+                    _close(states[b, :, h, n, p], ref, what=f"lfilter b{b} h{h} n{n} p{p}")
+    _close(hfin, states[:, -1], what="final state")
+
+
+def pin_single_token(orc):
+    """One token from a zero state: y_0 = dt_0·(C_0·B_0)·x_0."""
+    d = _inputs(3, L=1)
+    y, _, _ = orc.recurrence(d["x"], d["dt"], d["A"], d["Bm"], d["C"])
+    Bh, Ch = _heads(d["Bm"], 4), _heads(d["C"], 4)
+    ref = (d["dt"][:, 0, :, None] * np.einsum("bhn,bhn->bh", Ch[:, 0], Bh[:, 0])[..., None]
+           * d["x"][:, 0])
+    _close(y[:, 0], ref, what="single token")
+
+
+# ------------------------------------------------------------ chunked scan
+def pin_state_pass_matches_recurrence(orc):
+    """The chunk-boundary states of the chunked scan equal the sequential
+    recurrence's state at every chunk end, from a non-zero h0 too (the
+    chunked scan is exact; Pith review axiom ledger)."""
+    for S in (1, 4, 6):
+        d = _inputs(4, L=24)
+        rng = np.random.default_rng(40)
+        h0 = rng.standard_normal((2, 4, 3, 5))
+        _, hfin, states = orc.recurrence(d["x"], d["dt"], d["A"], d["Bm"], d["C"],
+                                         h0=h0, keep_states=True)
+        dH = orc.chunk_states(d["x"], d["dt"], d["A"], d["Bm"], S)
+        H_in = orc.state_pass(dH, d["dt"], d["A"], S, h0)
+        M = 24 // S
+        _close(H_in[:, :, 0], h0, what="H_in[0]")
+        for c in range(M):
+            _close(H_in[:, :, c + 1], states[:, (c + 1) * S - 1], what=f"S={S} chunk {c}")
+        _close(H_in[:, :, M], hfin, what="h_final")
+
+
+def pin_chunk_states_unit_chunk(orc):
+    """With S = 1 each chunk holds one token and nothing decays inside it:
+    ΔH[c] = dt_c·B_c x_cᵀ."""
+    d = _inputs(5, L=7)
+    dH = orc.chunk_states(d["x"], d["dt"], d["A"], d["Bm"], 1)
+    Bh = _heads(d["Bm"], 4)
+    ref = np.einsum("blh,blhn,blhp->bhlnp", d["dt"], Bh, d["x"])
+    _close(dH, ref, what="S=1 chunk states")
+
+
+def pin_chunk_states_zero_state_start(orc):
+    """ΔH[c] is the state the recurrence reaches at the end of chunk c when
+    started from zero at the start of chunk c (definition of a chunk's
+    contribution to the chunk-boundary state)."""
+    S = 5
+    d = _inputs(6, L=15)
+    dH = orc.chunk_states(d["x"], d["dt"], d["A"], d["Bm"], S)
+    for c in range(3):
+        sl = slice(c * S, (c + 1) * S)
+        _, hend, _ = orc.recurrence(d["x"][:, sl], d["dt"][:, sl], d["A"],
+                                    d["Bm"][:, sl], d["C"][:, sl])
+        _close(dH[:, :, c], hend, what=f"chunk {c}")
+
+
+def pin_chunk_output_matches_recurrence(orc):
+    """The quadratic (intra + inter chunk) output equals the recurrence at
+    every token (SSD duality)."""
+    for S in (1, 4, 8):
+        d = _inputs(7, L=24)
+        h0 = np.random.default_rng(70).standard_normal((2, 4, 3, 5))
+        y_rec, _, _ = orc.recurrence(d["x"], d["dt"], d["A"], d["Bm"], d["C"], h0=h0)
+        dH = orc.chunk_states(d["x"], d["dt"], d["A"], d["Bm"], S)
+        H_in = orc.state_pass(dH, d["dt"], d["A"], S, h0)
+        y = orc.chunk_output(d["x"], d["dt"], d["A"], d["Bm"], d["C"], H_in, S)
+        _close(y, y_rec, what=f"chunked output S={S}")
+
+
+# --------------------------------------------------------------------- SMA
+def _mem(seed, B, H, M, N, P):
+    return np.random.default_rng(seed).standard_normal((B, H, M, N, P))
+
+
+def pin_sma_first_chunk_zero_and_single_memory(orc):
+    """Tokens of chunk 0 see no completed chunk (readout zero); tokens of
+    chunk 1 see exactly one memory, so the softmax weight is 1 and the
+    readout is C_tᵀ ΔH[0] whatever the query and key."""
+    S, M = 4, 3
+    d = _inputs(8, L=S * M)
+    dH = _mem(80, 2, 4, M, 3, 5)
+    o = orc.sma(d["Q"], d["E"], d["C"], dH, S)
+    _close(o[:, :S], np.zeros_like(o[:, :S]), what="chunk 0")
+    Ch = _heads(d["C"], 4)
+    ref = np.einsum("bthn,bhnp->bthp", Ch[:, S:2 * S], dH[:, :, 0])
+    _close(o[:, S:2 * S], ref, what="single memory")
+
+
+def pin_sma_uniform_when_query_zero(orc):
+    """Q = 0 makes every score zero: uniform weights, readout
+    C_tᵀ·mean_{c<k} ΔH[c]."""
+    S, M = 3, 4
+    d = _inputs(9, L=S * M)
+    dH = _mem(90, 2, 4, M, 3, 5)
+    o = orc.sma(np.zeros_like(d["Q"]), d["E"], d["C"], dH, S)
+    Ch = _heads(d["C"], 4)
+    for k in range(1, M):
+        mean = dH[:, :, :k].mean(axis=2)
+        ref = np.einsum("bthn,bhnp->bthp", Ch[:, k * S:(k + 1) * S], mean)
+        _close(o[:, k * S:(k + 1) * S], ref, what=f"uniform chunk {k}")
+
+
+def pin_sma_planted_query(orc):
+    """A query aligned with the longest decoded key of a token makes the
+    softmax one-hot: the readout becomes C_tᵀ ΔH[c*].  The key of memory c for
+    token t is ΔH[c]·E_t (value axis contracted); with Q_t = λ·sqrt(N)·key*
+    the score gap to every other memory is λ·(|key*|² - key_c·key*) > 0
+    (Cauchy-Schwarz), and λ is set so that the gap is 40."""
+    S, M, N, P = 2, 5, 3, 4
+    B, H = 1, 2
+    rng = np.random.default_rng(11)
+    E = rng.standard_normal((B, S * M, H, P))
+    C = rng.standard_normal((B, S * M, H, N))
+    dH = rng.standard_normal((B, H, M, N, P))
+    Q = np.zeros((B, S * M, H, N))
+    target = {}
+    for t in range(S, S * M):
+        k = t // S
+        for h in range(H):
+            keys = np.array([dH[0, h, c] @ E[0, t, h] for c in range(k)])   # [k, N]
+            cstar = int(np.argmax(np.linalg.norm(keys, axis=1)))
+            kstar = keys[cstar]
+            others = [keys[c] @ kstar for c in range(k) if c != cstar]
+            gap = kstar @ kstar - (max(others) if others else 0.0)
+            assert gap > 0
+            Q[0, t, h] = (40.0 / gap) * math.sqrt(N) * kstar
+            target[(t, h)] = cstar
+    o = orc.sma(Q, E, C, dH, S)
+    for t in range(S, S * M):
+        for h in range(H):
+            ref = C[0, t, h] @ dH[0, h, target[(t, h)]]
+            _close(o[0, t, h], ref, tol=1e-8, what=f"planted t{t} h{h}")
+
+
+def pin_sma_memory_order_invariant(orc):
+    """Softmax attention is a set function of the (key, value) pairs: any
+    permutation of the memories a token sees leaves its readout unchanged."""
+    S, M = 3, 6
+    d = _inputs(12, L=S * M)
+    dH = _mem(120, 2, 4, M, 3, 5)
+    perm = np.array([3, 0, 4, 1, 2, 5])  # last chunk stays (not visible to itself)
+    o = orc.sma(d["Q"], d["E"], d["C"], dH, S)
+    o2 = orc.sma(d["Q"], d["E"], d["C"], dH[:, :, perm], S)
+    _close(o2[:, (M - 1) * S:], o[:, (M - 1) * S:], what="permuted memories")
+
+
+def pin_sma_against_library_attention(orc):
+    """When E_t is the same vector e for every token, keys K_c = ΔH[c]·e no
+    longer depend on t and SMA is ordinary masked softmax attention with
+    query Q_t, key K_c and value vec(ΔH[c]), followed by the contraction
+    with C_t.  torch's scaled_dot_product_attention (scale 1/sqrt(N), the
+    query width) computes the attention part independently."""
+    S, M, N, P = 4, 5, 6, 3
+    B, H, G = 2, 2, 1
+    rng = np.random.default_rng(13)
+    e = rng.standard_normal(P)
+    E = np.broadcast_to(e, (B, S * M, H, P)).copy()
+    Q = 3.0 * rng.standard_normal((B, S * M, G, N))
+    C = rng.standard_normal((B, S * M, G, N))
+    dH = rng.standard_normal((B, H, M, N, P))
+    o = orc.sma(Q, E, C, dH, S)
+    L = S * M
+    tok_chunk = np.arange(L) // S
+    mask = torch.from_numpy(np.arange(M)[None, :] < tok_chunk[:, None])      # [L, M]
+    for b in range(B):
+        for h in range(H):
+            q = torch.from_numpy(Q[b, :, 0])                                    # [L, N]
+            kk = torch.from_numpy(np.einsum("cnp,p->cn", dH[b, h], e))          # [M, N]
+            v = torch.from_numpy(dH[b, h].reshape(M, N * P))                    # [M, N*P]
+            u = torch.nn.functional.scaled_dot_product_attention(
+                q[None], kk[None], v[None], attn_mask=mask[None]).numpy()[0]
+            ref = np.einsum("tn,tnp->tp", C[b, :, 0], u.reshape(L, N, P))
+            _close(o[b, S:, h], ref[S:], what=f"sdpa b{b} h{h}")
+
+
+def pin_sma_bruteforce(orc):
+    """Scalar per-token, per-chunk loops agree with the vectorised readout."""
+    S, M = 2, 4
+    d = _inputs(14, B=1, L=S * M, H=2, G=1, N=3, P=2)
+    d["Q"] *= 4.0
+    dH = _mem(140, 1, 2, M, 3, 2)
+    _close(orc.sma(d["Q"], d["E"], d["C"], dH, S),
+           orc.sma_bruteforce(d["Q"], d["E"], d["C"], dH, S), what="brute force")
+
+
+# -------------------------------------------------------------------- gate
+def pin_gate(orc):
+    """g = 0 removes the SMA branch (y = y_ssd, the kernel-level form of the
+    paper's 'SMA removed' ablation); y is affine in g."""
+    S = 4
+    d = _inputs(15, L=16)
+    r0 = orc.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], 0.0, S)
+    r1 = orc.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], 1.0, S)
+    r7 = orc.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], 0.7, S)
+    _close(r0["y"], r0["y_ssd"], what="g=0")
+    _close(r7["y"], r0["y"] + 0.7 * (r1["y"] - r0["y"]), what="affine in g")
+    assert np.max(np.abs(r1["y"] - r0["y"])) > 1e-3, "SMA branch has no effect"
+
+
+# ------------------------------------------------------------ worked example
+def pin_worked_scalar_example(orc):
+    """Hand-derived scalar case (N = P = 1, S = 1, H = 1): every quantity is
+    a short closed form written with math.exp.
+
+    x = (1, 2, -1), dt = (0.5, 0.25, 0.2), A = -2, B = (1, 2, 1),
+    C = (1, 1, 2), Q = (1, 1, 1), E = (1, 1, 3), h0 = 0.5, g = 0.5.
+    Memories: ΔH = (0.5, 1.0, -0.2).
+    States:   h_0 = e^{-1}·0.5 + 0.5,  h_1 = e^{-0.5}·h_0 + 1.0,
+              h_2 = e^{-0.4}·h_1 - 0.2;  y_ssd = (h_0, h_1, 2·h_2).
+    SMA:      token 0 sees nothing; token 1 sees ΔH[0] only: o_1 = 1·0.5;
+              token 2 sees ΔH[0], ΔH[1] with scores 1·0.5·3 = 1.5 and
+              1·1.0·3 = 3 and values 2·0.5 = 1 and 2·1.0 = 2.
+    """
+    x = np.array([1.0, 2.0, -1.0]).reshape(1, 3, 1, 1)
+    dt = np.array([0.5, 0.25, 0.2]).reshape(1, 3, 1)
+    A = np.array([-2.0])
+    Bm = np.array([1.0, 2.0, 1.0]).reshape(1, 3, 1, 1)
+    C = np.array([1.0, 1.0, 2.0]).reshape(1, 3, 1, 1)
+    Q = np.ones((1, 3, 1, 1))
+    E = np.array([1.0, 1.0, 3.0]).reshape(1, 3, 1, 1)
+    h0 = np.full((1, 1, 1, 1), 0.5)
+    r = orc.prefill(x, dt, A, Bm, C, Q, E, 0.5, 1, h0=h0)
+    e = math.exp
+    h_0 = e(-1.0) * 0.5 + 0.5
+    h_1 = e(-0.5) * h_0 + 1.0
+    h_2 = e(-0.4) * h_1 - 0.2
+    y_ssd = [h_0, h_1, 2.0 * h_2]
+    a0, a1 = e(1.5) / (e(1.5) + e(3.0)), e(3.0) / (e(1.5) + e(3.0))
+    o = [0.0, 0.5, a0 * 1.0 + a1 * 2.0]
+    _close(r["dH"].ravel(), [0.5, 1.0, -0.2], what="memories")
+    _close(r["y_ssd"].ravel(), y_ssd, what="y_ssd")
+    _close(r["o"].ravel(), o, what="sma")
+    _close(r["y"].ravel(), [ys + 0.5 * oo for ys, oo in zip(y_ssd, o)], what="y")
+    _close(r["h_final"].ravel(), [h_2], what="final state")
+
+
+# ------------------------------------------------------------------ decode
+def pin_decode_equals_prefill(orc):
+    """Decoding token by token from the state after k completed chunks
+    reproduces the prefill outputs, memories and final state (the decode
+    cache is exactly the prefill's chunk memories)."""
+    S, M, k0 = 3, 4, 1
+    B, H, G, N, P = 2, 4, 2, 3, 5
+    d = _inputs(16, B=B, L=S * M, H=H, G=G, N=N, P=P)
+    g = 0.8
+    r = orc.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], g, S)
+    state = {"cache": np.zeros((B, H, M, N, P)), "h": r["H_in"][:, :, k0].copy(),
+             "dH_cur": np.zeros((B, H, N, P)), "n_chunks": np.full(B, k0),
+             "pos": np.zeros(B, dtype=np.int64)}
+    state["cache"][:, :, :k0] = r["dH"][:, :, :k0]
+    for t in range(k0 * S, S * M):
+        y, state = orc.decode_step(state, d["x"][:, t], d["dt"][:, t], d["A"],
+                                   d["Bm"][:, t], d["C"][:, t], d["Q"][:, t],
+                                   d["E"][:, t], g, S, cache_bf16=False)
+        _close(y, r["y"][:, t], what=f"decode token {t}")
+    _close(state["cache"], r["dH"], what="appended memories")
+    _close(state["h"], r["h_final"], what="final state")
+    assert list(state["n_chunks"]) == [M] * B and list(state["pos"]) == [0] * B
+
+
+# ------------------------------------------------------------ cache ratio
+def pin_cache_ratio_golden(orc):
+    """The printed figure: at S=256, N=128 the DART cache is 25% of the
+    matched attention cache (75% saving), for any L multiple of S and any P."""
+    with open(os.path.join(GOLDEN, "cache_ratio.json")) as f:
+        gold = json.load(f)
+    for L in (256, 4096, 32768):
+        for P in (64, 128):
+            r = orc.cache_ratio(L, gold["S"], gold["N"], P)
+            assert abs(r - gold["ratio"]) < 1e-15, r
+            assert abs((1 - r) - gold["saving"]) < 1e-15
+    dart, attn = orc.cache_elements(128 * 256, 256, 128, 64)   # 32K context
+    assert (dart, attn) == (1048576, 4194304)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,87 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check
+that at least one pin catches each: the pins are strong enough to trust."""
+import importlib.util
+import os
+import types
+
+import pytest
+
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "dart_oracle.py")
+
+# (name, original text, mutated text): each text occurs in the oracle source
+MUTATIONS = [
+    ("decay dropped in recurrence",
+     "h = a[:, :, None, None] * h + inp\n        y[:, t]",
+     "h = h + inp\n        y[:, t]"),
+    ("input term without dt",
+     "inp = dt[:, t, :, None, None] * Bh[:, t, :, :, None] * x[:, t, :, None, :]",
+     "inp = Bh[:, t, :, :, None] * x[:, t, :, None, :]"),
+    ("chunk decay includes own token",
+     "dtc[:, i + 1:, :].sum(axis=1)", "dtc[:, i:, :].sum(axis=1)"),
+    ("chunk weight missing dt",
+     "w = np.exp(tail * A[None, None, :]) * dtc", "w = np.exp(tail * A[None, None, :])"),
+    ("state pass sign",
+     "* H_in[:, :, c] + dH[:, :, c]", "* H_in[:, :, c] - dH[:, :, c]"),
+    ("state pass without decay",
+     "H_in[:, :, c + 1] = decay[:, :, None, None] * H_in[:, :, c]",
+     "H_in[:, :, c + 1] = H_in[:, :, c]"),
+    ("inter-chunk decay sign",
+     "np.exp(cs * A)[..., None] * inter", "np.exp(-cs * A)[..., None] * inter"),
+    ("intra-chunk anti-causal",
+     "causal = np.tril(np.ones((S, S), dtype=bool))",
+     "causal = np.triu(np.ones((S, S), dtype=bool))"),
+    ("intra-chunk weight missing dt",
+     "wts = cb * decay * dtk[:, None, :, :]", "wts = cb * decay"),
+    ("score scale sqrt(P)",
+     'scores = np.einsum("tn,tcn->tc", Qh[b, ts, h], keys) / math.sqrt(N)',
+     'scores = np.einsum("tn,tcn->tc", Qh[b, ts, h], keys) / math.sqrt(P)'),
+    ("decode score scale sqrt(P)",
+     "scores = keys @ Qh[b, hh] / math.sqrt(N)", "scores = keys @ Qh[b, hh] / math.sqrt(P)"),
+    ("decode value read with the query",
+     'vals = np.einsum("n,cnp->cp", Ch[b, hh], mem)', 'vals = np.einsum("n,cnp->cp", Qh[b, hh], mem)'),
+    ("query replaced by C",
+     'np.einsum("tn,tcn->tc", Qh[b, ts, h], keys)',
+     'np.einsum("tn,tcn->tc", Ch[b, ts, h], keys)'),
+    ("own chunk visible",
+     "mem = dH[b, h, :k]                                  # [k,N,P]",
+     "mem = dH[b, h, :k + 1]                              # [k,N,P]"),
+    ("value decoded with E instead of C",
+     'vals = np.einsum("tn,cnp->tcp", Ch[b, ts, h], mem)',
+     'vals = np.einsum("tn,cnp->tcp", Qh[b, ts, h], mem)'),
+    ("softmax sign",
+     "e = np.exp(s - m)", "e = np.exp(m - s)"),
+    ("convex gate",
+     "return _f64(y_ssd) + float(g) * _f64(o)",
+     "return (1.0 - float(g)) * _f64(y_ssd) + float(g) * _f64(o)"),
+    ("groups interleaved",
+     "return np.arange(H) // (H // G)", "return np.arange(H) % G"),
+    ("decode closes chunk one token late",
+     "if pos[b] == S - 1:", "if pos[b] == S:"),
+    ("decode skips the SSM decay of the chunk memory",
+     "dHc = a[:, :, None, None] * dHc + inp", "dHc = dHc + inp"),
+    ("cache ratio counts keys only",
+     "return (L // S) * N * P, 2 * L * P", "return (L // S) * N * P, L * P"),
+]
+
+
+def _load_mutant(old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("dart_oracle_mutant")
+    exec(compile(src.replace(old, new), "dart_oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_some_pin_catches(name, old, new):
+    mutant = _load_mutant(old, new)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mutant)
+        except Exception as exc:  # noqa: BLE001 - any failure counts as caught
+            caught.append((pin.__name__, type(exc).__name__))
+    assert caught, f"no pin catches mutation '{name}'"

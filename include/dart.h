@@ -1,0 +1,180 @@
+/*
+ * dart.h - C ABI of the DART hot path on AMD Instinct MI355X (gfx950).
+ *
+ * DART ("Decoded Attention over Recurrent sTates") keeps the per-chunk state
+ * contributions of the Mamba-2 chunked scan as chunk memories dH[c] (N x P),
+ * decodes a token-conditioned key dH[c]·E_t and value C_tᵀ·dH[c] from each,
+ * runs softmax attention (state-memory attention, SMA) over the completed
+ * chunks with query Q_t, and adds the readout to the Mamba-2 output through
+ * a scalar gate.  Sources: DART abstract (aipentium and mlsanity pages); Pith
+ * review of DART, "Core claim", "What carries the argument", referee major
+ * comment 3 (paper §3 Eq. 8) and minor comment 1 (paper §4 Eq. 14).
+ *
+ * Prefill is three calls on one stream, in this order:
+ *   dart_chunk_state -> dart_state_pass -> dart_sma_fwd
+ * Decode is one call per generated token: dart_sma_decode.
+ *
+ * Conventions for every call
+ * --------------------------
+ * - Every tensor argument is a pointer to DEVICE memory owned by the caller,
+ *   dense row-major in the layout given, 16-byte aligned.  The library never
+ *   allocates, frees or keeps memory, and holds no global state.
+ * - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *   enqueue work and return; results are ready once the stream reaches them.
+ * - Dimensions and pointers are validated on the host before any HIP call; a
+ *   non-OK status means nothing was enqueued.  DART_ERR_HIP reports a launch
+ *   failure; a fault inside a kernel surfaces at the caller's next
+ *   synchronisation.
+ * - Outputs never alias inputs (decode state arguments are in/out).
+ * - Symbols: B batch, L sequence length, H heads, G groups (B, C and Q are
+ *   shared by H/G consecutive heads), N state size (key axis), P head dim
+ *   (value axis), S chunk size, M = L/S chunks, k = floor(t/S) the chunk of
+ *   token t.  "io" is the element type named by dart_dims.io.
+ * - State matrices (dH, H_in, h0, decode cache, h, dH_cur) are N x P
+ *   matrices stored value-axis-major: element (n, p) sits at [p][n], i.e.
+ *   the key axis N is contiguous.
+ *
+ * Supported shapes: io = DART_F32 with (N, P) in {(16,16), (32,32)};
+ * io = DART_BF16 with (N, P) in {(32,32), (64,64), (128,64), (128,128)};
+ * S a multiple of 32 with 32 <= S <= 256; L a multiple of S.  Anything else
+ * returns DART_ERR_UNSUPPORTED (shape) or DART_ERR_BAD_DIMS (inconsistent).
+ */
+#ifndef DART_H
+#define DART_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dart_status {
+  DART_OK = 0,
+  DART_ERR_NULL_PTR = 1,    /* a required pointer is NULL                   */
+  DART_ERR_BAD_DIMS = 2,    /* non-positive dim, L % S != 0, H % G != 0 ... */
+  DART_ERR_UNSUPPORTED = 3, /* (dtype, N, P, S) outside the compiled set    */
+  DART_ERR_DTYPE = 4,       /* io is not a dart_dtype value                 */
+  DART_ERR_WORKSPACE = 5,   /* decode workspace missing or too small        */
+  DART_ERR_HIP = 6,         /* a HIP launch reported an error               */
+  DART_ERR_ALIGN = 7        /* a pointer is not 16-byte aligned             */
+} dart_status;
+
+typedef enum dart_dtype { DART_F32 = 0, DART_BF16 = 1 } dart_dtype;
+
+/* Prefill dimensions. */
+typedef struct dart_dims {
+  int64_t batch, seqlen, nheads, ngroups, dstate /* N */, headdim /* P */, chunk /* S */;
+  int32_t io; /* dart_dtype of x, Bm, C, Q, E, dH and y */
+} dart_dims;
+
+/* Decode dimensions; max_chunks is the cache capacity per (sequence, head). */
+typedef struct dart_decode_dims {
+  int64_t batch, nheads, ngroups, dstate, headdim, chunk, max_chunks;
+  int32_t io; /* dart_dtype of x, Bm, C, Q, E, cache and y */
+} dart_decode_dims;
+
+/*
+ * Chunk state memories (first step of the Mamba-2 chunked scan).
+ * Source: Pith review of DART, "What carries the argument" (dH[c] is the
+ * N x P contribution of chunk c to the chunk-boundary state) and the axiom
+ * ledger (the chunked scan yields these contributions).
+ *
+ *   acum[b,h,c,s] = sum_{j<=s} dt[b,cS+j,h]·A[h]            (inclusive)
+ *   dH[b,h,c]     = sum_{i in c} exp(acum_end - acum_i)·dt_i·B_i x_iᵀ
+ *
+ * in:  x [B,L,H,P] io; dt [B,L,H] f32 (> 0); A [H] f32 (< 0);
+ *      Bm [B,L,G,N] io
+ * out: acum [B,H,M,S] f32; dH [B,H,M,P,N] io (rounded to nearest even);
+ *      dH_f32 [B,H,M,P,N] f32 (the same memories unrounded, for the state
+ *      recurrence).
+ */
+dart_status dart_chunk_state(const dart_dims* dims, const void* x, const float* dt,
+                             const float* A, const void* Bm, float* acum, void* dH,
+                             float* dH_f32, void* stream);
+
+/*
+ * Inter-chunk state passing and the native Mamba-2 output y_ssd.
+ * Source: Pith review of DART, axiom ledger (SSD as structured causal
+ * attention, paper Eq. 4; intra- and inter-chunk terms of the chunked scan)
+ * and "Core claim" (Mamba-2 reads values from its state as C_t·H_t).
+ *
+ *   H_in[0] = h0 (zero when h0 == NULL)
+ *   H_in[c+1] = exp(acum[c, S-1])·H_in[c] + dH_f32[c]       (H_in[M] = final)
+ *   y_ssd[t] = sum_{j in k, j<=t} (C_t·B_j)·exp(acum_t - acum_j)·dt_j·x_j
+ *            + exp(acum_t)·C_tᵀ·H_in[k]
+ *
+ * in:  x, dt, Bm as above; C [B,L,G,N] io; acum, dH_f32 from
+ *      dart_chunk_state; h0 [B,H,P,N] f32 or NULL
+ * out: H_in [B,H,M+1,P,N] f32; y_ssd [B,L,H,P] f32
+ */
+dart_status dart_state_pass(const dart_dims* dims, const void* x, const float* dt,
+                            const void* Bm, const void* C, const float* acum,
+                            const float* dH_f32, const float* h0, float* H_in,
+                            float* y_ssd, void* stream);
+
+/*
+ * State-memory attention over completed chunks plus the gated add.
+ * Source: Pith review of DART, "Core claim" and "What carries the argument"
+ * (key dH[c]·E_t, value C_tᵀ·dH[c], query Q_t, scalar gate), referee major
+ * comment 3 (paper §3 Eq. 8: raw memories, no decay); DART abstract.
+ *
+ *   s[t,c] = Q_tᵀ·dH[c]·E_t / sqrt(N)          for c < k (k = chunk of t)
+ *   o_t    = sum_{c<k} softmax_c(s[t,c])·C_tᵀ·dH[c]   (o_t = 0 when k = 0)
+ *   y_t    = y_ssd_t + gate·o_t
+ *
+ * in:  Q [B,L,G,N] io; E [B,L,H,P] io; C [B,L,G,N] io; dH [B,H,M,P,N] io;
+ *      y_ssd [B,L,H,P] f32
+ * out: y [B,L,H,P] io
+ */
+dart_status dart_sma_fwd(const dart_dims* dims, const void* Q, const void* E,
+                         const void* C, const void* dH, const float* y_ssd, float gate,
+                         void* y, void* stream);
+
+/* Bytes of device workspace dart_sma_decode needs for these dims (a
+ * multiple of 256; 0 if the dims are invalid). */
+size_t dart_sma_decode_workspace(const dart_decode_dims* dims);
+
+/*
+ * One decode step: one new token per sequence over the chunk-memory cache.
+ * Source: DART abstract (the length-dependent inference cache is the set of
+ * chunk memories); Pith review minor comment 1 (paper §4 Eq. 14).
+ *
+ * For each (b, h), with k = n_chunks[b] and the token at position pos[b] of
+ * chunk k:
+ *   1. a = exp(dt·A); h <- a·h + dt·B xᵀ; dH_cur <- a·dH_cur + dt·B xᵀ;
+ *      y_ssd = Cᵀ·h
+ *   2. o = SMA over cache[0..k-1] with the dart_sma_fwd formulas
+ *   3. y = y_ssd + gate·o
+ *   4. if pos[b] == S-1: cache[k] <- io(dH_cur), dH_cur <- 0,
+ *      n_chunks[b] += 1, pos[b] <- 0; else pos[b] += 1.
+ *
+ * in:     x [B,H,P] io; dt [B,H] f32; A [H] f32; Bm, C, Q [B,G,N] io;
+ *         E [B,H,P] io
+ * in/out: cache [B,H,max_chunks,P,N] io; h, dH_cur [B,H,P,N] f32;
+ *         n_chunks [B] int32; pos [B] int32 (all device memory)
+ * out:    y [B,H,P] io
+ * workspace: device memory of at least dart_sma_decode_workspace(dims)
+ *         bytes; its first int32 is set to 1 (never cleared by the library)
+ *         when a chunk could not be appended because n_chunks[b] had reached
+ *         max_chunks (the cache is never written out of bounds; n_chunks
+ *         then stays at max_chunks).
+ */
+dart_status dart_sma_decode(const dart_decode_dims* dims, const void* x, const float* dt,
+                            const float* A, const void* Bm, const void* C, const void* Q,
+                            const void* E, float gate, void* cache, float* h,
+                            float* dH_cur, int32_t* n_chunks, int32_t* pos, void* y,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host-only checks (no HIP call; usable without a GPU). */
+dart_status dart_validate_dims(const dart_dims* dims);
+dart_status dart_validate_decode_dims(const dart_decode_dims* dims);
+
+/* Static, human-readable name of a status. */
+const char* dart_status_str(dart_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DART_H */

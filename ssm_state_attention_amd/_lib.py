@@ -1,0 +1,74 @@
+"""ctypes view of libdart.so (the C ABI declared in include/dart.h)."""
+
+import ctypes
+import os
+
+from ._build import LIB_PATH
+
+DART_F32, DART_BF16 = 0, 1
+
+STATUS_NAMES = {
+    0: "DART_OK", 1: "DART_ERR_NULL_PTR", 2: "DART_ERR_BAD_DIMS", 3: "DART_ERR_UNSUPPORTED",
+    4: "DART_ERR_DTYPE", 5: "DART_ERR_WORKSPACE", 6: "DART_ERR_HIP", 7: "DART_ERR_ALIGN",
+}
+
+
+class DartDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("io", ctypes.c_int32)]
+
+
+class DartDecodeDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("ngroups", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("chunk", ctypes.c_int64),
+                ("max_chunks", ctypes.c_int64), ("io", ctypes.c_int32)]
+
+
+class DartError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}")
+
+
+_VP = ctypes.c_void_p
+_F = ctypes.c_float
+_SIG = {
+    "dart_chunk_state": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+    "dart_state_pass": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                        _VP],
+    "dart_sma_fwd": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _F, _VP, _VP],
+    "dart_sma_decode_workspace": [ctypes.POINTER(DartDecodeDims)],
+    "dart_sma_decode": [ctypes.POINTER(DartDecodeDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F,
+                        _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+    "dart_validate_dims": [ctypes.POINTER(DartDims)],
+    "dart_validate_decode_dims": [ctypes.POINTER(DartDecodeDims)],
+    "dart_status_str": [ctypes.c_int],
+}
+_RES = {"dart_sma_decode_workspace": ctypes.c_size_t, "dart_status_str": ctypes.c_char_p}
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: the HIP extension must be built "
+                "(ssm_state_attention_amd._build.build_library())")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIG.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = _RES.get(name, ctypes.c_int)
+        _lib = handle
+    return _lib
+
+
+def check(status, where):
+    if status != 0:
+        raise DartError(status, where)

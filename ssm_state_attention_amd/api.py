@@ -1,0 +1,182 @@
+"""Thin Python binding of the DART C ABI (include/dart.h).
+
+Functions named like the C entry points take torch tensors that already
+live on the GPU, check their dtype, shape, device and contiguity, and pass
+raw pointers plus torch's current HIP stream.  Every step of the hot path
+runs inside libdart's HIP kernels; torch only provides device memory and
+the stream.  ``prefill`` and ``decode_step`` allocate the outputs with torch
+and chain the entry points.
+"""
+
+import torch
+
+from ._lib import DART_BF16, DART_F32, DartDecodeDims, DartDims, check, lib
+
+_IO = {torch.float32: DART_F32, torch.bfloat16: DART_BF16}
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t, name, dtype=None, shape=None, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _io_code(dtype):
+    if dtype not in _IO:
+        raise TypeError(f"element type must be float32 or bfloat16 (got {dtype})")
+    return _IO[dtype]
+
+
+def prefill_dims(x, Bm, chunk):
+    """dart_dims from x [B, L, H, P] and Bm [B, L, G, N]."""
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    return DartDims(B, L, H, G, N, P, int(chunk), _io_code(x.dtype))
+
+
+def dart_chunk_state(x, dt, A, Bm, acum, dH, dH_f32, chunk):
+    """Chunk state memories: acum [B,H,M,S] f32, dH [B,H,M,P,N] io and
+    dH_f32 [B,H,M,P,N] f32 from x, dt, A, Bm."""
+    d = prefill_dims(x, Bm, chunk)
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    M, io, dev = L // chunk, x.dtype, x.device
+    args = [_ptr(x, "x", io, (B, L, H, P), dev), _ptr(dt, "dt", torch.float32, (B, L, H), dev),
+            _ptr(A, "A", torch.float32, (H,), dev), _ptr(Bm, "Bm", io, (B, L, G, N), dev),
+            _ptr(acum, "acum", torch.float32, (B, H, M, chunk), dev),
+            _ptr(dH, "dH", io, (B, H, M, P, N), dev),
+            _ptr(dH_f32, "dH_f32", torch.float32, (B, H, M, P, N), dev)]
+    check(lib().dart_chunk_state(d, *args, _stream()), "dart_chunk_state")
+
+
+def dart_state_pass(x, dt, Bm, C, acum, dH_f32, h0, H_in, y_ssd, chunk):
+    """State passing H_in [B,H,M+1,P,N] f32 and native output y_ssd
+    [B,L,H,P] f32; h0 [B,H,P,N] f32 or None (zero)."""
+    d = prefill_dims(x, Bm, chunk)
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    M, io, dev = L // chunk, x.dtype, x.device
+    args = [_ptr(x, "x", io, (B, L, H, P), dev), _ptr(dt, "dt", torch.float32, (B, L, H), dev),
+            _ptr(Bm, "Bm", io, (B, L, G, N), dev), _ptr(C, "C", io, (B, L, G, N), dev),
+            _ptr(acum, "acum", torch.float32, (B, H, M, chunk), dev),
+            _ptr(dH_f32, "dH_f32", torch.float32, (B, H, M, P, N), dev),
+            _ptr(h0, "h0", torch.float32, (B, H, P, N), dev),
+            _ptr(H_in, "H_in", torch.float32, (B, H, M + 1, P, N), dev),
+            _ptr(y_ssd, "y_ssd", torch.float32, (B, L, H, P), dev)]
+    check(lib().dart_state_pass(d, *args, _stream()), "dart_state_pass")
+
+
+def dart_sma_fwd(Q, E, C, dH, y_ssd, gate, y, chunk):
+    """State-memory attention + gated add: y [B,L,H,P] io."""
+    B, L, H, P = E.shape
+    G, N = Q.shape[2], Q.shape[3]
+    d = DartDims(B, L, H, G, N, P, int(chunk), _io_code(E.dtype))
+    M, io, dev = L // chunk, E.dtype, E.device
+    args = [_ptr(Q, "Q", io, (B, L, G, N), dev), _ptr(E, "E", io, (B, L, H, P), dev),
+            _ptr(C, "C", io, (B, L, G, N), dev), _ptr(dH, "dH", io, (B, H, M, P, N), dev),
+            _ptr(y_ssd, "y_ssd", torch.float32, (B, L, H, P), dev)]
+    yp = _ptr(y, "y", io, (B, L, H, P), dev)
+    check(lib().dart_sma_fwd(d, *args, float(gate), yp, _stream()), "dart_sma_fwd")
+
+
+def decode_dims(batch, nheads, ngroups, dstate, headdim, chunk, max_chunks, dtype):
+    return DartDecodeDims(batch, nheads, ngroups, dstate, headdim, int(chunk), int(max_chunks),
+                          _io_code(dtype))
+
+
+def dart_sma_decode_workspace(dims):
+    """Workspace bytes for dart_sma_decode (0 for invalid dims)."""
+    return int(lib().dart_sma_decode_workspace(dims))
+
+
+def dart_sma_decode(x, dt, A, Bm, C, Q, E, gate, cache, h, dH_cur, n_chunks, pos, y,
+                    workspace, chunk):
+    """One decode step (see include/dart.h).  cache [B,H,max_chunks,P,N] io,
+    h / dH_cur [B,H,P,N] f32, n_chunks / pos [B] int32 are updated in place;
+    y [B,H,P] io is written; workspace is a uint8 device tensor."""
+    B, H, P = x.shape
+    G, N = Bm.shape[1], Bm.shape[2]
+    max_chunks = cache.shape[2]
+    io, dev = x.dtype, x.device
+    d = decode_dims(B, H, G, N, P, chunk, max_chunks, io)
+    args = [_ptr(x, "x", io, (B, H, P), dev), _ptr(dt, "dt", torch.float32, (B, H), dev),
+            _ptr(A, "A", torch.float32, (H,), dev), _ptr(Bm, "Bm", io, (B, G, N), dev),
+            _ptr(C, "C", io, (B, G, N), dev), _ptr(Q, "Q", io, (B, G, N), dev),
+            _ptr(E, "E", io, (B, H, P), dev)]
+    state = [_ptr(cache, "cache", io, (B, H, max_chunks, P, N), dev),
+             _ptr(h, "h", torch.float32, (B, H, P, N), dev),
+             _ptr(dH_cur, "dH_cur", torch.float32, (B, H, P, N), dev),
+             _ptr(n_chunks, "n_chunks", torch.int32, (B,), dev),
+             _ptr(pos, "pos", torch.int32, (B,), dev), _ptr(y, "y", io, (B, H, P), dev)]
+    wsp = _ptr(workspace, "workspace", torch.uint8, None, dev)
+    check(lib().dart_sma_decode(d, *args, float(gate), *state, wsp, workspace.numel(),
+                                _stream()), "dart_sma_decode")
+
+
+# ----------------------------------------------------------------- helpers
+def prefill(x, dt, A, Bm, C, Q, E, gate, chunk, h0=None):
+    """Whole prefill path; returns a dict of device tensors: y, y_ssd, dH
+    ([B,H,M,P,N] io), dH_f32, H_in ([B,H,M+1,P,N] f32; H_in[:, :, -1] is the
+    final state) and acum."""
+    B, L, H, P = x.shape
+    N = Bm.shape[3]
+    M, dev = L // chunk, x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {
+        "acum": torch.empty(B, H, M, chunk, **f32),
+        "dH": torch.empty(B, H, M, P, N, dtype=x.dtype, device=dev),
+        "dH_f32": torch.empty(B, H, M, P, N, **f32),
+        "H_in": torch.empty(B, H, M + 1, P, N, **f32),
+        "y_ssd": torch.empty(B, L, H, P, **f32),
+        "y": torch.empty(B, L, H, P, dtype=x.dtype, device=dev),
+    }
+    dart_chunk_state(x, dt, A, Bm, out["acum"], out["dH"], out["dH_f32"], chunk)
+    dart_state_pass(x, dt, Bm, C, out["acum"], out["dH_f32"], h0, out["H_in"], out["y_ssd"],
+                    chunk)
+    dart_sma_fwd(Q, E, C, out["dH"], out["y_ssd"], gate, out["y"], chunk)
+    return out
+
+
+def new_decode_state(batch, nheads, ngroups, dstate, headdim, chunk, max_chunks, dtype, device):
+    """Zeroed decode state: cache, h, dH_cur, n_chunks, pos and workspace."""
+    dims = decode_dims(batch, nheads, ngroups, dstate, headdim, chunk, max_chunks, dtype)
+    ws = dart_sma_decode_workspace(dims)
+    if ws == 0:
+        raise ValueError("unsupported decode dimensions")
+    f32 = dict(dtype=torch.float32, device=device)
+    return {
+        "chunk": int(chunk),
+        "cache": torch.zeros(batch, nheads, max_chunks, headdim, dstate, dtype=dtype,
+                             device=device),
+        "h": torch.zeros(batch, nheads, headdim, dstate, **f32),
+        "dH_cur": torch.zeros(batch, nheads, headdim, dstate, **f32),
+        "n_chunks": torch.zeros(batch, dtype=torch.int32, device=device),
+        "pos": torch.zeros(batch, dtype=torch.int32, device=device),
+        "workspace": torch.zeros(ws, dtype=torch.uint8, device=device),
+    }
+
+
+def decode_step(state, x, dt, A, Bm, C, Q, E, gate, y=None):
+    """Advance ``state`` (from new_decode_state) by one token per sequence;
+    returns y [B,H,P]."""
+    if y is None:
+        y = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    dart_sma_decode(x, dt, A, Bm, C, Q, E, gate, state["cache"], state["h"], state["dH_cur"],
+                    state["n_chunks"], state["pos"], y, state["workspace"], state["chunk"])
+    return y

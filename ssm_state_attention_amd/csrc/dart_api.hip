@@ -1,0 +1,161 @@
+// extern "C" entry points of libdart: host validation, then dispatch on the
+// element type and (N, P) to the compiled kernel set.
+#include <stdint.h>
+
+#include "dart.h"
+#include "dart_launch.hpp"
+#include "dart_shapes.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+template <typename... Ps>
+dart_status check_ptrs(Ps... ps) {
+  const void* arr[] = {static_cast<const void*>(ps)...};
+  for (const void* p : arr)
+    if (!p) return DART_ERR_NULL_PTR;
+  for (const void* p : arr)
+    if (!aligned16(p)) return DART_ERR_ALIGN;
+  return DART_OK;
+}
+
+dart::PrefillShape prefill_shape(const dart_dims* d) {
+  return {static_cast<int>(d->batch), static_cast<int>(d->seqlen), static_cast<int>(d->nheads),
+          static_cast<int>(d->ngroups), static_cast<int>(d->chunk)};
+}
+
+dart_status hip_status(hipError_t e) { return e == hipSuccess ? DART_OK : DART_ERR_HIP; }
+
+// Calls fn.template run<T, N, P>() for the compiled combination matching
+// (io, N, P); the caller has validated that one exists.
+template <typename Fn>
+dart_status dispatch(int io, int64_t N, int64_t P, Fn&& fn) {
+#define DART_DISPATCH_CASE(T, NN, PP)                                             \
+  if (io == (std::is_same<T, float>::value ? DART_F32 : DART_BF16) && N == NN && \
+      P == PP)                                                                    \
+    return hip_status(fn.template run<T, NN, PP>());
+  DART_FOR_EACH_SHAPE(DART_DISPATCH_CASE)
+#undef DART_DISPATCH_CASE
+  return DART_ERR_UNSUPPORTED;
+}
+
+struct ChunkStateFn {
+  dart::PrefillShape sh;
+  const void *x, *Bm;
+  const float *dt, *A;
+  float* acum;
+  void* dH;
+  float* dHf;
+  hipStream_t st;
+  template <typename T, int N, int P>
+  hipError_t run() {
+    return dart::launch_chunk_state<T, N, P>(sh, static_cast<const T*>(x), dt, A,
+                                             static_cast<const T*>(Bm), acum, static_cast<T*>(dH),
+                                             dHf, st);
+  }
+};
+
+struct StatePassFn {
+  dart::PrefillShape sh;
+  const void *x, *Bm, *C;
+  const float *dt, *acum, *dHf, *h0;
+  float *H_in, *y_ssd;
+  hipStream_t st;
+  template <typename T, int N, int P>
+  hipError_t run() {
+    return dart::launch_state_pass<T, N, P>(sh, static_cast<const T*>(x), dt,
+                                            static_cast<const T*>(Bm), static_cast<const T*>(C),
+                                            acum, dHf, h0, H_in, y_ssd, st);
+  }
+};
+
+struct SmaFwdFn {
+  dart::PrefillShape sh;
+  const void *Q, *E, *C, *dH;
+  const float* y_ssd;
+  float gate;
+  void* y;
+  hipStream_t st;
+  template <typename T, int N, int P>
+  hipError_t run() {
+    return dart::launch_sma_fwd<T, N, P>(sh, static_cast<const T*>(Q), static_cast<const T*>(E),
+                                         static_cast<const T*>(C), static_cast<const T*>(dH),
+                                         y_ssd, gate, static_cast<T*>(y), st);
+  }
+};
+
+struct SmaDecodeFn {
+  dart::DecodeShape sh;
+  const void *x, *Bm, *C, *Q, *E;
+  const float *dt, *A;
+  float gate;
+  void* cache;
+  float *h, *dHc;
+  int *nc, *pos;
+  void *y, *ws;
+  hipStream_t st;
+  template <typename T, int N, int P>
+  hipError_t run() {
+    return dart::launch_sma_decode<T, N, P>(
+        sh, static_cast<const T*>(x), dt, A, static_cast<const T*>(Bm), static_cast<const T*>(C),
+        static_cast<const T*>(Q), static_cast<const T*>(E), gate, static_cast<T*>(cache), h, dHc,
+        nc, pos, static_cast<T*>(y), ws, st);
+  }
+};
+
+}  // namespace
+
+extern "C" dart_status dart_chunk_state(const dart_dims* dims, const void* x, const float* dt,
+                                        const float* A, const void* Bm, float* acum, void* dH,
+                                        float* dH_f32, void* stream) {
+  dart_status s = dart_validate_dims(dims);
+  if (s != DART_OK) return s;
+  if ((s = check_ptrs(x, dt, A, Bm, acum, dH, dH_f32)) != DART_OK) return s;
+  ChunkStateFn fn{prefill_shape(dims), x, Bm, dt, A, acum, dH, dH_f32, static_cast<hipStream_t>(stream)};
+  return dispatch(dims->io, dims->dstate, dims->headdim, fn);
+}
+
+extern "C" dart_status dart_state_pass(const dart_dims* dims, const void* x, const float* dt,
+                                       const void* Bm, const void* C, const float* acum,
+                                       const float* dH_f32, const float* h0, float* H_in,
+                                       float* y_ssd, void* stream) {
+  dart_status s = dart_validate_dims(dims);
+  if (s != DART_OK) return s;
+  if ((s = check_ptrs(x, dt, Bm, C, acum, dH_f32, H_in, y_ssd)) != DART_OK) return s;
+  if (h0 && !aligned16(h0)) return DART_ERR_ALIGN;
+  StatePassFn fn{prefill_shape(dims), x, Bm, C, dt, acum, dH_f32, h0, H_in, y_ssd,
+       static_cast<hipStream_t>(stream)};
+  return dispatch(dims->io, dims->dstate, dims->headdim, fn);
+}
+
+extern "C" dart_status dart_sma_fwd(const dart_dims* dims, const void* Q, const void* E,
+                                    const void* C, const void* dH, const float* y_ssd,
+                                    float gate, void* y, void* stream) {
+  dart_status s = dart_validate_dims(dims);
+  if (s != DART_OK) return s;
+  if ((s = check_ptrs(Q, E, C, dH, y_ssd, y)) != DART_OK) return s;
+  SmaFwdFn fn{prefill_shape(dims), Q, E, C, dH, y_ssd, gate, y, static_cast<hipStream_t>(stream)};
+  return dispatch(dims->io, dims->dstate, dims->headdim, fn);
+}
+
+extern "C" dart_status dart_sma_decode(const dart_decode_dims* dims, const void* x,
+                                       const float* dt, const float* A, const void* Bm,
+                                       const void* C, const void* Q, const void* E, float gate,
+                                       void* cache, float* h, float* dH_cur, int32_t* n_chunks,
+                                       int32_t* pos, void* y, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  dart_status s = dart_validate_decode_dims(dims);
+  if (s != DART_OK) return s;
+  if ((s = check_ptrs(x, dt, A, Bm, C, Q, E, cache, h, dH_cur, n_chunks, pos, y)) != DART_OK)
+    return s;
+  if (!workspace || workspace_bytes < dart::decode_workspace_bytes(*dims))
+    return DART_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DART_ERR_ALIGN;
+  const dart::DecodeShape sh{static_cast<int>(dims->batch),      static_cast<int>(dims->nheads),
+                             static_cast<int>(dims->ngroups),    static_cast<int>(dims->chunk),
+                             static_cast<int>(dims->max_chunks), dart::decode_splits(*dims)};
+  SmaDecodeFn fn{sh, x, Bm, C, Q, E, dt, A, gate, cache, h, dH_cur, n_chunks, pos, y, workspace,
+       static_cast<hipStream_t>(stream)};
+  return dispatch(dims->io, dims->dstate, dims->headdim, fn);
+}

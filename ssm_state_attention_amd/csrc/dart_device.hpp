@@ -1,0 +1,109 @@
+// Device-side building blocks for the DART kernels on gfx950 (CDNA4, wave64).
+//
+// Matrix-core fragments follow the 16x16 MFMA family:
+//   v_mfma_f32_16x16x32_bf16 for bfloat16 inputs (K = 32, 8 values per lane)
+//   v_mfma_f32_16x16x4_f32   for float32 inputs  (K = 4,  1 value per lane)
+// With lane = 16·grp + col (grp in 0..3, col in 0..15):
+//   A (16 x K, row-major rows):  lane supplies row `col`, k-slots grp·KL .. +KL
+//   B (K x 16):                  lane supplies column `col`, the same k-slots
+//   D (16 x 16, fp32):           lane holds D[4·grp + i][col], i = 0..3
+// Only the pairing of A's and B's k-slots matters for the sum over K, so a
+// kernel may assign any bijection of K indices to (grp, slot) as long as both
+// operands use the same one.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace dart {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+// e^x for x <= 0 (decays); exp2 of a prescaled argument
+__device__ __forceinline__ float exp_neg(float x) { return exp2_fast(x * kLog2e); }
+
+__device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float v) {
+  return static_cast<T>(v);  // bfloat16: round to nearest even
+}
+
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<bf16> {
+  static constexpr int K = 32;
+  static constexpr int KL = 8;
+  typedef bf16x8 frag;
+  __device__ __forceinline__ static floatx4 mma(frag a, frag b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag load(const bf16* p) {
+    return *reinterpret_cast<const frag*>(p);
+  }
+};
+
+template <>
+struct Mma<float> {
+  static constexpr int K = 4;
+  static constexpr int KL = 1;
+  typedef float frag;
+  __device__ __forceinline__ static floatx4 mma(frag a, frag b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag load(const float* p) { return *p; }
+};
+
+// four consecutive elements <-> fp32
+__device__ __forceinline__ floatx4 load4_f32(const bf16* p) {
+  bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return floatx4{to_f32(v[0]), to_f32(v[1]), to_f32(v[2]), to_f32(v[3])};
+}
+__device__ __forceinline__ floatx4 load4_f32(const float* p) {
+  return *reinterpret_cast<const floatx4*>(p);
+}
+__device__ __forceinline__ void store4(bf16* p, floatx4 v) {
+  bf16x4 o;
+  o[0] = from_f32<bf16>(v[0]);
+  o[1] = from_f32<bf16>(v[1]);
+  o[2] = from_f32<bf16>(v[2]);
+  o[3] = from_f32<bf16>(v[3]);
+  *reinterpret_cast<bf16x4*>(p) = o;
+}
+__device__ __forceinline__ void store4(float* p, floatx4 v) {
+  *reinterpret_cast<floatx4*>(p) = v;
+}
+
+// 16-byte vector of T and its element count
+template <typename T>
+struct Vec16 {
+  static constexpr int n = 16 / sizeof(T);
+  typedef T vec __attribute__((ext_vector_type(16 / sizeof(T))));
+};
+
+template <typename T>
+__device__ __forceinline__ typename Vec16<T>::vec load16(const T* p) {
+  return *reinterpret_cast<const typename Vec16<T>::vec*>(p);
+}
+template <typename T>
+__device__ __forceinline__ typename Vec16<T>::vec load16_nt(const T* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const typename Vec16<T>::vec*>(p));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+}  // namespace dart

@@ -1,0 +1,47 @@
+// Internal launch interface between the C ABI (dart_api.hip) and the kernel
+// files.  Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "dart_device.hpp"
+
+namespace dart {
+
+struct PrefillShape {
+  int B, L, H, G, S;  // batch, length, heads, groups, chunk
+};
+
+struct DecodeShape {
+  int B, H, G, S, max_chunks, splits;
+};
+
+template <typename T, int N, int P>
+hipError_t launch_chunk_state(const PrefillShape& s, const T* x, const float* dt, const float* A,
+                              const T* Bm, float* acum, T* dH, float* dH_f32, hipStream_t st);
+
+template <typename T, int N, int P>
+hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt, const T* Bm,
+                             const T* C, const float* acum, const float* dH_f32,
+                             const float* h0, float* H_in, float* y_ssd, hipStream_t st);
+
+template <typename T, int N, int P>
+hipError_t launch_sma_fwd(const PrefillShape& s, const T* Q, const T* E, const T* C,
+                          const T* dH, const float* y_ssd, float gate, T* y, hipStream_t st);
+
+template <typename T, int N, int P>
+hipError_t launch_sma_decode(const DecodeShape& s, const T* x, const float* dt, const float* A,
+                             const T* Bm, const T* C, const T* Q, const T* E, float gate,
+                             T* cache, float* h, float* dH_cur, int* n_chunks, int* pos, T* y,
+                             void* workspace, hipStream_t st);
+
+}  // namespace dart
+
+// (T, N, P) combinations compiled into the library; must match
+// dart::shape_supported().
+#define DART_FOR_EACH_SHAPE(X) \
+  X(float, 16, 16)             \
+  X(float, 32, 32)             \
+  X(dart::bf16, 32, 32)        \
+  X(dart::bf16, 64, 64)        \
+  X(dart::bf16, 128, 64)       \
+  X(dart::bf16, 128, 128)

@@ -1,0 +1,300 @@
+// Mamba-2 chunked scan on gfx950: chunk state memories, inter-chunk state
+// passing and the native chunk output (Pith review of DART, axiom ledger:
+// the chunked scan splits the SSM output into intra- and inter-chunk terms
+// and yields the chunk contributions dH[c]; "What carries the argument":
+// dH[c] is the N x P contribution of chunk c to the chunk-boundary state).
+//
+// Decays are always formed as exp of a non-positive difference of log-decay
+// sums (never exp(-acum) on its own, which overflows fp32 for long chunks).
+#include "dart_launch.hpp"
+#include "dart_shapes.hpp"
+
+namespace dart {
+namespace {
+
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kKB = 64;        // tokens per K-block staged by k_chunk_state
+
+// One workgroup per (chunk c, head h, batch b).
+//   acum[s] = inclusive prefix sum of dt·A over the chunk (wave scan)
+//   w_s     = exp(acum_end - acum_s)·dt_s
+//   dH[c]   = Σ_s B_s (w_s x_s)ᵀ   as 16x16 MFMA tiles D[n][p], K = tokens
+// Tokens are the contraction axis but the slow axis in memory, so each
+// K-block of B and w∘x is written transposed into LDS ([n][s], [p][s]) and
+// read back as contiguous fragments.
+template <typename T, int N, int P>
+__global__ __launch_bounds__(kThreads) void k_chunk_state(
+    const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
+    const T* __restrict__ Bm, float* __restrict__ acum, T* __restrict__ dH,
+    float* __restrict__ dHf, int L, int H, int G, int S) {
+  using MM = Mma<T>;
+  constexpr int K = MM::K, KL = MM::KL;
+  constexpr int VE = Vec16<T>::n;
+  constexpr int LDK = kKB + VE;            // LDS row stride in elements (16-byte pad)
+  constexpr int NT = (N / 16) * (P / 16);  // 16x16 output tiles
+  constexpr int TPW = (NT + 3) / 4;        // tiles per wave
+  __shared__ float sh_w[kMaxChunk];
+  __shared__ float sh_part[4];
+  __shared__ __align__(16) T sh_bt[N * LDK];
+  __shared__ __align__(16) T sh_xt[P * LDK];
+
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int M = L / S, g = h / (H / G);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const long tok0 = (long)b * L + (long)c * S;  // row of the chunk's first token in [B*L]
+  const long pair = (long)b * H + h;
+
+  // 1. log-decay prefix sum, one token per thread (S <= 256)
+  const float dtv = tid < S ? dt[(tok0 + tid) * H + h] : 0.f;
+  float v = dtv * A[h];
+  for (int off = 1; off < 64; off <<= 1) {
+    const float u = __shfl_up(v, off);
+    if (lane >= off) v += u;
+  }
+  if (lane == 63) sh_part[w] = v;
+  __syncthreads();
+  for (int i = 0; i < w; ++i) v += sh_part[i];
+  const float total = sh_part[0] + sh_part[1] + sh_part[2] + sh_part[3];
+  if (tid < S) {
+    acum[(pair * M + c) * S + tid] = v;
+    sh_w[tid] = exp_neg(total - v) * dtv;
+  }
+  __syncthreads();
+
+  // 2. dH = Bᵀ (w∘x) over K-blocks of kKB tokens
+  floatx4 accv[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) accv[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += kKB) {
+    for (int i = tid; i < kKB * (P / VE); i += kThreads) {
+      const int s = i % kKB, pv = i / kKB;
+      typename Vec16<T>::vec raw = {};
+      float wv = 0.f;
+      if (s0 + s < S) {
+        raw = load16(x + ((tok0 + s0 + s) * H + h) * P + pv * VE);
+        wv = sh_w[s0 + s];
+      }
+#pragma unroll
+      for (int e = 0; e < VE; ++e) sh_xt[(pv * VE + e) * LDK + s] = from_f32<T>(to_f32(raw[e]) * wv);
+    }
+    for (int i = tid; i < kKB * (N / VE); i += kThreads) {
+      const int s = i % kKB, nv = i / kKB;
+      typename Vec16<T>::vec raw = {};
+      if (s0 + s < S) raw = load16(Bm + ((tok0 + s0 + s) * G + g) * N + nv * VE);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) sh_bt[(nv * VE + e) * LDK + s] = raw[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kKB; ks += K) {
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) {
+        const int tile = w + 4 * j;
+        if (tile < NT) {
+          const int nb = tile / (P / 16), pb = tile % (P / 16);
+          const auto a = MM::load(&sh_bt[(nb * 16 + col) * LDK + ks + grp * KL]);
+          const auto bb = MM::load(&sh_xt[(pb * 16 + col) * LDK + ks + grp * KL]);
+          accv[j] = MM::mma(a, bb, accv[j]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // 3. store memory c value-axis-major: lane holds n = nb*16 + 4*grp + i, p = pb*16 + col
+  const long base = (pair * M + c) * (long)(P * N);
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int tile = w + 4 * j;
+    if (tile < NT) {
+      const int nb = tile / (P / 16), pb = tile % (P / 16);
+      const long off = base + (long)(pb * 16 + col) * N + nb * 16 + 4 * grp;
+      store4(dH + off, accv[j]);
+      store4(dHf + off, accv[j]);
+    }
+  }
+}
+
+// H_in[0] = h0, H_in[c+1] = exp(acum_end[c])·H_in[c] + dH_f32[c]; one thread
+// per four state entries of one (batch, head), serial over chunks.
+__global__ __launch_bounds__(kThreads) void k_state_pass(
+    const float* __restrict__ acum, const float* __restrict__ dHf, const float* __restrict__ h0,
+    float* __restrict__ H_in, int H, int M, int S, int PN) {
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int e4 = blockIdx.x * kThreads + threadIdx.x;
+  if (e4 * 4 >= PN) return;
+  const long pair = (long)b * H + h;
+  const int q = PN / 4;
+  const floatx4* src = reinterpret_cast<const floatx4*>(dHf + pair * M * (long)PN) + e4;
+  floatx4* dst = reinterpret_cast<floatx4*>(H_in + pair * (M + 1) * (long)PN) + e4;
+  const float* ac_end = acum + pair * M * (long)S + (S - 1);
+  floatx4 st = h0 ? reinterpret_cast<const floatx4*>(h0 + pair * PN)[e4] : floatx4{0.f, 0.f, 0.f, 0.f};
+  dst[0] = st;
+#pragma unroll 4
+  for (int c = 0; c < M; ++c) {
+    const float dec = exp_neg(ac_end[(long)c * S]);
+    st = dec * st + src[(long)c * q];
+    dst[(long)(c + 1) * q] = st;
+  }
+}
+
+// One workgroup per (chunk k, head, batch); each wave owns 16-token blocks.
+// Per token block, in transposed form (rows p, columns = tokens t):
+//   inter: Yᵀ += H_in[k]ᵀ C_tᵀ                     (K = n), scaled by exp(acum_t)
+//   intra: Gᵀ[j][t] = B_j·C_t (K = n), masked to j <= t, times
+//          exp(acum_t - acum_j)·dt_j, then Yᵀ += xᵀ Gᵀ  (K = j)
+// The masked Gᵀ tile stays in registers: its D layout (lane holds rows
+// j = 16·jb + 4·grp + i of column t) is used directly as the B operand of the
+// second product, with the k-slots of xᵀ's A operand assigned the same j's.
+template <typename T, int N, int P>
+__global__ __launch_bounds__(kThreads) void k_chunk_out(
+    const T* __restrict__ x, const float* __restrict__ dt, const T* __restrict__ Bm,
+    const T* __restrict__ C, const float* __restrict__ acum, const float* __restrict__ H_in,
+    float* __restrict__ y_ssd, int L, int H, int G, int S) {
+  using MM = Mma<T>;
+  constexpr int K = MM::K, KL = MM::KL;
+  constexpr int VE = Vec16<T>::n;
+  constexpr int LDX = kMaxChunk + VE;  // xᵀ rows [p][j]
+  constexpr int LDH = N + VE;          // H_inᵀ rows [p][n]
+  __shared__ float sh_acum[kMaxChunk], sh_dt[kMaxChunk];
+  __shared__ __align__(16) T sh_xt[P * LDX];
+  __shared__ __align__(16) T sh_ht[P * LDH];
+
+  const int k = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int M = L / S, g = h / (H / G);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const long tok0 = (long)b * L + (long)k * S;
+  const long pair = (long)b * H + h;
+
+  for (int s = tid; s < S; s += kThreads) {
+    sh_acum[s] = acum[(pair * M + k) * S + s];
+    sh_dt[s] = dt[(tok0 + s) * H + h];
+  }
+  for (int i = tid; i < S * (P / VE); i += kThreads) {
+    const int s = i % S, pv = i / S;
+    const auto raw = load16(x + ((tok0 + s) * H + h) * P + pv * VE);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) sh_xt[(pv * VE + e) * LDX + s] = raw[e];
+  }
+  const float* hsrc = H_in + (pair * (M + 1) + k) * (long)(P * N);
+  for (int i = tid; i < P * N / 4; i += kThreads) {
+    const floatx4 f = reinterpret_cast<const floatx4*>(hsrc)[i];
+    const int p = (i * 4) / N, n = (i * 4) % N;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sh_ht[p * LDH + n + e] = from_f32<T>(f[e]);
+  }
+  __syncthreads();
+
+  for (int tb = w; tb < S / 16; tb += 4) {
+    const int t = tb * 16 + col;  // this lane's token inside the chunk
+    typename MM::frag cf[N / K];
+#pragma unroll
+    for (int kk = 0; kk < N / K; ++kk)
+      cf[kk] = MM::load(C + ((tok0 + t) * G + g) * N + kk * K + grp * KL);
+    floatx4 yin[P / 16], yia[P / 16];
+#pragma unroll
+    for (int pb = 0; pb < P / 16; ++pb) {
+      yin[pb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      yia[pb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int pb = 0; pb < P / 16; ++pb)
+#pragma unroll
+      for (int kk = 0; kk < N / K; ++kk)
+        yin[pb] = MM::mma(MM::load(&sh_ht[(pb * 16 + col) * LDH + kk * K + grp * KL]), cf[kk],
+                          yin[pb]);
+    const float ac_t = sh_acum[t];
+    if constexpr (std::is_same<T, float>::value) {
+      for (int jb = 0; jb <= tb; ++jb) {
+        floatx4 gt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < N / K; ++kk)
+          gt = MM::mma(MM::load(Bm + ((tok0 + jb * 16 + col) * G + g) * N + kk * K + grp * KL),
+                       cf[kk], gt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = jb * 16 + 4 * grp + i;
+          const float wgt = j <= t ? gt[i] * exp_neg(ac_t - sh_acum[j]) * sh_dt[j] : 0.f;
+#pragma unroll
+          for (int pb = 0; pb < P / 16; ++pb)
+            yia[pb] = MM::mma(sh_xt[(pb * 16 + col) * LDX + j], wgt, yia[pb]);
+        }
+      }
+    } else {
+      // S % 32 == 0, so the pair (jb0, jb0 + 1) never leaves the chunk
+      for (int jb0 = 0; jb0 <= tb; jb0 += 2) {
+        bf16x8 bfr;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int jb = jb0 + q;
+          floatx4 gt = {0.f, 0.f, 0.f, 0.f};
+          if (jb <= tb) {
+#pragma unroll
+            for (int kk = 0; kk < N / K; ++kk)
+              gt = MM::mma(
+                  MM::load(Bm + ((tok0 + jb * 16 + col) * G + g) * N + kk * K + grp * KL),
+                  cf[kk], gt);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = jb * 16 + 4 * grp + i;
+            const float wgt = j <= t ? gt[i] * exp_neg(ac_t - sh_acum[j]) * sh_dt[j] : 0.f;
+            bfr[4 * q + i] = from_f32<bf16>(wgt);
+          }
+        }
+#pragma unroll
+        for (int pb = 0; pb < P / 16; ++pb) {
+          const bf16* row = &sh_xt[(pb * 16 + col) * LDX];
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + jb0 * 16 + 4 * grp);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + (jb0 + 1) * 16 + 4 * grp);
+          const bf16x8 afr = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          yia[pb] = MM::mma(afr, bfr, yia[pb]);
+        }
+      }
+    }
+    const float dec_t = exp_neg(ac_t);
+#pragma unroll
+    for (int pb = 0; pb < P / 16; ++pb)
+      store4(y_ssd + ((tok0 + t) * H + h) * P + pb * 16 + 4 * grp, yia[pb] + dec_t * yin[pb]);
+  }
+}
+
+}  // namespace
+
+template <typename T, int N, int P>
+hipError_t launch_chunk_state(const PrefillShape& s, const T* x, const float* dt, const float* A,
+                              const T* Bm, float* acum, T* dH, float* dH_f32, hipStream_t st) {
+  const int M = s.L / s.S;
+  hipLaunchKernelGGL((k_chunk_state<T, N, P>), dim3(M, s.H, s.B), dim3(kThreads), 0, st, x, dt,
+                     A, Bm, acum, dH, dH_f32, s.L, s.H, s.G, s.S);
+  return hipGetLastError();
+}
+
+template <typename T, int N, int P>
+hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt, const T* Bm,
+                             const T* C, const float* acum, const float* dH_f32,
+                             const float* h0, float* H_in, float* y_ssd, hipStream_t st) {
+  const int M = s.L / s.S;
+  constexpr int PN = P * N;
+  hipLaunchKernelGGL(k_state_pass, dim3((PN / 4 + kThreads - 1) / kThreads, s.H, s.B),
+                     dim3(kThreads), 0, st, acum, dH_f32, h0, H_in, s.H, M, s.S, PN);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_chunk_out<T, N, P>), dim3(M, s.H, s.B), dim3(kThreads), 0, st, x, dt, Bm,
+                     C, acum, H_in, y_ssd, s.L, s.H, s.G, s.S);
+  return hipGetLastError();
+}
+
+#define DART_INST_SCAN(T, N, P)                                                              \
+  template hipError_t launch_chunk_state<T, N, P>(const PrefillShape&, const T*, const float*, \
+                                                  const float*, const T*, float*, T*, float*,  \
+                                                  hipStream_t);                                \
+  template hipError_t launch_state_pass<T, N, P>(const PrefillShape&, const T*, const float*,  \
+                                                 const T*, const T*, const float*,             \
+                                                 const float*, const float*, float*, float*,   \
+                                                 hipStream_t);
+DART_FOR_EACH_SHAPE(DART_INST_SCAN)
+
+}  // namespace dart

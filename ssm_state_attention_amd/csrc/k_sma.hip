@@ -1,0 +1,448 @@
+// State-memory attention (SMA) on gfx950: prefill over all tokens and the
+// single-token decode step over the chunk-memory cache.
+//
+// Definitions (Pith review of DART, "Core claim" and "What carries the
+// argument"; referee major comment 3, paper §3 Eq. 8; DART abstract): for a
+// token t of chunk k and each completed chunk c < k
+//   key    dH[c]·E_t (value axis contracted)   value  C_tᵀ·dH[c]
+//   score  Q_tᵀ·dH[c]·E_t / sqrt(N)            o_t = Σ_c softmax_c(score)·value
+// and y_t = y_ssd_t + gate·o_t (o_t = 0 for chunk 0).
+//
+// Evaluation order used here: with Zq = dH[c]ᵀQ_t and Zc = dH[c]ᵀC_t (both in
+// R^P) the score is E_t·Zq / sqrt(N) and the value is Zc, so each memory is
+// one product with the stacked [Q; C] operand.  The same quantities, summed
+// in a different association order.
+#include "dart_launch.hpp"
+#include "dart_shapes.hpp"
+
+namespace dart {
+namespace {
+
+// tokens per wave = 16·NTB; the largest shape keeps one 16-token block per
+// wave to stay inside the register file
+template <int N, int P>
+struct SmaTile {
+  static constexpr int NTB = (N * P >= 128 * 128) ? 1 : 2;
+};
+
+// Prefill SMA.  One workgroup = WAVES waves × 16·NTB tokens of ONE chunk k,
+// so every token of the workgroup sees the same memories c < k (no mask).
+// Per memory c: dH[c]ᵀ (P x N, value-axis-major in HBM) is staged into LDS
+// (double-buffered, one barrier per memory); each wave multiplies it with
+// its resident [Q; C] fragments (16x16 MFMA, rows p, columns = tokens),
+// finishes the score with an in-lane dot against E_t plus two lane-group
+// exchanges, and folds the value into an online softmax.
+//
+// Grid mapping: workgroups are dealt to the 8 XCDs round-robin, so
+// blockIdx % 8 selects an XCD and all tiles of one (batch, head) pair land
+// on the same XCD (its memories stay in that XCD's L2).  Within an XCD the
+// tiles run heaviest first (largest k), which bounds the tail.
+template <typename T, int N, int P, int NTB, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
+    const T* __restrict__ Q, const T* __restrict__ E, const T* __restrict__ C,
+    const T* __restrict__ dH, const float* __restrict__ y_ssd, float gate, T* __restrict__ y,
+    int BH, int L, int H, int G, int S, int npq, float scale_log2) {
+  using MM = Mma<T>;
+  constexpr int K = MM::K, KL = MM::KL, VE = Vec16<T>::n;
+  constexpr int LDN = N + VE;  // LDS row stride (elements): 16-byte pad
+  constexpr int TW = 16 * NTB, TWG = TW * WAVES;
+  constexpr int NVEC = P * N / VE;  // 16-byte vectors per memory
+  constexpr int NTHR = 64 * WAVES;
+  constexpr int VPT = (NVEC + NTHR - 1) / NTHR;
+  constexpr int NPB = P / 16, NKK = N / K;
+  typedef typename Vec16<T>::vec vec_t;
+  __shared__ __align__(16) T sh_mem[2][P * LDN];
+
+  const int M = L / S, tpc = S / TWG;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int sub = slot % tpc, r = slot / tpc;
+  const int ql = r % npq, kr = r / npq;
+  const int k = M - 1 - kr;
+  const int pair = ql * 8 + xcd;
+  if (pair >= BH || k < 0) return;  // uniform over the workgroup
+  const int b = pair / H, h = pair % H, g = h / (H / G);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const long row_w = (long)b * L + (long)k * S + sub * TWG + w * TW;
+
+  typename MM::frag qf[NTB][NKK], cf[NTB][NKK];
+  float ev[NTB][NPB][4];
+#pragma unroll
+  for (int tb = 0; tb < NTB; ++tb) {
+    const long row = row_w + tb * 16 + col;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      qf[tb][kk] = MM::load(Q + (row * G + g) * N + kk * K + grp * KL);
+      cf[tb][kk] = MM::load(C + (row * G + g) * N + kk * K + grp * KL);
+    }
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb) {
+      const floatx4 e4 = load4_f32(E + (row * H + h) * P + pb * 16 + 4 * grp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ev[tb][pb][i] = e4[i];
+    }
+  }
+  floatx4 acc[NTB][NPB];
+  float mx[NTB], ls[NTB];
+#pragma unroll
+  for (int tb = 0; tb < NTB; ++tb) {
+    mx[tb] = -INFINITY;
+    ls[tb] = 0.f;
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb) acc[tb][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const T* mem = dH + (long)pair * M * (P * N);
+  vec_t stg[VPT];
+  auto gload = [&](int c) {
+    const vec_t* src = reinterpret_cast<const vec_t*>(mem + (long)c * (P * N));
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      const int vi = tid + v * NTHR;
+      if (vi < NVEC) stg[v] = src[vi];
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      const int vi = tid + v * NTHR;
+      if (vi < NVEC) {
+        const int p = vi / (N / VE), nv = vi % (N / VE);
+        *reinterpret_cast<vec_t*>(&sh_mem[buf][p * LDN + nv * VE]) = stg[v];
+      }
+    }
+  };
+
+  if (k > 0) {
+    gload(0);
+    swrite(0);
+  }
+  __syncthreads();
+  for (int c = 0; c < k; ++c) {
+    const int cur = c & 1;
+    if (c + 1 < k) gload(c + 1);
+    floatx4 zq[NTB][NPB], zc[NTB][NPB];
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb) {
+        zq[tb][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        zc[tb][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const auto a = MM::load(&sh_mem[cur][(pb * 16 + col) * LDN + kk * K + grp * KL]);
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+          zq[tb][pb] = MM::mma(a, qf[tb][kk], zq[tb][pb]);
+          zc[tb][pb] = MM::mma(a, cf[tb][kk], zc[tb][pb]);
+        }
+      }
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+      float s = 0.f;
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s += zq[tb][pb][i] * ev[tb][pb][i];
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      s *= scale_log2;
+      const float mn = fmaxf(mx[tb], s);
+      const float al = exp2_fast(mx[tb] - mn);
+      const float pw = exp2_fast(s - mn);
+      ls[tb] = ls[tb] * al + pw;
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb) acc[tb][pb] = acc[tb][pb] * al + pw * zc[tb][pb];
+      mx[tb] = mn;
+    }
+    if (c + 1 < k) swrite(cur ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int tb = 0; tb < NTB; ++tb) {
+    const long row = row_w + tb * 16 + col;
+    const float inv = k > 0 ? 1.f / ls[tb] : 0.f;
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb) {
+      const long off = (row * H + h) * P + pb * 16 + 4 * grp;
+      const floatx4 ys = load4_f32(y_ssd + off);
+      store4(y + off, ys + (gate * inv) * acc[tb][pb]);
+    }
+  }
+}
+
+// Decode.  One workgroup (4 waves) per (split, head, batch).  Split 0 also
+// advances the SSM state of its (batch, head) and, when the token closes its
+// chunk, appends the finished memory to the cache.  Each wave streams whole
+// memories c = first + wave, first + wave + 4, ... once from HBM
+// (non-temporal 16-byte loads): lane (nv, pr) holds key entries
+// n in [nv·VE, nv·VE + VE) of rows p = it·RP + pr, forms partial
+// Q·dH[c] and C·dH[c] over its n-range, reduces the score across the wave
+// and keeps an online softmax whose value accumulator stays partial over n
+// until the end.
+template <typename T, int N, int P>
+__global__ __launch_bounds__(256) void k_sma_decode(
+    const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
+    const T* __restrict__ Bm, const T* __restrict__ C, const T* __restrict__ Q,
+    const T* __restrict__ E, float gate, T* __restrict__ cache, float* __restrict__ hst,
+    float* __restrict__ dHc, const int* __restrict__ n_chunks, const int* __restrict__ pos,
+    T* __restrict__ y, int* __restrict__ ws_flag, float* __restrict__ ws_yssd,
+    float* __restrict__ ws_part, int H, int G, int S, int max_chunks, int splits, int cps,
+    float scale_log2) {
+  constexpr int VE = Vec16<T>::n;
+  constexpr int NV = N / VE;   // 16-byte vectors per memory row
+  constexpr int RP = 64 / NV;  // rows per wave pass
+  constexpr int NPASS = P / RP;
+  constexpr int NW = 4;
+  constexpr int Q4 = N / 4;
+  static_assert(64 % NV == 0 && P % RP == 0, "decode lane mapping");
+  static_assert((P * N / 4) % 64 == 0 && 64 % Q4 == 0, "decode state mapping");
+  typedef typename Vec16<T>::vec vec_t;
+  __shared__ float sh_q[N], sh_c[N], sh_b[N], sh_e[P], sh_x[P], sh_y[P];
+  __shared__ float sh_wm[NW], sh_wl[NW];
+  __shared__ float sh_wacc[NW][P];
+
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (H / G);
+  const long pair = (long)b * H + h;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int kc = n_chunks[b];
+  kc = kc < 0 ? 0 : (kc > max_chunks ? max_chunks : kc);
+  const int ps = pos[b];
+
+  for (int i = tid; i < N; i += 256) {
+    const long o = ((long)b * G + g) * N + i;
+    sh_q[i] = to_f32(Q[o]);
+    sh_c[i] = to_f32(C[o]);
+    sh_b[i] = to_f32(Bm[o]);
+  }
+  for (int i = tid; i < P; i += 256) {
+    sh_e[i] = to_f32(E[pair * P + i]);
+    sh_x[i] = to_f32(x[pair * P + i]);
+  }
+  __syncthreads();
+
+  if (split == 0) {
+    const float dtv = dt[pair];
+    const float a = exp_neg(dtv * A[h]);
+    const bool close = ps == S - 1;
+    const bool append = close && kc < max_chunks;
+    floatx4* hp = reinterpret_cast<floatx4*>(hst + pair * (P * N));
+    floatx4* dp = reinterpret_cast<floatx4*>(dHc + pair * (P * N));
+    T* cdst = cache + (pair * max_chunks + kc) * (long)(P * N);
+    for (int i = tid; i < P * N / 4; i += 256) {
+      const int p = i / Q4, n = (i % Q4) * 4;
+      floatx4 hv = hp[i], dv = dp[i];
+      const float xd = dtv * sh_x[p];
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float u = xd * sh_b[n + e];
+        hv[e] = a * hv[e] + u;
+        dv[e] = a * dv[e] + u;
+        part += sh_c[n + e] * hv[e];
+      }
+      hp[i] = hv;
+      if (append) store4(cdst + (long)i * 4, dv);
+      dp[i] = close ? floatx4{0.f, 0.f, 0.f, 0.f} : dv;
+#pragma unroll
+      for (int off = 1; off < Q4; off <<= 1) part += __shfl_xor(part, off);
+      if ((i % Q4) == 0) sh_y[p] = part;
+    }
+    if (close && !append && tid == 0) atomicOr(ws_flag, 1);
+  }
+
+  const int c_begin = split * cps;
+  const int c_end = min(kc, c_begin + cps);
+  const int nv = lane % NV, pr = lane / NV;
+  float qv[VE], cv[VE], ev[NPASS], acc[NPASS];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) {
+    qv[e] = sh_q[nv * VE + e];
+    cv[e] = sh_c[nv * VE + e];
+  }
+#pragma unroll
+  for (int it = 0; it < NPASS; ++it) {
+    ev[it] = sh_e[it * RP + pr];
+    acc[it] = 0.f;
+  }
+  float mx = -INFINITY, ls = 0.f;
+  const T* base = cache + pair * (long)max_chunks * (P * N);
+  for (int c = c_begin + w; c < c_end; c += NW) {
+    const T* src = base + (long)c * (P * N);
+    vec_t raw[NPASS];
+#pragma unroll
+    for (int it = 0; it < NPASS; ++it) raw[it] = load16_nt(src + ((it * RP + pr) * NV + nv) * VE);
+    float s = 0.f, zc[NPASS];
+#pragma unroll
+    for (int it = 0; it < NPASS; ++it) {
+      float zq = 0.f, z2 = 0.f;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        const float v = to_f32(raw[it][e]);
+        zq += qv[e] * v;
+        z2 += cv[e] * v;
+      }
+      zc[it] = z2;
+      s += ev[it] * zq;
+    }
+    s = wave_sum(s) * scale_log2;
+    const float mn = fmaxf(mx, s);
+    const float al = exp2_fast(mx - mn);
+    const float pw = exp2_fast(s - mn);
+    ls = ls * al + pw;
+#pragma unroll
+    for (int it = 0; it < NPASS; ++it) acc[it] = acc[it] * al + pw * zc[it];
+    mx = mn;
+  }
+#pragma unroll
+  for (int it = 0; it < NPASS; ++it)
+#pragma unroll
+    for (int off = 1; off < NV; off <<= 1) acc[it] += __shfl_xor(acc[it], off);
+  if (nv == 0) {
+#pragma unroll
+    for (int it = 0; it < NPASS; ++it) sh_wacc[w][it * RP + pr] = acc[it];
+  }
+  if (lane == 0) {
+    sh_wm[w] = mx;
+    sh_wl[w] = ls;
+  }
+  __syncthreads();
+
+  float mall = -INFINITY;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) mall = fmaxf(mall, sh_wm[ww]);
+  for (int p = tid; p < P; p += 256) {
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      if (sh_wm[ww] > -INFINITY) {
+        const float f = exp2_fast(sh_wm[ww] - mall);
+        num += f * sh_wacc[ww][p];
+        den += f * sh_wl[ww];
+      }
+    }
+    if (splits == 1) {
+      const float o = den > 0.f ? num / den : 0.f;
+      y[pair * P + p] = from_f32<T>(sh_y[p] + gate * o);
+    } else {
+      float* part = ws_part + (pair * splits + split) * (P + 2);
+      part[2 + p] = num;
+      if (p == 0) {
+        part[0] = mall;
+        part[1] = den;
+      }
+      if (split == 0) ws_yssd[pair * P + p] = sh_y[p];
+    }
+  }
+}
+
+// Merge the per-split (max, denominator, numerator[P]) partials of one
+// (batch, head) and apply the gate.
+template <typename T>
+__global__ __launch_bounds__(128) void k_decode_combine(const float* __restrict__ ws_yssd,
+                                                        const float* __restrict__ ws_part,
+                                                        float gate, T* __restrict__ y, int P,
+                                                        int splits) {
+  const long pair = blockIdx.x;
+  const float* part = ws_part + pair * splits * (P + 2);
+  float mall = -INFINITY;
+  for (int s = 0; s < splits; ++s) mall = fmaxf(mall, part[s * (P + 2)]);
+  for (int p = threadIdx.x; p < P; p += blockDim.x) {
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float m = part[s * (P + 2)];
+      if (m > -INFINITY) {
+        const float f = exp2_fast(m - mall);
+        num += f * part[s * (P + 2) + 2 + p];
+        den += f * part[s * (P + 2) + 1];
+      }
+    }
+    const float o = den > 0.f ? num / den : 0.f;
+    y[pair * P + p] = from_f32<T>(ws_yssd[pair * P + p] + gate * o);
+  }
+}
+
+// Advance the per-sequence position after every head has read it.
+__global__ void k_decode_advance(int* __restrict__ n_chunks, int* __restrict__ pos, int B, int S,
+                                 int max_chunks) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  if (pos[b] == S - 1) {
+    const int k = n_chunks[b];
+    n_chunks[b] = k < max_chunks ? k + 1 : max_chunks;
+    pos[b] = 0;
+  } else {
+    pos[b] += 1;
+  }
+}
+
+template <typename T, int N, int P, int NTB, int WAVES>
+hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T* C, const T* dH,
+                         const float* y_ssd, float gate, T* y, hipStream_t st) {
+  const int M = s.L / s.S;
+  const int BH = s.B * s.H;
+  const int npq = (BH + 7) / 8;  // (batch, head) pairs per XCD
+  const int tpc = s.S / (16 * NTB * WAVES);
+  const long blocks = 8L * npq * M * tpc;
+  const float scale_log2 = kLog2e / sqrtf(static_cast<float>(N));
+  hipLaunchKernelGGL((k_sma_fwd<T, N, P, NTB, WAVES>), dim3(blocks), dim3(64 * WAVES), 0, st, Q,
+                     E, C, dH, y_ssd, gate, y, BH, s.L, s.H, s.G, s.S, npq, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+template <typename T, int N, int P>
+hipError_t launch_sma_fwd(const PrefillShape& s, const T* Q, const T* E, const T* C,
+                          const T* dH, const float* y_ssd, float gate, T* y, hipStream_t st) {
+  constexpr int NTB = SmaTile<N, P>::NTB;
+  const int r = s.S / (16 * NTB);  // S % 32 == 0, so r >= 1
+  if (r % 8 == 0) return sma_fwd_waves<T, N, P, NTB, 8>(s, Q, E, C, dH, y_ssd, gate, y, st);
+  if (r % 4 == 0) return sma_fwd_waves<T, N, P, NTB, 4>(s, Q, E, C, dH, y_ssd, gate, y, st);
+  if (r % 2 == 0) return sma_fwd_waves<T, N, P, NTB, 2>(s, Q, E, C, dH, y_ssd, gate, y, st);
+  return sma_fwd_waves<T, N, P, NTB, 1>(s, Q, E, C, dH, y_ssd, gate, y, st);
+}
+
+template <typename T, int N, int P>
+hipError_t launch_sma_decode(const DecodeShape& s, const T* x, const float* dt, const float* A,
+                             const T* Bm, const T* C, const T* Q, const T* E, float gate,
+                             T* cache, float* h, float* dH_cur, int* n_chunks, int* pos, T* y,
+                             void* workspace, hipStream_t st) {
+  const long pairs = (long)s.B * s.H;
+  char* ws = static_cast<char*>(workspace);
+  int* flag = reinterpret_cast<int*>(ws);
+  float* ws_yssd = reinterpret_cast<float*>(ws + 256);
+  float* ws_part = reinterpret_cast<float*>(
+      ws + 256 + ((pairs * P * sizeof(float) + 255) / 256) * 256);
+  const int cps = (s.max_chunks + s.splits - 1) / s.splits;
+  const float scale_log2 = kLog2e / sqrtf(static_cast<float>(N));
+  hipLaunchKernelGGL((k_sma_decode<T, N, P>), dim3(s.splits, s.H, s.B), dim3(256), 0, st, x, dt,
+                     A, Bm, C, Q, E, gate, cache, h, dH_cur, n_chunks, pos, y, flag, ws_yssd,
+                     ws_part, s.H, s.G, s.S, s.max_chunks, s.splits, cps, scale_log2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (s.splits > 1) {
+    hipLaunchKernelGGL((k_decode_combine<T>), dim3(pairs), dim3(128), 0, st, ws_yssd, ws_part,
+                       gate, y, P, s.splits);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_decode_advance, dim3((s.B + 255) / 256), dim3(256), 0, st, n_chunks, pos,
+                     s.B, s.S, s.max_chunks);
+  return hipGetLastError();
+}
+
+#define DART_INST_SMA(T, N, P)                                                                 \
+  template hipError_t launch_sma_fwd<T, N, P>(const PrefillShape&, const T*, const T*, const T*, \
+                                              const T*, const float*, float, T*, hipStream_t);   \
+  template hipError_t launch_sma_decode<T, N, P>(                                                \
+      const DecodeShape&, const T*, const float*, const float*, const T*, const T*, const T*,    \
+      const T*, float, T*, float*, float*, int*, int*, T*, void*, hipStream_t);
+DART_FOR_EACH_SHAPE(DART_INST_SMA)
+
+}  // namespace dart

@@ -1,0 +1,304 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.
+
+Bar: fp32 max|gpu - ref| <= 1e-4; bfloat16 (fp32 accumulate)
+max|gpu - ref| <= 2e-2 * max|ref|, per output tensor.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ssm_state_attention_amd import api, synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def assert_parity(gpu, ref, io, what):
+    g = gpu if isinstance(gpu, np.ndarray) else synth.as_f64(gpu)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert g.shape == ref.shape, f"{what}: shape {g.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = float(np.max(np.abs(g - ref))) if g.size else 0.0
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    bound = 1e-4 if io == torch.float32 else 2e-2 * scale
+    print(f"{what}: max err {err:.3e} bound {bound:.3e} (max|ref| {scale:.3e})", flush=True)
+    assert err <= bound, f"{what}: max err {err:.3e} > bound {bound:.3e}"
+
+
+def _np(d):
+    return {k: synth.as_f64(v) for k, v in d.items()}
+
+
+def _to_dev(d):
+    return {k: v.to(DEV) for k, v in d.items()}
+
+
+def _pn_to_np(t):
+    """Library state layout [..., P, N] -> oracle layout [..., N, P]."""
+    return np.swapaxes(synth.as_f64(t), -1, -2)
+
+
+def run_prefill_case(B, L, H, G, N, P, S, io, seed=0, gate=0.5, qscale=1.0, h0_std=0.0):
+    _need_gpu()
+    print(f"prefill case B{B} L{L} H{H} G{G} N{N} P{P} S{S} {io} seed{seed} "
+          f"qscale{qscale} h0_std{h0_std}", flush=True)
+    inp = synth.draw_prefill(seed, B, L, H, G, N, P, io=io, qscale=qscale)
+    h0 = None
+    if h0_std:
+        h0 = synth.draw_state(seed + 1, (B, H, P, N), h0_std, torch.float32)
+    d = _to_dev(inp)
+    out = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate, S,
+                      h0=None if h0 is None else h0.to(DEV))
+    torch.cuda.synchronize()
+    n = _np(inp)
+    ref = oracle.prefill(n["x"], n["dt"], n["A"], n["Bm"], n["C"], n["Q"], n["E"], gate, S,
+                         h0=None if h0 is None else _pn_to_np(h0))
+    assert_parity(_pn_to_np(out["dH_f32"]), ref["dH"], io, "dH_f32")
+    assert_parity(_pn_to_np(out["dH"]), ref["dH"], io, "dH")
+    assert_parity(_pn_to_np(out["H_in"]), ref["H_in"], io, "H_in")
+    assert_parity(out["y_ssd"], ref["y_ssd"], io, "y_ssd")
+    assert_parity(out["y"], ref["y"], io, "y")
+    # the SMA branch alone, so that a wrong readout cannot hide under y_ssd
+    o_gpu = (synth.as_f64(out["y"]) - synth.as_f64(out["y_ssd"])) / gate
+    if io == torch.float32:
+        assert_parity(o_gpu, ref["o"], io, "o")
+    return out, ref
+
+
+def test_config0_fp32_tiny_layer():
+    """Tiny DART layer fp32: batch 1, 1 head, L=1024, S=64, N=16, P=16, g=0.5, seed 0."""
+    run_prefill_case(1, 1024, 1, 1, 16, 16, 64, torch.float32)
+
+
+def test_config1_bf16_prefill():
+    """Prefill bf16: batch 1, 8 heads, L=4096, S=256, N=128, P=64."""
+    run_prefill_case(1, 4096, 8, 8, 128, 64, 256, torch.bfloat16)
+
+
+@pytest.mark.parametrize("B,L,H,G,N,P,S,io", [
+    (1, 32, 1, 1, 32, 32, 32, torch.bfloat16),        # M = 1: SMA output is zero
+    (2, 64, 3, 1, 32, 32, 32, torch.bfloat16),        # M = 2, B·H not a multiple of 8
+    (3, 96, 5, 5, 64, 64, 32, torch.bfloat16),        # ragged pair count, 1-wave tiles
+    (1, 384, 4, 2, 64, 64, 128, torch.bfloat16),      # 4-wave tiles, grouped B/C/Q
+    (2, 512, 2, 2, 128, 128, 256, torch.bfloat16),    # largest shape, one token block/wave
+    (1, 768, 3, 3, 128, 64, 256, torch.bfloat16),     # M = 3
+    (2, 96, 3, 3, 32, 32, 96, torch.float32),         # S not a power of two
+    (1, 320, 2, 1, 16, 16, 32, torch.float32),
+])
+def test_prefill_shapes(B, L, H, G, N, P, S, io):
+    run_prefill_case(B, L, H, G, N, P, S, io, seed=B * 100 + L + H)
+
+
+@pytest.mark.parametrize("qscale", [1e2, 1e4])
+def test_prefill_sharpened_softmax(qscale):
+    """Scaled queries make the softmax nearly one-hot, so a wrong score
+    (scale, key axis, index) moves y far beyond the tolerance."""
+    out, ref = run_prefill_case(2, 1024, 4, 2, 128, 64, 256, torch.bfloat16, seed=7,
+                                qscale=qscale, gate=1.0)
+    o_gpu = synth.as_f64(out["y"]) - synth.as_f64(out["y_ssd"])
+    assert_parity(o_gpu, ref["o"], torch.bfloat16, "o (sharpened)")
+
+
+def test_prefill_sharpened_fp32():
+    run_prefill_case(1, 256, 2, 1, 32, 32, 32, torch.float32, seed=8, qscale=1e3)
+
+
+def test_prefill_with_initial_state():
+    run_prefill_case(2, 512, 4, 4, 64, 64, 128, torch.bfloat16, seed=9, h0_std=0.05)
+    run_prefill_case(1, 256, 1, 1, 16, 16, 64, torch.float32, seed=10, h0_std=0.5)
+
+
+def test_gate_zero_returns_ssm_output():
+    """g = 0 removes the SMA branch: y equals y_ssd rounded to the io type."""
+    _need_gpu()
+    inp = _to_dev(synth.draw_prefill(11, 1, 1024, 4, 4, 128, 64, io=torch.bfloat16))
+    out = api.prefill(inp["x"], inp["dt"], inp["A"], inp["Bm"], inp["C"], inp["Q"], inp["E"],
+                      0.0, 256)
+    torch.cuda.synchronize()
+    assert torch.equal(out["y"], out["y_ssd"].to(torch.bfloat16))
+
+
+def test_memories_rounded_from_f32():
+    """The io-typed memories are the f32 memories rounded to nearest even."""
+    _need_gpu()
+    inp = _to_dev(synth.draw_prefill(12, 1, 512, 2, 2, 128, 64, io=torch.bfloat16))
+    out = api.prefill(inp["x"], inp["dt"], inp["A"], inp["Bm"], inp["C"], inp["Q"], inp["E"],
+                      0.5, 256)
+    torch.cuda.synchronize()
+    assert torch.equal(out["dH"], out["dH_f32"].to(torch.bfloat16))
+
+
+# ------------------------------------------------------------------ decode
+def _decode_case(B, H, G, N, P, S, max_chunks, n_chunks, pos, io, seed, gate=0.5, qscale=1.0):
+    _need_gpu()
+    print(f"decode case B{B} H{H} G{G} N{N} P{P} S{S} max{max_chunks} n{n_chunks} pos{pos} "
+          f"{io} seed{seed}", flush=True)
+    st = api.new_decode_state(B, H, G, N, P, S, max_chunks, io, DEV)
+    st["cache"].copy_(synth.draw_state(seed, (B, H, max_chunks, P, N), 0.01, io))
+    st["h"].copy_(synth.draw_state(seed + 1, (B, H, P, N), 0.01, torch.float32))
+    st["dH_cur"].copy_(synth.draw_state(seed + 2, (B, H, P, N), 0.01, torch.float32))
+    st["n_chunks"].copy_(torch.tensor(n_chunks, dtype=torch.int32))
+    st["pos"].copy_(torch.tensor(pos, dtype=torch.int32))
+    ostate = {"cache": _pn_to_np(st["cache"]), "h": _pn_to_np(st["h"]),
+              "dH_cur": _pn_to_np(st["dH_cur"]), "n_chunks": np.array(n_chunks),
+              "pos": np.array(pos)}
+    tok = synth.draw_decode_token(seed + 3, B, H, G, N, P, io=io, qscale=qscale)
+    d = _to_dev(tok)
+    y = api.decode_step(st, d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate)
+    torch.cuda.synchronize()
+    n = _np(tok)
+    y_ref, new = oracle.decode_step(ostate, n["x"], n["dt"], n["A"], n["Bm"], n["C"], n["Q"],
+                                    n["E"], gate, S, cache_bf16=io == torch.bfloat16)
+    assert_parity(y, y_ref, io, "decode y")
+    assert_parity(_pn_to_np(st["h"]), new["h"], io, "decode h")
+    assert_parity(_pn_to_np(st["dH_cur"]), new["dH_cur"], io, "decode dH_cur")
+    assert_parity(_pn_to_np(st["cache"]), new["cache"], io, "decode cache")
+    assert st["n_chunks"].cpu().tolist() == list(new["n_chunks"])
+    assert st["pos"].cpu().tolist() == list(new["pos"])
+    return st
+
+
+@pytest.mark.parametrize("io,N,P", [(torch.bfloat16, 128, 64), (torch.bfloat16, 64, 64),
+                                    (torch.bfloat16, 128, 128), (torch.float32, 16, 16),
+                                    (torch.float32, 32, 32)])
+def test_decode_small(io, N, P):
+    """Few (sequence, head) pairs: the chunk range is split across
+    workgroups and merged by the combine kernel; one sequence closes its
+    chunk (append), one starts from an empty cache."""
+    _decode_case(3, 4, 2, N, P, 64, 12, [5, 0, 11], [63, 0, 17], io, seed=20)
+
+
+def test_decode_sharpened():
+    _decode_case(2, 4, 4, 128, 64, 256, 16, [16, 9], [3, 255], torch.bfloat16, seed=21,
+                 qscale=1e4)
+
+
+def test_decode_many_pairs_single_split():
+    """Enough pairs that each workgroup streams its whole cache (no combine)."""
+    _decode_case(32, 32, 32, 128, 64, 256, 8, list(range(1, 9)) * 4, [255, 0] * 16,
+                 torch.bfloat16, seed=22)
+
+
+def test_decode_cache_full_sets_flag():
+    """Closing a chunk with a full cache appends nothing, raises the
+    workspace flag and saturates n_chunks; nothing is written out of bounds."""
+    _need_gpu()
+    B, H, N, P, S, mx = 2, 2, 64, 64, 32, 3
+    st = api.new_decode_state(B, H, H, N, P, S, mx, torch.bfloat16, DEV)
+    st["cache"].copy_(synth.draw_state(30, (B, H, mx, P, N), 0.01, torch.bfloat16))
+    before = st["cache"].clone()
+    st["n_chunks"].fill_(mx)
+    st["pos"].fill_(S - 1)
+    d = _to_dev(synth.draw_decode_token(31, B, H, H, N, P, io=torch.bfloat16))
+    api.decode_step(st, d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], 0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(st["cache"], before)
+    assert int(st["workspace"][:4].view(torch.int32).item()) == 1
+    assert st["n_chunks"].tolist() == [mx] * B and st["pos"].tolist() == [0] * B
+
+
+@pytest.mark.parametrize("io,N,P,S", [(torch.bfloat16, 128, 64, 64), (torch.float32, 16, 16, 32)])
+def test_decode_continues_prefill(io, N, P, S):
+    """Prefill k chunks, then decode the next chunk token by token: decode
+    outputs match the prefill of the longer sequence, and the appended
+    memory matches the prefill's memory (GPU against GPU and oracle)."""
+    _need_gpu()
+    B, H, G, k0, M = 2, 4, 2, 2, 3
+    L = S * M
+    inp = synth.draw_prefill(40, B, L, H, G, N, P, io=io, qscale=30.0)
+    d = _to_dev(inp)
+    gate = 0.75
+    full = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate, S)
+    st = api.new_decode_state(B, H, G, N, P, S, M, io, DEV)
+    st["cache"][:, :, :k0].copy_(full["dH"][:, :, :k0])
+    st["h"].copy_(full["H_in"][:, :, k0])
+    st["n_chunks"].fill_(k0)
+    ys = []
+    for t in range(k0 * S, L):
+        ys.append(api.decode_step(st, d["x"][:, t].contiguous(), d["dt"][:, t].contiguous(),
+                                  d["A"], d["Bm"][:, t].contiguous(), d["C"][:, t].contiguous(),
+                                  d["Q"][:, t].contiguous(), d["E"][:, t].contiguous(), gate))
+    torch.cuda.synchronize()
+    y_dec = torch.stack(ys, dim=1)
+    n = _np(inp)
+    ref = oracle.prefill(n["x"], n["dt"], n["A"], n["Bm"], n["C"], n["Q"], n["E"], gate, S)
+    assert_parity(y_dec, ref["y"][:, k0 * S:], io, "decoded y vs oracle prefill")
+    assert_parity(y_dec, synth.as_f64(full["y"][:, k0 * S:]), io, "decoded y vs GPU prefill")
+    assert_parity(_pn_to_np(st["cache"][:, :, k0]), ref["dH"][:, :, k0], io, "appended memory")
+    assert_parity(_pn_to_np(st["h"]), ref["h_final"], io, "final state")
+    assert st["n_chunks"].tolist() == [M] * B and st["pos"].tolist() == [0] * B
+
+
+# ------------------------------------------------------ full-size samples
+def _oracle_pair(n, b, h, H, G, S, gate, tokens=None):
+    """Oracle outputs of one (batch, head) pair, from sliced inputs."""
+    g = h // (H // G)
+    sl = dict(x=n["x"][b:b + 1, :, h:h + 1], dt=n["dt"][b:b + 1, :, h:h + 1],
+              A=n["A"][h:h + 1], Bm=n["Bm"][b:b + 1, :, g:g + 1], C=n["C"][b:b + 1, :, g:g + 1],
+              Q=n["Q"][b:b + 1, :, g:g + 1], E=n["E"][b:b + 1, :, h:h + 1])
+    dH = oracle.chunk_states(sl["x"], sl["dt"], sl["A"], sl["Bm"], S)
+    H_in = oracle.state_pass(dH, sl["dt"], sl["A"], S)
+    y_ssd = oracle.chunk_output(sl["x"], sl["dt"], sl["A"], sl["Bm"], sl["C"], H_in, S)
+    o = oracle.sma(sl["Q"], sl["E"], sl["C"], dH, S, tokens=tokens)
+    return dH[0, 0], H_in[0, 0], y_ssd[0, :, 0], o[0, :, 0], \
+        oracle.gated_output(y_ssd, o, gate)[0, :, 0]
+
+
+def test_config2_full_size_sampled_pairs():
+    """Prefill bf16 at the Mamba-2 ~370M layer shape (batch 4, 32 heads,
+    groups of 8 heads, L=8192, S=256, N=128, P=64), the configuration the
+    benchmark times; every output of three sampled (batch, head) pairs is
+    checked against the oracle."""
+    _need_gpu()
+    B, L, H, G, N, P, S, gate = 4, 8192, 32, 4, 128, 64, 256, 0.5
+    inp = synth.draw_prefill(0, B, L, H, G, N, P, io=torch.bfloat16)
+    d = _to_dev(inp)
+    out = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate, S)
+    torch.cuda.synchronize()
+    n = _np(inp)
+    for b, h in [(0, 0), (1, 13), (3, 31)]:
+        dH, H_in, y_ssd, o, y = _oracle_pair(n, b, h, H, G, S, gate)
+        io = torch.bfloat16
+        assert_parity(_pn_to_np(out["dH"][b, h]), dH, io, f"c2 dH b{b} h{h}")
+        assert_parity(_pn_to_np(out["H_in"][b, h]), H_in, io, f"c2 H_in b{b} h{h}")
+        assert_parity(out["y_ssd"][b, :, h], y_ssd, io, f"c2 y_ssd b{b} h{h}")
+        assert_parity(out["y"][b, :, h], y, io, f"c2 y b{b} h{h}")
+
+
+def test_config4_full_size_decode_sampled_pairs():
+    """Decode bf16: batch 64, 32 heads, N=128, P=64, S=256, 128 cached chunks
+    per sequence (4 GiB cache), one new token at the start of chunk 128; the
+    outputs of sampled sequences (all heads) against the oracle."""
+    _need_gpu()
+    B, H, N, P, S, mx = 64, 32, 128, 64, 256, 128
+    io = torch.bfloat16
+    st = api.new_decode_state(B, H, H, N, P, S, mx, io, DEV)
+    st["cache"].copy_(synth.draw_state(50, (B, H, mx, P, N), 0.01, io, device=DEV))
+    st["h"].copy_(synth.draw_state(51, (B, H, P, N), 0.01, torch.float32, device=DEV))
+    st["dH_cur"].copy_(synth.draw_state(52, (B, H, P, N), 0.01, torch.float32, device=DEV))
+    st["n_chunks"].fill_(mx)
+    samples = (0, 17, 63)
+    pre = {b: {"cache": _pn_to_np(st["cache"][b:b + 1]), "h": _pn_to_np(st["h"][b:b + 1]),
+               "dH_cur": _pn_to_np(st["dH_cur"][b:b + 1]), "n_chunks": np.array([mx]),
+               "pos": np.array([0])} for b in samples}
+    tok = synth.draw_decode_token(53, B, H, H, N, P, io=io)
+    d = _to_dev(tok)
+    y = api.decode_step(st, d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], 0.5)
+    torch.cuda.synchronize()
+    n = _np(tok)
+    for b in samples:
+        sl = {k: v[b:b + 1] for k, v in n.items() if k != "A"}
+        y_ref, new = oracle.decode_step(pre[b], sl["x"], sl["dt"], n["A"], sl["Bm"], sl["C"],
+                                        sl["Q"], sl["E"], 0.5, S)
+        assert_parity(y[b:b + 1], y_ref, io, f"c4 decode y b{b}")
+        assert_parity(_pn_to_np(st["h"][b:b + 1]), new["h"], io, f"c4 decode h b{b}")

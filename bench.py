@@ -1,0 +1,282 @@
+"""Benchmark of the DART hot path on one MI355X.
+
+A step is one prefill pass (chunk state memories -> state passing + native
+chunk output -> state-memory attention + gated add) over a batch of the
+Mamba-2 ~370M layer shape: batch 4, 32 heads, groups of 8 heads sharing
+B/C/Q, L = 8192, S = 256, N = 128, P = 64, bfloat16 inputs with fp32
+accumulation.  `value` is prefill tokens/s (batch·L / step time).  The
+decode step over a 4 GiB chunk-memory cache (batch 64, 32 heads, 128
+cached chunks) is timed in the same run and reported under "decode".
+
+Prints one JSON line.  `python bench.py --steps K --warmup W`.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+BASE = {"B": 4, "L": 8192, "H": 32, "G": 4, "N": 128, "P": 64, "S": 256, "gate": 0.5}
+DECODE = {"B": 64, "H": 32, "G": 32, "N": 128, "P": 64, "S": 256, "chunks": 128}
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+METRIC = "SMA+scan prefill tokens/s & MFMA% at L=8K; decode chunk-memory HBM GB/s"
+
+# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this
+# benchmark, calibrated against a 1 GiB copy (profiles/); valid only for the
+# kernel source they were measured on.
+KERNEL_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                             "ssm_state_attention_amd", "csrc", "k_sma.hip")
+PROFILED_TRAFFIC = {"source_sha1": "a88c4a6543c9c0fe81b3f7a2c6ad1b024ebdabfc",
+                    "k_sma_fwd": (1081.4 + 134.2) * 1e6,
+                    "k_sma_decode": (4431.4 + 134.5) * 1e6}
+
+
+def profiled_traffic(kernel):
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        if hashlib.sha1(f.read()).hexdigest() != PROFILED_TRAFFIC["source_sha1"]:
+            return None
+    return PROFILED_TRAFFIC[kernel]
+
+
+def sma_flops(c):
+    """Algorithmic SMA FLOPs: 4·N·P per visible (token, memory) pair (two
+    N x P contractions per pair), S·M(M-1)/2 pairs per (batch, head)."""
+    M = c["L"] // c["S"]
+    return 4.0 * c["N"] * c["P"] * c["S"] * M * (M - 1) / 2 * c["B"] * c["H"]
+
+
+def scan_flops(c):
+    """Algorithmic chunked-scan FLOPs: chunk states 2·S·N·P per chunk;
+    chunk output S(S+1)/2·P (intra) + S·N·P (inter) MACs per chunk and head,
+    plus the C·Bᵀ products S(S+1)/2·N per chunk and group."""
+    M = c["L"] // c["S"]
+    S, N, P = c["S"], c["N"], c["P"]
+    per_head = 2 * M * (S * (S + 1) / 2 * P + 2 * S * N * P)
+    per_group = 2 * M * S * (S + 1) / 2 * N
+    return (per_head * c["H"] + per_group * c["G"]) * c["B"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run one plain 1 GiB device-to-device copy, the reference "
+                         "kernel that HBM byte counters are calibrated against")
+    return ap.parse_args()
+
+
+def bench_prefill(args, torch, api, synth):
+    c = BASE
+    inp = synth.draw_prefill(0, c["B"], c["L"], c["H"], c["G"], c["N"], c["P"],
+                             io=torch.bfloat16)
+    d = {k: v.to("cuda:0") for k, v in inp.items()}
+    B, L, H, N, P, S = c["B"], c["L"], c["H"], c["N"], c["P"], c["S"]
+    M = L // S
+    f32 = dict(dtype=torch.float32, device="cuda:0")
+    out = {
+        "acum": torch.empty(B, H, M, S, **f32),
+        "dH": torch.empty(B, H, M, P, N, dtype=torch.bfloat16, device="cuda:0"),
+        "dH_f32": torch.empty(B, H, M, P, N, **f32),
+        "H_in": torch.empty(B, H, M + 1, P, N, **f32),
+        "y_ssd": torch.empty(B, L, H, P, **f32),
+        "y": torch.empty(B, L, H, P, dtype=torch.bfloat16, device="cuda:0"),
+    }
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        api.dart_chunk_state(d["x"], d["dt"], d["A"], d["Bm"], out["acum"], out["dH"],
+                             out["dH_f32"], S)
+        if ev:
+            ev[1].record()
+        api.dart_state_pass(d["x"], d["dt"], d["Bm"], d["C"], out["acum"], out["dH_f32"], None,
+                            out["H_in"], out["y_ssd"], S)
+        if ev:
+            ev[2].record()
+        api.dart_sma_fwd(d["Q"], d["E"], d["C"], out["dH"], out["y_ssd"], c["gate"], out["y"], S)
+        if ev:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    split = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(3)]
+    flops_sma, flops_scan = sma_flops(c), scan_flops(c)
+    sma_ms = split[2]
+    return {
+        "ms_per_step": ms,
+        "tokens_per_s": B * L / (ms / 1e3),
+        "kernel_ms": {"chunk_state": split[0], "state_pass+chunk_out": split[1],
+                      "sma_fwd": sma_ms},
+        "flops": {"sma": flops_sma, "scan": flops_scan},
+        "roofline": {
+            "kernel": "k_sma_fwd",
+            "bound": "mfma",
+            "achieved": flops_sma / (sma_ms / 1e3) / 1e12,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": flops_sma / (sma_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+            "traffic": profiled_traffic("k_sma_fwd"),
+        },
+        "mfma_frac_whole_prefill": (flops_sma + flops_scan) / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+        "inputs": inp,
+    }
+
+
+def bench_decode(args, torch, api, synth):
+    c = DECODE
+    B, H, G, N, P, S, k = c["B"], c["H"], c["G"], c["N"], c["P"], c["S"], c["chunks"]
+    st = api.new_decode_state(B, H, G, N, P, S, k, torch.bfloat16, "cuda:0")
+    st["cache"].copy_(synth.draw_state(50, (B, H, k, P, N), 0.01, torch.bfloat16,
+                                       device="cuda:0"))
+    st["h"].copy_(synth.draw_state(51, (B, H, P, N), 0.01, torch.float32, device="cuda:0"))
+    st["n_chunks"].fill_(k)
+    tok = {kk: v.to("cuda:0") for kk, v in
+           synth.draw_decode_token(53, B, H, G, N, P, io=torch.bfloat16).items()}
+    y = torch.empty(B, H, P, dtype=torch.bfloat16, device="cuda:0")
+
+    def step():
+        api.decode_step(st, tok["x"], tok["dt"], tok["A"], tok["Bm"], tok["C"], tok["Q"],
+                        tok["E"], 0.5, y=y)
+
+    steps = max(1, min(args.steps, S - 2))  # stay inside one chunk: no append in the loop
+    warm = max(0, min(args.warmup, S - 2 - steps))
+    for _ in range(warm):
+        step()
+    st["pos"].zero_()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    cache_bytes = B * H * k * N * P * 2
+    state_bytes = 2 * 2 * B * H * N * P * 4  # h and dH_cur read + written
+    gbs = cache_bytes / (ms / 1e3) / 1e9
+    return {
+        "metric": "decode chunk-memory HBM GB/s",
+        "value": gbs,
+        "unit": "GB/s",
+        "ms_per_step": ms,
+        "steps": steps,
+        "chunk_memory_bytes": cache_bytes,
+        "total_bytes_incl_state": cache_bytes + state_bytes,
+        "total_GBps_incl_state": (cache_bytes + state_bytes) / (ms / 1e3) / 1e9,
+        "config": {"workload": "DART decode over the chunk-memory cache", "batch": B,
+                   "heads": H, "dstate": N, "headdim": P, "chunk": S, "cached_chunks": k,
+                   "io": "bf16"},
+        "roofline": {"kernel": "k_sma_decode", "bound": "hbm", "achieved": gbs,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                     "traffic": profiled_traffic("k_sma_decode")},
+    }
+
+
+def cpu_baseline(inp, seconds):
+    """The fp64 oracle, unmodified, on whole (batch, head) pairs of the same
+    workload until about `seconds` of CPU time; the full-layer rate follows
+    from the time per pair (every pair is the same amount of work)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from ssm_state_attention_amd import synth
+
+    c = BASE
+    H, G, S, L = c["H"], c["G"], c["S"], c["L"]
+    pairs = [(b, h) for b in range(c["B"]) for h in range(H)]
+    pairs = pairs[::7] + [p for p in pairs if p not in pairs[::7]]
+    done, t_total = 0, 0.0
+    with threadpool_limits(limits=1):
+        for b, h in pairs:
+            g = h // (H // G)
+            sl = {k: synth.as_f64(inp[k][b:b + 1, :, h:h + 1]) for k in ("x", "dt", "E")}
+            for k in ("Bm", "C", "Q"):
+                sl[k] = synth.as_f64(inp[k][b:b + 1, :, g:g + 1])
+            A = synth.as_f64(inp["A"][h:h + 1])
+            t0 = time.perf_counter()
+            oracle.prefill(sl["x"], sl["dt"], A, sl["Bm"], sl["C"], sl["Q"], sl["E"],
+                           c["gate"], S)
+            t_total += time.perf_counter() - t0
+            done += 1
+            if t_total >= seconds:
+                break
+    per_pair = t_total / done
+    return {
+        "value": L / (per_pair * H),
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} of {len(pairs)} (batch, head) pairs of the L=8192 layer, whole "
+                  f"sequence each, {t_total:.1f} s; full-layer tokens/s = L / (time per pair "
+                  f"x 32 heads); BLAS and numpy limited to 1 thread; host has "
+                  f"{os.cpu_count()} logical CPUs",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: the DART hot path here is a single-GPU "
+              "build (every (batch, head) pair is independent; no multi-GPU path exists). "
+              "Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from ssm_state_attention_amd import api, synth
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    result = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, BASE recipe)",
+              "config": {"workload": "DART prefill at the Mamba-2 ~370M layer shape",
+                         "batch": BASE["B"], "seqlen": BASE["L"], "heads": BASE["H"],
+                         "groups": BASE["G"], "dstate": BASE["N"], "headdim": BASE["P"],
+                         "chunk": BASE["S"], "io": "bf16", "accumulate": "fp32",
+                         "parallelism": "single GPU"}}
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    pre = None
+    if not args.no_prefill:
+        pre = bench_prefill(args, torch, api, synth)
+        result["value"] = pre["tokens_per_s"]
+        result["ms_per_step"] = pre["ms_per_step"]
+        result["roofline"] = pre["roofline"]
+        result["kernel_ms"] = pre["kernel_ms"]
+        result["mfma_frac_whole_prefill"] = pre["mfma_frac_whole_prefill"]
+        result["algorithmic_gflop_per_step"] = {k: v / 1e9 for k, v in pre["flops"].items()}
+    if not args.no_decode:
+        torch.cuda.empty_cache()
+        result["decode"] = bench_decode(args, torch, api, synth)
+    if not args.no_cpu_baseline and pre is not None:
+        result["cpu_baseline"] = cpu_baseline(pre["inputs"], args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -62,30 +62,48 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
   }
   __syncthreads();
 
-  // 2. dH = Bᵀ (w∘x) over K-blocks of kKB tokens
+  // 2. dH = Bᵀ (w∘x) over K-blocks of kKB tokens; the global loads of block
+  //    i+1 are in flight while the MFMAs of block i run
+  typedef typename Vec16<T>::vec vec_t;
+  constexpr int XV = kKB * (P / VE) / kThreads;  // vectors per thread per block
+  constexpr int BV = kKB * (N / VE) / kThreads;
+  static_assert(XV * kThreads == kKB * (P / VE) && BV * kThreads == kKB * (N / VE),
+                "k_chunk_state staging split");
+  vec_t xr[XV], br[BV];
+  auto fetch = [&](int s0) {
+#pragma unroll
+    for (int v = 0; v < XV; ++v) {
+      const int i = tid + v * kThreads, s = i % kKB, pv = i / kKB;
+      xr[v] = s0 + s < S ? load16(x + ((tok0 + s0 + s) * H + h) * P + pv * VE) : vec_t{};
+    }
+#pragma unroll
+    for (int v = 0; v < BV; ++v) {
+      const int i = tid + v * kThreads, s = i % kKB, nv = i / kKB;
+      br[v] = s0 + s < S ? load16(Bm + ((tok0 + s0 + s) * G + g) * N + nv * VE) : vec_t{};
+    }
+  };
   floatx4 accv[TPW];
 #pragma unroll
   for (int j = 0; j < TPW; ++j) accv[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  fetch(0);
   for (int s0 = 0; s0 < S; s0 += kKB) {
-    for (int i = tid; i < kKB * (P / VE); i += kThreads) {
-      const int s = i % kKB, pv = i / kKB;
-      typename Vec16<T>::vec raw = {};
-      float wv = 0.f;
-      if (s0 + s < S) {
-        raw = load16(x + ((tok0 + s0 + s) * H + h) * P + pv * VE);
-        wv = sh_w[s0 + s];
-      }
+    // lanes take consecutive tokens, so the transposed LDS writes of one row
+    // are contiguous
 #pragma unroll
-      for (int e = 0; e < VE; ++e) sh_xt[(pv * VE + e) * LDK + s] = from_f32<T>(to_f32(raw[e]) * wv);
+    for (int v = 0; v < XV; ++v) {
+      const int i = tid + v * kThreads, s = i % kKB, pv = i / kKB;
+      const float wv = s0 + s < S ? sh_w[s0 + s] : 0.f;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) sh_xt[(pv * VE + e) * LDK + s] = from_f32<T>(to_f32(xr[v][e]) * wv);
     }
-    for (int i = tid; i < kKB * (N / VE); i += kThreads) {
-      const int s = i % kKB, nv = i / kKB;
-      typename Vec16<T>::vec raw = {};
-      if (s0 + s < S) raw = load16(Bm + ((tok0 + s0 + s) * G + g) * N + nv * VE);
 #pragma unroll
-      for (int e = 0; e < VE; ++e) sh_bt[(nv * VE + e) * LDK + s] = raw[e];
+    for (int v = 0; v < BV; ++v) {
+      const int i = tid + v * kThreads, s = i % kKB, nv = i / kKB;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) sh_bt[(nv * VE + e) * LDK + s] = br[v][e];
     }
     __syncthreads();
+    if (s0 + kKB < S) fetch(s0 + kKB);
 #pragma unroll
     for (int ks = 0; ks < kKB; ks += K) {
 #pragma unroll
@@ -139,8 +157,23 @@ __global__ __launch_bounds__(kThreads) void k_state_pass(
   }
 }
 
-// One workgroup per (chunk k, head, batch); each wave owns 16-token blocks.
-// Per token block, in transposed form (rows p, columns = tokens t):
+constexpr int kOutThreads = 512;  // 8 waves, two per SIMD
+
+// LDS footprint of k_chunk_out when B_k is staged too; above the budget the
+// B fragments are read from global memory (L2) instead
+template <typename T, int N, int P>
+struct ChunkOutLds {
+  static constexpr int VE = Vec16<T>::n;
+  static constexpr size_t common =
+      (size_t(P) * (kMaxChunk + VE) + size_t(P) * (N + VE)) * sizeof(T) + 2 * kMaxChunk * 4;
+  static constexpr size_t with_b = common + size_t(kMaxChunk) * (N + VE) * sizeof(T);
+  static constexpr bool stage_b = with_b <= 150 * 1024;
+};
+
+// One workgroup per (chunk k, head, batch).  The 16-token blocks of the chunk
+// are dealt to the 8 waves in zigzag order (0..7, 7..0, ...), so the causal
+// work (block tb costs tb+1 blocks of keys) is balanced.  Per token block, in
+// transposed form (rows p, columns = tokens t):
 //   inter: Yᵀ += H_in[k]ᵀ C_tᵀ                     (K = n), scaled by exp(acum_t)
 //   intra: Gᵀ[j][t] = B_j·C_t (K = n), masked to j <= t, times
 //          exp(acum_t - acum_j)·dt_j, then Yᵀ += xᵀ Gᵀ  (K = j)
@@ -148,18 +181,26 @@ __global__ __launch_bounds__(kThreads) void k_state_pass(
 // j = 16·jb + 4·grp + i of column t) is used directly as the B operand of the
 // second product, with the k-slots of xᵀ's A operand assigned the same j's.
 template <typename T, int N, int P>
-__global__ __launch_bounds__(kThreads) void k_chunk_out(
+__global__ __launch_bounds__(kOutThreads) void k_chunk_out(
     const T* __restrict__ x, const float* __restrict__ dt, const T* __restrict__ Bm,
     const T* __restrict__ C, const float* __restrict__ acum, const float* __restrict__ H_in,
     float* __restrict__ y_ssd, int L, int H, int G, int S) {
   using MM = Mma<T>;
+  using Lds = ChunkOutLds<T, N, P>;
   constexpr int K = MM::K, KL = MM::KL;
   constexpr int VE = Vec16<T>::n;
   constexpr int LDX = kMaxChunk + VE;  // xᵀ rows [p][j]
   constexpr int LDH = N + VE;          // H_inᵀ rows [p][n]
-  __shared__ float sh_acum[kMaxChunk], sh_dt[kMaxChunk];
+  constexpr int LDB = N + VE;          // B rows [j][n]
+  constexpr int NW = kOutThreads / 64;
+  // per token s of the chunk: at[s] = acum_s·log2(e) and
+  // bj[s] = log2(dt_s) - acum_s·log2(e), so that the intra-chunk weight of
+  // (t, j) is exp2(at[t] + bj[j]) = exp(acum_t - acum_j)·dt_j
+  __shared__ __align__(16) float sh_at[kMaxChunk];
+  __shared__ __align__(16) float sh_bj[kMaxChunk];
   __shared__ __align__(16) T sh_xt[P * LDX];
   __shared__ __align__(16) T sh_ht[P * LDH];
+  __shared__ __align__(16) T sh_b[Lds::stage_b ? kMaxChunk * LDB : 1];
 
   const int k = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int M = L / S, g = h / (H / G);
@@ -168,26 +209,89 @@ __global__ __launch_bounds__(kThreads) void k_chunk_out(
   const long tok0 = (long)b * L + (long)k * S;
   const long pair = (long)b * H + h;
 
-  for (int s = tid; s < S; s += kThreads) {
-    sh_acum[s] = acum[(pair * M + k) * S + s];
-    sh_dt[s] = dt[(tok0 + s) * H + h];
-  }
-  for (int i = tid; i < S * (P / VE); i += kThreads) {
-    const int s = i % S, pv = i / S;
-    const auto raw = load16(x + ((tok0 + s) * H + h) * P + pv * VE);
-#pragma unroll
-    for (int e = 0; e < VE; ++e) sh_xt[(pv * VE + e) * LDX + s] = raw[e];
-  }
+  // Staging: every global load of the chunk is issued before any LDS write
+  // (fixed per-thread maxima, predicated on the runtime chunk size), so the
+  // workgroup pays one memory round trip instead of one per loop trip.
+  typedef typename Vec16<T>::vec vec_t;
+  constexpr int XV = (kMaxChunk * (P / VE) + kOutThreads - 1) / kOutThreads;
+  constexpr int BV = Lds::stage_b ? (kMaxChunk * (N / VE) + kOutThreads - 1) / kOutThreads : 0;
+  constexpr int HV = (P * N / 4 + kOutThreads - 1) / kOutThreads;
+  vec_t xr[XV], br[BV > 0 ? BV : 1];
+  floatx4 hr[HV];
+  float ar = 0.f, dr = 1.f;
   const float* hsrc = H_in + (pair * (M + 1) + k) * (long)(P * N);
-  for (int i = tid; i < P * N / 4; i += kThreads) {
-    const floatx4 f = reinterpret_cast<const floatx4*>(hsrc)[i];
-    const int p = (i * 4) / N, n = (i * 4) % N;
+  if (tid < S) {
+    ar = acum[(pair * M + k) * S + tid];
+    dr = dt[(tok0 + tid) * H + h];
+  }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sh_ht[p * LDH + n + e] = from_f32<T>(f[e]);
+  for (int v = 0; v < XV; ++v) {
+    const int i = tid + v * kOutThreads;
+    if (i < S * (P / VE)) {
+      const int s = i % S, pv = i / S;
+      xr[v] = load16(x + ((tok0 + s) * H + h) * P + pv * VE);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < BV; ++v) {
+    const int i = tid + v * kOutThreads;
+    if (i < S * (N / VE)) {
+      const int s = i / (N / VE), nv = i % (N / VE);
+      br[v] = load16(Bm + ((tok0 + s) * G + g) * N + nv * VE);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < HV; ++v) {
+    const int i = tid + v * kOutThreads;
+    if (i < P * N / 4) hr[v] = reinterpret_cast<const floatx4*>(hsrc)[i];
+  }
+  if (tid < S) {
+    const float a2 = ar * kLog2e;
+    sh_at[tid] = a2;
+    sh_bj[tid] = __builtin_amdgcn_logf(dr) - a2;
+  }
+#pragma unroll
+  for (int v = 0; v < XV; ++v) {
+    const int i = tid + v * kOutThreads;
+    if (i < S * (P / VE)) {
+      const int s = i % S, pv = i / S;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) sh_xt[(pv * VE + e) * LDX + s] = xr[v][e];
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < BV; ++v) {
+    const int i = tid + v * kOutThreads;
+    if (i < S * (N / VE)) {
+      const int s = i / (N / VE), nv = i % (N / VE);
+      *reinterpret_cast<vec_t*>(&sh_b[s * LDB + nv * VE]) = br[v];
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < HV; ++v) {
+    const int i = tid + v * kOutThreads;
+    if (i < P * N / 4) {
+      const int p = (i * 4) / N, n = (i * 4) % N;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sh_ht[p * LDH + n + e] = from_f32<T>(hr[v][e]);
+    }
   }
   __syncthreads();
 
-  for (int tb = w; tb < S / 16; tb += 4) {
+  // A-operand fragment of B rows j = jb*16 + col at k-step kk
+  auto b_frag = [&](int jb, int kk) {
+    if constexpr (Lds::stage_b)
+      return MM::load(&sh_b[(jb * 16 + col) * LDB + kk * K + grp * KL]);
+    else
+      return MM::load(Bm + ((tok0 + jb * 16 + col) * G + g) * N + kk * K + grp * KL);
+  };
+
+  const int nblk = S / 16;
+  for (int i = 0; i < nblk; ++i) {
+    const int round = i / NW;
+    const int owner = (round & 1) ? NW - 1 - (i % NW) : (i % NW);
+    if (owner != w) continue;
+    const int tb = i;
     const int t = tb * 16 + col;  // this lane's token inside the chunk
     typename MM::frag cf[N / K];
 #pragma unroll
@@ -205,45 +309,48 @@ __global__ __launch_bounds__(kThreads) void k_chunk_out(
       for (int kk = 0; kk < N / K; ++kk)
         yin[pb] = MM::mma(MM::load(&sh_ht[(pb * 16 + col) * LDH + kk * K + grp * KL]), cf[kk],
                           yin[pb]);
-    const float ac_t = sh_acum[t];
+    const float at_t = sh_at[t];
+    // weights of one 16x16 Gᵀ tile (rows j = jb*16 + 4*grp + i, column t):
+    // branch-free; entries above the diagonal are selected away (their
+    // exponent may overflow, the select discards it)
+    auto weights = [&](int jb, floatx4 gt) {
+      const floatx4 bj = *reinterpret_cast<const floatx4*>(&sh_bj[jb * 16 + 4 * grp]);
+      floatx4 wv;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float wgt = gt[i4] * exp2_fast(at_t + bj[i4]);
+        wv[i4] = (jb * 16 + 4 * grp + i4 <= t) ? wgt : 0.f;
+      }
+      return wv;
+    };
     if constexpr (std::is_same<T, float>::value) {
       for (int jb = 0; jb <= tb; ++jb) {
         floatx4 gt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < N / K; ++kk)
-          gt = MM::mma(MM::load(Bm + ((tok0 + jb * 16 + col) * G + g) * N + kk * K + grp * KL),
-                       cf[kk], gt);
+        for (int kk = 0; kk < N / K; ++kk) gt = MM::mma(b_frag(jb, kk), cf[kk], gt);
+        const floatx4 wv = weights(jb, gt);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = jb * 16 + 4 * grp + i;
-          const float wgt = j <= t ? gt[i] * exp_neg(ac_t - sh_acum[j]) * sh_dt[j] : 0.f;
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int j = jb * 16 + 4 * grp + i4;
 #pragma unroll
           for (int pb = 0; pb < P / 16; ++pb)
-            yia[pb] = MM::mma(sh_xt[(pb * 16 + col) * LDX + j], wgt, yia[pb]);
+            yia[pb] = MM::mma(sh_xt[(pb * 16 + col) * LDX + j], wv[i4], yia[pb]);
         }
       }
     } else {
       // S % 32 == 0, so the pair (jb0, jb0 + 1) never leaves the chunk
       for (int jb0 = 0; jb0 <= tb; jb0 += 2) {
-        bf16x8 bfr;
+        floatx4 gt0 = {0.f, 0.f, 0.f, 0.f}, gt1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int jb = jb0 + q;
-          floatx4 gt = {0.f, 0.f, 0.f, 0.f};
-          if (jb <= tb) {
+        for (int kk = 0; kk < N / K; ++kk) gt0 = MM::mma(b_frag(jb0, kk), cf[kk], gt0);
+        if (jb0 + 1 <= tb) {
 #pragma unroll
-            for (int kk = 0; kk < N / K; ++kk)
-              gt = MM::mma(
-                  MM::load(Bm + ((tok0 + jb * 16 + col) * G + g) * N + kk * K + grp * KL),
-                  cf[kk], gt);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = jb * 16 + 4 * grp + i;
-            const float wgt = j <= t ? gt[i] * exp_neg(ac_t - sh_acum[j]) * sh_dt[j] : 0.f;
-            bfr[4 * q + i] = from_f32<bf16>(wgt);
-          }
+          for (int kk = 0; kk < N / K; ++kk) gt1 = MM::mma(b_frag(jb0 + 1, kk), cf[kk], gt1);
         }
+        const floatx4 w0 = weights(jb0, gt0), w1 = weights(jb0 + 1, gt1);
+        const bf16x8 bfr = {from_f32<bf16>(w0[0]), from_f32<bf16>(w0[1]), from_f32<bf16>(w0[2]),
+                            from_f32<bf16>(w0[3]), from_f32<bf16>(w1[0]), from_f32<bf16>(w1[1]),
+                            from_f32<bf16>(w1[2]), from_f32<bf16>(w1[3])};
 #pragma unroll
         for (int pb = 0; pb < P / 16; ++pb) {
           const bf16* row = &sh_xt[(pb * 16 + col) * LDX];
@@ -254,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_out(
         }
       }
     }
-    const float dec_t = exp_neg(ac_t);
+    const float dec_t = exp2_fast(at_t);
 #pragma unroll
     for (int pb = 0; pb < P / 16; ++pb)
       store4(y_ssd + ((tok0 + t) * H + h) * P + pb * 16 + 4 * grp, yia[pb] + dec_t * yin[pb]);
@@ -282,7 +389,7 @@ hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt,
                      dim3(kThreads), 0, st, acum, dH_f32, h0, H_in, s.H, M, s.S, PN);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_chunk_out<T, N, P>), dim3(M, s.H, s.B), dim3(kThreads), 0, st, x, dt, Bm,
+  hipLaunchKernelGGL((k_chunk_out<T, N, P>), dim3(M, s.H, s.B), dim3(kOutThreads), 0, st, x, dt, Bm,
                      C, acum, H_in, y_ssd, s.L, s.H, s.G, s.S);
   return hipGetLastError();
 }

@@ -25,18 +25,38 @@ struct SmaTile {
   static constexpr int NTB = (N * P >= 128 * 128) ? 1 : 2;
 };
 
+// (batch, head) pairs per ordering group of one XCD (see k_sma_fwd)
+constexpr int kPairsPerGroup = 4;
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// Sum of v over lanes l and l^16, then over l and l^32 (gfx950 permlane
+// swaps: no LDS round trip).
+__device__ __forceinline__ float sum_lane_groups(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const unsigned u2 = __float_as_uint(v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
 // Prefill SMA.  One workgroup = WAVES waves × 16·NTB tokens of ONE chunk k,
 // so every token of the workgroup sees the same memories c < k (no mask).
-// Per memory c: dH[c]ᵀ (P x N, value-axis-major in HBM) is staged into LDS
-// (double-buffered, one barrier per memory); each wave multiplies it with
-// its resident [Q; C] fragments (16x16 MFMA, rows p, columns = tokens),
-// finishes the score with an in-lane dot against E_t plus two lane-group
-// exchanges, and folds the value into an online softmax.
+// Per memory c, dH[c]ᵀ (P x N, value-axis-major in HBM) is staged in LDS
+// (two buffers, one barrier per memory; each memory is fetched into
+// registers two steps before it is written to LDS).  Each wave multiplies
+// it with its resident [Q; C] fragments (16x16 MFMA, rows p, columns =
+// tokens), finishes the score with an in-lane dot against E_t plus two
+// lane-group exchanges, and folds the value into an online softmax.
 //
 // Grid mapping: workgroups are dealt to the 8 XCDs round-robin, so
 // blockIdx % 8 selects an XCD and all tiles of one (batch, head) pair land
-// on the same XCD (its memories stay in that XCD's L2).  Within an XCD the
-// tiles run heaviest first (largest k), which bounds the tail.
+// on the same XCD.  Inside an XCD the pairs are taken kPairsPerGroup at a
+// time, heaviest tiles (largest k) first within each group: the memories of
+// a group (4 x 512 KB at the largest shape) stay resident in the XCD's
+// 4 MB L2 while the k-ordering keeps the tail short.
 template <typename T, int N, int P, int NTB, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     const T* __restrict__ Q, const T* __restrict__ E, const T* __restrict__ C,
@@ -50,16 +70,20 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   constexpr int NTHR = 64 * WAVES;
   constexpr int VPT = (NVEC + NTHR - 1) / NTHR;
   constexpr int NPB = P / 16, NKK = N / K;
+  constexpr int GP = kPairsPerGroup;
   typedef typename Vec16<T>::vec vec_t;
   __shared__ __align__(16) T sh_mem[2][P * LDN];
 
   const int M = L / S, tpc = S / TWG;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int sub = slot % tpc, r = slot / tpc;
-  const int ql = r % npq, kr = r / npq;
+  const int per_group = GP * M * tpc;
+  const int grp_i = slot / per_group, rem = slot % per_group;
+  const int sub = rem % tpc, r = rem / tpc;
+  const int qg = r % GP, kr = r / GP;
+  const int ql = grp_i * GP + qg;
   const int k = M - 1 - kr;
   const int pair = ql * 8 + xcd;
-  if (pair >= BH || k < 0) return;  // uniform over the workgroup
+  if (pair >= BH || ql >= npq) return;  // uniform over the workgroup
   const int b = pair / H, h = pair % H, g = h / (H / G);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -93,34 +117,27 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   }
 
   const T* mem = dH + (long)pair * M * (P * N);
-  vec_t stg[VPT];
-  auto gload = [&](int c) {
+  vec_t stg0[VPT], stg1[VPT];
+  auto gload = [&](int c, vec_t (&stg)[VPT]) {
     const vec_t* src = reinterpret_cast<const vec_t*>(mem + (long)c * (P * N));
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
       const int vi = tid + v * NTHR;
-      if (vi < NVEC) stg[v] = src[vi];
+      if (NVEC % NTHR == 0 || vi < NVEC) stg[v] = src[vi];
     }
   };
-  auto swrite = [&](int buf) {
+  auto swrite = [&](int buf, vec_t (&stg)[VPT]) {
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
       const int vi = tid + v * NTHR;
-      if (vi < NVEC) {
+      if (NVEC % NTHR == 0 || vi < NVEC) {
         const int p = vi / (N / VE), nv = vi % (N / VE);
         *reinterpret_cast<vec_t*>(&sh_mem[buf][p * LDN + nv * VE]) = stg[v];
       }
     }
   };
-
-  if (k > 0) {
-    gload(0);
-    swrite(0);
-  }
-  __syncthreads();
-  for (int c = 0; c < k; ++c) {
-    const int cur = c & 1;
-    if (c + 1 < k) gload(c + 1);
+  // MFMAs and online softmax of the memory in LDS buffer `cur`
+  auto compute = [&](int cur) {
     floatx4 zq[NTB][NPB], zc[NTB][NPB];
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb)
@@ -130,16 +147,19 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
         zc[tb][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-    for (int pb = 0; pb < NPB; ++pb)
+    for (int pb = 0; pb < NPB; ++pb) {
+      typename MM::frag a[NKK];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const auto a = MM::load(&sh_mem[cur][(pb * 16 + col) * LDN + kk * K + grp * KL]);
+      for (int kk = 0; kk < NKK; ++kk)
+        a[kk] = MM::load(&sh_mem[cur][(pb * 16 + col) * LDN + kk * K + grp * KL]);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
-          zq[tb][pb] = MM::mma(a, qf[tb][kk], zq[tb][pb]);
-          zc[tb][pb] = MM::mma(a, cf[tb][kk], zc[tb][pb]);
+          zq[tb][pb] = MM::mma(a[kk], qf[tb][kk], zq[tb][pb]);
+          zc[tb][pb] = MM::mma(a[kk], cf[tb][kk], zc[tb][pb]);
         }
-      }
+    }
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
       float s = 0.f;
@@ -147,19 +167,34 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
       for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) s += zq[tb][pb][i] * ev[tb][pb][i];
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      s *= scale_log2;
+      s = sum_lane_groups(s) * scale_log2;
       const float mn = fmaxf(mx[tb], s);
-      const float al = exp2_fast(mx[tb] - mn);
+      const float al = exp2_fast(mx[tb] - mn);  // 0 for the first memory
       const float pw = exp2_fast(s - mn);
       ls[tb] = ls[tb] * al + pw;
 #pragma unroll
       for (int pb = 0; pb < NPB; ++pb) acc[tb][pb] = acc[tb][pb] * al + pw * zc[tb][pb];
       mx[tb] = mn;
     }
-    if (c + 1 < k) swrite(cur ^ 1);
+  };
+  // step c: memory c is in buffer PAR, memory c+1 in registers stg_n;
+  // fetch memory c+2 into stg_c (its previous content, memory c, is in LDS)
+  auto iter = [&](int c, auto par_tag, vec_t (&stg_c)[VPT], vec_t (&stg_n)[VPT]) {
+    constexpr int PAR = decltype(par_tag)::value;
+    if (c + 2 < k) gload(c + 2, stg_c);
+    compute(PAR);
+    if (c + 1 < k) swrite(PAR ^ 1, stg_n);
     __syncthreads();
+  };
+  if (k > 0) {
+    gload(0, stg0);
+    swrite(0, stg0);
+    if (k > 1) gload(1, stg1);
+    __syncthreads();
+    for (int c = 0; c < k; c += 2) {
+      iter(c, IC<0>{}, stg0, stg1);
+      if (c + 1 < k) iter(c + 1, IC<1>{}, stg1, stg0);
+    }
   }
 
 #pragma unroll
@@ -388,7 +423,8 @@ hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T*
   const int BH = s.B * s.H;
   const int npq = (BH + 7) / 8;  // (batch, head) pairs per XCD
   const int tpc = s.S / (16 * NTB * WAVES);
-  const long blocks = 8L * npq * M * tpc;
+  const int ngrp = (npq + kPairsPerGroup - 1) / kPairsPerGroup;
+  const long blocks = 8L * ngrp * kPairsPerGroup * M * tpc;
   const float scale_log2 = kLog2e / sqrtf(static_cast<float>(N));
   hipLaunchKernelGGL((k_sma_fwd<T, N, P, NTB, WAVES>), dim3(blocks), dim3(64 * WAVES), 0, st, Q,
                      E, C, dH, y_ssd, gate, y, BH, s.L, s.H, s.G, s.S, npq, scale_log2);

@@ -1,0 +1,197 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/dart.h declares, and rejects bad arguments on the host before any
+HIP call (error paths only; no compute call is made here)."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+import torch
+
+import ssm_state_attention_amd as dart
+from ssm_state_attention_amd import _lib, api
+from ssm_state_attention_amd._lib import DartDecodeDims, DartDims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dart.h")
+
+OK, NULLP, BAD, UNSUP, DTYPE, WS, HIP, ALIGN = range(8)
+F32, BF16 = 0, 1
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\*\s]+?)\b(dart_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("dart_chunk_state", "dart_state_pass", "dart_sma_fwd", "dart_sma_decode"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    lib = dart.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libdart.so does not export {name}"
+    if shutil.which("nm"):
+        out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
+                             capture_output=True, text=True, check=True).stdout
+        exported = set(re.findall(r"\bT (dart_\w+)", out))
+        assert set(declared_functions()) <= exported
+
+
+def test_status_strings():
+    lib = dart.lib()
+    for code in range(8):
+        s = lib.dart_status_str(code).decode()
+        assert s.startswith("DART_") and s == s.strip()
+    assert lib.dart_status_str(99).decode() == "DART_ERR_UNKNOWN"
+
+
+def dims(B=1, L=1024, H=1, G=1, N=16, P=16, S=64, io=F32):
+    return DartDims(B, L, H, G, N, P, S, io)
+
+
+@pytest.mark.parametrize("d", [
+    dims(),                                         # tiny fp32 layer
+    dims(1, 4096, 8, 8, 128, 64, 256, BF16),        # L=4K bf16 prefill
+    dims(4, 8192, 32, 4, 128, 64, 256, BF16),       # ~370M layer shape
+    dims(1, 65536, 32, 32, 128, 64, 256, BF16),     # long context
+    dims(2, 96, 3, 3, 32, 32, 96, F32),
+    dims(1, 512, 2, 2, 128, 128, 256, BF16),
+])
+def test_validate_accepts(d):
+    assert dart.lib().dart_validate_dims(d) == OK
+
+
+@pytest.mark.parametrize("d,code", [
+    (dims(B=0), BAD), (dims(L=-64), BAD), (dims(H=0), BAD), (dims(S=0), BAD),
+    (dims(L=1000), BAD),                            # L % S != 0
+    (dims(H=3, G=2), BAD),                          # H % G != 0
+    (dims(N=16, P=32), UNSUP),                      # shape not compiled
+    (dims(N=16, P=16, io=BF16), UNSUP),             # bf16 needs N >= 32
+    (dims(S=48, L=960), UNSUP),                     # S % 32 != 0
+    (dims(S=512, L=1024), UNSUP),                   # S > 256
+    (dims(io=7), DTYPE),
+    (dims(B=70000, L=64, S=64), BAD),               # grid limit
+])
+def test_validate_rejects(d, code):
+    assert dart.lib().dart_validate_dims(d) == code
+
+
+def test_validate_null():
+    assert dart.lib().dart_validate_dims(None) == NULLP
+    assert dart.lib().dart_validate_decode_dims(None) == NULLP
+
+
+def ddims(B=64, H=32, G=32, N=128, P=64, S=256, mx=128, io=BF16):
+    return DartDecodeDims(B, H, G, N, P, S, mx, io)
+
+
+def test_decode_workspace():
+    lib = dart.lib()
+    for d in (ddims(), ddims(2, 4, 4, 128, 64, 256, 8), ddims(1, 1, 1, 16, 16, 64, 3, F32)):
+        assert lib.dart_validate_decode_dims(d) == OK
+        ws = api.dart_sma_decode_workspace(d)
+        assert ws > 0 and ws % 256 == 0
+    assert api.dart_sma_decode_workspace(ddims(mx=0)) == 0
+    assert lib.dart_validate_decode_dims(ddims(H=6, G=4)) == BAD
+    assert lib.dart_validate_decode_dims(ddims(N=96)) == UNSUP
+
+
+# Fake device addresses: never dereferenced, because every call below fails
+# host-side validation before any HIP call.
+A16 = 0x10000
+MIS = 0x10004
+
+
+def test_entry_points_reject_null_pointers():
+    lib = dart.lib()
+    d = dims()
+    p = [A16] * 7
+    for i in range(7):
+        q = list(p)
+        q[i] = None
+        assert lib.dart_chunk_state(d, *q, None) == NULLP
+    assert lib.dart_state_pass(d, A16, A16, A16, A16, A16, A16, None, A16, None, None) == NULLP
+    assert lib.dart_sma_fwd(d, A16, A16, None, A16, A16, 0.5, A16, None) == NULLP
+
+
+def test_entry_points_reject_misaligned_pointers():
+    lib = dart.lib()
+    d = dims()
+    assert lib.dart_chunk_state(d, A16, A16, A16, MIS, A16, A16, A16, None) == ALIGN
+    assert lib.dart_state_pass(d, A16, A16, A16, A16, A16, A16, MIS, A16, A16, None) == ALIGN
+    assert lib.dart_sma_fwd(d, A16, A16, A16, A16, A16, 0.5, MIS, None) == ALIGN
+
+
+def test_entry_points_reject_bad_dims_before_pointers():
+    lib = dart.lib()
+    assert lib.dart_sma_fwd(dims(L=1000), None, None, None, None, None, 0.5, None,
+                            None) == BAD
+    assert lib.dart_chunk_state(dims(N=16, P=32), *([A16] * 7), None) == UNSUP
+
+
+def test_decode_rejects_small_workspace():
+    lib = dart.lib()
+    d = ddims(2, 4, 4, 128, 64, 256, 8)
+    need = api.dart_sma_decode_workspace(d)
+    args = [A16] * 7
+    state = [A16] * 6
+    assert lib.dart_sma_decode(d, *args, 0.5, *state, A16, need - 256, None) == WS
+    assert lib.dart_sma_decode(d, *args, 0.5, *state, None, need, None) == WS
+    assert lib.dart_sma_decode(d, *args, 0.5, *state, MIS, need, None) == ALIGN
+
+
+def test_binding_checks_tensors_before_calling():
+    x = torch.zeros(1, 64, 1, 16)
+    with pytest.raises(ValueError, match="GPU"):
+        api.dart_chunk_state(x, torch.zeros(1, 64, 1), torch.zeros(1), torch.zeros(1, 64, 1, 16),
+                             torch.zeros(1, 1, 1, 64), torch.zeros(1, 1, 1, 16, 16),
+                             torch.zeros(1, 1, 1, 16, 16), 64)
+    with pytest.raises(TypeError):
+        api.prefill_dims(torch.zeros(1, 64, 1, 16, dtype=torch.float16),
+                         torch.zeros(1, 64, 1, 16), 64)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libdart.so"))
+    with pytest.raises(RuntimeError, match="must be built"):
+        _lib.lib()
+
+
+VALIDATE_DRIVER = r"""
+#include <stdio.h>
+#include "dart.h"
+int main(void) {
+  dart_dims d = {4, 8192, 32, 4, 128, 64, 256, DART_BF16};
+  int bad = 0;
+  bad |= dart_validate_dims(&d) != DART_OK;
+  d.seqlen = 8000; bad |= dart_validate_dims(&d) != DART_ERR_BAD_DIMS;
+  d.seqlen = 8192; d.dstate = 100; bad |= dart_validate_dims(&d) != DART_ERR_UNSUPPORTED;
+  dart_decode_dims dd = {64, 32, 32, 128, 64, 256, 128, DART_BF16};
+  bad |= dart_sma_decode_workspace(&dd) == 0;
+  for (int s = -1; s < 10; ++s) bad |= dart_status_str((dart_status)s) == 0;
+  printf("%s\n", bad ? "FAIL" : "OK");
+  return bad;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+def test_validators_under_host_sanitizers(tmp_path):
+    """The host validation code, built without HIP under ASan/UBSan."""
+    drv = tmp_path / "drv.c"
+    drv.write_text(VALIDATE_DRIVER)
+    exe = tmp_path / "drv"
+    csrc = os.path.join(ROOT, "ssm_state_attention_amd", "csrc")
+    subprocess.run(["g++", "-x", "c++", str(drv), "-x", "c++",
+                    os.path.join(csrc, "dart_validate.cpp"), "-I", os.path.join(ROOT, "include"),
+                    "-I", csrc, "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                    "-g", "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0 and out.stdout.strip() == "OK", out.stdout + out.stderr

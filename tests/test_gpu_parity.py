@@ -302,3 +302,35 @@ def test_config4_full_size_decode_sampled_pairs():
                                         sl["Q"], sl["E"], 0.5, S)
         assert_parity(y[b:b + 1], y_ref, io, f"c4 decode y b{b}")
         assert_parity(_pn_to_np(st["h"][b:b + 1]), new["h"], io, f"c4 decode h b{b}")
+
+
+def test_config3_long_context_sampled_tokens():
+    """Long-context prefill bf16 (batch 1, 32 heads, L=65536, S=256, N=128,
+    P=64: 256 chunk memories per head).  For three heads the oracle computes
+    every memory, the boundary states and y_ssd, and the SMA readout of 64
+    tokens spread over all chunk indices (first, middle and last chunks
+    included)."""
+    _need_gpu()
+    B, L, H, G, N, P, S, gate = 1, 65536, 32, 32, 128, 64, 256, 0.5
+    M = L // S
+    inp = synth.draw_prefill(3, B, L, H, G, N, P, io=torch.bfloat16)
+    d = _to_dev(inp)
+    out = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate, S)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    chunks = np.unique(np.concatenate([[0, 1, 2, M // 2, M - 2, M - 1],
+                                       rng.integers(0, M, 58)]))
+    tokens = np.sort(chunks * S + rng.integers(0, S, chunks.size))
+    io = torch.bfloat16
+    for h in (0, 17, 31):
+        sl = {k: synth.as_f64(v[:, :, h:h + 1]) for k, v in inp.items() if k != "A"}
+        A = synth.as_f64(inp["A"][h:h + 1])
+        dH = oracle.chunk_states(sl["x"], sl["dt"], A, sl["Bm"], S)
+        H_in = oracle.state_pass(dH, sl["dt"], A, S)
+        y_ssd = oracle.chunk_output(sl["x"], sl["dt"], A, sl["Bm"], sl["C"], H_in, S)
+        o = oracle.sma(sl["Q"], sl["E"], sl["C"], dH, S, tokens=tokens)
+        y = oracle.gated_output(y_ssd, o, gate)
+        assert_parity(_pn_to_np(out["dH"][0, h]), dH[0, 0], io, f"c3 dH h{h}")
+        assert_parity(_pn_to_np(out["H_in"][0, h]), H_in[0, 0], io, f"c3 H_in h{h}")
+        assert_parity(out["y_ssd"][0, :, h], y_ssd[0, :, 0], io, f"c3 y_ssd h{h}")
+        assert_parity(out["y"][0, tokens, h], y[0, tokens, 0], io, f"c3 y (sampled) h{h}")

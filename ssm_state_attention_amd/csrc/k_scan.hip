@@ -157,29 +157,42 @@ __global__ __launch_bounds__(kThreads) void k_state_pass(
   }
 }
 
-constexpr int kOutThreads = 512;  // 8 waves, two per SIMD
+constexpr int kOutWaves = 8;  // two per SIMD
+constexpr int kOutThreads = 64 * kOutWaves;
+constexpr int kMaxBlk = kMaxChunk / 16;  // 16-token blocks per chunk
 
-// LDS footprint of k_chunk_out when B_k is staged too; above the budget the
-// B fragments are read from global memory (L2) instead
+// LDS of k_chunk_out: phase 1 holds B_k, phase 2 reuses the same bytes for
+// xᵀ and H_in[k]ᵀ of one head
 template <typename T, int N, int P>
 struct ChunkOutLds {
   static constexpr int VE = Vec16<T>::n;
-  static constexpr size_t common =
-      (size_t(P) * (kMaxChunk + VE) + size_t(P) * (N + VE)) * sizeof(T) + 2 * kMaxChunk * 4;
-  static constexpr size_t with_b = common + size_t(kMaxChunk) * (N + VE) * sizeof(T);
-  static constexpr bool stage_b = with_b <= 150 * 1024;
+  static constexpr int LDX = kMaxChunk + VE;  // xᵀ rows [p][j]
+  static constexpr int LDH = N + VE;          // H_inᵀ rows [p][n]
+  static constexpr int LDB = N + VE;          // B rows [j][n]
+  static constexpr size_t phase1 = size_t(kMaxChunk) * LDB * sizeof(T);
+  static constexpr size_t phase2 = (size_t(P) * LDX + size_t(P) * LDH) * sizeof(T);
+  static constexpr size_t bytes = phase1 > phase2 ? phase1 : phase2;
 };
 
-// One workgroup per (chunk k, head, batch).  The 16-token blocks of the chunk
-// are dealt to the 8 waves in zigzag order (0..7, 7..0, ...), so the causal
-// work (block tb costs tb+1 blocks of keys) is balanced.  Per token block, in
-// transposed form (rows p, columns = tokens t):
-//   inter: Yᵀ += H_in[k]ᵀ C_tᵀ                     (K = n), scaled by exp(acum_t)
-//   intra: Gᵀ[j][t] = B_j·C_t (K = n), masked to j <= t, times
-//          exp(acum_t - acum_j)·dt_j, then Yᵀ += xᵀ Gᵀ  (K = j)
-// The masked Gᵀ tile stays in registers: its D layout (lane holds rows
-// j = 16·jb + 4·grp + i of column t) is used directly as the B operand of the
-// second product, with the k-slots of xᵀ's A operand assigned the same j's.
+// Native chunk output for one (chunk k, head group g, batch b): the heads of
+// a group share B and C, so the C·Bᵀ tiles are computed once per workgroup
+// and reused for every head of the group.
+//
+// Phase 1: B_k is staged in LDS; each wave owns the 16-token blocks
+//   tb0 = w and tb1 = 15 - w (balanced causal work) and computes the tiles
+//   Gᵀ[j][t] = B_j·C_t (K = n) for every key block jb <= tb into registers.
+// Phase 2, per head: xᵀ and H_in[k]ᵀ are staged in LDS (over B) and
+//   inter: Yᵀ += H_in[k]ᵀ C_tᵀ              (K = n), scaled by exp(acum_t)
+//   intra: Yᵀ += xᵀ (Gᵀ ∘ W)                (K = j)
+//   with W[j][t] = exp(acum_t - acum_j)·dt_j for j <= t, 0 above.  W is
+//   factored per tile through the end of its key block, e(jb):
+//   u = 2^(A_t - A_e(jb)) (one exp per lane and tile) and
+//   v_j = 2^(A_e(jb) - A_j + log2 dt_j) (per key, once per head), A = acum·log2(e).
+//   Both factors stay in range (u <= 1 below the diagonal, v_j <= dt_j·2^|block|);
+//   an underflowing u means a weight far below fp32 resolution of the sum.
+// The weighted tile stays in registers: its D layout (rows j = 16·jb +
+// 4·grp + i of column t) is the B operand of the second product, with the
+// k-slots of xᵀ's A operand assigned the same j's.
 template <typename T, int N, int P>
 __global__ __launch_bounds__(kOutThreads) void k_chunk_out(
     const T* __restrict__ x, const float* __restrict__ dt, const T* __restrict__ Bm,
@@ -187,184 +200,205 @@ __global__ __launch_bounds__(kOutThreads) void k_chunk_out(
     float* __restrict__ y_ssd, int L, int H, int G, int S) {
   using MM = Mma<T>;
   using Lds = ChunkOutLds<T, N, P>;
-  constexpr int K = MM::K, KL = MM::KL;
-  constexpr int VE = Vec16<T>::n;
-  constexpr int LDX = kMaxChunk + VE;  // xᵀ rows [p][j]
-  constexpr int LDH = N + VE;          // H_inᵀ rows [p][n]
-  constexpr int LDB = N + VE;          // B rows [j][n]
-  constexpr int NW = kOutThreads / 64;
-  // per token s of the chunk: at[s] = acum_s·log2(e) and
-  // bj[s] = log2(dt_s) - acum_s·log2(e), so that the intra-chunk weight of
-  // (t, j) is exp2(at[t] + bj[j]) = exp(acum_t - acum_j)·dt_j
-  __shared__ __align__(16) float sh_at[kMaxChunk];
-  __shared__ __align__(16) float sh_bj[kMaxChunk];
-  __shared__ __align__(16) T sh_xt[P * LDX];
-  __shared__ __align__(16) T sh_ht[P * LDH];
-  __shared__ __align__(16) T sh_b[Lds::stage_b ? kMaxChunk * LDB : 1];
+  typedef typename Vec16<T>::vec vec_t;
+  constexpr int K = MM::K, KL = MM::KL, VE = Vec16<T>::n;
+  constexpr int LDX = Lds::LDX, LDH = Lds::LDH, LDB = Lds::LDB;
+  constexpr int NKK = N / K, NPB = P / 16;
+  __shared__ __align__(16) unsigned char sh_raw[Lds::bytes];
+  __shared__ __align__(16) float sh_at[kMaxChunk];  // A_s = acum_s·log2(e)
+  __shared__ __align__(16) float sh_v[kMaxChunk];   // v_j
+  __shared__ float sh_ae[kMaxBlk];                  // A at the end of each block
+  T* sh_b = reinterpret_cast<T*>(sh_raw);
+  T* sh_xt = reinterpret_cast<T*>(sh_raw);
+  T* sh_ht = reinterpret_cast<T*>(sh_raw) + P * LDX;
 
-  const int k = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int M = L / S, g = h / (H / G);
+  const int k = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int M = L / S, hpg = H / G, NB = S / 16;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const long tok0 = (long)b * L + (long)k * S;
-  const long pair = (long)b * H + h;
+  const int tb0 = w, tb1 = 2 * kOutWaves - 1 - w;
+  const bool has0 = tb0 < NB, has1 = tb1 < NB;
 
-  // Staging: every global load of the chunk is issued before any LDS write
-  // (fixed per-thread maxima, predicated on the runtime chunk size), so the
-  // workgroup pays one memory round trip instead of one per loop trip.
-  typedef typename Vec16<T>::vec vec_t;
-  constexpr int XV = (kMaxChunk * (P / VE) + kOutThreads - 1) / kOutThreads;
-  constexpr int BV = Lds::stage_b ? (kMaxChunk * (N / VE) + kOutThreads - 1) / kOutThreads : 0;
-  constexpr int HV = (P * N / 4 + kOutThreads - 1) / kOutThreads;
-  vec_t xr[XV], br[BV > 0 ? BV : 1];
-  floatx4 hr[HV];
-  float ar = 0.f, dr = 1.f;
-  const float* hsrc = H_in + (pair * (M + 1) + k) * (long)(P * N);
-  if (tid < S) {
-    ar = acum[(pair * M + k) * S + tid];
-    dr = dt[(tok0 + tid) * H + h];
-  }
+  // ---- phase 1: C·Bᵀ tiles of this wave's token blocks ----
+  {
+    constexpr int BV = (kMaxChunk * (N / VE) + kOutThreads - 1) / kOutThreads;
+    vec_t br[BV];
 #pragma unroll
-  for (int v = 0; v < XV; ++v) {
-    const int i = tid + v * kOutThreads;
-    if (i < S * (P / VE)) {
-      const int s = i % S, pv = i / S;
-      xr[v] = load16(x + ((tok0 + s) * H + h) * P + pv * VE);
+    for (int v = 0; v < BV; ++v) {
+      const int i = tid + v * kOutThreads;
+      if (i < S * (N / VE)) {
+        const int s = i / (N / VE), nv = i % (N / VE);
+        br[v] = load16(Bm + ((tok0 + s) * G + g) * N + nv * VE);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < BV; ++v) {
+      const int i = tid + v * kOutThreads;
+      if (i < S * (N / VE)) {
+        const int s = i / (N / VE), nv = i % (N / VE);
+        *reinterpret_cast<vec_t*>(&sh_b[s * LDB + nv * VE]) = br[v];
+      }
     }
   }
+  floatx4 g0[kMaxBlk], g1[kMaxBlk];
+  {
+  typename MM::frag cf0[NKK], cf1[NKK];
 #pragma unroll
-  for (int v = 0; v < BV; ++v) {
-    const int i = tid + v * kOutThreads;
-    if (i < S * (N / VE)) {
-      const int s = i / (N / VE), nv = i % (N / VE);
-      br[v] = load16(Bm + ((tok0 + s) * G + g) * N + nv * VE);
-    }
-  }
-#pragma unroll
-  for (int v = 0; v < HV; ++v) {
-    const int i = tid + v * kOutThreads;
-    if (i < P * N / 4) hr[v] = reinterpret_cast<const floatx4*>(hsrc)[i];
-  }
-  if (tid < S) {
-    const float a2 = ar * kLog2e;
-    sh_at[tid] = a2;
-    sh_bj[tid] = __builtin_amdgcn_logf(dr) - a2;
-  }
-#pragma unroll
-  for (int v = 0; v < XV; ++v) {
-    const int i = tid + v * kOutThreads;
-    if (i < S * (P / VE)) {
-      const int s = i % S, pv = i / S;
-#pragma unroll
-      for (int e = 0; e < VE; ++e) sh_xt[(pv * VE + e) * LDX + s] = xr[v][e];
-    }
-  }
-#pragma unroll
-  for (int v = 0; v < BV; ++v) {
-    const int i = tid + v * kOutThreads;
-    if (i < S * (N / VE)) {
-      const int s = i / (N / VE), nv = i % (N / VE);
-      *reinterpret_cast<vec_t*>(&sh_b[s * LDB + nv * VE]) = br[v];
-    }
-  }
-#pragma unroll
-  for (int v = 0; v < HV; ++v) {
-    const int i = tid + v * kOutThreads;
-    if (i < P * N / 4) {
-      const int p = (i * 4) / N, n = (i * 4) % N;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sh_ht[p * LDH + n + e] = from_f32<T>(hr[v][e]);
-    }
+  for (int kk = 0; kk < NKK; ++kk) {
+    const int t0 = has0 ? tb0 * 16 + col : 0, t1 = has1 ? tb1 * 16 + col : 0;
+    cf0[kk] = MM::load(C + ((tok0 + t0) * G + g) * N + kk * K + grp * KL);
+    cf1[kk] = MM::load(C + ((tok0 + t1) * G + g) * N + kk * K + grp * KL);
   }
   __syncthreads();
-
-  // A-operand fragment of B rows j = jb*16 + col at k-step kk
-  auto b_frag = [&](int jb, int kk) {
-    if constexpr (Lds::stage_b)
-      return MM::load(&sh_b[(jb * 16 + col) * LDB + kk * K + grp * KL]);
-    else
-      return MM::load(Bm + ((tok0 + jb * 16 + col) * G + g) * N + kk * K + grp * KL);
-  };
-
-  const int nblk = S / 16;
-  for (int i = 0; i < nblk; ++i) {
-    const int round = i / NW;
-    const int owner = (round & 1) ? NW - 1 - (i % NW) : (i % NW);
-    if (owner != w) continue;
-    const int tb = i;
-    const int t = tb * 16 + col;  // this lane's token inside the chunk
-    typename MM::frag cf[N / K];
 #pragma unroll
-    for (int kk = 0; kk < N / K; ++kk)
-      cf[kk] = MM::load(C + ((tok0 + t) * G + g) * N + kk * K + grp * KL);
-    floatx4 yin[P / 16], yia[P / 16];
+  for (int jb = 0; jb < kMaxBlk; ++jb) {
+    g0[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    g1[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (has0 && jb <= tb0) {
 #pragma unroll
-    for (int pb = 0; pb < P / 16; ++pb) {
-      yin[pb] = floatx4{0.f, 0.f, 0.f, 0.f};
-      yia[pb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < NKK; ++kk)
+        g0[jb] = MM::mma(MM::load(&sh_b[(jb * 16 + col) * LDB + kk * K + grp * KL]), cf0[kk],
+                         g0[jb]);
+    }
+    if (has1 && jb <= tb1) {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        g1[jb] = MM::mma(MM::load(&sh_b[(jb * 16 + col) * LDB + kk * K + grp * KL]), cf1[kk],
+                         g1[jb]);
+    }
+  }
+  }
+  __syncthreads();  // B is dead; phase 2 reuses its LDS
+
+  // ---- phase 2: the heads of the group ----
+  constexpr int XV = (kMaxChunk * (P / VE) + kOutThreads - 1) / kOutThreads;
+  constexpr int HV = (P * N / 4 + kOutThreads - 1) / kOutThreads;
+  for (int hh = 0; hh < hpg; ++hh) {
+    const int h = g * hpg + hh;
+    const long pair = (long)b * H + h;
+    const float* hsrc = H_in + (pair * (M + 1) + k) * (long)(P * N);
+    vec_t xr[XV];
+    floatx4 hr[HV];
+    float ar = 0.f, ae = 0.f, dr = 1.f;
+    if (tid < S) {
+      ar = acum[(pair * M + k) * S + tid];
+      ae = acum[(pair * M + k) * S + (tid | 15)];
+      dr = dt[(tok0 + tid) * H + h];
     }
 #pragma unroll
-    for (int pb = 0; pb < P / 16; ++pb)
-#pragma unroll
-      for (int kk = 0; kk < N / K; ++kk)
-        yin[pb] = MM::mma(MM::load(&sh_ht[(pb * 16 + col) * LDH + kk * K + grp * KL]), cf[kk],
-                          yin[pb]);
-    const float at_t = sh_at[t];
-    // weights of one 16x16 Gᵀ tile (rows j = jb*16 + 4*grp + i, column t):
-    // branch-free; entries above the diagonal are selected away (their
-    // exponent may overflow, the select discards it)
-    auto weights = [&](int jb, floatx4 gt) {
-      const floatx4 bj = *reinterpret_cast<const floatx4*>(&sh_bj[jb * 16 + 4 * grp]);
-      floatx4 wv;
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const float wgt = gt[i4] * exp2_fast(at_t + bj[i4]);
-        wv[i4] = (jb * 16 + 4 * grp + i4 <= t) ? wgt : 0.f;
+    for (int v = 0; v < XV; ++v) {
+      const int i = tid + v * kOutThreads;
+      if (i < S * (P / VE)) {
+        const int s = i % S, pv = i / S;
+        xr[v] = load16(x + ((tok0 + s) * H + h) * P + pv * VE);
       }
-      return wv;
+    }
+#pragma unroll
+    for (int v = 0; v < HV; ++v) {
+      const int i = tid + v * kOutThreads;
+      if (i < P * N / 4) hr[v] = reinterpret_cast<const floatx4*>(hsrc)[i];
+    }
+    if (tid < S) {
+      const float a2 = ar * kLog2e, e2 = ae * kLog2e;
+      sh_at[tid] = a2;
+      sh_v[tid] = exp2_fast(e2 - a2 + __builtin_amdgcn_logf(dr));
+      if ((tid & 15) == 15) sh_ae[tid >> 4] = a2;
+    }
+#pragma unroll
+    for (int v = 0; v < XV; ++v) {
+      const int i = tid + v * kOutThreads;
+      if (i < S * (P / VE)) {
+        const int s = i % S, pv = i / S;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) sh_xt[(pv * VE + e) * LDX + s] = xr[v][e];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < HV; ++v) {
+      const int i = tid + v * kOutThreads;
+      if (i < P * N / 4) {
+        const int p = (i * 4) / N, n = (i * 4) % N;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sh_ht[p * LDH + n + e] = from_f32<T>(hr[v][e]);
+      }
+    }
+    __syncthreads();
+
+    auto one_block = [&](int tb, const floatx4 (&gt)[kMaxBlk]) {
+      const int t = tb * 16 + col;
+      // C fragments again (L2 hits): keeping them live across the head loop
+      // would spill the tiles
+      typename MM::frag cf[NKK];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        cf[kk] = MM::load(C + ((tok0 + t) * G + g) * N + kk * K + grp * KL);
+      floatx4 yin[NPB], yia[NPB];
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb) {
+        yin[pb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        yia[pb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+          yin[pb] = MM::mma(MM::load(&sh_ht[(pb * 16 + col) * LDH + kk * K + grp * KL]), cf[kk],
+                            yin[pb]);
+      const float at_t = sh_at[t];
+      // weighted tile jb (rows j = jb*16 + 4*grp + i, column t)
+      auto weights = [&](int jb, floatx4 tile) {
+        const float u = exp2_fast(at_t - sh_ae[jb]);
+        const floatx4 vj = *reinterpret_cast<const floatx4*>(&sh_v[jb * 16 + 4 * grp]);
+        floatx4 wv;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          wv[i4] = (jb * 16 + 4 * grp + i4 <= t) ? tile[i4] * (u * vj[i4]) : 0.f;
+        return wv;
+      };
+      if constexpr (std::is_same<T, float>::value) {
+#pragma unroll
+        for (int jb = 0; jb < kMaxBlk; ++jb) {
+          if (jb <= tb) {
+            const floatx4 wv = weights(jb, gt[jb]);
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const int j = jb * 16 + 4 * grp + i4;
+#pragma unroll
+              for (int pb = 0; pb < NPB; ++pb)
+                yia[pb] = MM::mma(sh_xt[(pb * 16 + col) * LDX + j], wv[i4], yia[pb]);
+            }
+          }
+        }
+      } else {
+        // S % 32 == 0, so the pair (jb0, jb0 + 1) never leaves the chunk
+#pragma unroll
+        for (int jb0 = 0; jb0 < kMaxBlk; jb0 += 2) {
+          if (jb0 <= tb) {
+            const floatx4 w0 = weights(jb0, gt[jb0]), w1 = weights(jb0 + 1, gt[jb0 + 1]);
+            const bf16x8 bfr = {from_f32<bf16>(w0[0]), from_f32<bf16>(w0[1]),
+                                from_f32<bf16>(w0[2]), from_f32<bf16>(w0[3]),
+                                from_f32<bf16>(w1[0]), from_f32<bf16>(w1[1]),
+                                from_f32<bf16>(w1[2]), from_f32<bf16>(w1[3])};
+#pragma unroll
+            for (int pb = 0; pb < NPB; ++pb) {
+              const bf16* row = &sh_xt[(pb * 16 + col) * LDX];
+              const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + jb0 * 16 + 4 * grp);
+              const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + (jb0 + 1) * 16 + 4 * grp);
+              const bf16x8 afr = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              yia[pb] = MM::mma(afr, bfr, yia[pb]);
+            }
+          }
+        }
+      }
+      const float dec_t = exp2_fast(at_t);
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb)
+        store4(y_ssd + ((tok0 + t) * H + h) * P + pb * 16 + 4 * grp, yia[pb] + dec_t * yin[pb]);
     };
-    if constexpr (std::is_same<T, float>::value) {
-      for (int jb = 0; jb <= tb; ++jb) {
-        floatx4 gt = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < N / K; ++kk) gt = MM::mma(b_frag(jb, kk), cf[kk], gt);
-        const floatx4 wv = weights(jb, gt);
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int j = jb * 16 + 4 * grp + i4;
-#pragma unroll
-          for (int pb = 0; pb < P / 16; ++pb)
-            yia[pb] = MM::mma(sh_xt[(pb * 16 + col) * LDX + j], wv[i4], yia[pb]);
-        }
-      }
-    } else {
-      // S % 32 == 0, so the pair (jb0, jb0 + 1) never leaves the chunk
-      for (int jb0 = 0; jb0 <= tb; jb0 += 2) {
-        floatx4 gt0 = {0.f, 0.f, 0.f, 0.f}, gt1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < N / K; ++kk) gt0 = MM::mma(b_frag(jb0, kk), cf[kk], gt0);
-        if (jb0 + 1 <= tb) {
-#pragma unroll
-          for (int kk = 0; kk < N / K; ++kk) gt1 = MM::mma(b_frag(jb0 + 1, kk), cf[kk], gt1);
-        }
-        const floatx4 w0 = weights(jb0, gt0), w1 = weights(jb0 + 1, gt1);
-        const bf16x8 bfr = {from_f32<bf16>(w0[0]), from_f32<bf16>(w0[1]), from_f32<bf16>(w0[2]),
-                            from_f32<bf16>(w0[3]), from_f32<bf16>(w1[0]), from_f32<bf16>(w1[1]),
-                            from_f32<bf16>(w1[2]), from_f32<bf16>(w1[3])};
-#pragma unroll
-        for (int pb = 0; pb < P / 16; ++pb) {
-          const bf16* row = &sh_xt[(pb * 16 + col) * LDX];
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + jb0 * 16 + 4 * grp);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + (jb0 + 1) * 16 + 4 * grp);
-          const bf16x8 afr = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          yia[pb] = MM::mma(afr, bfr, yia[pb]);
-        }
-      }
-    }
-    const float dec_t = exp2_fast(at_t);
-#pragma unroll
-    for (int pb = 0; pb < P / 16; ++pb)
-      store4(y_ssd + ((tok0 + t) * H + h) * P + pb * 16 + 4 * grp, yia[pb] + dec_t * yin[pb]);
+    if (has0) one_block(tb0, g0);
+    if (has1) one_block(tb1, g1);
+    __syncthreads();  // the next head overwrites the LDS
   }
 }
 
@@ -389,7 +423,7 @@ hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt,
                      dim3(kThreads), 0, st, acum, dH_f32, h0, H_in, s.H, M, s.S, PN);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_chunk_out<T, N, P>), dim3(M, s.H, s.B), dim3(kOutThreads), 0, st, x, dt, Bm,
+  hipLaunchKernelGGL((k_chunk_out<T, N, P>), dim3(M, s.G, s.B), dim3(kOutThreads), 0, st, x, dt, Bm,
                      C, acum, H_in, y_ssd, s.L, s.H, s.G, s.S);
   return hipGetLastError();
 }

@@ -45,11 +45,13 @@ __device__ __forceinline__ float sum_lane_groups(float v) {
 // Prefill SMA.  One workgroup = WAVES waves × 16·NTB tokens of ONE chunk k,
 // so every token of the workgroup sees the same memories c < k (no mask).
 // Per memory c, dH[c]ᵀ (P x N, value-axis-major in HBM) is staged in LDS
-// (two buffers, one barrier per memory; each memory is fetched into
-// registers two steps before it is written to LDS).  Each wave multiplies
-// it with its resident [Q; C] fragments (16x16 MFMA, rows p, columns =
-// tokens), finishes the score with an in-lane dot against E_t plus two
-// lane-group exchanges, and folds the value into an online softmax.
+// (two buffers; each memory is fetched into registers one step before it is
+// written to LDS).  Each wave multiplies it with its resident [Q; C]
+// fragments (16x16 MFMA, rows p, columns = tokens), finishes the score with
+// an in-lane dot against E_t plus two lane-group exchanges, and folds the
+// value into an online softmax.  The waves are split in two halves that
+// alternate between the MFMA phase and the softmax phase (see half_steps),
+// so matrix core and vector ALU work of one SIMD overlap.
 //
 // Grid mapping: workgroups are dealt to the 8 XCDs round-robin, so
 // blockIdx % 8 selects an XCD and all tiles of one (batch, head) pair land
@@ -90,7 +92,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   const long row_w = (long)b * L + (long)k * S + sub * TWG + w * TW;
 
   typename MM::frag qf[NTB][NKK], cf[NTB][NKK];
-  float ev[NTB][NPB][4];
+  // E_t values of this lane's p rows, kept in their input type (bf16 pairs
+  // halve the registers) and widened when the score is formed
+  typedef typename std::conditional<std::is_same<T, bf16>::value, bf16x4, floatx4>::type e4_t;
+  e4_t ev[NTB][NPB];
 #pragma unroll
   for (int tb = 0; tb < NTB; ++tb) {
     const long row = row_w + tb * 16 + col;
@@ -100,11 +105,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
       cf[tb][kk] = MM::load(C + (row * G + g) * N + kk * K + grp * KL);
     }
 #pragma unroll
-    for (int pb = 0; pb < NPB; ++pb) {
-      const floatx4 e4 = load4_f32(E + (row * H + h) * P + pb * 16 + 4 * grp);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ev[tb][pb][i] = e4[i];
-    }
+    for (int pb = 0; pb < NPB; ++pb)
+      ev[tb][pb] = *reinterpret_cast<const e4_t*>(E + (row * H + h) * P + pb * 16 + 4 * grp);
   }
   floatx4 acc[NTB][NPB];
   float mx[NTB], ls[NTB];
@@ -117,8 +119,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   }
 
   const T* mem = dH + (long)pair * M * (P * N);
-  vec_t stg0[VPT], stg1[VPT];
-  auto gload = [&](int c, vec_t (&stg)[VPT]) {
+  vec_t stg[VPT];
+  auto gload = [&](int c) {
     const vec_t* src = reinterpret_cast<const vec_t*>(mem + (long)c * (P * N));
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
       if (NVEC % NTHR == 0 || vi < NVEC) stg[v] = src[vi];
     }
   };
-  auto swrite = [&](int buf, vec_t (&stg)[VPT]) {
+  auto swrite = [&](int buf) {
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
       const int vi = tid + v * NTHR;
@@ -136,9 +138,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
       }
     }
   };
-  // MFMAs and online softmax of the memory in LDS buffer `cur`
-  auto compute = [&](int cur) {
-    floatx4 zq[NTB][NPB], zc[NTB][NPB];
+  floatx4 zq[NTB][NPB], zc[NTB][NPB];
+  auto mma_mem = [&](int cur) {
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
@@ -146,27 +147,45 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
         zq[tb][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
         zc[tb][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
+    // A fragments of p-block pb+1 are read while the MFMAs of pb run
+    typename MM::frag a[2][NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      a[0][kk] = MM::load(&sh_mem[cur][(0 * 16 + col) * LDN + kk * K + grp * KL]);
 #pragma unroll
     for (int pb = 0; pb < NPB; ++pb) {
-      typename MM::frag a[NKK];
+      if (pb + 1 < NPB) {
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        a[kk] = MM::load(&sh_mem[cur][(pb * 16 + col) * LDN + kk * K + grp * KL]);
+        for (int kk = 0; kk < NKK; ++kk)
+          a[(pb + 1) & 1][kk] =
+              MM::load(&sh_mem[cur][((pb + 1) * 16 + col) * LDN + kk * K + grp * KL]);
+      }
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
-          zq[tb][pb] = MM::mma(a[kk], qf[tb][kk], zq[tb][pb]);
-          zc[tb][pb] = MM::mma(a[kk], cf[tb][kk], zc[tb][pb]);
+          zq[tb][pb] = MM::mma(a[pb & 1][kk], qf[tb][kk], zq[tb][pb]);
+          zc[tb][pb] = MM::mma(a[pb & 1][kk], cf[tb][kk], zc[tb][pb]);
         }
     }
+    // schedule: LDS fragment reads run two fragments ahead of the MFMAs
+    // that consume them (2·NTB MFMAs per fragment cover the LDS latency)
+    constexpr int R = NPB * NKK;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int f = 0; f < R; ++f) {
+      if (f + 4 < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NTB, 0);
+    }
+  };
+  auto softmax_mem = [&]() {
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
       float s = 0.f;
 #pragma unroll
       for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s += zq[tb][pb][i] * ev[tb][pb][i];
+        for (int i = 0; i < 4; ++i) s += zq[tb][pb][i] * to_f32(ev[tb][pb][i]);
       s = sum_lane_groups(s) * scale_log2;
       const float mn = fmaxf(mx[tb], s);
       const float al = exp2_fast(mx[tb] - mn);  // 0 for the first memory
@@ -177,23 +196,46 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
       mx[tb] = mn;
     }
   };
-  // step c: memory c is in buffer PAR, memory c+1 in registers stg_n;
-  // fetch memory c+2 into stg_c (its previous content, memory c, is in LDS)
-  auto iter = [&](int c, auto par_tag, vec_t (&stg_c)[VPT], vec_t (&stg_n)[VPT]) {
+  // Ping-pong: the first half of the waves (one per SIMD) runs its MFMAs
+  // while the second half runs its softmax, then they swap, so the matrix
+  // core and the vector ALU of every SIMD stay busy together.  Two barriers
+  // per memory; memory c sits in buffer c&1 during both halves of step c and
+  // memory c+1 is written into the other buffer in the second half (its
+  // previous content, memory c-1, was last read a full barrier earlier).
+  const bool lead = w < WAVES / 2;
+  auto half_steps = [&](int c, auto par_tag) {
     constexpr int PAR = decltype(par_tag)::value;
-    if (c + 2 < k) gload(c + 2, stg_c);
-    compute(PAR);
-    if (c + 1 < k) swrite(PAR ^ 1, stg_n);
+    // first half: lead waves multiply memory c, the others finish memory c-1
+    if (lead) {
+      if (c < k) mma_mem(PAR);
+    } else if (c > 0) {
+      softmax_mem();
+    }
+    __syncthreads();
+    // second half: lead waves finish memory c, the others multiply it
+    if (lead) {
+      if (c < k) softmax_mem();
+    } else if (c < k) {
+      mma_mem(PAR);
+    }
+    // unconditional, indices clamped to the last memory: a duplicate lands
+    // in a buffer that is not read again, and every path issues the same
+    // loads (so the wait before the LDS write covers only the older fetch)
+    swrite(PAR ^ 1);                 // memory c+1, fetched during step c-1
+    gload(min(c + 2, k - 1));        // memory c+2
     __syncthreads();
   };
   if (k > 0) {
-    gload(0, stg0);
-    swrite(0, stg0);
-    if (k > 1) gload(1, stg1);
+    gload(0);
+    swrite(0);
+    gload(min(1, k - 1));
+    // all prologue loads (Q/C fragments, E, first memory) complete here, so
+    // the loop's only load in flight is the memory prefetch
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    for (int c = 0; c < k; c += 2) {
-      iter(c, IC<0>{}, stg0, stg1);
-      if (c + 1 < k) iter(c + 1, IC<1>{}, stg1, stg0);
+    for (int c = 0; c <= k; c += 2) {
+      half_steps(c, IC<0>{});
+      if (c + 1 <= k) half_steps(c + 1, IC<1>{});
     }
   }
 

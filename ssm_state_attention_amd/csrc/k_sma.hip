@@ -66,7 +66,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     int BH, int L, int H, int G, int S, int npq, float scale_log2) {
   using MM = Mma<T>;
   constexpr int K = MM::K, KL = MM::KL, VE = Vec16<T>::n;
-  constexpr int LDN = N + VE;  // LDS row stride (elements): 16-byte pad
+  // LDS row stride (elements): a 32-byte pad keeps the 16-byte fragment reads
+  // (16 rows x 4 column groups per instruction) free of bank conflicts on the
+  // 64-bank LDS; a 16-byte pad leaves them 2-way conflicted
+  constexpr int LDN = N + 2 * VE;
   constexpr int TW = 16 * NTB, TWG = TW * WAVES;
   constexpr int NVEC = P * N / VE;  // 16-byte vectors per memory
   constexpr int NTHR = 64 * WAVES;

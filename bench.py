@@ -88,7 +88,7 @@ def bench_prefill(args, torch, api, synth):
         "dH": torch.empty(B, H, M, P, N, dtype=torch.bfloat16, device="cuda:0"),
         "dH_f32": torch.empty(B, H, M, P, N, **f32),
         "H_in": torch.empty(B, H, M + 1, P, N, **f32),
-        "y_ssd": torch.empty(B, L, H, P, **f32),
+        "y_ssd": torch.empty(B, L, H, P, dtype=torch.bfloat16, device="cuda:0"),
         "y": torch.empty(B, L, H, P, dtype=torch.bfloat16, device="cuda:0"),
     }
 

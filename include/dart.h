@@ -106,12 +106,13 @@ dart_status dart_chunk_state(const dart_dims* dims, const void* x, const float* 
  *
  * in:  x, dt, Bm as above; C [B,L,G,N] io; acum, dH_f32 from
  *      dart_chunk_state; h0 [B,H,P,N] f32 or NULL
- * out: H_in [B,H,M+1,P,N] f32; y_ssd [B,L,H,P] f32
+ * out: H_in [B,H,M+1,P,N] f32; y_ssd [B,L,H,P] io (rounded to the io type
+ *      once, like every io-typed output)
  */
 dart_status dart_state_pass(const dart_dims* dims, const void* x, const float* dt,
                             const void* Bm, const void* C, const float* acum,
                             const float* dH_f32, const float* h0, float* H_in,
-                            float* y_ssd, void* stream);
+                            void* y_ssd, void* stream);
 
 /*
  * State-memory attention over completed chunks plus the gated add.
@@ -124,11 +125,11 @@ dart_status dart_state_pass(const dart_dims* dims, const void* x, const float* d
  *   y_t    = y_ssd_t + gate·o_t
  *
  * in:  Q [B,L,G,N] io; E [B,L,H,P] io; C [B,L,G,N] io; dH [B,H,M,P,N] io;
- *      y_ssd [B,L,H,P] f32
+ *      y_ssd [B,L,H,P] io (as written by dart_state_pass)
  * out: y [B,L,H,P] io
  */
 dart_status dart_sma_fwd(const dart_dims* dims, const void* Q, const void* E,
-                         const void* C, const void* dH, const float* y_ssd, float gate,
+                         const void* C, const void* dH, const void* y_ssd, float gate,
                          void* y, void* stream);
 
 /* Bytes of device workspace dart_sma_decode needs for these dims (a

@@ -67,7 +67,7 @@ def dart_chunk_state(x, dt, A, Bm, acum, dH, dH_f32, chunk):
 
 def dart_state_pass(x, dt, Bm, C, acum, dH_f32, h0, H_in, y_ssd, chunk):
     """State passing H_in [B,H,M+1,P,N] f32 and native output y_ssd
-    [B,L,H,P] f32; h0 [B,H,P,N] f32 or None (zero)."""
+    [B,L,H,P] in the io type; h0 [B,H,P,N] f32 or None (zero)."""
     d = prefill_dims(x, Bm, chunk)
     B, L, H, P = x.shape
     G, N = Bm.shape[2], Bm.shape[3]
@@ -78,7 +78,7 @@ def dart_state_pass(x, dt, Bm, C, acum, dH_f32, h0, H_in, y_ssd, chunk):
             _ptr(dH_f32, "dH_f32", torch.float32, (B, H, M, P, N), dev),
             _ptr(h0, "h0", torch.float32, (B, H, P, N), dev),
             _ptr(H_in, "H_in", torch.float32, (B, H, M + 1, P, N), dev),
-            _ptr(y_ssd, "y_ssd", torch.float32, (B, L, H, P), dev)]
+            _ptr(y_ssd, "y_ssd", io, (B, L, H, P), dev)]
     check(lib().dart_state_pass(d, *args, _stream()), "dart_state_pass")
 
 
@@ -90,7 +90,7 @@ def dart_sma_fwd(Q, E, C, dH, y_ssd, gate, y, chunk):
     M, io, dev = L // chunk, E.dtype, E.device
     args = [_ptr(Q, "Q", io, (B, L, G, N), dev), _ptr(E, "E", io, (B, L, H, P), dev),
             _ptr(C, "C", io, (B, L, G, N), dev), _ptr(dH, "dH", io, (B, H, M, P, N), dev),
-            _ptr(y_ssd, "y_ssd", torch.float32, (B, L, H, P), dev)]
+            _ptr(y_ssd, "y_ssd", io, (B, L, H, P), dev)]
     yp = _ptr(y, "y", io, (B, L, H, P), dev)
     check(lib().dart_sma_fwd(d, *args, float(gate), yp, _stream()), "dart_sma_fwd")
 
@@ -143,7 +143,7 @@ def prefill(x, dt, A, Bm, C, Q, E, gate, chunk, h0=None):
         "dH": torch.empty(B, H, M, P, N, dtype=x.dtype, device=dev),
         "dH_f32": torch.empty(B, H, M, P, N, **f32),
         "H_in": torch.empty(B, H, M + 1, P, N, **f32),
-        "y_ssd": torch.empty(B, L, H, P, **f32),
+        "y_ssd": torch.empty(B, L, H, P, dtype=x.dtype, device=x.device),
         "y": torch.empty(B, L, H, P, dtype=x.dtype, device=dev),
     }
     dart_chunk_state(x, dt, A, Bm, out["acum"], out["dH"], out["dH_f32"], chunk)

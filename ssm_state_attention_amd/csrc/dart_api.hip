@@ -60,20 +60,20 @@ struct StatePassFn {
   dart::PrefillShape sh;
   const void *x, *Bm, *C;
   const float *dt, *acum, *dHf, *h0;
-  float *H_in, *y_ssd;
+  float* H_in;
+  void* y_ssd;
   hipStream_t st;
   template <typename T, int N, int P>
   hipError_t run() {
     return dart::launch_state_pass<T, N, P>(sh, static_cast<const T*>(x), dt,
                                             static_cast<const T*>(Bm), static_cast<const T*>(C),
-                                            acum, dHf, h0, H_in, y_ssd, st);
+                                            acum, dHf, h0, H_in, static_cast<T*>(y_ssd), st);
   }
 };
 
 struct SmaFwdFn {
   dart::PrefillShape sh;
-  const void *Q, *E, *C, *dH;
-  const float* y_ssd;
+  const void *Q, *E, *C, *dH, *y_ssd;
   float gate;
   void* y;
   hipStream_t st;
@@ -81,7 +81,8 @@ struct SmaFwdFn {
   hipError_t run() {
     return dart::launch_sma_fwd<T, N, P>(sh, static_cast<const T*>(Q), static_cast<const T*>(E),
                                          static_cast<const T*>(C), static_cast<const T*>(dH),
-                                         y_ssd, gate, static_cast<T*>(y), st);
+                                         static_cast<const T*>(y_ssd), gate, static_cast<T*>(y),
+                                         st);
   }
 };
 
@@ -119,7 +120,7 @@ extern "C" dart_status dart_chunk_state(const dart_dims* dims, const void* x, co
 extern "C" dart_status dart_state_pass(const dart_dims* dims, const void* x, const float* dt,
                                        const void* Bm, const void* C, const float* acum,
                                        const float* dH_f32, const float* h0, float* H_in,
-                                       float* y_ssd, void* stream) {
+                                       void* y_ssd, void* stream) {
   dart_status s = dart_validate_dims(dims);
   if (s != DART_OK) return s;
   if ((s = check_ptrs(x, dt, Bm, C, acum, dH_f32, H_in, y_ssd)) != DART_OK) return s;
@@ -130,7 +131,7 @@ extern "C" dart_status dart_state_pass(const dart_dims* dims, const void* x, con
 }
 
 extern "C" dart_status dart_sma_fwd(const dart_dims* dims, const void* Q, const void* E,
-                                    const void* C, const void* dH, const float* y_ssd,
+                                    const void* C, const void* dH, const void* y_ssd,
                                     float gate, void* y, void* stream) {
   dart_status s = dart_validate_dims(dims);
   if (s != DART_OK) return s;

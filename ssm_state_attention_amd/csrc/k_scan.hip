@@ -197,7 +197,7 @@ template <typename T, int N, int P>
 __global__ __launch_bounds__(kOutThreads) void k_chunk_out(
     const T* __restrict__ x, const float* __restrict__ dt, const T* __restrict__ Bm,
     const T* __restrict__ C, const float* __restrict__ acum, const float* __restrict__ H_in,
-    float* __restrict__ y_ssd, int L, int H, int G, int S) {
+    T* __restrict__ y_ssd, int L, int H, int G, int S) {
   using MM = Mma<T>;
   using Lds = ChunkOutLds<T, N, P>;
   typedef typename Vec16<T>::vec vec_t;
@@ -416,7 +416,7 @@ hipError_t launch_chunk_state(const PrefillShape& s, const T* x, const float* dt
 template <typename T, int N, int P>
 hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt, const T* Bm,
                              const T* C, const float* acum, const float* dH_f32,
-                             const float* h0, float* H_in, float* y_ssd, hipStream_t st) {
+                             const float* h0, float* H_in, T* y_ssd, hipStream_t st) {
   const int M = s.L / s.S;
   constexpr int PN = P * N;
   hipLaunchKernelGGL(k_state_pass, dim3((PN / 4 + kThreads - 1) / kThreads, s.H, s.B),
@@ -434,7 +434,7 @@ hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt,
                                                   hipStream_t);                                \
   template hipError_t launch_state_pass<T, N, P>(const PrefillShape&, const T*, const float*,  \
                                                  const T*, const T*, const float*,             \
-                                                 const float*, const float*, float*, float*,   \
+                                                 const float*, const float*, float*, T*,       \
                                                  hipStream_t);
 DART_FOR_EACH_SHAPE(DART_INST_SCAN)
 

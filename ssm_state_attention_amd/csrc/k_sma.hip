@@ -62,7 +62,7 @@ __device__ __forceinline__ float sum_lane_groups(float v) {
 template <typename T, int N, int P, int NTB, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     const T* __restrict__ Q, const T* __restrict__ E, const T* __restrict__ C,
-    const T* __restrict__ dH, const float* __restrict__ y_ssd, float gate, T* __restrict__ y,
+    const T* __restrict__ dH, const T* __restrict__ y_ssd, float gate, T* __restrict__ y,
     int BH, int L, int H, int G, int S, int npq, float scale_log2) {
   using MM = Mma<T>;
   constexpr int K = MM::K, KL = MM::KL, VE = Vec16<T>::n;
@@ -463,7 +463,7 @@ __global__ void k_decode_advance(int* __restrict__ n_chunks, int* __restrict__ p
 
 template <typename T, int N, int P, int NTB, int WAVES>
 hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T* C, const T* dH,
-                         const float* y_ssd, float gate, T* y, hipStream_t st) {
+                         const T* y_ssd, float gate, T* y, hipStream_t st) {
   const int M = s.L / s.S;
   const int BH = s.B * s.H;
   const int npq = (BH + 7) / 8;  // (batch, head) pairs per XCD
@@ -480,7 +480,7 @@ hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T*
 
 template <typename T, int N, int P>
 hipError_t launch_sma_fwd(const PrefillShape& s, const T* Q, const T* E, const T* C,
-                          const T* dH, const float* y_ssd, float gate, T* y, hipStream_t st) {
+                          const T* dH, const T* y_ssd, float gate, T* y, hipStream_t st) {
   constexpr int NTB = SmaTile<N, P>::NTB;
   const int r = s.S / (16 * NTB);  // S % 32 == 0, so r >= 1
   if (r % 8 == 0) return sma_fwd_waves<T, N, P, NTB, 8>(s, Q, E, C, dH, y_ssd, gate, y, st);
@@ -520,7 +520,7 @@ hipError_t launch_sma_decode(const DecodeShape& s, const T* x, const float* dt, 
 
 #define DART_INST_SMA(T, N, P)                                                                 \
   template hipError_t launch_sma_fwd<T, N, P>(const PrefillShape&, const T*, const T*, const T*, \
-                                              const T*, const float*, float, T*, hipStream_t);   \
+                                              const T*, const T*, float, T*, hipStream_t);   \
   template hipError_t launch_sma_decode<T, N, P>(                                                \
       const DecodeShape&, const T*, const float*, const float*, const T*, const T*, const T*,    \
       const T*, float, T*, float*, float*, int*, int*, T*, void*, hipStream_t);

@@ -66,18 +66,31 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     int BH, int L, int H, int G, int S, int npq, float scale_log2) {
   using MM = Mma<T>;
   constexpr int K = MM::K, KL = MM::KL, VE = Vec16<T>::n;
-  // LDS row stride (elements): a 32-byte pad keeps the 16-byte fragment reads
+  // LDS row strides (elements): a 32-byte pad keeps the 16-byte fragment reads
   // (16 rows x 4 column groups per instruction) free of bank conflicts on the
   // 64-bank LDS; a 16-byte pad leaves them 2-way conflicted
-  constexpr int LDN = N + 2 * VE;
+  constexpr int LDN = N + 2 * VE;  // memory rows [p][n], Q/C rows [t][n]
+  constexpr int LDE = P + 2 * VE;  // E and y rows [t][p]
   constexpr int TW = 16 * NTB, TWG = TW * WAVES;
   constexpr int NVEC = P * N / VE;  // 16-byte vectors per memory
   constexpr int NTHR = 64 * WAVES;
   constexpr int VPT = (NVEC + NTHR - 1) / NTHR;
   constexpr int NPB = P / 16, NKK = N / K;
   constexpr int GP = kPairsPerGroup;
+  // token-row tiles move between HBM and LDS as whole rows (a wave's 16-byte
+  // vectors cover complete cache lines; fragment-shaped global accesses cost
+  // about four times as much issue time per instruction)
+  constexpr int QV = TWG * (N / VE) / NTHR;  // vectors per thread, Q or C tile
+  constexpr int EV = TWG * (P / VE) / NTHR;  // vectors per thread, E or y tile
+  static_assert(QV * NTHR == TWG * (N / VE) && EV * NTHR == TWG * (P / VE), "tile split");
+  constexpr int R1A = TWG * LDN > TWG * LDE ? TWG * LDN : TWG * LDE;
+  constexpr int R1 = R1A > 2 * P * LDN ? R1A : 2 * P * LDN;
   typedef typename Vec16<T>::vec vec_t;
-  __shared__ __align__(16) T sh_mem[2][P * LDN];
+  // sh_r1: the Q, C and E tiles in turn during the prologue, then the two
+  // memory buffers; sh_ty: y_ssd, overwritten by y in the epilogue
+  __shared__ __align__(16) T sh_r1[R1];
+  __shared__ __align__(16) T sh_ty[TWG * LDE];
+  T(*sh_mem)[P * LDN] = reinterpret_cast<T(*)[P * LDN]>(sh_r1);
 
   const int M = L / S, tpc = S / TWG;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -92,25 +105,102 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   const int b = pair / H, h = pair % H, g = h / (H / G);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const long row_w = (long)b * L + (long)k * S + sub * TWG + w * TW;
+  const long row0 = (long)b * L + (long)k * S + sub * TWG;  // first token of the tile
+  auto lrow = [&](int tb) __attribute__((always_inline)) { return w * TW + tb * 16 + col; };
 
+  // ---- prologue: every load in flight before the first wait ----
+  vec_t qs[QV], cs[QV], es[EV], ys[EV];
+#pragma unroll
+  for (int v = 0; v < QV; ++v) {
+    const int i = tid + v * NTHR, t = i / (N / VE), nv = i % (N / VE);
+    qs[v] = load16(Q + ((row0 + t) * G + g) * N + nv * VE);
+  }
+#pragma unroll
+  for (int v = 0; v < EV; ++v) {
+    const int i = tid + v * NTHR, t = i / (P / VE), pv = i % (P / VE);
+    ys[v] = load16(y_ssd + ((row0 + t) * H + h) * P + pv * VE);
+  }
+#pragma unroll
+  for (int v = 0; v < QV; ++v) {
+    const int i = tid + v * NTHR, t = i / (N / VE), nv = i % (N / VE);
+    cs[v] = load16(C + ((row0 + t) * G + g) * N + nv * VE);
+  }
+#pragma unroll
+  for (int v = 0; v < EV; ++v) {
+    const int i = tid + v * NTHR, t = i / (P / VE), pv = i % (P / VE);
+    es[v] = load16(E + ((row0 + t) * H + h) * P + pv * VE);
+  }
+  const T* mem = dH + (long)pair * M * (P * N);
+  vec_t stg0[VPT], stg[VPT];
+  auto gload = [&](int c, vec_t (&dst)[VPT]) __attribute__((always_inline)) {
+    const vec_t* src = reinterpret_cast<const vec_t*>(mem + (long)c * (P * N));
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      const int vi = tid + v * NTHR;
+      if (NVEC % NTHR == 0 || vi < NVEC) dst[v] = src[vi];
+    }
+  };
+  auto swrite = [&](int buf, const vec_t (&src)[VPT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      const int vi = tid + v * NTHR;
+      if (NVEC % NTHR == 0 || vi < NVEC) {
+        const int p = vi / (N / VE), nv = vi % (N / VE);
+        *reinterpret_cast<vec_t*>(&sh_mem[buf][p * LDN + nv * VE]) = src[v];
+      }
+    }
+  };
+  if (k > 0) {
+    gload(0, stg0);
+    gload(min(1, k - 1), stg);
+  }
+  // Q tile -> fragments; y_ssd parked for the epilogue
+#pragma unroll
+  for (int v = 0; v < QV; ++v) {
+    const int i = tid + v * NTHR, t = i / (N / VE), nv = i % (N / VE);
+    *reinterpret_cast<vec_t*>(&sh_r1[t * LDN + nv * VE]) = qs[v];
+  }
+#pragma unroll
+  for (int v = 0; v < EV; ++v) {
+    const int i = tid + v * NTHR, t = i / (P / VE), pv = i % (P / VE);
+    *reinterpret_cast<vec_t*>(&sh_ty[t * LDE + pv * VE]) = ys[v];
+  }
+  __syncthreads();
   typename MM::frag qf[NTB][NKK], cf[NTB][NKK];
-  // E_t values of this lane's p rows, kept in their input type (bf16 pairs
-  // halve the registers) and widened when the score is formed
+#pragma unroll
+  for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qf[tb][kk] = MM::load(&sh_r1[lrow(tb) * LDN + kk * K + grp * KL]);
+  __syncthreads();
+  // C tile -> fragments
+#pragma unroll
+  for (int v = 0; v < QV; ++v) {
+    const int i = tid + v * NTHR, t = i / (N / VE), nv = i % (N / VE);
+    *reinterpret_cast<vec_t*>(&sh_r1[t * LDN + nv * VE]) = cs[v];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) cf[tb][kk] = MM::load(&sh_r1[lrow(tb) * LDN + kk * K + grp * KL]);
+  __syncthreads();
+  // E tile -> this lane's p rows, kept in the input type (bf16 pairs halve
+  // the registers) and widened when the score is formed
+#pragma unroll
+  for (int v = 0; v < EV; ++v) {
+    const int i = tid + v * NTHR, t = i / (P / VE), pv = i % (P / VE);
+    *reinterpret_cast<vec_t*>(&sh_r1[t * LDE + pv * VE]) = es[v];
+  }
+  __syncthreads();
   typedef typename std::conditional<std::is_same<T, bf16>::value, bf16x4, floatx4>::type e4_t;
   e4_t ev[NTB][NPB];
 #pragma unroll
-  for (int tb = 0; tb < NTB; ++tb) {
-    const long row = row_w + tb * 16 + col;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      qf[tb][kk] = MM::load(Q + (row * G + g) * N + kk * K + grp * KL);
-      cf[tb][kk] = MM::load(C + (row * G + g) * N + kk * K + grp * KL);
-    }
+  for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
     for (int pb = 0; pb < NPB; ++pb)
-      ev[tb][pb] = *reinterpret_cast<const e4_t*>(E + (row * H + h) * P + pb * 16 + 4 * grp);
-  }
+      ev[tb][pb] = *reinterpret_cast<const e4_t*>(&sh_r1[lrow(tb) * LDE + pb * 16 + 4 * grp]);
+  __syncthreads();  // sh_r1 becomes the memory buffers
+
   floatx4 acc[NTB][NPB];
   float mx[NTB], ls[NTB];
 #pragma unroll
@@ -121,28 +211,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     for (int pb = 0; pb < NPB; ++pb) acc[tb][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const T* mem = dH + (long)pair * M * (P * N);
-  vec_t stg[VPT];
-  auto gload = [&](int c) {
-    const vec_t* src = reinterpret_cast<const vec_t*>(mem + (long)c * (P * N));
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      const int vi = tid + v * NTHR;
-      if (NVEC % NTHR == 0 || vi < NVEC) stg[v] = src[vi];
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      const int vi = tid + v * NTHR;
-      if (NVEC % NTHR == 0 || vi < NVEC) {
-        const int p = vi / (N / VE), nv = vi % (N / VE);
-        *reinterpret_cast<vec_t*>(&sh_mem[buf][p * LDN + nv * VE]) = stg[v];
-      }
-    }
-  };
   floatx4 zq[NTB][NPB], zc[NTB][NPB];
-  auto mma_mem = [&](int cur) {
+  auto mma_mem = [&](int cur) __attribute__((always_inline)) {
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
@@ -171,7 +241,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
           zc[tb][pb] = MM::mma(a[pb & 1][kk], cf[tb][kk], zc[tb][pb]);
         }
     }
-    // schedule: LDS fragment reads run two fragments ahead of the MFMAs
+    // schedule: LDS fragment reads run four fragments ahead of the MFMAs
     // that consume them (2·NTB MFMAs per fragment cover the LDS latency)
     constexpr int R = NPB * NKK;
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -181,7 +251,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * NTB, 0);
     }
   };
-  auto softmax_mem = [&]() {
+  auto softmax_mem = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
       float s = 0.f;
@@ -206,7 +276,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   // memory c+1 is written into the other buffer in the second half (its
   // previous content, memory c-1, was last read a full barrier earlier).
   const bool lead = w < WAVES / 2;
-  auto half_steps = [&](int c, auto par_tag) {
+  auto half_steps = [&](int c, auto par_tag) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par_tag)::value;
     // first half: lead waves multiply memory c, the others finish memory c-1
     if (lead) {
@@ -224,16 +294,14 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     // unconditional, indices clamped to the last memory: a duplicate lands
     // in a buffer that is not read again, and every path issues the same
     // loads (so the wait before the LDS write covers only the older fetch)
-    swrite(PAR ^ 1);                 // memory c+1, fetched during step c-1
-    gload(min(c + 2, k - 1));        // memory c+2
+    swrite(PAR ^ 1, stg);            // memory c+1, fetched during step c-1
+    gload(min(c + 2, k - 1), stg);   // memory c+2
     __syncthreads();
   };
   if (k > 0) {
-    gload(0);
-    swrite(0);
-    gload(min(1, k - 1));
-    // all prologue loads (Q/C fragments, E, first memory) complete here, so
-    // the loop's only load in flight is the memory prefetch
+    swrite(0, stg0);
+    // memory 1 has arrived too, so the loop's only load in flight is the
+    // memory prefetch
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     for (int c = 0; c <= k; c += 2) {
@@ -242,16 +310,22 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     }
   }
 
+  // ---- epilogue: y = y_ssd + gate·o in LDS, then whole-row stores ----
 #pragma unroll
   for (int tb = 0; tb < NTB; ++tb) {
-    const long row = row_w + tb * 16 + col;
-    const float inv = k > 0 ? 1.f / ls[tb] : 0.f;
+    const float f = k > 0 ? gate / ls[tb] : 0.f;
 #pragma unroll
     for (int pb = 0; pb < NPB; ++pb) {
-      const long off = (row * H + h) * P + pb * 16 + 4 * grp;
-      const floatx4 ys = load4_f32(y_ssd + off);
-      store4(y + off, ys + (gate * inv) * acc[tb][pb]);
+      T* p = &sh_ty[lrow(tb) * LDE + pb * 16 + 4 * grp];
+      store4(p, load4_f32(p) + f * acc[tb][pb]);
     }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < EV; ++v) {
+    const int i = tid + v * NTHR, t = i / (P / VE), pv = i % (P / VE);
+    *reinterpret_cast<vec_t*>(y + ((row0 + t) * H + h) * P + pv * VE) =
+        *reinterpret_cast<const vec_t*>(&sh_ty[t * LDE + pv * VE]);
   }
 }
 

@@ -55,15 +55,19 @@ __device__ __forceinline__ float sum_lane_groups(float v) {
 //
 // Grid mapping: workgroups are dealt to the 8 XCDs round-robin, so
 // blockIdx % 8 selects an XCD and all tiles of one (batch, head) pair land
-// on the same XCD.  Inside an XCD the pairs are taken kPairsPerGroup at a
-// time, heaviest tiles (largest k) first within each group: the memories of
-// a group (4 x 512 KB at the largest shape) stay resident in the XCD's
-// 4 MB L2 while the k-ordering keeps the tail short.
+// on the same XCD.  When heads share B/C/Q groups (and the batch·group count
+// fills the 8 XCDs evenly) the heads of one (batch, group) go to the same
+// XCD and are ordered next to each other, so the Q_t/C_t tiles they share
+// are read from HBM once per XCD rather than once per head.  Inside an XCD
+// the pairs are taken kPairsPerGroup at a time, heaviest tiles (largest k)
+// first within each group: the memories of a group (4 x 512 KB at the
+// largest shape) stay resident in the XCD's 4 MB L2 while the k-ordering
+// keeps the tail short.
 template <typename T, int N, int P, int NTB, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     const T* __restrict__ Q, const T* __restrict__ E, const T* __restrict__ C,
     const T* __restrict__ dH, const T* __restrict__ y_ssd, float gate, T* __restrict__ y,
-    int BH, int L, int H, int G, int S, int npq, float scale_log2) {
+    int BH, int L, int H, int G, int S, int npq, int bg_major, float scale_log2) {
   using MM = Mma<T>;
   constexpr int K = MM::K, KL = MM::KL, VE = Vec16<T>::n;
   // LDS row strides (elements): a 32-byte pad keeps the 16-byte fragment reads
@@ -100,8 +104,18 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   const int qg = r % GP, kr = r / GP;
   const int ql = grp_i * GP + qg;
   const int k = M - 1 - kr;
-  const int pair = ql * 8 + xcd;
-  if (pair >= BH || ql >= npq) return;  // uniform over the workgroup
+  // bg_major: the heads of one (batch, group) run on one XCD, adjacent in
+  // the ordering, so their shared Q_t/C_t tiles are reused from L2
+  int pair;
+  if (bg_major) {
+    const int hpg = H / G;
+    const int bg = (ql / hpg) * 8 + xcd;
+    pair = (bg / G) * H + (bg % G) * hpg + ql % hpg;
+    if (bg >= BH / hpg || ql >= npq) return;
+  } else {
+    pair = ql * 8 + xcd;
+    if (pair >= BH || ql >= npq) return;  // uniform over the workgroup
+  }
   const int b = pair / H, h = pair % H, g = h / (H / G);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -540,13 +554,16 @@ hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T*
                          const T* y_ssd, float gate, T* y, hipStream_t st) {
   const int M = s.L / s.S;
   const int BH = s.B * s.H;
-  const int npq = (BH + 7) / 8;  // (batch, head) pairs per XCD
+  const int hpg = s.H / s.G;
+  const int bg_major = hpg > 1 && (s.B * s.G) % 8 == 0;
+  const int npq = bg_major ? (s.B * s.G / 8) * hpg : (BH + 7) / 8;  // pairs per XCD
   const int tpc = s.S / (16 * NTB * WAVES);
   const int ngrp = (npq + kPairsPerGroup - 1) / kPairsPerGroup;
   const long blocks = 8L * ngrp * kPairsPerGroup * M * tpc;
   const float scale_log2 = kLog2e / sqrtf(static_cast<float>(N));
   hipLaunchKernelGGL((k_sma_fwd<T, N, P, NTB, WAVES>), dim3(blocks), dim3(64 * WAVES), 0, st, Q,
-                     E, C, dH, y_ssd, gate, y, BH, s.L, s.H, s.G, s.S, npq, scale_log2);
+                     E, C, dH, y_ssd, gate, y, BH, s.L, s.H, s.G, s.S, npq, bg_major,
+                     scale_log2);
   return hipGetLastError();
 }
 

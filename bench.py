@@ -28,8 +28,8 @@ METRIC = "SMA+scan prefill tokens/s & MFMA% at L=8K; decode chunk-memory HBM GB/
 # kernel source they were measured on.
 KERNEL_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                              "ssm_state_attention_amd", "csrc", "k_sma.hip")
-PROFILED_TRAFFIC = {"source_sha1": "b402f63d89f3dc831106922e8889de2ce6a53749",
-                    "k_sma_fwd": (948.1 + 134.2) * 1e6,
+PROFILED_TRAFFIC = {"source_sha1": "0b734b445ac6d359a25227bd04b7f679f68df28d",
+                    "k_sma_fwd": (548.1 + 134.2) * 1e6,
                     "k_sma_decode": (4431.6 + 134.5) * 1e6}
 
 

@@ -101,6 +101,20 @@ __device__ __forceinline__ typename Vec16<T>::vec load16_nt(const T* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const typename Vec16<T>::vec*>(p));
 }
 
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Inside each group of 16
+// lanes, lane i receives element i%4 of the 8-byte reads addressed by lanes
+// i/4, 4 + i/4, 8 + i/4 and 12 + i/4 of the group.  When lane j of a group
+// addresses row r0 + j/4, columns c0 + 4·(j%4) .. +3 of a row-major tile,
+// lane i therefore receives column c0 + i of rows r0 .. r0+3: four
+// consecutive rows of one column, which is the k-run an MFMA operand lane
+// supplies when the tile's rows are the contraction axis.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s4 lds_s4;
+  const s4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(const_cast<bf16*>(p)));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);

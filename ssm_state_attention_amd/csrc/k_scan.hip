@@ -402,6 +402,267 @@ __global__ __launch_bounds__(kOutThreads) void k_chunk_out(
   }
 }
 
+// LDS plan of k_chunk_out_tr.  Row strides carry a 32-byte pad (see the
+// fragment-read notes in k_sma.hip); phase 1 holds the B and C tiles,
+// phase 2 reuses the same bytes for x, H_in[k]ᵀ and, when it fits, y.
+template <int N, int P>
+struct ChunkOutTr {
+  static constexpr int LDC = N + 16;  // B and C rows [s][n]
+  static constexpr int LDX = P + 16;  // x rows [s][p]
+  static constexpr int LDH = N + 16;  // H_in[k]ᵀ rows [p][n], rounded to bf16
+  static constexpr int LDY = P + 16;  // y rows [t][p]
+  // the next head's x and H_in[k] are fetched into registers while the
+  // current head computes, and y leaves through LDS as whole token rows,
+  // when registers and LDS allow (P <= 64)
+  static constexpr bool kPrefetch = P <= 64;
+  static constexpr bool kStageY = P <= 64;
+  static constexpr size_t phase1 = 2ull * kMaxChunk * LDC * sizeof(bf16);
+  static constexpr size_t phase2 =
+      (size_t(kMaxChunk) * LDX + size_t(P) * LDH + (kStageY ? size_t(kMaxChunk) * LDY : 0)) *
+      sizeof(bf16);
+  static constexpr size_t bytes = phase1 > phase2 ? phase1 : phase2;
+};
+
+// Native chunk output, 16-bit io: the arithmetic of k_chunk_out (same
+// tiles, same factored weights, same k-slot pairing of two key blocks), with
+// every HBM access in whole token rows.  x stays row-major in LDS and the
+// xᵀ operand of the intra product is read with LDS transpose reads; B and C
+// are staged row-major once per workgroup.  The C·Bᵀ tiles of a wave's two
+// token blocks (at most kMaxBlk + 2 with the pairing) sit in one slot array:
+// token block tb0's tile jb in slot jb, tb1's tile jb in slot
+// kMaxBlk + 1 - jb, so every register index stays a compile-time constant.
+template <int N, int P>
+__global__ __launch_bounds__(kOutThreads) void k_chunk_out_tr(
+    const bf16* __restrict__ x, const float* __restrict__ dt, const bf16* __restrict__ Bm,
+    const bf16* __restrict__ C, const float* __restrict__ acum, const float* __restrict__ H_in,
+    bf16* __restrict__ y_ssd, int L, int H, int G, int S) {
+  using MM = Mma<bf16>;
+  using Lds = ChunkOutTr<N, P>;
+  typedef bf16x8 vec_t;
+  constexpr int VE = 8, K = MM::K, KL = MM::KL;
+  constexpr int LDC = Lds::LDC, LDX = Lds::LDX, LDH = Lds::LDH, LDY = Lds::LDY;
+  constexpr int NKK = N / K, NPB = P / 16;
+  constexpr int NSLOT = kMaxBlk + 2;
+  constexpr int RV = kMaxChunk * (N / VE) / kOutThreads;  // B or C vectors per thread
+  constexpr int XV = kMaxChunk * (P / VE) / kOutThreads;  // x or y vectors per thread
+  constexpr int HQ = P * N / 4;                           // H_in[k] as float4s
+  constexpr int HV = (HQ + kOutThreads - 1) / kOutThreads;
+  static_assert(RV * kOutThreads == kMaxChunk * (N / VE) &&
+                    XV * kOutThreads == kMaxChunk * (P / VE),
+                "k_chunk_out_tr staging split");
+  static_assert(kOutWaves * 2 == kMaxBlk, "two token blocks per wave");
+  __shared__ __align__(16) unsigned char sh_raw[Lds::bytes];
+  __shared__ __align__(16) float sh_at[kMaxChunk];  // A_s = acum_s·log2(e)
+  __shared__ __align__(16) float sh_v[kMaxChunk];   // v_j
+  bf16* sh_b = reinterpret_cast<bf16*>(sh_raw);
+  bf16* sh_c = sh_b + kMaxChunk * LDC;
+  bf16* sh_x = reinterpret_cast<bf16*>(sh_raw);
+  bf16* sh_h = sh_x + kMaxChunk * LDX;
+  bf16* sh_y = sh_h + P * LDH;
+
+  const int k = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int M = L / S, hpg = H / G, NB = S / 16;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const long tok0 = (long)b * L + (long)k * S;
+  const int tb0 = w, tb1 = 2 * kOutWaves - 1 - w;
+  const bool has0 = tb0 < NB, has1 = tb1 < NB;
+  const int n0 = has0 ? 2 * (tb0 / 2 + 1) : 0;  // slots of tb0 (pairs of key blocks)
+  const int n1 = has1 ? 2 * (tb1 / 2 + 1) : 0;
+
+  // per-head inputs, fetched one head ahead when kPrefetch
+  vec_t xr[XV];
+  floatx4 hr[HV];
+  float ar = 0.f, dr = 1.f;
+  auto load_head = [&](int hh) __attribute__((always_inline)) {
+    const int h = g * hpg + hh;
+    const long pair = (long)b * H + h;
+#pragma unroll
+    for (int v = 0; v < XV; ++v) {
+      const int i = tid + v * kOutThreads, s = i / (P / VE), pv = i % (P / VE);
+      if (s < S) xr[v] = load16(x + ((tok0 + s) * H + h) * P + pv * VE);
+    }
+    const floatx4* hsrc =
+        reinterpret_cast<const floatx4*>(H_in + (pair * (M + 1) + k) * (long)(P * N));
+#pragma unroll
+    for (int v = 0; v < HV; ++v) {
+      const int i = tid + v * kOutThreads;
+      if (HQ % kOutThreads == 0 || i < HQ) hr[v] = hsrc[i];
+    }
+    if (tid < S) {
+      ar = acum[(pair * M + k) * S + tid];
+      dr = dt[(tok0 + tid) * H + h];
+    }
+  };
+
+  // ---- phase 1: B and C rows -> LDS; C·Bᵀ tiles of this wave's blocks ----
+  {
+    vec_t br[RV], cr[RV];
+#pragma unroll
+    for (int v = 0; v < RV; ++v) {
+      const int i = tid + v * kOutThreads, s = i / (N / VE), nv = i % (N / VE);
+      if (s < S) {
+        br[v] = load16(Bm + ((tok0 + s) * G + g) * N + nv * VE);
+        cr[v] = load16(C + ((tok0 + s) * G + g) * N + nv * VE);
+      }
+    }
+    if (Lds::kPrefetch) load_head(0);
+#pragma unroll
+    for (int v = 0; v < RV; ++v) {
+      const int i = tid + v * kOutThreads, s = i / (N / VE), nv = i % (N / VE);
+      if (s < S) {
+        *reinterpret_cast<vec_t*>(&sh_b[s * LDC + nv * VE]) = br[v];
+        *reinterpret_cast<vec_t*>(&sh_c[s * LDC + nv * VE]) = cr[v];
+      }
+    }
+  }
+  __syncthreads();
+  // C fragments (B operand: column t, k-slots n) of the two token blocks
+  typename MM::frag cf0[NKK], cf1[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const int t0 = has0 ? tb0 * 16 + col : col, t1 = has1 ? tb1 * 16 + col : col;
+    cf0[kk] = MM::load(&sh_c[t0 * LDC + kk * K + grp * KL]);
+    cf1[kk] = MM::load(&sh_c[t1 * LDC + kk * K + grp * KL]);
+  }
+  floatx4 gs[NSLOT];
+#pragma unroll
+  for (int sl = 0; sl < NSLOT; ++sl) {
+    gs[sl] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const bool is0 = sl < n0;
+    const int jb = is0 ? sl : NSLOT - 1 - sl;
+    const bool live = is0 ? sl <= tb0 : (jb < n1 && jb <= tb1);
+    if (live) {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        gs[sl] = MM::mma(MM::load(&sh_b[(jb * 16 + col) * LDC + kk * K + grp * KL]),
+                         is0 ? cf0[kk] : cf1[kk], gs[sl]);
+    }
+  }
+  __syncthreads();  // B and C are dead; phase 2 reuses their LDS
+
+  // ---- phase 2: the heads of the group ----
+  for (int hh = 0; hh < hpg; ++hh) {
+    const int h = g * hpg + hh;
+    if (!Lds::kPrefetch) load_head(hh);
+    // stage head hh: x rows, H_in[k]ᵀ rows in bf16, log-decay factors
+#pragma unroll
+    for (int v = 0; v < XV; ++v) {
+      const int i = tid + v * kOutThreads, s = i / (P / VE), pv = i % (P / VE);
+      if (s < S) *reinterpret_cast<vec_t*>(&sh_x[s * LDX + pv * VE]) = xr[v];
+    }
+#pragma unroll
+    for (int v = 0; v < HV; ++v) {
+      const int i = tid + v * kOutThreads;
+      if (HQ % kOutThreads == 0 || i < HQ) {
+        const int p = (i * 4) / N, n = (i * 4) % N;
+        const floatx4 hv = hr[v];
+        *reinterpret_cast<bf16x4*>(&sh_h[p * LDH + n]) =
+            bf16x4{from_f32<bf16>(hv[0]), from_f32<bf16>(hv[1]), from_f32<bf16>(hv[2]),
+                   from_f32<bf16>(hv[3])};
+      }
+    }
+    {
+      // A at the end of this thread's 16-token block comes from lane tid|15
+      // of the same wave
+      const float a2 = ar * kLog2e;
+      const float e2 = __shfl(a2, lane | 15);
+      if (tid < S) {
+        sh_at[tid] = a2;
+        sh_v[tid] = exp2_fast(e2 - a2 + __builtin_amdgcn_logf(dr));
+      }
+    }
+    __syncthreads();
+    if (Lds::kPrefetch && hh + 1 < hpg) load_head(hh + 1);
+
+    // one token block, in NPH passes over the value axis of NPP p-blocks each
+    // (four passes at P = 128 keep the accumulators inside the register file)
+    constexpr int NPH = NPB > 4 ? 4 : 1, NPP = NPB / NPH;
+    auto block_out = [&](int tb, const typename MM::frag (&cf)[NKK], auto pick)
+        __attribute__((always_inline)) {
+      const int t = tb * 16 + col;
+      const float at_t = sh_at[t];
+#pragma unroll
+      for (int ph = 0; ph < NPH; ++ph) {
+      floatx4 yin[NPP], yia[NPP];
+#pragma unroll
+      for (int q = 0; q < NPP; ++q) {
+        const int pb = ph * NPP + q;
+        yin[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+        yia[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+          yin[q] = MM::mma(MM::load(&sh_h[(pb * 16 + col) * LDH + kk * K + grp * KL]), cf[kk],
+                           yin[q]);
+      }
+      // weighted tile jb (rows j = jb*16 + 4*grp + i, column t)
+      auto weights = [&](int jb, floatx4 tile) __attribute__((always_inline)) {
+        const float u = exp2_fast(at_t - sh_at[jb * 16 + 15]);
+        const floatx4 vj = *reinterpret_cast<const floatx4*>(&sh_v[jb * 16 + 4 * grp]);
+        floatx4 wv;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          wv[i4] = (jb * 16 + 4 * grp + i4 <= t) ? tile[i4] * (u * vj[i4]) : 0.f;
+        return wv;
+      };
+#pragma unroll
+      for (int jb0 = 0; jb0 < kMaxBlk; jb0 += 2) {
+        if (jb0 <= tb) {
+          floatx4 t0, t1;
+          pick(jb0, t0, t1);
+          const floatx4 w0 = weights(jb0, t0), w1 = weights(jb0 + 1, t1);
+          const bf16x8 bfr = {from_f32<bf16>(w0[0]), from_f32<bf16>(w0[1]),
+                              from_f32<bf16>(w0[2]), from_f32<bf16>(w0[3]),
+                              from_f32<bf16>(w1[0]), from_f32<bf16>(w1[1]),
+                              from_f32<bf16>(w1[2]), from_f32<bf16>(w1[3])};
+          // xᵀ operand: rows p, k-slots j = jb0*16 + 4*grp + 0..3 and
+          // (jb0+1)*16 + 4*grp + 0..3, by transpose reads of the x rows
+          const int r0 = jb0 * 16 + 4 * grp + (col >> 2), c0 = 4 * (col & 3);
+#pragma unroll
+          for (int q = 0; q < NPP; ++q) {
+            const int pb = ph * NPP + q;
+            const bf16x4 lo = lds_read_tr4(&sh_x[r0 * LDX + pb * 16 + c0]);
+            const bf16x4 hi = lds_read_tr4(&sh_x[(r0 + 16) * LDX + pb * 16 + c0]);
+            const bf16x8 afr = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            yia[q] = MM::mma(afr, bfr, yia[q]);
+          }
+        }
+      }
+      const float dec_t = exp2_fast(at_t);
+#pragma unroll
+      for (int q = 0; q < NPP; ++q) {
+        const int pb = ph * NPP + q;
+        const floatx4 v = yia[q] + dec_t * yin[q];
+        if constexpr (Lds::kStageY)
+          store4(&sh_y[t * LDY + pb * 16 + 4 * grp], v);
+        else
+          store4(y_ssd + ((tok0 + t) * H + h) * P + pb * 16 + 4 * grp, v);
+      }
+      }
+    };
+    if (has0)
+      block_out(tb0, cf0, [&](int jb0, floatx4& t0, floatx4& t1) __attribute__((always_inline)) {
+        t0 = gs[jb0];
+        t1 = gs[jb0 + 1];
+      });
+    if (has1)
+      block_out(tb1, cf1, [&](int jb0, floatx4& t0, floatx4& t1) __attribute__((always_inline)) {
+        t0 = gs[NSLOT - 1 - jb0];
+        t1 = gs[NSLOT - 2 - jb0];
+      });
+    __syncthreads();  // x, H and the factors of head hh are dead; y is complete
+    if constexpr (Lds::kStageY) {
+#pragma unroll
+      for (int v = 0; v < XV; ++v) {
+        const int i = tid + v * kOutThreads, t = i / (P / VE), pv = i % (P / VE);
+        if (t < S)
+          *reinterpret_cast<vec_t*>(y_ssd + ((tok0 + t) * H + h) * P + pv * VE) =
+              *reinterpret_cast<const vec_t*>(&sh_y[t * LDY + pv * VE]);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 template <typename T, int N, int P>
@@ -423,8 +684,12 @@ hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt,
                      dim3(kThreads), 0, st, acum, dH_f32, h0, H_in, s.H, M, s.S, PN);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_chunk_out<T, N, P>), dim3(M, s.G, s.B), dim3(kOutThreads), 0, st, x, dt, Bm,
-                     C, acum, H_in, y_ssd, s.L, s.H, s.G, s.S);
+  if constexpr (std::is_same<T, bf16>::value)
+    hipLaunchKernelGGL((k_chunk_out_tr<N, P>), dim3(M, s.G, s.B), dim3(kOutThreads), 0, st, x, dt,
+                       Bm, C, acum, H_in, y_ssd, s.L, s.H, s.G, s.S);
+  else
+    hipLaunchKernelGGL((k_chunk_out<T, N, P>), dim3(M, s.G, s.B), dim3(kOutThreads), 0, st, x, dt,
+                       Bm, C, acum, H_in, y_ssd, s.L, s.H, s.G, s.S);
   return hipGetLastError();
 }
 

@@ -462,7 +462,8 @@ __global__ __launch_bounds__(kOutThreads) void k_chunk_out_tr(
 
   const int k = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int M = L / S, hpg = H / G, NB = S / 16;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index is uniform: scalar branches on the token blocks it owns
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const long tok0 = (long)b * L + (long)k * S;
   const int tb0 = w, tb1 = 2 * kOutWaves - 1 - w;
@@ -537,6 +538,12 @@ __global__ __launch_bounds__(kOutThreads) void k_chunk_out_tr(
       for (int kk = 0; kk < NKK; ++kk)
         gs[sl] = MM::mma(MM::load(&sh_b[(jb * 16 + col) * LDC + kk * K + grp * KL]),
                          is0 ? cf0[kk] : cf1[kk], gs[sl]);
+      // causal mask of the diagonal tile (key j = jb*16 + 4*grp + i after
+      // query t = jb*16 + col), applied once for all heads
+      if (jb == (is0 ? tb0 : tb1)) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) gs[sl][i4] = 4 * grp + i4 <= col ? gs[sl][i4] : 0.f;
+      }
     }
   }
   __syncthreads();  // B and C are dead; phase 2 reuses their LDS
@@ -595,14 +602,16 @@ __global__ __launch_bounds__(kOutThreads) void k_chunk_out_tr(
           yin[q] = MM::mma(MM::load(&sh_h[(pb * 16 + col) * LDH + kk * K + grp * KL]), cf[kk],
                            yin[q]);
       }
-      // weighted tile jb (rows j = jb*16 + 4*grp + i, column t)
+      // weighted tile jb (rows j = jb*16 + 4*grp + i, column t).  The tiles
+      // are causally masked already and zero above the diagonal block; the
+      // clamp keeps u finite there (u <= 1 below the diagonal), so a zero
+      // tile stays zero.
       auto weights = [&](int jb, floatx4 tile) __attribute__((always_inline)) {
-        const float u = exp2_fast(at_t - sh_at[jb * 16 + 15]);
+        const float u = exp2_fast(fminf(at_t - sh_at[jb * 16 + 15], 126.f));
         const floatx4 vj = *reinterpret_cast<const floatx4*>(&sh_v[jb * 16 + 4 * grp]);
         floatx4 wv;
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-          wv[i4] = (jb * 16 + 4 * grp + i4 <= t) ? tile[i4] * (u * vj[i4]) : 0.f;
+        for (int i4 = 0; i4 < 4; ++i4) wv[i4] = (tile[i4] * u) * vj[i4];
         return wv;
       };
 #pragma unroll

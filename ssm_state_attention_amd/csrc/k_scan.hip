@@ -134,6 +134,150 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
   }
 }
 
+constexpr int kStKB = 64;  // tokens per K-block of k_chunk_state_tr
+
+// Chunk state memories, 16-bit io: the arithmetic of k_chunk_state with
+// every HBM access in whole token rows.  B and w∘x K-blocks sit row-major in
+// LDS ([s][n], [s][p]) and both MFMA operands are read with LDS transpose
+// reads, so the token axis becomes each lane's k-run without a transposing
+// store.  Lane group grp takes the k-slots s = ks + 4·grp + 0..3 and
+// ks + 16 + 4·grp + 0..3 of a 32-token step in both operands (each read
+// covers 16 consecutive rows: no LDS bank conflicts at either row stride).
+// The loads of K-block i+1 are in flight while block i multiplies.
+template <int N, int P>
+__global__ __launch_bounds__(kThreads) void k_chunk_state_tr(
+    const bf16* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
+    const bf16* __restrict__ Bm, float* __restrict__ acum, bf16* __restrict__ dH,
+    float* __restrict__ dHf, int L, int H, int G, int S) {
+  using MM = Mma<bf16>;
+  typedef bf16x8 vec_t;
+  constexpr int VE = 8, K = MM::K;
+  constexpr int LDB = N + 16, LDX = P + 16;  // row strides (elements)
+  constexpr int NB = N / 16;
+  constexpr int NPB = P / 16;
+  constexpr int NT = NB * NPB;        // 16x16 output tiles
+  constexpr int TPW = (NT + 3) / 4;   // tiles per wave
+  // wave w owns n-blocks w, w+4, ... (NBW of them) for every p-block when
+  // NB % 4 == 0 (each operand fragment then feeds several tiles); otherwise
+  // tile w + 4·j
+  constexpr bool kGrid = NB % 4 == 0;
+  constexpr int NBW = kGrid ? NB / 4 : 1;
+  constexpr int XV = kStKB * (P / VE) / kThreads;  // vectors per thread per K-block
+  constexpr int BV = kStKB * (N / VE) / kThreads;
+  static_assert(XV * kThreads == kStKB * (P / VE) && BV * kThreads == kStKB * (N / VE),
+                "k_chunk_state_tr staging split");
+  __shared__ __align__(16) bf16 sh_b[kStKB * LDB];
+  __shared__ __align__(16) bf16 sh_x[kStKB * LDX];
+  __shared__ float sh_w[kMaxChunk];
+  __shared__ float sh_part[4];
+
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int M = L / S, g = h / (H / G);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const long tok0 = (long)b * L + (long)c * S;
+  const long pair = (long)b * H + h;
+
+  vec_t xr[XV], br[BV];
+  auto fetch = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < XV; ++v) {
+      const int i = tid + v * kThreads, s = i / (P / VE), pv = i % (P / VE);
+      xr[v] = s0 + s < S ? load16(x + ((tok0 + s0 + s) * H + h) * P + pv * VE) : vec_t{};
+    }
+#pragma unroll
+    for (int v = 0; v < BV; ++v) {
+      const int i = tid + v * kThreads, s = i / (N / VE), nv = i % (N / VE);
+      br[v] = s0 + s < S ? load16(Bm + ((tok0 + s0 + s) * G + g) * N + nv * VE) : vec_t{};
+    }
+  };
+  const float dtv = tid < S ? dt[(tok0 + tid) * H + h] : 0.f;
+  fetch(0);
+
+  // 1. log-decay prefix sum, one token per thread (S <= 256)
+  float v = dtv * A[h];
+  for (int off = 1; off < 64; off <<= 1) {
+    const float u = __shfl_up(v, off);
+    if (lane >= off) v += u;
+  }
+  if (lane == 63) sh_part[w] = v;
+  __syncthreads();
+  for (int i = 0; i < w; ++i) v += sh_part[i];
+  const float total = sh_part[0] + sh_part[1] + sh_part[2] + sh_part[3];
+  if (tid < S) {
+    acum[(pair * M + c) * S + tid] = v;
+    sh_w[tid] = exp_neg(total - v) * dtv;
+  }
+  __syncthreads();
+
+  // 2. dH[n][p] = sum_s B[s][n]·w_s·x[s][p] over K-blocks of kStKB tokens
+  floatx4 acc[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += kStKB) {
+#pragma unroll
+    for (int v2 = 0; v2 < BV; ++v2) {
+      const int i = tid + v2 * kThreads, s = i / (N / VE), nv = i % (N / VE);
+      *reinterpret_cast<vec_t*>(&sh_b[s * LDB + nv * VE]) = br[v2];
+    }
+#pragma unroll
+    for (int v2 = 0; v2 < XV; ++v2) {
+      const int i = tid + v2 * kThreads, s = i / (P / VE), pv = i % (P / VE);
+      const float wv = s0 + s < S ? sh_w[s0 + s] : 0.f;
+      vec_t o;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) o[e] = from_f32<bf16>(to_f32(xr[v2][e]) * wv);
+      *reinterpret_cast<vec_t*>(&sh_x[s * LDX + pv * VE]) = o;
+    }
+    __syncthreads();
+    if (s0 + kStKB < S) fetch(s0 + kStKB);
+#pragma unroll
+    for (int ks = 0; ks < kStKB; ks += K) {
+      const int r0 = ks + 4 * grp + (col >> 2), c0 = 4 * (col & 3);
+      // k-slots r0 .. (4 rows) and r0 + 16 .. of column c + col
+      auto frag = [&](const bf16* tile, int ld, int c) __attribute__((always_inline)) {
+        const bf16x4 lo = lds_read_tr4(&tile[r0 * ld + c + c0]);
+        const bf16x4 hi = lds_read_tr4(&tile[(r0 + 16) * ld + c + c0]);
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      if constexpr (kGrid) {
+        bf16x8 af[NBW], bfr[NPB];
+#pragma unroll
+        for (int q = 0; q < NBW; ++q) af[q] = frag(sh_b, LDB, (w + 4 * q) * 16);
+#pragma unroll
+        for (int pb = 0; pb < NPB; ++pb) bfr[pb] = frag(sh_x, LDX, pb * 16);
+#pragma unroll
+        for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+          for (int q = 0; q < NBW; ++q)
+            acc[pb * NBW + q] = MM::mma(af[q], bfr[pb], acc[pb * NBW + q]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+          const int tt = w + 4 * j;
+          if (tt < NT)
+            acc[j] = MM::mma(frag(sh_b, LDB, (tt % NB) * 16), frag(sh_x, LDX, (tt / NB) * 16),
+                             acc[j]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // 3. store memory c value-axis-major: lane holds n = nb*16 + 4*grp + i, p = pb*16 + col
+  const long base = (pair * M + c) * (long)(P * N);
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int tt = w + 4 * j;
+    if (kGrid || tt < NT) {
+      const int nb = kGrid ? w + 4 * (j % NBW) : tt % NB, pb = kGrid ? j / NBW : tt / NB;
+      const long off = base + (long)(pb * 16 + col) * N + nb * 16 + 4 * grp;
+      store4(dH + off, acc[j]);
+      store4(dHf + off, acc[j]);
+    }
+  }
+}
+
 // H_in[0] = h0, H_in[c+1] = exp(acum_end[c])·H_in[c] + dH_f32[c]; one thread
 // per four state entries of one (batch, head), serial over chunks.
 __global__ __launch_bounds__(kThreads) void k_state_pass(
@@ -678,8 +822,12 @@ template <typename T, int N, int P>
 hipError_t launch_chunk_state(const PrefillShape& s, const T* x, const float* dt, const float* A,
                               const T* Bm, float* acum, T* dH, float* dH_f32, hipStream_t st) {
   const int M = s.L / s.S;
-  hipLaunchKernelGGL((k_chunk_state<T, N, P>), dim3(M, s.H, s.B), dim3(kThreads), 0, st, x, dt,
-                     A, Bm, acum, dH, dH_f32, s.L, s.H, s.G, s.S);
+  if constexpr (std::is_same<T, bf16>::value)
+    hipLaunchKernelGGL((k_chunk_state_tr<N, P>), dim3(M, s.H, s.B), dim3(kThreads), 0, st, x, dt,
+                       A, Bm, acum, dH, dH_f32, s.L, s.H, s.G, s.S);
+  else
+    hipLaunchKernelGGL((k_chunk_state<T, N, P>), dim3(M, s.H, s.B), dim3(kThreads), 0, st, x, dt,
+                       A, Bm, acum, dH, dH_f32, s.L, s.H, s.G, s.S);
   return hipGetLastError();
 }
 

@@ -87,7 +87,8 @@ def bench_prefill(args, torch, api, synth):
         "acum": torch.empty(B, H, M, S, **f32),
         "dH": torch.empty(B, H, M, P, N, dtype=torch.bfloat16, device="cuda:0"),
         "dH_f32": torch.empty(B, H, M, P, N, **f32),
-        "H_in": torch.empty(B, H, M + 1, P, N, **f32),
+        "H_in": torch.empty(B, H, M, P, N, dtype=torch.bfloat16, device="cuda:0"),
+        "h_final": torch.empty(B, H, P, N, **f32),
         "y_ssd": torch.empty(B, L, H, P, dtype=torch.bfloat16, device="cuda:0"),
         "y": torch.empty(B, L, H, P, dtype=torch.bfloat16, device="cuda:0"),
     }
@@ -100,7 +101,7 @@ def bench_prefill(args, torch, api, synth):
         if ev:
             ev[1].record()
         api.dart_state_pass(d["x"], d["dt"], d["Bm"], d["C"], out["acum"], out["dH_f32"], None,
-                            out["H_in"], out["y_ssd"], S)
+                            out["H_in"], out["h_final"], out["y_ssd"], S)
         if ev:
             ev[2].record()
         api.dart_sma_fwd(d["Q"], d["E"], d["C"], out["dH"], out["y_ssd"], c["gate"], out["y"], S)

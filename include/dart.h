@@ -99,20 +99,24 @@ dart_status dart_chunk_state(const dart_dims* dims, const void* x, const float* 
  * attention, paper Eq. 4; intra- and inter-chunk terms of the chunked scan)
  * and "Core claim" (Mamba-2 reads values from its state as C_t·H_t).
  *
- *   H_in[0] = h0 (zero when h0 == NULL)
- *   H_in[c+1] = exp(acum[c, S-1])·H_in[c] + dH_f32[c]       (H_in[M] = final)
+ *   H[0] = h0 (zero when h0 == NULL)
+ *   H[c+1] = exp(acum[c, S-1])·H[c] + dH_f32[c]      (recurrence in f32)
+ *   H_in[c] = io(H[c]) for c < M;  h_final = H[M]
  *   y_ssd[t] = sum_{j in k, j<=t} (C_t·B_j)·exp(acum_t - acum_j)·dt_j·x_j
  *            + exp(acum_t)·C_tᵀ·H_in[k]
  *
  * in:  x, dt, Bm as above; C [B,L,G,N] io; acum, dH_f32 from
  *      dart_chunk_state; h0 [B,H,P,N] f32 or NULL
- * out: H_in [B,H,M+1,P,N] f32; y_ssd [B,L,H,P] io (rounded to the io type
- *      once, like every io-typed output)
+ * out: H_in [B,H,M,P,N] io, the state entering each chunk, rounded to the io
+ *      type once (the precision y_ssd's inter-chunk product uses);
+ *      h_final [B,H,P,N] f32, the state after the last chunk (the decode
+ *      state h that continues this sequence); y_ssd [B,L,H,P] io (rounded
+ *      to the io type once, like every io-typed output)
  */
 dart_status dart_state_pass(const dart_dims* dims, const void* x, const float* dt,
                             const void* Bm, const void* C, const float* acum,
-                            const float* dH_f32, const float* h0, float* H_in,
-                            void* y_ssd, void* stream);
+                            const float* dH_f32, const float* h0, void* H_in,
+                            float* h_final, void* y_ssd, void* stream);
 
 /*
  * State-memory attention over completed chunks plus the gated add.

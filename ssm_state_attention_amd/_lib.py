@@ -38,7 +38,7 @@ _F = ctypes.c_float
 _SIG = {
     "dart_chunk_state": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "dart_state_pass": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
-                        _VP],
+                        _VP, _VP],
     "dart_sma_fwd": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _F, _VP, _VP],
     "dart_sma_decode_workspace": [ctypes.POINTER(DartDecodeDims)],
     "dart_sma_decode": [ctypes.POINTER(DartDecodeDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F,

@@ -65,9 +65,10 @@ def dart_chunk_state(x, dt, A, Bm, acum, dH, dH_f32, chunk):
     check(lib().dart_chunk_state(d, *args, _stream()), "dart_chunk_state")
 
 
-def dart_state_pass(x, dt, Bm, C, acum, dH_f32, h0, H_in, y_ssd, chunk):
-    """State passing H_in [B,H,M+1,P,N] f32 and native output y_ssd
-    [B,L,H,P] in the io type; h0 [B,H,P,N] f32 or None (zero)."""
+def dart_state_pass(x, dt, Bm, C, acum, dH_f32, h0, H_in, h_final, y_ssd, chunk):
+    """State passing: H_in [B,H,M,P,N] io (state entering each chunk),
+    h_final [B,H,P,N] f32 and the native output y_ssd [B,L,H,P] io;
+    h0 [B,H,P,N] f32 or None (zero)."""
     d = prefill_dims(x, Bm, chunk)
     B, L, H, P = x.shape
     G, N = Bm.shape[2], Bm.shape[3]
@@ -77,7 +78,8 @@ def dart_state_pass(x, dt, Bm, C, acum, dH_f32, h0, H_in, y_ssd, chunk):
             _ptr(acum, "acum", torch.float32, (B, H, M, chunk), dev),
             _ptr(dH_f32, "dH_f32", torch.float32, (B, H, M, P, N), dev),
             _ptr(h0, "h0", torch.float32, (B, H, P, N), dev),
-            _ptr(H_in, "H_in", torch.float32, (B, H, M + 1, P, N), dev),
+            _ptr(H_in, "H_in", io, (B, H, M, P, N), dev),
+            _ptr(h_final, "h_final", torch.float32, (B, H, P, N), dev),
             _ptr(y_ssd, "y_ssd", io, (B, L, H, P), dev)]
     check(lib().dart_state_pass(d, *args, _stream()), "dart_state_pass")
 
@@ -132,8 +134,9 @@ def dart_sma_decode(x, dt, A, Bm, C, Q, E, gate, cache, h, dH_cur, n_chunks, pos
 # ----------------------------------------------------------------- helpers
 def prefill(x, dt, A, Bm, C, Q, E, gate, chunk, h0=None):
     """Whole prefill path; returns a dict of device tensors: y, y_ssd, dH
-    ([B,H,M,P,N] io), dH_f32, H_in ([B,H,M+1,P,N] f32; H_in[:, :, -1] is the
-    final state) and acum."""
+    ([B,H,M,P,N] io), dH_f32, H_in ([B,H,M,P,N] io, the state entering each
+    chunk), h_final ([B,H,P,N] f32, the state after the last chunk) and
+    acum."""
     B, L, H, P = x.shape
     N = Bm.shape[3]
     M, dev = L // chunk, x.device
@@ -142,13 +145,14 @@ def prefill(x, dt, A, Bm, C, Q, E, gate, chunk, h0=None):
         "acum": torch.empty(B, H, M, chunk, **f32),
         "dH": torch.empty(B, H, M, P, N, dtype=x.dtype, device=dev),
         "dH_f32": torch.empty(B, H, M, P, N, **f32),
-        "H_in": torch.empty(B, H, M + 1, P, N, **f32),
+        "H_in": torch.empty(B, H, M, P, N, dtype=x.dtype, device=dev),
+        "h_final": torch.empty(B, H, P, N, **f32),
         "y_ssd": torch.empty(B, L, H, P, dtype=x.dtype, device=x.device),
         "y": torch.empty(B, L, H, P, dtype=x.dtype, device=dev),
     }
     dart_chunk_state(x, dt, A, Bm, out["acum"], out["dH"], out["dH_f32"], chunk)
-    dart_state_pass(x, dt, Bm, C, out["acum"], out["dH_f32"], h0, out["H_in"], out["y_ssd"],
-                    chunk)
+    dart_state_pass(x, dt, Bm, C, out["acum"], out["dH_f32"], h0, out["H_in"], out["h_final"],
+                    out["y_ssd"], chunk)
     dart_sma_fwd(Q, E, C, out["dH"], out["y_ssd"], gate, out["y"], chunk)
     return out
 

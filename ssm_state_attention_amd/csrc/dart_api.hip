@@ -60,14 +60,16 @@ struct StatePassFn {
   dart::PrefillShape sh;
   const void *x, *Bm, *C;
   const float *dt, *acum, *dHf, *h0;
-  float* H_in;
+  void* H_in;
+  float* h_final;
   void* y_ssd;
   hipStream_t st;
   template <typename T, int N, int P>
   hipError_t run() {
     return dart::launch_state_pass<T, N, P>(sh, static_cast<const T*>(x), dt,
                                             static_cast<const T*>(Bm), static_cast<const T*>(C),
-                                            acum, dHf, h0, H_in, static_cast<T*>(y_ssd), st);
+                                            acum, dHf, h0, static_cast<T*>(H_in), h_final,
+                                            static_cast<T*>(y_ssd), st);
   }
 };
 
@@ -119,13 +121,13 @@ extern "C" dart_status dart_chunk_state(const dart_dims* dims, const void* x, co
 
 extern "C" dart_status dart_state_pass(const dart_dims* dims, const void* x, const float* dt,
                                        const void* Bm, const void* C, const float* acum,
-                                       const float* dH_f32, const float* h0, float* H_in,
-                                       void* y_ssd, void* stream) {
+                                       const float* dH_f32, const float* h0, void* H_in,
+                                       float* h_final, void* y_ssd, void* stream) {
   dart_status s = dart_validate_dims(dims);
   if (s != DART_OK) return s;
-  if ((s = check_ptrs(x, dt, Bm, C, acum, dH_f32, H_in, y_ssd)) != DART_OK) return s;
+  if ((s = check_ptrs(x, dt, Bm, C, acum, dH_f32, H_in, h_final, y_ssd)) != DART_OK) return s;
   if (h0 && !aligned16(h0)) return DART_ERR_ALIGN;
-  StatePassFn fn{prefill_shape(dims), x, Bm, C, dt, acum, dH_f32, h0, H_in, y_ssd,
+  StatePassFn fn{prefill_shape(dims), x, Bm, C, dt, acum, dH_f32, h0, H_in, h_final, y_ssd,
        static_cast<hipStream_t>(stream)};
   return dispatch(dims->io, dims->dstate, dims->headdim, fn);
 }

@@ -22,7 +22,8 @@ hipError_t launch_chunk_state(const PrefillShape& s, const T* x, const float* dt
 template <typename T, int N, int P>
 hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt, const T* Bm,
                              const T* C, const float* acum, const float* dH_f32,
-                             const float* h0, float* H_in, T* y_ssd, hipStream_t st);
+                             const float* h0, T* H_in, float* h_final, T* y_ssd,
+                             hipStream_t st);
 
 template <typename T, int N, int P>
 hipError_t launch_sma_fwd(const PrefillShape& s, const T* Q, const T* E, const T* C,

@@ -166,8 +166,17 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state_tr(
   constexpr int BV = kStKB * (N / VE) / kThreads;
   static_assert(XV * kThreads == kStKB * (P / VE) && BV * kThreads == kStKB * (N / VE),
                 "k_chunk_state_tr staging split");
-  __shared__ __align__(16) bf16 sh_b[kStKB * LDB];
-  __shared__ __align__(16) bf16 sh_x[kStKB * LDX];
+  // K-block tiles during the product; afterwards the finished memory as fp32
+  // rows [p][n] (a 16-byte pad keeps the fragment writes conflict-free), so
+  // both outputs leave as whole contiguous rows
+  constexpr int LDO = N + 4;
+  constexpr int KB_ELEMS = kStKB * (LDB + LDX);
+  constexpr int OUT_BYTES = P * LDO * 4;
+  constexpr int RAW = KB_ELEMS * 2 > OUT_BYTES ? KB_ELEMS * 2 : OUT_BYTES;
+  __shared__ __align__(16) unsigned char sh_raw[RAW];
+  bf16* sh_b = reinterpret_cast<bf16*>(sh_raw);
+  bf16* sh_x = sh_b + kStKB * LDB;
+  float* sh_o = reinterpret_cast<float*>(sh_raw);
   __shared__ float sh_w[kMaxChunk];
   __shared__ float sh_part[4];
 
@@ -264,41 +273,65 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state_tr(
     __syncthreads();
   }
 
-  // 3. store memory c value-axis-major: lane holds n = nb*16 + 4*grp + i, p = pb*16 + col
-  const long base = (pair * M + c) * (long)(P * N);
+  // 3. memory c value-axis-major ([p][n]): lane holds n = nb*16 + 4*grp + i,
+  //    p = pb*16 + col; through LDS, then whole rows to both outputs (the
+  //    loop's last barrier has released the K-block tiles)
 #pragma unroll
   for (int j = 0; j < TPW; ++j) {
     const int tt = w + 4 * j;
     if (kGrid || tt < NT) {
       const int nb = kGrid ? w + 4 * (j % NBW) : tt % NB, pb = kGrid ? j / NBW : tt / NB;
-      const long off = base + (long)(pb * 16 + col) * N + nb * 16 + 4 * grp;
-      store4(dH + off, acc[j]);
-      store4(dHf + off, acc[j]);
+      *reinterpret_cast<floatx4*>(&sh_o[(pb * 16 + col) * LDO + nb * 16 + 4 * grp]) = acc[j];
     }
+  }
+  __syncthreads();
+  const long base = (pair * M + c) * (long)(P * N);
+  constexpr int F4 = P * N / 4;  // float4s of one memory
+#pragma unroll
+  for (int v = 0; v < (F4 + kThreads - 1) / kThreads; ++v) {
+    const int i = tid + v * kThreads;
+    if (F4 % kThreads != 0 && i >= F4) break;
+    const int p = i / (N / 4), n = (i % (N / 4)) * 4;
+    *reinterpret_cast<floatx4*>(dHf + base + (long)i * 4) =
+        *reinterpret_cast<const floatx4*>(&sh_o[p * LDO + n]);
+  }
+#pragma unroll
+  for (int v = 0; v < (F4 / 2 + kThreads - 1) / kThreads; ++v) {
+    const int i = tid + v * kThreads;
+    if ((F4 / 2) % kThreads != 0 && i >= F4 / 2) break;
+    const int p = i / (N / 8), n = (i % (N / 8)) * 8;
+    const floatx4 lo = *reinterpret_cast<const floatx4*>(&sh_o[p * LDO + n]);
+    const floatx4 hi = *reinterpret_cast<const floatx4*>(&sh_o[p * LDO + n + 4]);
+    *reinterpret_cast<bf16x8*>(dH + base + (long)i * 8) =
+        bf16x8{from_f32<bf16>(lo[0]), from_f32<bf16>(lo[1]), from_f32<bf16>(lo[2]),
+               from_f32<bf16>(lo[3]), from_f32<bf16>(hi[0]), from_f32<bf16>(hi[1]),
+               from_f32<bf16>(hi[2]), from_f32<bf16>(hi[3])};
   }
 }
 
-// H_in[0] = h0, H_in[c+1] = exp(acum_end[c])·H_in[c] + dH_f32[c]; one thread
-// per four state entries of one (batch, head), serial over chunks.
+// H[0] = h0, H[c+1] = exp(acum_end[c])·H[c] + dH_f32[c] in f32; H_in[c] =
+// io(H[c]) for c < M and h_final = H[M].  One thread per four state entries
+// of one (batch, head), serial over chunks.
+template <typename T>
 __global__ __launch_bounds__(kThreads) void k_state_pass(
     const float* __restrict__ acum, const float* __restrict__ dHf, const float* __restrict__ h0,
-    float* __restrict__ H_in, int H, int M, int S, int PN) {
+    T* __restrict__ H_in, float* __restrict__ h_final, int H, int M, int S, int PN) {
   const int b = blockIdx.z, h = blockIdx.y;
   const int e4 = blockIdx.x * kThreads + threadIdx.x;
   if (e4 * 4 >= PN) return;
   const long pair = (long)b * H + h;
   const int q = PN / 4;
   const floatx4* src = reinterpret_cast<const floatx4*>(dHf + pair * M * (long)PN) + e4;
-  floatx4* dst = reinterpret_cast<floatx4*>(H_in + pair * (M + 1) * (long)PN) + e4;
+  T* dst = H_in + pair * M * (long)PN + e4 * 4;
   const float* ac_end = acum + pair * M * (long)S + (S - 1);
   floatx4 st = h0 ? reinterpret_cast<const floatx4*>(h0 + pair * PN)[e4] : floatx4{0.f, 0.f, 0.f, 0.f};
-  dst[0] = st;
 #pragma unroll 4
   for (int c = 0; c < M; ++c) {
+    store4(dst + (long)c * PN, st);
     const float dec = exp_neg(ac_end[(long)c * S]);
     st = dec * st + src[(long)c * q];
-    dst[(long)(c + 1) * q] = st;
   }
+  reinterpret_cast<floatx4*>(h_final + pair * PN)[e4] = st;
 }
 
 constexpr int kOutWaves = 8;  // two per SIMD
@@ -340,8 +373,9 @@ struct ChunkOutLds {
 template <typename T, int N, int P>
 __global__ __launch_bounds__(kOutThreads) void k_chunk_out(
     const T* __restrict__ x, const float* __restrict__ dt, const T* __restrict__ Bm,
-    const T* __restrict__ C, const float* __restrict__ acum, const float* __restrict__ H_in,
+    const T* __restrict__ C, const float* __restrict__ acum, const T* __restrict__ H_in,
     T* __restrict__ y_ssd, int L, int H, int G, int S) {
+  static_assert(std::is_same<T, float>::value, "16-bit io uses k_chunk_out_tr");
   using MM = Mma<T>;
   using Lds = ChunkOutLds<T, N, P>;
   typedef typename Vec16<T>::vec vec_t;
@@ -421,7 +455,7 @@ __global__ __launch_bounds__(kOutThreads) void k_chunk_out(
   for (int hh = 0; hh < hpg; ++hh) {
     const int h = g * hpg + hh;
     const long pair = (long)b * H + h;
-    const float* hsrc = H_in + (pair * (M + 1) + k) * (long)(P * N);
+    const float* hsrc = H_in + (pair * M + k) * (long)(P * N);
     vec_t xr[XV];
     floatx4 hr[HV];
     float ar = 0.f, ae = 0.f, dr = 1.f;
@@ -553,7 +587,7 @@ template <int N, int P>
 struct ChunkOutTr {
   static constexpr int LDC = N + 16;  // B and C rows [s][n]
   static constexpr int LDX = P + 16;  // x rows [s][p]
-  static constexpr int LDH = N + 16;  // H_in[k]ᵀ rows [p][n], rounded to bf16
+  static constexpr int LDH = N + 16;  // H_in[k]ᵀ rows [p][n]
   static constexpr int LDY = P + 16;  // y rows [t][p]
   // the next head's x and H_in[k] are fetched into registers while the
   // current head computes, and y leaves through LDS as whole token rows,
@@ -578,7 +612,7 @@ struct ChunkOutTr {
 template <int N, int P>
 __global__ __launch_bounds__(kOutThreads) void k_chunk_out_tr(
     const bf16* __restrict__ x, const float* __restrict__ dt, const bf16* __restrict__ Bm,
-    const bf16* __restrict__ C, const float* __restrict__ acum, const float* __restrict__ H_in,
+    const bf16* __restrict__ C, const float* __restrict__ acum, const bf16* __restrict__ H_in,
     bf16* __restrict__ y_ssd, int L, int H, int G, int S) {
   using MM = Mma<bf16>;
   using Lds = ChunkOutTr<N, P>;
@@ -589,7 +623,7 @@ __global__ __launch_bounds__(kOutThreads) void k_chunk_out_tr(
   constexpr int NSLOT = kMaxBlk + 2;
   constexpr int RV = kMaxChunk * (N / VE) / kOutThreads;  // B or C vectors per thread
   constexpr int XV = kMaxChunk * (P / VE) / kOutThreads;  // x or y vectors per thread
-  constexpr int HQ = P * N / 4;                           // H_in[k] as float4s
+  constexpr int HQ = P * N / VE;                          // H_in[k] as 16-byte vectors
   constexpr int HV = (HQ + kOutThreads - 1) / kOutThreads;
   static_assert(RV * kOutThreads == kMaxChunk * (N / VE) &&
                     XV * kOutThreads == kMaxChunk * (P / VE),
@@ -616,8 +650,7 @@ __global__ __launch_bounds__(kOutThreads) void k_chunk_out_tr(
   const int n1 = has1 ? 2 * (tb1 / 2 + 1) : 0;
 
   // per-head inputs, fetched one head ahead when kPrefetch
-  vec_t xr[XV];
-  floatx4 hr[HV];
+  vec_t xr[XV], hr[HV];
   float ar = 0.f, dr = 1.f;
   auto load_head = [&](int hh) __attribute__((always_inline)) {
     const int h = g * hpg + hh;
@@ -627,8 +660,7 @@ __global__ __launch_bounds__(kOutThreads) void k_chunk_out_tr(
       const int i = tid + v * kOutThreads, s = i / (P / VE), pv = i % (P / VE);
       if (s < S) xr[v] = load16(x + ((tok0 + s) * H + h) * P + pv * VE);
     }
-    const floatx4* hsrc =
-        reinterpret_cast<const floatx4*>(H_in + (pair * (M + 1) + k) * (long)(P * N));
+    const vec_t* hsrc = reinterpret_cast<const vec_t*>(H_in + (pair * M + k) * (long)(P * N));
 #pragma unroll
     for (int v = 0; v < HV; ++v) {
       const int i = tid + v * kOutThreads;
@@ -696,7 +728,7 @@ __global__ __launch_bounds__(kOutThreads) void k_chunk_out_tr(
   for (int hh = 0; hh < hpg; ++hh) {
     const int h = g * hpg + hh;
     if (!Lds::kPrefetch) load_head(hh);
-    // stage head hh: x rows, H_in[k]ᵀ rows in bf16, log-decay factors
+    // stage head hh: x rows, H_in[k]ᵀ rows, log-decay factors
 #pragma unroll
     for (int v = 0; v < XV; ++v) {
       const int i = tid + v * kOutThreads, s = i / (P / VE), pv = i % (P / VE);
@@ -706,11 +738,8 @@ __global__ __launch_bounds__(kOutThreads) void k_chunk_out_tr(
     for (int v = 0; v < HV; ++v) {
       const int i = tid + v * kOutThreads;
       if (HQ % kOutThreads == 0 || i < HQ) {
-        const int p = (i * 4) / N, n = (i * 4) % N;
-        const floatx4 hv = hr[v];
-        *reinterpret_cast<bf16x4*>(&sh_h[p * LDH + n]) =
-            bf16x4{from_f32<bf16>(hv[0]), from_f32<bf16>(hv[1]), from_f32<bf16>(hv[2]),
-                   from_f32<bf16>(hv[3])};
+        const int p = (i * VE) / N, n = (i * VE) % N;
+        *reinterpret_cast<vec_t*>(&sh_h[p * LDH + n]) = hr[v];
       }
     }
     {
@@ -834,11 +863,12 @@ hipError_t launch_chunk_state(const PrefillShape& s, const T* x, const float* dt
 template <typename T, int N, int P>
 hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt, const T* Bm,
                              const T* C, const float* acum, const float* dH_f32,
-                             const float* h0, float* H_in, T* y_ssd, hipStream_t st) {
+                             const float* h0, T* H_in, float* h_final, T* y_ssd,
+                             hipStream_t st) {
   const int M = s.L / s.S;
   constexpr int PN = P * N;
-  hipLaunchKernelGGL(k_state_pass, dim3((PN / 4 + kThreads - 1) / kThreads, s.H, s.B),
-                     dim3(kThreads), 0, st, acum, dH_f32, h0, H_in, s.H, M, s.S, PN);
+  hipLaunchKernelGGL(k_state_pass<T>, dim3((PN / 4 + kThreads - 1) / kThreads, s.H, s.B),
+                     dim3(kThreads), 0, st, acum, dH_f32, h0, H_in, h_final, s.H, M, s.S, PN);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (std::is_same<T, bf16>::value)
@@ -856,7 +886,7 @@ hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt,
                                                   hipStream_t);                                \
   template hipError_t launch_state_pass<T, N, P>(const PrefillShape&, const T*, const float*,  \
                                                  const T*, const T*, const float*,             \
-                                                 const float*, const float*, float*, T*,       \
+                                                 const float*, const float*, T*, float*, T*,   \
                                                  hipStream_t);
 DART_FOR_EACH_SHAPE(DART_INST_SCAN)
 

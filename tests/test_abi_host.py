@@ -116,7 +116,12 @@ def test_entry_points_reject_null_pointers():
         q = list(p)
         q[i] = None
         assert lib.dart_chunk_state(d, *q, None) == NULLP
-    assert lib.dart_state_pass(d, A16, A16, A16, A16, A16, A16, None, A16, None, None) == NULLP
+    # x, dt, Bm, C, acum, dH_f32, h0 (may be NULL), H_in, h_final, y_ssd
+    for i in (0, 1, 2, 3, 4, 5, 7, 8, 9):
+        q = [A16] * 10
+        q[6] = None
+        q[i] = None
+        assert lib.dart_state_pass(d, *q, None) == NULLP
     assert lib.dart_sma_fwd(d, A16, A16, None, A16, A16, 0.5, A16, None) == NULLP
 
 
@@ -124,7 +129,8 @@ def test_entry_points_reject_misaligned_pointers():
     lib = dart.lib()
     d = dims()
     assert lib.dart_chunk_state(d, A16, A16, A16, MIS, A16, A16, A16, None) == ALIGN
-    assert lib.dart_state_pass(d, A16, A16, A16, A16, A16, A16, MIS, A16, A16, None) == ALIGN
+    assert lib.dart_state_pass(d, A16, A16, A16, A16, A16, A16, MIS, A16, A16, A16,
+                               None) == ALIGN
     assert lib.dart_sma_fwd(d, A16, A16, A16, A16, A16, 0.5, MIS, None) == ALIGN
 
 

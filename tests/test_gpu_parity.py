@@ -65,7 +65,8 @@ def run_prefill_case(B, L, H, G, N, P, S, io, seed=0, gate=0.5, qscale=1.0, h0_s
                          h0=None if h0 is None else _pn_to_np(h0))
     assert_parity(_pn_to_np(out["dH_f32"]), ref["dH"], io, "dH_f32")
     assert_parity(_pn_to_np(out["dH"]), ref["dH"], io, "dH")
-    assert_parity(_pn_to_np(out["H_in"]), ref["H_in"], io, "H_in")
+    assert_parity(_pn_to_np(out["H_in"]), ref["H_in"][:, :, :-1], io, "H_in")
+    assert_parity(_pn_to_np(out["h_final"]), ref["h_final"], io, "h_final")
     assert_parity(out["y_ssd"], ref["y_ssd"], io, "y_ssd")
     assert_parity(out["y"], ref["y"], io, "y")
     # the SMA branch alone, so that a wrong readout cannot hide under y_ssd
@@ -219,9 +220,13 @@ def test_decode_continues_prefill(io, N, P, S):
     d = _to_dev(inp)
     gate = 0.75
     full = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate, S)
+    # the first k0 chunks alone: their memories and f32 final state seed decode
+    pre = {k: v[:, :k0 * S].contiguous() if k != "A" else v for k, v in d.items()}
+    head = api.prefill(pre["x"], pre["dt"], pre["A"], pre["Bm"], pre["C"], pre["Q"], pre["E"],
+                       gate, S)
     st = api.new_decode_state(B, H, G, N, P, S, M, io, DEV)
-    st["cache"][:, :, :k0].copy_(full["dH"][:, :, :k0])
-    st["h"].copy_(full["H_in"][:, :, k0])
+    st["cache"][:, :, :k0].copy_(head["dH"])
+    st["h"].copy_(head["h_final"])
     st["n_chunks"].fill_(k0)
     ys = []
     for t in range(k0 * S, L):
@@ -270,7 +275,8 @@ def test_config2_full_size_sampled_pairs():
         dH, H_in, y_ssd, o, y = _oracle_pair(n, b, h, H, G, S, gate)
         io = torch.bfloat16
         assert_parity(_pn_to_np(out["dH"][b, h]), dH, io, f"c2 dH b{b} h{h}")
-        assert_parity(_pn_to_np(out["H_in"][b, h]), H_in, io, f"c2 H_in b{b} h{h}")
+        assert_parity(_pn_to_np(out["H_in"][b, h]), H_in[:-1], io, f"c2 H_in b{b} h{h}")
+        assert_parity(_pn_to_np(out["h_final"][b, h]), H_in[-1], io, f"c2 h_final b{b} h{h}")
         assert_parity(out["y_ssd"][b, :, h], y_ssd, io, f"c2 y_ssd b{b} h{h}")
         assert_parity(out["y"][b, :, h], y, io, f"c2 y b{b} h{h}")
 
@@ -331,6 +337,7 @@ def test_config3_long_context_sampled_tokens():
         o = oracle.sma(sl["Q"], sl["E"], sl["C"], dH, S, tokens=tokens)
         y = oracle.gated_output(y_ssd, o, gate)
         assert_parity(_pn_to_np(out["dH"][0, h]), dH[0, 0], io, f"c3 dH h{h}")
-        assert_parity(_pn_to_np(out["H_in"][0, h]), H_in[0, 0], io, f"c3 H_in h{h}")
+        assert_parity(_pn_to_np(out["H_in"][0, h]), H_in[0, 0, :-1], io, f"c3 H_in h{h}")
+        assert_parity(_pn_to_np(out["h_final"][0, h]), H_in[0, 0, -1], io, f"c3 h_final h{h}")
         assert_parity(out["y_ssd"][0, :, h], y_ssd[0, :, 0], io, f"c3 y_ssd h{h}")
         assert_parity(out["y"][0, tokens, h], y[0, tokens, 0], io, f"c3 y (sampled) h{h}")

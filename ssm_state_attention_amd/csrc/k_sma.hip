@@ -28,6 +28,10 @@ struct SmaTile {
 // (batch, head) pairs per ordering group of one XCD (see k_sma_fwd)
 constexpr int kPairsPerGroup = 4;
 
+// online-softmax slack: weights may reach 2^kLazyLog2 before the running max
+// (and with it every accumulator) is rescaled
+constexpr float kLazyLog2 = 8.f;
+
 template <int V>
 using IC = std::integral_constant<int, V>;
 
@@ -274,13 +278,22 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
 #pragma unroll
         for (int i = 0; i < 4; ++i) s += zq[tb][pb][i] * to_f32(ev[tb][pb][i]);
       s = sum_lane_groups(s) * scale_log2;
-      const float mn = fmaxf(mx[tb], s);
-      const float al = exp2_fast(mx[tb] - mn);  // 0 for the first memory
-      const float pw = exp2_fast(s - mn);
-      ls[tb] = ls[tb] * al + pw;
+      // The reference max mx is raised only when a score passes it by more
+      // than kLazyLog2 (a wave-uniform branch, taken at the first memory and
+      // rarely after); otherwise the weights 2^(s - mx) stay below
+      // 2^kLazyLog2 and the running sums need no rescale.
+      if (__any(s > mx[tb] + kLazyLog2)) {
+        const float mn = fmaxf(mx[tb], s);
+        const float al = exp2_fast(mx[tb] - mn);  // 0 for the first memory
+        ls[tb] *= al;
 #pragma unroll
-      for (int pb = 0; pb < NPB; ++pb) acc[tb][pb] = acc[tb][pb] * al + pw * zc[tb][pb];
-      mx[tb] = mn;
+        for (int pb = 0; pb < NPB; ++pb) acc[tb][pb] *= al;
+        mx[tb] = mn;
+      }
+      const float pw = exp2_fast(s - mx[tb]);
+      ls[tb] += pw;
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb) acc[tb][pb] += pw * zc[tb][pb];
     }
   };
   // Ping-pong: the first half of the waves (one per SIMD) runs its MFMAs
@@ -292,24 +305,32 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   const bool lead = w < WAVES / 2;
   auto half_steps = [&](int c, auto par_tag) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par_tag)::value;
+    // Each wave stages its share of memory c+1 (fetched during step c-1)
+    // into the other buffer in its softmax half, off the MFMA path: that
+    // buffer last held memory c-1, whose final reads ended at the previous
+    // barrier.  Unconditional, indices clamped to the last memory: a
+    // duplicate lands in a buffer that is not read again, and every path
+    // issues the same loads (so the wait before the LDS write covers only
+    // the older fetch).
+    auto stage_next = [&]() __attribute__((always_inline)) {
+      swrite(PAR ^ 1, stg);           // memory c+1
+      gload(min(c + 2, k - 1), stg);  // memory c+2
+    };
     // first half: lead waves multiply memory c, the others finish memory c-1
     if (lead) {
       if (c < k) mma_mem(PAR);
-    } else if (c > 0) {
-      softmax_mem();
+    } else {
+      if (c > 0) softmax_mem();
+      stage_next();
     }
     __syncthreads();
     // second half: lead waves finish memory c, the others multiply it
     if (lead) {
       if (c < k) softmax_mem();
+      stage_next();
     } else if (c < k) {
       mma_mem(PAR);
     }
-    // unconditional, indices clamped to the last memory: a duplicate lands
-    // in a buffer that is not read again, and every path issues the same
-    // loads (so the wait before the LDS write covers only the older fetch)
-    swrite(PAR ^ 1, stg);            // memory c+1, fetched during step c-1
-    gload(min(c + 2, k - 1), stg);   // memory c+2
     __syncthreads();
   };
   if (k > 0) {

@@ -46,6 +46,136 @@ __device__ __forceinline__ float sum_lane_groups(float v) {
   return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
+// Per-wave tile arithmetic of the prefill kernel: a wave owns TW = 16·NTB
+// tokens of the workgroup's tile.  Each policy holds the wave's resident
+// [Q; C] operand fragments, its E values, the products Zq = dH[c]ᵀQ and
+// Zc = dH[c]ᵀC of the current memory and the online-softmax state, with
+// every register index a compile-time constant.
+//
+// SmaMath16: 16x16 MFMA tiles (rows p, columns tokens, K = 32 along n for
+// 16-bit io, K = 4 for fp32); NTB 16-token blocks per wave.
+template <typename T, int N, int P, int NTB>
+struct SmaMath16 {
+  using MM = Mma<T>;
+  static constexpr int K = MM::K, KL = MM::KL;
+  static constexpr int NPB = P / 16, NKK = N / K, TW = 16 * NTB;
+  typedef typename std::conditional<std::is_same<T, bf16>::value, bf16x4, floatx4>::type e4_t;
+  typename MM::frag qf[NTB][NKK], cf[NTB][NKK];
+  e4_t ev[NTB][NPB];
+  floatx4 zq[NTB][NPB], zc[NTB][NPB], acc[NTB][NPB];
+  float mx[NTB], ls[NTB];
+  int row0, col, grp;  // first token row of the wave; lane coordinates
+
+  __device__ __forceinline__ void init(int w, int lane) {
+    row0 = w * TW;
+    col = lane & 15;
+    grp = lane >> 4;
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+      mx[tb] = -INFINITY;
+      ls[tb] = 0.f;
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb) acc[tb][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  __device__ __forceinline__ int lrow(int tb) const { return row0 + tb * 16 + col; }
+  // B operand fragments (column t, k-slots along n) from token rows [t][n]
+  __device__ __forceinline__ void load_frags(typename MM::frag (&f)[NTB][NKK], const T* tile,
+                                             int ld) {
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) f[tb][kk] = MM::load(&tile[lrow(tb) * ld + kk * K + grp * KL]);
+  }
+  __device__ __forceinline__ void load_q(const T* tile, int ld) { load_frags(qf, tile, ld); }
+  __device__ __forceinline__ void load_c(const T* tile, int ld) { load_frags(cf, tile, ld); }
+  // this lane's p rows of E (kept in the input type, widened in the score)
+  __device__ __forceinline__ void load_e(const T* tile, int ld) {
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb)
+        ev[tb][pb] = *reinterpret_cast<const e4_t*>(&tile[lrow(tb) * ld + pb * 16 + 4 * grp]);
+  }
+  // Zq, Zc of one memory held as rows [p][n] in LDS
+  __device__ __forceinline__ void mma(const T* mem, int ld) {
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb) {
+        zq[tb][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        zc[tb][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    // A fragments of p-block pb+1 are read while the MFMAs of pb run
+    typename MM::frag a[2][NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) a[0][kk] = MM::load(&mem[col * ld + kk * K + grp * KL]);
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb) {
+      if (pb + 1 < NPB) {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+          a[(pb + 1) & 1][kk] = MM::load(&mem[((pb + 1) * 16 + col) * ld + kk * K + grp * KL]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+          zq[tb][pb] = MM::mma(a[pb & 1][kk], qf[tb][kk], zq[tb][pb]);
+          zc[tb][pb] = MM::mma(a[pb & 1][kk], cf[tb][kk], zc[tb][pb]);
+        }
+    }
+    // schedule: LDS fragment reads run four fragments ahead of the MFMAs
+    // that consume them (2·NTB MFMAs per fragment cover the LDS latency)
+    constexpr int R = NPB * NKK;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int f = 0; f < R; ++f) {
+      if (f + 4 < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NTB, 0);
+    }
+  }
+  __device__ __forceinline__ void softmax(float scale_log2) {
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+      float s = 0.f;
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s += zq[tb][pb][i] * to_f32(ev[tb][pb][i]);
+      s = sum_lane_groups(s) * scale_log2;
+      // The reference max mx is raised only when a score passes it by more
+      // than kLazyLog2 (a wave-uniform branch, taken at the first memory and
+      // rarely after); otherwise the weights 2^(s - mx) stay below
+      // 2^kLazyLog2 and the running sums need no rescale.
+      if (__any(s > mx[tb] + kLazyLog2)) {
+        const float mn = fmaxf(mx[tb], s);
+        const float al = exp2_fast(mx[tb] - mn);  // 0 for the first memory
+        ls[tb] *= al;
+#pragma unroll
+        for (int pb = 0; pb < NPB; ++pb) acc[tb][pb] *= al;
+        mx[tb] = mn;
+      }
+      const float pw = exp2_fast(s - mx[tb]);
+      ls[tb] += pw;
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb) acc[tb][pb] += pw * zc[tb][pb];
+    }
+  }
+  // y = y_ssd + gate·o in the LDS rows [t][p] that hold y_ssd
+  __device__ __forceinline__ void finish(T* ty, int ld, float gate, bool any) {
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+      const float f = any ? gate / ls[tb] : 0.f;
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb) {
+        T* q = &ty[lrow(tb) * ld + pb * 16 + 4 * grp];
+        store4(q, load4_f32(q) + f * acc[tb][pb]);
+      }
+    }
+  }
+};
+
 // Prefill SMA.  One workgroup = WAVES waves × 16·NTB tokens of ONE chunk k,
 // so every token of the workgroup sees the same memories c < k (no mask).
 // Per memory c, dH[c]ᵀ (P x N, value-axis-major in HBM) is staged in LDS
@@ -124,7 +254,6 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const long row0 = (long)b * L + (long)k * S + sub * TWG;  // first token of the tile
-  auto lrow = [&](int tb) __attribute__((always_inline)) { return w * TW + tb * 16 + col; };
 
   // ---- prologue: every load in flight before the first wait ----
   vec_t qs[QV], cs[QV], es[EV], ys[EV];
@@ -184,11 +313,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     *reinterpret_cast<vec_t*>(&sh_ty[t * LDE + pv * VE]) = ys[v];
   }
   __syncthreads();
-  typename MM::frag qf[NTB][NKK], cf[NTB][NKK];
-#pragma unroll
-  for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qf[tb][kk] = MM::load(&sh_r1[lrow(tb) * LDN + kk * K + grp * KL]);
+  SmaMath16<T, N, P, NTB> tm;
+  tm.init(w, lane);
+  tm.load_q(sh_r1, LDN);
   __syncthreads();
   // C tile -> fragments
 #pragma unroll
@@ -197,10 +324,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     *reinterpret_cast<vec_t*>(&sh_r1[t * LDN + nv * VE]) = cs[v];
   }
   __syncthreads();
-#pragma unroll
-  for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) cf[tb][kk] = MM::load(&sh_r1[lrow(tb) * LDN + kk * K + grp * KL]);
+  tm.load_c(sh_r1, LDN);
   __syncthreads();
   // E tile -> this lane's p rows, kept in the input type (bf16 pairs halve
   // the registers) and widened when the score is formed
@@ -210,92 +334,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     *reinterpret_cast<vec_t*>(&sh_r1[t * LDE + pv * VE]) = es[v];
   }
   __syncthreads();
-  typedef typename std::conditional<std::is_same<T, bf16>::value, bf16x4, floatx4>::type e4_t;
-  e4_t ev[NTB][NPB];
-#pragma unroll
-  for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-    for (int pb = 0; pb < NPB; ++pb)
-      ev[tb][pb] = *reinterpret_cast<const e4_t*>(&sh_r1[lrow(tb) * LDE + pb * 16 + 4 * grp]);
+  tm.load_e(sh_r1, LDE);
   __syncthreads();  // sh_r1 becomes the memory buffers
 
-  floatx4 acc[NTB][NPB];
-  float mx[NTB], ls[NTB];
-#pragma unroll
-  for (int tb = 0; tb < NTB; ++tb) {
-    mx[tb] = -INFINITY;
-    ls[tb] = 0.f;
-#pragma unroll
-    for (int pb = 0; pb < NPB; ++pb) acc[tb][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  floatx4 zq[NTB][NPB], zc[NTB][NPB];
-  auto mma_mem = [&](int cur) __attribute__((always_inline)) {
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-      for (int pb = 0; pb < NPB; ++pb) {
-        zq[tb][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
-        zc[tb][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
-    // A fragments of p-block pb+1 are read while the MFMAs of pb run
-    typename MM::frag a[2][NKK];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-      a[0][kk] = MM::load(&sh_mem[cur][(0 * 16 + col) * LDN + kk * K + grp * KL]);
-#pragma unroll
-    for (int pb = 0; pb < NPB; ++pb) {
-      if (pb + 1 < NPB) {
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-          a[(pb + 1) & 1][kk] =
-              MM::load(&sh_mem[cur][((pb + 1) * 16 + col) * LDN + kk * K + grp * KL]);
-      }
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-          zq[tb][pb] = MM::mma(a[pb & 1][kk], qf[tb][kk], zq[tb][pb]);
-          zc[tb][pb] = MM::mma(a[pb & 1][kk], cf[tb][kk], zc[tb][pb]);
-        }
-    }
-    // schedule: LDS fragment reads run four fragments ahead of the MFMAs
-    // that consume them (2·NTB MFMAs per fragment cover the LDS latency)
-    constexpr int R = NPB * NKK;
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int f = 0; f < R; ++f) {
-      if (f + 4 < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NTB, 0);
-    }
-  };
-  auto softmax_mem = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb) {
-      float s = 0.f;
-#pragma unroll
-      for (int pb = 0; pb < NPB; ++pb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s += zq[tb][pb][i] * to_f32(ev[tb][pb][i]);
-      s = sum_lane_groups(s) * scale_log2;
-      // The reference max mx is raised only when a score passes it by more
-      // than kLazyLog2 (a wave-uniform branch, taken at the first memory and
-      // rarely after); otherwise the weights 2^(s - mx) stay below
-      // 2^kLazyLog2 and the running sums need no rescale.
-      if (__any(s > mx[tb] + kLazyLog2)) {
-        const float mn = fmaxf(mx[tb], s);
-        const float al = exp2_fast(mx[tb] - mn);  // 0 for the first memory
-        ls[tb] *= al;
-#pragma unroll
-        for (int pb = 0; pb < NPB; ++pb) acc[tb][pb] *= al;
-        mx[tb] = mn;
-      }
-      const float pw = exp2_fast(s - mx[tb]);
-      ls[tb] += pw;
-#pragma unroll
-      for (int pb = 0; pb < NPB; ++pb) acc[tb][pb] += pw * zc[tb][pb];
-    }
-  };
+  auto mma_mem = [&](int cur) __attribute__((always_inline)) { tm.mma(sh_mem[cur], LDN); };
+  auto softmax_mem = [&]() __attribute__((always_inline)) { tm.softmax(scale_log2); };
   // Ping-pong: the first half of the waves (one per SIMD) runs its MFMAs
   // while the second half runs its softmax, then they swap, so the matrix
   // core and the vector ALU of every SIMD stay busy together.  Two barriers
@@ -346,15 +389,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   }
 
   // ---- epilogue: y = y_ssd + gate·o in LDS, then whole-row stores ----
-#pragma unroll
-  for (int tb = 0; tb < NTB; ++tb) {
-    const float f = k > 0 ? gate / ls[tb] : 0.f;
-#pragma unroll
-    for (int pb = 0; pb < NPB; ++pb) {
-      T* p = &sh_ty[lrow(tb) * LDE + pb * 16 + 4 * grp];
-      store4(p, load4_f32(p) + f * acc[tb][pb]);
-    }
-  }
+  tm.finish(sh_ty, LDE, gate, k > 0);
   __syncthreads();
 #pragma unroll
   for (int v = 0; v < EV; ++v) {

@@ -136,6 +136,23 @@ dart_status dart_sma_fwd(const dart_dims* dims, const void* Q, const void* E,
                          const void* C, const void* dH, const void* y_ssd, float gate,
                          void* y, void* stream);
 
+/*
+ * The decay-included variant of dart_sma_fwd, the ablation the Pith review
+ * of DART asks for (referee major comment 3, paper §3 Eq. 8): key and value
+ * of memory c are scaled, for token t of chunk k > c, by the decay the SSM
+ * applies between the end of chunk c and t,
+ *
+ *   d[t,c] = exp(sum_{j = end(c)+1 .. t} dt_j·A) = exp(acum[k, t-kS] + sum_{c<c'<k} acum[c', S-1])
+ *   s[t,c] = d[t,c]·Q_tᵀ·dH[c]·E_t / sqrt(N),
+ *   o_t    = sum_{c<k} softmax_c(s[t,c])·d[t,c]·C_tᵀ·dH[c],   y_t = y_ssd_t + gate·o_t
+ *
+ * in:  as dart_sma_fwd, plus acum [B,H,M,S] f32 from dart_chunk_state
+ * out: y [B,L,H,P] io
+ */
+dart_status dart_sma_fwd_decayed(const dart_dims* dims, const void* Q, const void* E,
+                                 const void* C, const void* dH, const float* acum,
+                                 const void* y_ssd, float gate, void* y, void* stream);
+
 /* Bytes of device workspace dart_sma_decode needs for these dims (a
  * multiple of 256; 0 if the dims are invalid). */
 size_t dart_sma_decode_workspace(const dart_decode_dims* dims);

@@ -22,7 +22,8 @@ Sources (cited by page and section; the pages print no code):
   N×P contribution of chunk c to the chunk-boundary state (key axis N, value
   axis P); query Q_t.
 * [pith-maj3]  Pith review, referee major comment 3 (paper §3 Eq. 8): the
-  readouts use the raw ΔH[c], with no inter-chunk decay applied.
+  readouts use the raw ΔH[c], with no inter-chunk decay applied; the referee
+  asks for the variant with the decay A_{e(c)+1:t} applied as an ablation.
 * [pith-eq14]  Pith review, minor comment 1 and circularity check (paper §4
   Eq. 14): per head the DART cache holds M·N·P values against 2·L·P for a
   token-level attention layer.
@@ -56,6 +57,7 @@ __all__ = [
     "chunk_output",
     "sma",
     "sma_bruteforce",
+    "sma_decayed",
     "gated_output",
     "prefill",
     "decode_step",
@@ -259,6 +261,41 @@ def sma_bruteforce(Q, E, C, dH, S):
     return o
 
 
+def sma_decayed(Q, E, C, dH, dt, A, S, tokens=None):
+    """The decay-included SMA variant that the review asks to ablate
+    [pith-maj3]: memory c enters the readout of token t (chunk k > c) scaled
+    by the decay the SSM applies to chunk c's contribution between the chunk
+    boundary e(c) = (c+1)·S − 1 and t,
+
+        d_{t,c} = exp(A_h · Σ_{j=e(c)+1}^{t} dt_j),
+        key   d_{t,c}·ΔH[c]·E_t,   value   d_{t,c}·C_tᵀ·ΔH[c],
+        score d_{t,c}·Q_t·(ΔH[c]·E_t) / sqrt(N),   o_t = Σ_c softmax_c·value.
+
+    The segment sum of dt is a difference of an inclusive fp64 cumsum.
+    Returns o [B,L,H,P] (rows not listed in ``tokens`` stay zero)."""
+    E, dH, dt, A = _f64(E), _f64(dH), _f64(dt), _f64(A)
+    Bsz, L, H, P = E.shape
+    Qh, Ch = _per_head(Q, H), _per_head(C, H)
+    N = Qh.shape[-1]
+    o = np.zeros((Bsz, L, H, P))
+    t_all = np.arange(L) if tokens is None else np.asarray(tokens)
+    for b in range(Bsz):
+        for h in range(H):
+            cs = np.cumsum(dt[b, :, h])                             # inclusive
+            for k in range(1, L // S):
+                ts = t_all[(t_all >= k * S) & (t_all < (k + 1) * S)]
+                if ts.size == 0:
+                    continue
+                ends = np.arange(k) * S + (S - 1)                   # e(c)
+                d = np.exp(A[h] * (cs[ts][:, None] - cs[ends][None, :]))  # [t,c]
+                mem = dH[b, h, :k]  # undecayed memories, [k,N,P]
+                keys = np.einsum("cnp,tp->tcn", mem, E[b, ts, h])
+                scores = d * np.einsum("tn,tcn->tc", Qh[b, ts, h], keys) / math.sqrt(N)
+                vals = d[:, :, None] * np.einsum("tn,cnp->tcp", Ch[b, ts, h], mem)
+                o[b, ts, h] = np.einsum("tc,tcp->tp", _softmax(scores), vals)
+    return o
+
+
 # --------------------------------------------------------------------------
 # O7 - gated residual
 # --------------------------------------------------------------------------
@@ -268,13 +305,14 @@ def gated_output(y_ssd, o, g):
     return _f64(y_ssd) + float(g) * _f64(o)
 
 
-def prefill(x, dt, A, Bm, C, Q, E, g, S, h0=None):
-    """The whole prefill path O3 -> O4 -> O5 -> O6 -> O7.
+def prefill(x, dt, A, Bm, C, Q, E, g, S, h0=None, decayed=False):
+    """The whole prefill path O3 -> O4 -> O5 -> O6 -> O7 (O6 in the
+    decay-included variant when ``decayed``).
     Returns a dict with dH, H_in, y_ssd, o, y, h_final."""
     dH = chunk_states(x, dt, A, Bm, S)
     H_in = state_pass(dH, dt, A, S, h0)
     y_ssd = chunk_output(x, dt, A, Bm, C, H_in, S)
-    o = sma(Q, E, C, dH, S)
+    o = sma_decayed(Q, E, C, dH, dt, A, S) if decayed else sma(Q, E, C, dH, S)
     return {"dH": dH, "H_in": H_in, "y_ssd": y_ssd, "o": o,
             "y": gated_output(y_ssd, o, g), "h_final": H_in[:, :, -1]}
 

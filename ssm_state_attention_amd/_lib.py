@@ -40,6 +40,8 @@ _SIG = {
     "dart_state_pass": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                         _VP, _VP],
     "dart_sma_fwd": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _F, _VP, _VP],
+    "dart_sma_fwd_decayed": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _VP, _F, _VP,
+                             _VP],
     "dart_sma_decode_workspace": [ctypes.POINTER(DartDecodeDims)],
     "dart_sma_decode": [ctypes.POINTER(DartDecodeDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F,
                         _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],

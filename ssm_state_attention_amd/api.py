@@ -97,6 +97,22 @@ def dart_sma_fwd(Q, E, C, dH, y_ssd, gate, y, chunk):
     check(lib().dart_sma_fwd(d, *args, float(gate), yp, _stream()), "dart_sma_fwd")
 
 
+def dart_sma_fwd_decayed(Q, E, C, dH, acum, y_ssd, gate, y, chunk):
+    """Decay-included SMA + gated add (see include/dart.h): acum [B,H,M,S]
+    f32 from dart_chunk_state; y [B,L,H,P] io."""
+    B, L, H, P = E.shape
+    G, N = Q.shape[2], Q.shape[3]
+    d = DartDims(B, L, H, G, N, P, int(chunk), _io_code(E.dtype))
+    M, io, dev = L // chunk, E.dtype, E.device
+    args = [_ptr(Q, "Q", io, (B, L, G, N), dev), _ptr(E, "E", io, (B, L, H, P), dev),
+            _ptr(C, "C", io, (B, L, G, N), dev), _ptr(dH, "dH", io, (B, H, M, P, N), dev),
+            _ptr(acum, "acum", torch.float32, (B, H, M, chunk), dev),
+            _ptr(y_ssd, "y_ssd", io, (B, L, H, P), dev)]
+    yp = _ptr(y, "y", io, (B, L, H, P), dev)
+    check(lib().dart_sma_fwd_decayed(d, *args, float(gate), yp, _stream()),
+          "dart_sma_fwd_decayed")
+
+
 def decode_dims(batch, nheads, ngroups, dstate, headdim, chunk, max_chunks, dtype):
     return DartDecodeDims(batch, nheads, ngroups, dstate, headdim, int(chunk), int(max_chunks),
                           _io_code(dtype))
@@ -132,7 +148,7 @@ def dart_sma_decode(x, dt, A, Bm, C, Q, E, gate, cache, h, dH_cur, n_chunks, pos
 
 
 # ----------------------------------------------------------------- helpers
-def prefill(x, dt, A, Bm, C, Q, E, gate, chunk, h0=None):
+def prefill(x, dt, A, Bm, C, Q, E, gate, chunk, h0=None, decayed=False):
     """Whole prefill path; returns a dict of device tensors: y, y_ssd, dH
     ([B,H,M,P,N] io), dH_f32, H_in ([B,H,M,P,N] io, the state entering each
     chunk), h_final ([B,H,P,N] f32, the state after the last chunk) and
@@ -153,7 +169,10 @@ def prefill(x, dt, A, Bm, C, Q, E, gate, chunk, h0=None):
     dart_chunk_state(x, dt, A, Bm, out["acum"], out["dH"], out["dH_f32"], chunk)
     dart_state_pass(x, dt, Bm, C, out["acum"], out["dH_f32"], h0, out["H_in"], out["h_final"],
                     out["y_ssd"], chunk)
-    dart_sma_fwd(Q, E, C, out["dH"], out["y_ssd"], gate, out["y"], chunk)
+    if decayed:
+        dart_sma_fwd_decayed(Q, E, C, out["dH"], out["acum"], out["y_ssd"], gate, out["y"], chunk)
+    else:
+        dart_sma_fwd(Q, E, C, out["dH"], out["y_ssd"], gate, out["y"], chunk)
     return out
 
 

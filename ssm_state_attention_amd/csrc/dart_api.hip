@@ -76,6 +76,7 @@ struct StatePassFn {
 struct SmaFwdFn {
   dart::PrefillShape sh;
   const void *Q, *E, *C, *dH, *y_ssd;
+  const float* acum;
   float gate;
   void* y;
   hipStream_t st;
@@ -83,8 +84,8 @@ struct SmaFwdFn {
   hipError_t run() {
     return dart::launch_sma_fwd<T, N, P>(sh, static_cast<const T*>(Q), static_cast<const T*>(E),
                                          static_cast<const T*>(C), static_cast<const T*>(dH),
-                                         static_cast<const T*>(y_ssd), gate, static_cast<T*>(y),
-                                         st);
+                                         static_cast<const T*>(y_ssd), acum, gate,
+                                         static_cast<T*>(y), st);
   }
 };
 
@@ -138,7 +139,20 @@ extern "C" dart_status dart_sma_fwd(const dart_dims* dims, const void* Q, const 
   dart_status s = dart_validate_dims(dims);
   if (s != DART_OK) return s;
   if ((s = check_ptrs(Q, E, C, dH, y_ssd, y)) != DART_OK) return s;
-  SmaFwdFn fn{prefill_shape(dims), Q, E, C, dH, y_ssd, gate, y, static_cast<hipStream_t>(stream)};
+  SmaFwdFn fn{prefill_shape(dims), Q, E, C, dH, y_ssd, nullptr, gate, y,
+              static_cast<hipStream_t>(stream)};
+  return dispatch(dims->io, dims->dstate, dims->headdim, fn);
+}
+
+extern "C" dart_status dart_sma_fwd_decayed(const dart_dims* dims, const void* Q, const void* E,
+                                            const void* C, const void* dH, const float* acum,
+                                            const void* y_ssd, float gate, void* y,
+                                            void* stream) {
+  dart_status s = dart_validate_dims(dims);
+  if (s != DART_OK) return s;
+  if ((s = check_ptrs(Q, E, C, dH, acum, y_ssd, y)) != DART_OK) return s;
+  SmaFwdFn fn{prefill_shape(dims), Q, E, C, dH, y_ssd, acum, gate, y,
+              static_cast<hipStream_t>(stream)};
   return dispatch(dims->io, dims->dstate, dims->headdim, fn);
 }
 

@@ -64,6 +64,7 @@ struct SmaMath16 {
   e4_t ev[NTB][NPB];
   floatx4 zq[NTB][NPB], zc[NTB][NPB], acc[NTB][NPB];
   float mx[NTB], ls[NTB];
+  float at[NTB];       // decayed variant: log-decay from the chunk start to the token
   int row0, col, grp;  // first token row of the wave; lane coordinates
 
   __device__ __forceinline__ void init(int w, int lane) {
@@ -135,7 +136,11 @@ struct SmaMath16 {
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * NTB, 0);
     }
   }
-  __device__ __forceinline__ void softmax(float scale_log2) {
+  // DECAY: key and value of the memory are scaled by d = exp(at + dlog),
+  // the SSM decay from the memory's chunk end to the token (dlog: the
+  // log-decay over the chunks between that end and the token's chunk)
+  template <bool DECAY = false>
+  __device__ __forceinline__ void softmax(float scale_log2, float dlog = 0.f) {
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
       float s = 0.f;
@@ -144,6 +149,8 @@ struct SmaMath16 {
 #pragma unroll
         for (int i = 0; i < 4; ++i) s += zq[tb][pb][i] * to_f32(ev[tb][pb][i]);
       s = sum_lane_groups(s) * scale_log2;
+      const float d = DECAY ? exp2_fast((at[tb] + dlog) * kLog2e) : 1.f;
+      if (DECAY) s *= d;
       // The reference max mx is raised only when a score passes it by more
       // than kLazyLog2 (a wave-uniform branch, taken at the first memory and
       // rarely after); otherwise the weights 2^(s - mx) stay below
@@ -158,8 +165,9 @@ struct SmaMath16 {
       }
       const float pw = exp2_fast(s - mx[tb]);
       ls[tb] += pw;
+      const float pv = DECAY ? pw * d : pw;
 #pragma unroll
-      for (int pb = 0; pb < NPB; ++pb) acc[tb][pb] += pw * zc[tb][pb];
+      for (int pb = 0; pb < NPB; ++pb) acc[tb][pb] += pv * zc[tb][pb];
     }
   }
   // y = y_ssd + gate·o in the LDS rows [t][p] that hold y_ssd
@@ -211,11 +219,18 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 // first within each group: the memories of a group (4 x 512 KB at the
 // largest shape) stay resident in the XCD's 4 MB L2 while the k-ordering
 // keeps the tail short.
-template <typename T, int N, int P, int NTB, int WAVES>
+//
+// DECAY (the decay-included variant): key and value of memory c are scaled
+// for token t by the SSM decay from the end of chunk c to t, d_{t,c} =
+// exp(acum_k[t] + Σ_{c<c'<k} acum_end[c']).  The memories are then taken
+// newest first, so the chunk sum is a running sum of non-positive terms
+// (no cancellation); the softmax does not depend on the order.
+template <typename T, int N, int P, int NTB, int WAVES, bool DECAY>
 __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     const T* __restrict__ Q, const T* __restrict__ E, const T* __restrict__ C,
-    const T* __restrict__ dH, const T* __restrict__ y_ssd, float gate, T* __restrict__ y,
-    int BH, int L, int H, int G, int S, int npq, int bg_major, float scale_log2) {
+    const T* __restrict__ dH, const T* __restrict__ y_ssd, const float* __restrict__ acum,
+    float gate, T* __restrict__ y, int BH, int L, int H, int G, int S, int npq, int bg_major,
+    float scale_log2) {
   using MM = Mma<T>;
   constexpr int K = MM::K, KL = MM::KL, VE = Vec16<T>::n;
   // LDS row strides (elements): a 32-byte pad keeps the 16-byte fragment reads
@@ -292,9 +307,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     es[v] = load16(E + ((row0 + t) * H + h) * P + pv * VE);
   }
   const T* mem = dH + (long)pair * M * (P * N);
+  // loop step i multiplies memory mi(i): oldest first, or newest first with DECAY
+  auto mi = [&](int i) __attribute__((always_inline)) { return DECAY ? k - 1 - i : i; };
   vec_t stg0[VPT], stg[VPT];
-  auto gload = [&](int c, vec_t (&dst)[VPT]) __attribute__((always_inline)) {
-    const vec_t* src = reinterpret_cast<const vec_t*>(mem + (long)c * (P * N));
+  auto gload = [&](int i, vec_t (&dst)[VPT]) __attribute__((always_inline)) {
+    const vec_t* src = reinterpret_cast<const vec_t*>(mem + (long)mi(i) * (P * N));
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
       const int vi = tid + v * NTHR;
@@ -330,6 +347,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   SmaMath16<T, N, P, NTB> tm;
   tm.init(w, lane);
   tm.load_q(sh_r1, LDN);
+  const float* acum_pair = DECAY ? acum + (long)pair * M * S : nullptr;
+  if (DECAY) {
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) tm.at[tb] = acum_pair[(long)k * S + sub * TWG + tm.lrow(tb)];
+  }
   __syncthreads();
   // C tile -> fragments
 #pragma unroll
@@ -351,8 +373,18 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   tm.load_e(sh_r1, LDE);
   __syncthreads();  // sh_r1 becomes the memory buffers
 
-  auto mma_mem = [&](int cur) __attribute__((always_inline)) { tm.mma(sh_mem[cur], LDN); };
-  auto softmax_mem = [&]() __attribute__((always_inline)) { tm.softmax(scale_log2); };
+  // DECAY: dlog is the log-decay over the chunks after the memory being
+  // finished (a running sum over memories taken newest first); each wave
+  // reads the next chunk-end value during its MFMA half
+  float dlog = 0.f, ae = 0.f;
+  auto mma_mem = [&](int cur, int c) __attribute__((always_inline)) {
+    if (DECAY) ae = acum_pair[(long)mi(c) * S + (S - 1)];
+    tm.mma(sh_mem[cur], LDN);
+  };
+  auto softmax_mem = [&]() __attribute__((always_inline)) {
+    tm.template softmax<DECAY>(scale_log2, dlog);
+    if (DECAY) dlog += ae;
+  };
   // Ping-pong: the first half of the waves (one per SIMD) runs its MFMAs
   // while the second half runs its softmax, then they swap, so the matrix
   // core and the vector ALU of every SIMD stay busy together.  Two barriers
@@ -375,7 +407,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     };
     // first half: lead waves multiply memory c, the others finish memory c-1
     if (lead) {
-      if (c < k) mma_mem(PAR);
+      if (c < k) mma_mem(PAR, c);
     } else {
       if (c > 0) softmax_mem();
       stage_next();
@@ -386,7 +418,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
       if (c < k) softmax_mem();
       stage_next();
     } else if (c < k) {
-      mma_mem(PAR);
+      mma_mem(PAR, c);
     }
     __syncthreads();
   };
@@ -691,7 +723,7 @@ __global__ void k_decode_advance(int* __restrict__ n_chunks, int* __restrict__ p
 
 template <typename T, int N, int P, int NTB, int WAVES>
 hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T* C, const T* dH,
-                         const T* y_ssd, float gate, T* y, hipStream_t st) {
+                         const T* y_ssd, const float* acum, float gate, T* y, hipStream_t st) {
   const int M = s.L / s.S;
   const int BH = s.B * s.H;
   const int hpg = s.H / s.G;
@@ -701,9 +733,14 @@ hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T*
   const int ngrp = (npq + kPairsPerGroup - 1) / kPairsPerGroup;
   const long blocks = 8L * ngrp * kPairsPerGroup * M * tpc;
   const float scale_log2 = kLog2e / sqrtf(static_cast<float>(N));
-  hipLaunchKernelGGL((k_sma_fwd<T, N, P, NTB, WAVES>), dim3(blocks), dim3(64 * WAVES), 0, st, Q,
-                     E, C, dH, y_ssd, gate, y, BH, s.L, s.H, s.G, s.S, npq, bg_major,
-                     scale_log2);
+  if (acum)
+    hipLaunchKernelGGL((k_sma_fwd<T, N, P, NTB, WAVES, true>), dim3(blocks), dim3(64 * WAVES), 0,
+                       st, Q, E, C, dH, y_ssd, acum, gate, y, BH, s.L, s.H, s.G, s.S, npq,
+                       bg_major, scale_log2);
+  else
+    hipLaunchKernelGGL((k_sma_fwd<T, N, P, NTB, WAVES, false>), dim3(blocks), dim3(64 * WAVES), 0,
+                       st, Q, E, C, dH, y_ssd, acum, gate, y, BH, s.L, s.H, s.G, s.S, npq,
+                       bg_major, scale_log2);
   return hipGetLastError();
 }
 
@@ -711,13 +748,14 @@ hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T*
 
 template <typename T, int N, int P>
 hipError_t launch_sma_fwd(const PrefillShape& s, const T* Q, const T* E, const T* C,
-                          const T* dH, const T* y_ssd, float gate, T* y, hipStream_t st) {
+                          const T* dH, const T* y_ssd, const float* acum, float gate, T* y,
+                          hipStream_t st) {
   constexpr int NTB = SmaTile<N, P>::NTB;
   const int r = s.S / (16 * NTB);  // S % 32 == 0, so r >= 1
-  if (r % 8 == 0) return sma_fwd_waves<T, N, P, NTB, 8>(s, Q, E, C, dH, y_ssd, gate, y, st);
-  if (r % 4 == 0) return sma_fwd_waves<T, N, P, NTB, 4>(s, Q, E, C, dH, y_ssd, gate, y, st);
-  if (r % 2 == 0) return sma_fwd_waves<T, N, P, NTB, 2>(s, Q, E, C, dH, y_ssd, gate, y, st);
-  return sma_fwd_waves<T, N, P, NTB, 1>(s, Q, E, C, dH, y_ssd, gate, y, st);
+  if (r % 8 == 0) return sma_fwd_waves<T, N, P, NTB, 8>(s, Q, E, C, dH, y_ssd, acum, gate, y, st);
+  if (r % 4 == 0) return sma_fwd_waves<T, N, P, NTB, 4>(s, Q, E, C, dH, y_ssd, acum, gate, y, st);
+  if (r % 2 == 0) return sma_fwd_waves<T, N, P, NTB, 2>(s, Q, E, C, dH, y_ssd, acum, gate, y, st);
+  return sma_fwd_waves<T, N, P, NTB, 1>(s, Q, E, C, dH, y_ssd, acum, gate, y, st);
 }
 
 template <typename T, int N, int P>
@@ -754,7 +792,8 @@ hipError_t launch_sma_decode(const DecodeShape& s, const T* x, const float* dt, 
 
 #define DART_INST_SMA(T, N, P)                                                                 \
   template hipError_t launch_sma_fwd<T, N, P>(const PrefillShape&, const T*, const T*, const T*, \
-                                              const T*, const T*, float, T*, hipStream_t);   \
+                                              const T*, const T*, const float*, float, T*,   \
+                                              hipStream_t);                                  \
   template hipError_t launch_sma_decode<T, N, P>(                                                \
       const DecodeShape&, const T*, const float*, const float*, const T*, const T*, const T*,    \
       const T*, float, T*, float*, float*, int*, int*, T*, void*, hipStream_t);

@@ -360,4 +360,53 @@ def pin_cache_ratio_golden(orc):
     assert (dart, attn) == (1048576, 4194304)
 
 
+def pin_sma_decayed_no_decay(orc):
+    """With A = 0 nothing decays (d = 1) and the decay-included variant is
+    the plain SMA."""
+    d = _inputs(21, B=1, L=16, H=2, G=1, N=3, P=4, A_zero=True)
+    S = 4
+    dH = orc.chunk_states(d["x"], d["dt"], d["A"], d["Bm"], S)
+    _close(orc.sma_decayed(d["Q"], d["E"], d["C"], dH, d["dt"], d["A"], S),
+           orc.sma(d["Q"], d["E"], d["C"], dH, S), what="A=0 decayed SMA")
+
+
+def pin_sma_decayed_from_recurrence(orc):
+    """The decayed memory of chunk c seen from token t is, by linearity, the
+    recurrent state at t when only chunk c's tokens feed the recurrence.
+    Building keys, values and the softmax from those states by hand (scalar
+    loops) must give the decay-included readout (Pith review, major comment
+    3: the decay A_{e(c)+1:t} applied to ΔH[c])."""
+    d = _inputs(22, B=1, L=12, H=2, G=1, N=3, P=4)
+    d["Q"] = d["Q"] * 3.0                      # a peaked softmax
+    S = 3
+    B, L, H, P = d["x"].shape
+    N = d["Bm"].shape[-1]
+    M = L // S
+    dH = orc.chunk_states(d["x"], d["dt"], d["A"], d["Bm"], S)
+    got = orc.sma_decayed(d["Q"], d["E"], d["C"], dH, d["dt"], d["A"], S)
+    # states[c][t]: recurrence fed by chunk c alone
+    states = []
+    for c in range(M):
+        xc = np.zeros_like(d["x"])
+        xc[:, c * S:(c + 1) * S] = d["x"][:, c * S:(c + 1) * S]
+        _, _, st = orc.recurrence(xc, d["dt"], d["A"], d["Bm"], d["C"], keep_states=True)
+        states.append(st)
+    ref = np.zeros((B, L, H, P))
+    for h in range(H):
+        for t in range(S, L):
+            k = t // S
+            sc, vals = [], []
+            for c in range(k):
+                m = states[c][0, t, h]               # [N, P]
+                key = [sum(m[n, p] * d["E"][0, t, h, p] for p in range(P)) for n in range(N)]
+                sc.append(sum(d["Q"][0, t, 0, n] * key[n] for n in range(N)) / math.sqrt(N))
+                vals.append([sum(d["C"][0, t, 0, n] * m[n, p] for n in range(N))
+                             for p in range(P)])
+            mx = max(sc)
+            w = [math.exp(v - mx) for v in sc]
+            for p in range(P):
+                ref[0, t, h, p] = sum(wi * v[p] for wi, v in zip(w, vals)) / sum(w)
+    _close(got, ref, tol=1e-9, what="decayed SMA vs recurrence states")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

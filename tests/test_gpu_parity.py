@@ -48,21 +48,22 @@ def _pn_to_np(t):
     return np.swapaxes(synth.as_f64(t), -1, -2)
 
 
-def run_prefill_case(B, L, H, G, N, P, S, io, seed=0, gate=0.5, qscale=1.0, h0_std=0.0):
+def run_prefill_case(B, L, H, G, N, P, S, io, seed=0, gate=0.5, qscale=1.0, h0_std=0.0,
+                     decayed=False):
     _need_gpu()
     print(f"prefill case B{B} L{L} H{H} G{G} N{N} P{P} S{S} {io} seed{seed} "
-          f"qscale{qscale} h0_std{h0_std}", flush=True)
+          f"qscale{qscale} h0_std{h0_std} decayed{decayed}", flush=True)
     inp = synth.draw_prefill(seed, B, L, H, G, N, P, io=io, qscale=qscale)
     h0 = None
     if h0_std:
         h0 = synth.draw_state(seed + 1, (B, H, P, N), h0_std, torch.float32)
     d = _to_dev(inp)
     out = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate, S,
-                      h0=None if h0 is None else h0.to(DEV))
+                      h0=None if h0 is None else h0.to(DEV), decayed=decayed)
     torch.cuda.synchronize()
     n = _np(inp)
     ref = oracle.prefill(n["x"], n["dt"], n["A"], n["Bm"], n["C"], n["Q"], n["E"], gate, S,
-                         h0=None if h0 is None else _pn_to_np(h0))
+                         h0=None if h0 is None else _pn_to_np(h0), decayed=decayed)
     assert_parity(_pn_to_np(out["dH_f32"]), ref["dH"], io, "dH_f32")
     assert_parity(_pn_to_np(out["dH"]), ref["dH"], io, "dH")
     assert_parity(_pn_to_np(out["H_in"]), ref["H_in"][:, :, :-1], io, "H_in")
@@ -108,6 +109,22 @@ def test_prefill_sharpened_softmax(qscale):
                                 qscale=qscale, gate=1.0)
     o_gpu = synth.as_f64(out["y"]) - synth.as_f64(out["y_ssd"])
     assert_parity(o_gpu, ref["o"], torch.bfloat16, "o (sharpened)")
+
+
+@pytest.mark.parametrize("B,L,H,G,N,P,S,io,qscale", [
+    (1, 768, 3, 3, 128, 64, 256, torch.bfloat16, 1.0),   # M = 3, 8-wave tiles
+    (2, 512, 2, 2, 128, 128, 256, torch.bfloat16, 1.0),  # one token block per wave
+    (1, 384, 4, 2, 64, 64, 128, torch.bfloat16, 1e2),    # sharpened, grouped B/C/Q
+    (2, 64, 3, 1, 32, 32, 32, torch.bfloat16, 1.0),      # M = 2
+    (2, 96, 3, 3, 32, 32, 96, torch.float32, 1e2),       # S not a power of two
+    (1, 320, 2, 1, 16, 16, 32, torch.float32, 1.0),      # M = 10: old memories decay to ~0
+])
+def test_prefill_decayed(B, L, H, G, N, P, S, io, qscale):
+    """The decay-included SMA variant (dart_sma_fwd_decayed) against the
+    oracle's sma_decayed, through the whole prefill."""
+    out, ref = run_prefill_case(B, L, H, G, N, P, S, io, seed=7 + L, qscale=qscale,
+                                decayed=True)
+    assert out["y"].isfinite().all()
 
 
 def test_prefill_sharpened_fp32():

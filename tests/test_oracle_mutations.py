@@ -35,6 +35,12 @@ MUTATIONS = [
      "causal = np.triu(np.ones((S, S), dtype=bool))"),
     ("intra-chunk weight missing dt",
      "wts = cb * decay * dtk[:, None, :, :]", "wts = cb * decay"),
+    ("decayed SMA: decay starts at the chunk's last token",
+     "ends = np.arange(k) * S + (S - 1)", "ends = np.arange(k) * S + (S - 2)"),
+    ("decayed SMA: decay on the score only",
+     "vals = d[:, :, None] * np.einsum", "vals = 1.0 * np.einsum"),
+    ("decayed SMA: decay on the value only",
+     "scores = d * np.einsum(\"tn,tcn->tc\"", "scores = 1.0 * np.einsum(\"tn,tcn->tc\""),
     ("score scale sqrt(P)",
      'scores = np.einsum("tn,tcn->tc", Qh[b, ts, h], keys) / math.sqrt(N)',
      'scores = np.einsum("tn,tcn->tc", Qh[b, ts, h], keys) / math.sqrt(P)'),
@@ -43,8 +49,8 @@ MUTATIONS = [
     ("decode value read with the query",
      'vals = np.einsum("n,cnp->cp", Ch[b, hh], mem)', 'vals = np.einsum("n,cnp->cp", Qh[b, hh], mem)'),
     ("query replaced by C",
-     'np.einsum("tn,tcn->tc", Qh[b, ts, h], keys)',
-     'np.einsum("tn,tcn->tc", Ch[b, ts, h], keys)'),
+     'scores = np.einsum("tn,tcn->tc", Qh[b, ts, h], keys)',
+     'scores = np.einsum("tn,tcn->tc", Ch[b, ts, h], keys)'),
     ("own chunk visible",
      "mem = dH[b, h, :k]                                  # [k,N,P]",
      "mem = dH[b, h, :k + 1]                              # [k,N,P]"),

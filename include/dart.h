@@ -137,6 +137,27 @@ dart_status dart_sma_fwd(const dart_dims* dims, const void* Q, const void* E,
                          void* y, void* stream);
 
 /*
+ * Continuation of sequences that already hold prior_chunks completed chunks
+ * (chunked prefill after an earlier prefill or decode).  The L = M·S tokens
+ * of dims are chunks prior_chunks .. prior_chunks+M-1 of their sequences;
+ * their memories dH come from dart_chunk_state on these tokens and their
+ * y_ssd from dart_state_pass with h0 = the state after the prior chunks.
+ * Token t of local chunk j attends to memories c < prior_chunks + j:
+ * memory c < prior_chunks is cache[b,h,c], memory prior_chunks + i is
+ * dH[b,h,i]; otherwise the formulas of dart_sma_fwd.  prior_chunks = 0 is
+ * dart_sma_fwd.
+ *
+ * in:  Q, E, C, dH, y_ssd as dart_sma_fwd; cache [B,H,cache_chunks,P,N] io
+ *      (the dart_sma_decode cache layout; may be NULL when prior_chunks = 0)
+ * out: y [B,L,H,P] io
+ * errors: DART_ERR_BAD_DIMS unless 0 <= prior_chunks <= cache_chunks
+ */
+dart_status dart_sma_fwd_cont(const dart_dims* dims, int64_t prior_chunks, int64_t cache_chunks,
+                              const void* Q, const void* E, const void* C, const void* cache,
+                              const void* dH, const void* y_ssd, float gate, void* y,
+                              void* stream);
+
+/*
  * The decay-included variant of dart_sma_fwd, the ablation the Pith review
  * of DART asks for (referee major comment 3, paper §3 Eq. 8): key and value
  * of memory c are scaled, for token t of chunk k > c, by the decay the SSM

@@ -58,6 +58,7 @@ __all__ = [
     "sma",
     "sma_bruteforce",
     "sma_decayed",
+    "sma_continue",
     "gated_output",
     "prefill",
     "decode_step",
@@ -258,6 +259,33 @@ def sma_bruteforce(Q, E, C, dH, S):
                 tot = sum(wts)
                 for p in range(P):
                     o[b, t, h, p] = sum(w * v[p] for w, v in zip(wts, vals)) / tot
+    return o
+
+
+def sma_continue(Q, E, C, dH_prior, dH, S):
+    """SMA readout of tokens that continue sequences already holding
+    k0 = dH_prior.shape[2] completed chunks (chunked prefill): token t of
+    local chunk j is token k0·S + t of the whole sequence and attends to the
+    k0 prior memories and the first j new ones, with the formulas of
+    :func:`sma`.  Returns o [B,L,H,P] for the new tokens."""
+    E = _f64(E)
+    Bsz, L, H, P = E.shape
+    Qh, Ch = _per_head(Q, H), _per_head(C, H)
+    N = Qh.shape[-1]
+    mem_all = np.concatenate([_f64(dH_prior), _f64(dH)], axis=2)
+    k0 = dH_prior.shape[2]
+    o = np.zeros((Bsz, L, H, P))
+    for b in range(Bsz):
+        for h in range(H):
+            for j in range(L // S):
+                if k0 + j == 0:
+                    continue
+                ts = np.arange(j * S, (j + 1) * S)
+                seen = mem_all[b, h, :k0 + j]                       # [k0+j,N,P]
+                key = np.einsum("cnp,tp->tcn", seen, E[b, ts, h])
+                sc = np.einsum("tn,tcn->tc", Qh[b, ts, h], key) / math.sqrt(N)
+                val = np.einsum("tn,cnp->tcp", Ch[b, ts, h], seen)
+                o[b, ts, h] = np.einsum("tc,tcp->tp", _softmax(sc), val)
     return o
 
 

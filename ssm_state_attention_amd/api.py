@@ -97,6 +97,25 @@ def dart_sma_fwd(Q, E, C, dH, y_ssd, gate, y, chunk):
     check(lib().dart_sma_fwd(d, *args, float(gate), yp, _stream()), "dart_sma_fwd")
 
 
+def dart_sma_fwd_cont(Q, E, C, cache, prior_chunks, dH, y_ssd, gate, y, chunk):
+    """SMA + gated add for tokens that continue sequences holding
+    ``prior_chunks`` memories in ``cache`` [B,H,max_chunks,P,N] io (see
+    include/dart.h); dH [B,H,M,P,N] are the new tokens' memories."""
+    B, L, H, P = E.shape
+    G, N = Q.shape[2], Q.shape[3]
+    d = DartDims(B, L, H, G, N, P, int(chunk), _io_code(E.dtype))
+    M, io, dev = L // chunk, E.dtype, E.device
+    cache_chunks = cache.shape[2]
+    args = [_ptr(Q, "Q", io, (B, L, G, N), dev), _ptr(E, "E", io, (B, L, H, P), dev),
+            _ptr(C, "C", io, (B, L, G, N), dev),
+            _ptr(cache, "cache", io, (B, H, cache_chunks, P, N), dev),
+            _ptr(dH, "dH", io, (B, H, M, P, N), dev),
+            _ptr(y_ssd, "y_ssd", io, (B, L, H, P), dev)]
+    yp = _ptr(y, "y", io, (B, L, H, P), dev)
+    check(lib().dart_sma_fwd_cont(d, int(prior_chunks), int(cache_chunks), *args, float(gate),
+                                  yp, _stream()), "dart_sma_fwd_cont")
+
+
 def dart_sma_fwd_decayed(Q, E, C, dH, acum, y_ssd, gate, y, chunk):
     """Decay-included SMA + gated add (see include/dart.h): acum [B,H,M,S]
     f32 from dart_chunk_state; y [B,L,H,P] io."""
@@ -173,6 +192,33 @@ def prefill(x, dt, A, Bm, C, Q, E, gate, chunk, h0=None, decayed=False):
         dart_sma_fwd_decayed(Q, E, C, out["dH"], out["acum"], out["y_ssd"], gate, out["y"], chunk)
     else:
         dart_sma_fwd(Q, E, C, out["dH"], out["y_ssd"], gate, out["y"], chunk)
+    return out
+
+
+def prefill_continue(x, dt, A, Bm, C, Q, E, gate, chunk, cache, prior_chunks, h0):
+    """Chunked prefill: the tokens are chunks prior_chunks, prior_chunks+1, ...
+    of sequences whose first prior_chunks memories are in ``cache``
+    [B,H,max_chunks,P,N] (the decode cache) and whose state after them is
+    ``h0`` [B,H,P,N] f32.  Returns the dict of :func:`prefill` for the new
+    tokens; the new memories (out["dH"]) are not written into the cache."""
+    B, L, H, P = x.shape
+    N = Bm.shape[3]
+    M, dev = L // chunk, x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {
+        "acum": torch.empty(B, H, M, chunk, **f32),
+        "dH": torch.empty(B, H, M, P, N, dtype=x.dtype, device=dev),
+        "dH_f32": torch.empty(B, H, M, P, N, **f32),
+        "H_in": torch.empty(B, H, M, P, N, dtype=x.dtype, device=dev),
+        "h_final": torch.empty(B, H, P, N, **f32),
+        "y_ssd": torch.empty(B, L, H, P, dtype=x.dtype, device=dev),
+        "y": torch.empty(B, L, H, P, dtype=x.dtype, device=dev),
+    }
+    dart_chunk_state(x, dt, A, Bm, out["acum"], out["dH"], out["dH_f32"], chunk)
+    dart_state_pass(x, dt, Bm, C, out["acum"], out["dH_f32"], h0, out["H_in"], out["h_final"],
+                    out["y_ssd"], chunk)
+    dart_sma_fwd_cont(Q, E, C, cache, prior_chunks, out["dH"], out["y_ssd"], gate, out["y"],
+                      chunk)
     return out
 
 

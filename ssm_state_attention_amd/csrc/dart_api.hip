@@ -79,13 +79,16 @@ struct SmaFwdFn {
   const float* acum;
   float gate;
   void* y;
+  const void* prior;
+  int k0, pstride;
   hipStream_t st;
   template <typename T, int N, int P>
   hipError_t run() {
     return dart::launch_sma_fwd<T, N, P>(sh, static_cast<const T*>(Q), static_cast<const T*>(E),
                                          static_cast<const T*>(C), static_cast<const T*>(dH),
                                          static_cast<const T*>(y_ssd), acum, gate,
-                                         static_cast<T*>(y), st);
+                                         static_cast<T*>(y), static_cast<const T*>(prior), k0,
+                                         pstride, st);
   }
 };
 
@@ -139,8 +142,25 @@ extern "C" dart_status dart_sma_fwd(const dart_dims* dims, const void* Q, const 
   dart_status s = dart_validate_dims(dims);
   if (s != DART_OK) return s;
   if ((s = check_ptrs(Q, E, C, dH, y_ssd, y)) != DART_OK) return s;
-  SmaFwdFn fn{prefill_shape(dims), Q, E, C, dH, y_ssd, nullptr, gate, y,
+  SmaFwdFn fn{prefill_shape(dims), Q, E, C, dH, y_ssd, nullptr, gate, y, nullptr, 0, 0,
               static_cast<hipStream_t>(stream)};
+  return dispatch(dims->io, dims->dstate, dims->headdim, fn);
+}
+
+extern "C" dart_status dart_sma_fwd_cont(const dart_dims* dims, int64_t prior_chunks,
+                                         int64_t cache_chunks, const void* Q, const void* E,
+                                         const void* C, const void* cache, const void* dH,
+                                         const void* y_ssd, float gate, void* y, void* stream) {
+  dart_status s = dart_validate_dims(dims);
+  if (s != DART_OK) return s;
+  if (prior_chunks < 0 || cache_chunks < prior_chunks || prior_chunks > INT32_MAX ||
+      cache_chunks > INT32_MAX || prior_chunks + dims->seqlen / dims->chunk > INT32_MAX)
+    return DART_ERR_BAD_DIMS;
+  if ((s = check_ptrs(Q, E, C, dH, y_ssd, y)) != DART_OK) return s;
+  if (prior_chunks > 0 && (s = check_ptrs(cache)) != DART_OK) return s;
+  SmaFwdFn fn{prefill_shape(dims), Q, E, C, dH, y_ssd, nullptr, gate, y,
+              prior_chunks > 0 ? cache : nullptr, static_cast<int>(prior_chunks),
+              static_cast<int>(cache_chunks), static_cast<hipStream_t>(stream)};
   return dispatch(dims->io, dims->dstate, dims->headdim, fn);
 }
 
@@ -151,7 +171,7 @@ extern "C" dart_status dart_sma_fwd_decayed(const dart_dims* dims, const void* Q
   dart_status s = dart_validate_dims(dims);
   if (s != DART_OK) return s;
   if ((s = check_ptrs(Q, E, C, dH, acum, y_ssd, y)) != DART_OK) return s;
-  SmaFwdFn fn{prefill_shape(dims), Q, E, C, dH, y_ssd, acum, gate, y,
+  SmaFwdFn fn{prefill_shape(dims), Q, E, C, dH, y_ssd, acum, gate, y, nullptr, 0, 0,
               static_cast<hipStream_t>(stream)};
   return dispatch(dims->io, dims->dstate, dims->headdim, fn);
 }

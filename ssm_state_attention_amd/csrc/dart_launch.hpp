@@ -26,10 +26,12 @@ hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt,
                              hipStream_t st);
 
 template <typename T, int N, int P>
-// acum == nullptr: the SMA of the pages; otherwise the decay-included variant
+// acum == nullptr: the SMA of the pages; otherwise the decay-included variant.
+// k0 > 0: the tokens continue sequences whose first k0 memories are in prior
+// (pstride memories per (batch, head)).
 hipError_t launch_sma_fwd(const PrefillShape& s, const T* Q, const T* E, const T* C,
                           const T* dH, const T* y_ssd, const float* acum, float gate, T* y,
-                          hipStream_t st);
+                          const T* prior, int k0, int pstride, hipStream_t st);
 
 template <typename T, int N, int P>
 hipError_t launch_sma_decode(const DecodeShape& s, const T* x, const float* dt, const float* A,

@@ -225,12 +225,17 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 // exp(acum_k[t] + Σ_{c<c'<k} acum_end[c']).  The memories are then taken
 // newest first, so the chunk sum is a running sum of non-positive terms
 // (no cancellation); the softmax does not depend on the order.
+//
+// Continuation (k0 > 0): the L tokens are chunks k0 .. k0+M-1 of their
+// sequences; memories c < k0 come from `prior` (one row of `pstride`
+// memories per (batch, head), the decode cache layout), memories c >= k0
+// from dH (chunk c - k0).
 template <typename T, int N, int P, int NTB, int WAVES, bool DECAY>
 __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     const T* __restrict__ Q, const T* __restrict__ E, const T* __restrict__ C,
     const T* __restrict__ dH, const T* __restrict__ y_ssd, const float* __restrict__ acum,
     float gate, T* __restrict__ y, int BH, int L, int H, int G, int S, int npq, int bg_major,
-    float scale_log2) {
+    float scale_log2, const T* __restrict__ prior, int k0, int pstride) {
   using MM = Mma<T>;
   constexpr int K = MM::K, KL = MM::KL, VE = Vec16<T>::n;
   // LDS row strides (elements): a 32-byte pad keeps the 16-byte fragment reads
@@ -266,7 +271,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   const int sub = rem % tpc, r = rem / tpc;
   const int qg = r % GP, kr = r / GP;
   const int ql = grp_i * GP + qg;
-  const int k = M - 1 - kr;
+  const int kl = M - 1 - kr;  // the tile's chunk among the L tokens
+  const int k = k0 + kl;      // memories it attends
   // bg_major: the heads of one (batch, group) run on one XCD, adjacent in
   // the ordering, so their shared Q_t/C_t tiles are reused from L2
   int pair;
@@ -282,7 +288,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   const int b = pair / H, h = pair % H, g = h / (H / G);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const long row0 = (long)b * L + (long)k * S + sub * TWG;  // first token of the tile
+  const long row0 = (long)b * L + (long)kl * S + sub * TWG;  // first token of the tile
 
   // ---- prologue: every load in flight before the first wait ----
   vec_t qs[QV], cs[QV], es[EV], ys[EV];
@@ -307,11 +313,14 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     es[v] = load16(E + ((row0 + t) * H + h) * P + pv * VE);
   }
   const T* mem = dH + (long)pair * M * (P * N);
+  const T* pmem = k0 > 0 ? prior + (long)pair * pstride * (P * N) : nullptr;
   // loop step i multiplies memory mi(i): oldest first, or newest first with DECAY
   auto mi = [&](int i) __attribute__((always_inline)) { return DECAY ? k - 1 - i : i; };
   vec_t stg0[VPT], stg[VPT];
   auto gload = [&](int i, vec_t (&dst)[VPT]) __attribute__((always_inline)) {
-    const vec_t* src = reinterpret_cast<const vec_t*>(mem + (long)mi(i) * (P * N));
+    const int c = mi(i);
+    const vec_t* src = reinterpret_cast<const vec_t*>(
+        c < k0 ? pmem + (long)c * (P * N) : mem + (long)(c - k0) * (P * N));
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
       const int vi = tid + v * NTHR;
@@ -350,7 +359,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   const float* acum_pair = DECAY ? acum + (long)pair * M * S : nullptr;
   if (DECAY) {
 #pragma unroll
-    for (int tb = 0; tb < NTB; ++tb) tm.at[tb] = acum_pair[(long)k * S + sub * TWG + tm.lrow(tb)];
+    for (int tb = 0; tb < NTB; ++tb) tm.at[tb] = acum_pair[(long)kl * S + sub * TWG + tm.lrow(tb)];
   }
   __syncthreads();
   // C tile -> fragments
@@ -723,7 +732,8 @@ __global__ void k_decode_advance(int* __restrict__ n_chunks, int* __restrict__ p
 
 template <typename T, int N, int P, int NTB, int WAVES>
 hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T* C, const T* dH,
-                         const T* y_ssd, const float* acum, float gate, T* y, hipStream_t st) {
+                         const T* y_ssd, const float* acum, float gate, T* y, const T* prior,
+                         int k0, int pstride, hipStream_t st) {
   const int M = s.L / s.S;
   const int BH = s.B * s.H;
   const int hpg = s.H / s.G;
@@ -736,11 +746,11 @@ hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T*
   if (acum)
     hipLaunchKernelGGL((k_sma_fwd<T, N, P, NTB, WAVES, true>), dim3(blocks), dim3(64 * WAVES), 0,
                        st, Q, E, C, dH, y_ssd, acum, gate, y, BH, s.L, s.H, s.G, s.S, npq,
-                       bg_major, scale_log2);
+                       bg_major, scale_log2, prior, k0, pstride);
   else
     hipLaunchKernelGGL((k_sma_fwd<T, N, P, NTB, WAVES, false>), dim3(blocks), dim3(64 * WAVES), 0,
                        st, Q, E, C, dH, y_ssd, acum, gate, y, BH, s.L, s.H, s.G, s.S, npq,
-                       bg_major, scale_log2);
+                       bg_major, scale_log2, prior, k0, pstride);
   return hipGetLastError();
 }
 
@@ -749,13 +759,20 @@ hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T*
 template <typename T, int N, int P>
 hipError_t launch_sma_fwd(const PrefillShape& s, const T* Q, const T* E, const T* C,
                           const T* dH, const T* y_ssd, const float* acum, float gate, T* y,
-                          hipStream_t st) {
+                          const T* prior, int k0, int pstride, hipStream_t st) {
   constexpr int NTB = SmaTile<N, P>::NTB;
   const int r = s.S / (16 * NTB);  // S % 32 == 0, so r >= 1
-  if (r % 8 == 0) return sma_fwd_waves<T, N, P, NTB, 8>(s, Q, E, C, dH, y_ssd, acum, gate, y, st);
-  if (r % 4 == 0) return sma_fwd_waves<T, N, P, NTB, 4>(s, Q, E, C, dH, y_ssd, acum, gate, y, st);
-  if (r % 2 == 0) return sma_fwd_waves<T, N, P, NTB, 2>(s, Q, E, C, dH, y_ssd, acum, gate, y, st);
-  return sma_fwd_waves<T, N, P, NTB, 1>(s, Q, E, C, dH, y_ssd, acum, gate, y, st);
+  if (r % 8 == 0)
+    return sma_fwd_waves<T, N, P, NTB, 8>(s, Q, E, C, dH, y_ssd, acum, gate, y, prior, k0,
+                                           pstride, st);
+  if (r % 4 == 0)
+    return sma_fwd_waves<T, N, P, NTB, 4>(s, Q, E, C, dH, y_ssd, acum, gate, y, prior, k0,
+                                           pstride, st);
+  if (r % 2 == 0)
+    return sma_fwd_waves<T, N, P, NTB, 2>(s, Q, E, C, dH, y_ssd, acum, gate, y, prior, k0,
+                                           pstride, st);
+  return sma_fwd_waves<T, N, P, NTB, 1>(s, Q, E, C, dH, y_ssd, acum, gate, y, prior, k0, pstride,
+                                        st);
 }
 
 template <typename T, int N, int P>
@@ -793,7 +810,7 @@ hipError_t launch_sma_decode(const DecodeShape& s, const T* x, const float* dt, 
 #define DART_INST_SMA(T, N, P)                                                                 \
   template hipError_t launch_sma_fwd<T, N, P>(const PrefillShape&, const T*, const T*, const T*, \
                                               const T*, const T*, const float*, float, T*,   \
-                                              hipStream_t);                                  \
+                                              const T*, int, int, hipStream_t);              \
   template hipError_t launch_sma_decode<T, N, P>(                                                \
       const DecodeShape&, const T*, const float*, const float*, const T*, const T*, const T*,    \
       const T*, float, T*, float*, float*, int*, int*, T*, void*, hipStream_t);

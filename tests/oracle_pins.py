@@ -360,6 +360,19 @@ def pin_cache_ratio_golden(orc):
     assert (dart, attn) == (1048576, 4194304)
 
 
+def pin_sma_continue_is_suffix_of_whole(orc):
+    """Continuing a sequence after its first k0 chunks reads the same as the
+    whole sequence's readout of those tokens (chunked prefill changes where
+    the work is split, not what is computed)."""
+    d = _inputs(23, B=2, L=20, H=2, G=1, N=3, P=4)
+    S, k0 = 4, 2
+    dH = orc.chunk_states(d["x"], d["dt"], d["A"], d["Bm"], S)
+    whole = orc.sma(d["Q"], d["E"], d["C"], dH, S)
+    tail = {k: v[:, k0 * S:] for k, v in d.items() if k in ("Q", "E", "C")}
+    got = orc.sma_continue(tail["Q"], tail["E"], tail["C"], dH[:, :, :k0], dH[:, :, k0:], S)
+    _close(got, whole[:, k0 * S:], what="continued SMA")
+
+
 def pin_sma_decayed_no_decay(orc):
     """With A = 0 nothing decays (d = 1) and the decay-included variant is
     the plain SMA."""

@@ -261,6 +261,61 @@ def test_decode_continues_prefill(io, N, P, S):
     assert st["n_chunks"].tolist() == [M] * B and st["pos"].tolist() == [0] * B
 
 
+@pytest.mark.parametrize("io,N,P,S,k0,M", [(torch.bfloat16, 128, 64, 256, 2, 2),
+                                             (torch.bfloat16, 64, 64, 64, 3, 2),
+                                             (torch.float32, 16, 16, 32, 4, 3)])
+def test_prefill_continuation(io, N, P, S, k0, M):
+    """Chunked prefill: prefill k0 chunks, keep their memories in a decode
+    cache and their final state, then prefill the next M chunks from there;
+    the continued outputs, memories and final state match the oracle's
+    prefill of the whole sequence."""
+    _need_gpu()
+    B, H, G = 2, 4, 2
+    L = (k0 + M) * S
+    print(f"continuation {io} N{N} P{P} S{S} k0={k0} M={M}", flush=True)
+    inp = synth.draw_prefill(60 + k0, B, L, H, G, N, P, io=io, qscale=10.0)
+    d = _to_dev(inp)
+    gate = 0.5
+    part = lambda lo, hi: {k: (v if k == "A" else v[:, lo:hi].contiguous()) for k, v in d.items()}
+    pre, tail = part(0, k0 * S), part(k0 * S, L)
+    head = api.prefill(pre["x"], pre["dt"], pre["A"], pre["Bm"], pre["C"], pre["Q"], pre["E"],
+                       gate, S)
+    cache = torch.zeros(B, H, k0 + M + 1, P, N, dtype=io, device=DEV)
+    cache[:, :, :k0].copy_(head["dH"])
+    cont = api.prefill_continue(tail["x"], tail["dt"], tail["A"], tail["Bm"], tail["C"],
+                                tail["Q"], tail["E"], gate, S, cache, k0, head["h_final"])
+    torch.cuda.synchronize()
+    n = _np(inp)
+    ref = oracle.prefill(n["x"], n["dt"], n["A"], n["Bm"], n["C"], n["Q"], n["E"], gate, S)
+    assert_parity(_pn_to_np(cont["dH"]), ref["dH"][:, :, k0:], io, "continued memories")
+    assert_parity(cont["y_ssd"], ref["y_ssd"][:, k0 * S:], io, "continued y_ssd")
+    assert_parity(_pn_to_np(cont["h_final"]), ref["h_final"], io, "continued final state")
+    assert_parity(cont["y"], ref["y"][:, k0 * S:], io, "continued y")
+
+
+def test_sma_continuation_arbitrary_cache():
+    """dart_sma_fwd_cont over prior memories that no prefill produced (a
+    seeded cache with spare capacity) against the oracle's sma_continue."""
+    _need_gpu()
+    B, H, G, N, P, S, k0, M = 2, 3, 3, 32, 32, 32, 5, 3
+    io = torch.float32
+    L = M * S
+    inp = synth.draw_prefill(70, B, L, H, G, N, P, io=io, qscale=10.0)
+    d = _to_dev(inp)
+    cache = synth.draw_state(71, (B, H, k0 + 2, P, N), 0.05, io, device=DEV)
+    h0 = synth.draw_state(72, (B, H, P, N), 0.05, torch.float32, device=DEV)
+    gate = 0.75
+    cont = api.prefill_continue(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate,
+                                S, cache, k0, h0)
+    torch.cuda.synchronize()
+    n = _np(inp)
+    prior = _pn_to_np(cache)[:, :, :k0]
+    dH = oracle.chunk_states(n["x"], n["dt"], n["A"], n["Bm"], S)
+    o_ref = oracle.sma_continue(n["Q"], n["E"], n["C"], prior, dH, S)
+    o_gpu = (synth.as_f64(cont["y"]) - synth.as_f64(cont["y_ssd"])) / gate
+    assert_parity(o_gpu, o_ref, io, "continued SMA readout")
+
+
 # ------------------------------------------------------ full-size samples
 def _oracle_pair(n, b, h, H, G, S, gate, tokens=None):
     """Oracle outputs of one (batch, head) pair, from sliced inputs."""

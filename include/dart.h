@@ -209,6 +209,54 @@ dart_status dart_sma_decode(const dart_decode_dims* dims, const void* x, const f
                             float* dH_cur, int32_t* n_chunks, int32_t* pos, void* y,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fp8 chunk-memory cache.  Source: Pith review of DART, "Where Pith is
+ * reading between the lines" (editorial extensions: because SMA reads the
+ * chunked scan's own dH, the memory cache can be combined with cache
+ * quantisation).  The pages fix no format; this library's format is:
+ *
+ *   cache8 [B,H,max_chunks,P,N] uint8: OCP FP8 E4M3 codes (sign, 4 exponent
+ *          bits with bias 7, 3 mantissa bits; no infinities, 0x7F and 0xFF
+ *          are NaN, largest finite value 448), in the layout of the io cache
+ *   scale  [B,H,max_chunks] f32: one power-of-two scale per memory
+ *
+ * Memory c of (b, h) stands for decode(cache8[b,h,c])·scale[b,h,c].  For a
+ * memory M with largest magnitude amax = f·2^E (0.5 <= f < 1) the scale is
+ * 2^e with e = max(E - 8, -126) (1 when amax = 0), and each code is M·2^-e
+ * rounded to the nearest E4M3 value, ties to even mantissa; |M·2^-e| < 256,
+ * so no code saturates.  The memories must be finite.
+ */
+
+/*
+ * Encode f32 memories into fp8 cache slots: for each (b, h) and i < n_mem,
+ * memory dH_f32[b,h,i] goes to slot first + i (codes and scale as above).
+ * Used after a prefill (dH_f32 of dart_chunk_state) to fill the cache that
+ * dart_sma_decode_fp8 reads.
+ *
+ * dims:   the decode dims of the cache (batch, nheads, dstate N, headdim P,
+ *         max_chunks, io; ngroups and chunk are validated but unused)
+ * in:     dH_f32 [B,H,n_mem,P,N] f32
+ * out:    cache8 slots [first, first + n_mem) and their scales
+ * errors: DART_ERR_BAD_DIMS unless 0 <= n_mem and 0 <= first <= max_chunks
+ *         - n_mem; n_mem = 0 writes nothing.
+ */
+dart_status dart_cache_fp8_store(const dart_decode_dims* dims, const float* dH_f32,
+                                 int64_t n_mem, int64_t first, uint8_t* cache8, float* scale,
+                                 void* stream);
+
+/*
+ * dart_sma_decode over the fp8 cache: identical steps and arguments except
+ * that the cache is (cache8, scale) in the format above.  Step 2 reads the
+ * memories decode(code)·scale; step 4 appends dH_cur (f32) encoded with its
+ * own scale.  Workspace: dart_sma_decode_workspace(dims) bytes, as for
+ * dart_sma_decode.
+ */
+dart_status dart_sma_decode_fp8(const dart_decode_dims* dims, const void* x, const float* dt,
+                                const float* A, const void* Bm, const void* C, const void* Q,
+                                const void* E, float gate, uint8_t* cache8, float* scale,
+                                float* h, float* dH_cur, int32_t* n_chunks, int32_t* pos, void* y,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Host-only checks (no HIP call; usable without a GPU). */
 dart_status dart_validate_dims(const dart_dims* dims);
 dart_status dart_validate_decode_dims(const dart_decode_dims* dims);

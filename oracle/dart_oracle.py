@@ -30,6 +30,9 @@ Sources (cited by page and section; the pages print no code):
 * [pith-axioms]  Pith review, axiom ledger: SSD writes Mamba-2 as structured
   causal attention (paper Eq. 4); the chunked scan splits the output into
   intra-chunk and inter-chunk terms and yields ΔH[c].
+* [pith-ext]  Pith review, "Where Pith is reading between the lines"
+  (editorial extensions): since SMA reads the scan's own ΔH, the memory cache
+  could be combined with cache quantisation.
 
 Readings where the pages are silent (each one is listed in the design doc):
 * Mamba-2 recurrence h_t = exp(dt_t·A)·h_{t-1} + dt_t·B_t x_tᵀ, y_t = C_tᵀ h_t
@@ -39,6 +42,9 @@ Readings where the pages are silent (each one is listed in the design doc):
 * Score scale 1/sqrt(N) (N is the key dimension).
 * Gate: y = y_ssd + g·o with g a raw scalar.
 * B, C and Q are shared by groups of H/G consecutive heads; x, E, dt per head.
+* Quantised cache [pith-ext] (the pages name no format): each memory is kept
+  as OCP FP8 E4M3 codes times one power-of-two scale per memory, see
+  :func:`fp8_quantize_memory`.
 
 Layouts (row-major numpy arrays, float64):
   x, E   [B, L, H, P]      dt [B, L, H]      A [H]
@@ -65,6 +71,12 @@ __all__ = [
     "cache_elements",
     "cache_ratio",
     "round_bf16",
+    "fp8_e4m3_decode",
+    "fp8_e4m3_encode",
+    "fp8_memory_scale",
+    "fp8_quantize_memory",
+    "fp8_dequantize",
+    "decode_step_fp8",
 ]
 
 
@@ -430,3 +442,106 @@ def cache_ratio(L, S, N, P):
     """DART cache / attention cache, per head [pith-eq14]."""
     dart, attn = cache_elements(L, S, N, P)
     return dart / attn
+
+
+# --------------------------------------------------------------------------
+# O10 - fp8 chunk-memory cache [pith-ext]
+# --------------------------------------------------------------------------
+# OCP 8-bit floating point, E4M3 variant: sign bit, 4 exponent bits with bias
+# 7, 3 mantissa bits; exponent field 0 holds the subnormals m·2^-9; there are
+# no infinities, the codes 0x7F and 0xFF are NaN, the largest finite value is
+# 1.75·2^8 = 448.
+E4M3_MAX = 448.0
+
+
+def fp8_e4m3_decode(codes):
+    """Value of each E4M3 code (uint8 array) as fp64; NaN codes give NaN."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c >= 128, -1.0, 1.0)
+    field = (c >> 3) & 15
+    mant = c & 7
+    normal = (1.0 + mant / 8.0) * np.exp2(field - 7.0)
+    sub = mant * 2.0 ** -9
+    v = sign * np.where(field == 0, sub, normal)
+    return np.where((field == 15) & (mant == 7), np.nan, v)
+
+
+def fp8_e4m3_encode(v):
+    """E4M3 code (uint8) of each value, rounded to the nearest representable
+    value with ties to the even mantissa.  The values must round to at most
+    448 in magnitude (ValueError otherwise): the scaled cache never gets
+    near that bound.  A value that rounds to zero keeps its sign (0x80 is
+    negative zero)."""
+    v = np.asarray(v, dtype=np.float64)
+    if not np.all(np.isfinite(v)):
+        raise ValueError("fp8_e4m3_encode: non-finite value")
+    neg = np.signbit(v)
+    a = np.abs(v)
+    # binade 2^e of |v| (frexp: a = f·2^E, 0.5 <= f < 1, so e = E - 1);
+    # the grid spacing is 2^(e-3), and 2^-9 throughout the subnormal range
+    _, E = np.frexp(a)
+    e = np.maximum(E - 1, -6)
+    step = np.exp2(e - 3.0)
+    r = np.round(a / step) * step  # numpy rounds halves to even
+    if np.any(r > E4M3_MAX):
+        raise ValueError("fp8_e4m3_encode: value beyond the E4M3 range")
+    # fields of the rounded magnitude (rounding may carry into the next binade)
+    _, Er = np.frexp(r)
+    er = Er - 1
+    is_sub = (r < 2.0 ** -6)
+    field = np.where(is_sub, 0, er + 7)
+    mant = np.where(is_sub, r / 2.0 ** -9,
+                    (r / np.exp2(np.where(is_sub, 0, er).astype(np.float64)) - 1.0) * 8.0)
+    mant = np.rint(mant).astype(np.int64)
+    code = np.where(neg, 128, 0) + field.astype(np.int64) * 8 + mant
+    return code.astype(np.uint8)
+
+
+def fp8_memory_scale(mem):
+    """Scale of one memory: 2^e with e = max(E - 8, -126), where the largest
+    magnitude of the memory is f·2^E, 0.5 <= f < 1; 1 for an all-zero memory.
+    The scaled memory then has its largest magnitude in [128, 256), inside
+    the E4M3 range with one binade to spare."""
+    amax = float(np.max(np.abs(np.asarray(mem, dtype=np.float64))))
+    if amax == 0.0:
+        return 1.0
+    _, E = math.frexp(amax)
+    return math.ldexp(1.0, max(E - 8, -126))
+
+
+def fp8_quantize_memory(mem):
+    """(codes uint8 of mem's shape, scale): codes = E4M3(mem / scale).  The
+    division by a power of two is exact, so the codes are the rounding of
+    the memory itself on a grid scaled by the scale."""
+    mem = np.asarray(mem, dtype=np.float64)
+    s = fp8_memory_scale(mem)
+    return fp8_e4m3_encode(mem / s), s
+
+
+def fp8_dequantize(codes, scale):
+    """Memories from codes [..., N, P] and scales [...]: decode(code)·scale."""
+    return fp8_e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[..., None, None]
+
+
+def decode_step_fp8(state, x, dt, A, Bm, C, Q, E, g, S):
+    """:func:`decode_step` over an fp8 cache.
+
+    state: as for decode_step, with the cache held as codes [B,H,Mmax,N,P]
+    (uint8) and scales [B,H,Mmax] instead of "cache".  The SMA reads the
+    dequantised memories decode(code)·scale; a memory appended by this step
+    is quantised with :func:`fp8_quantize_memory` (one scale per head)."""
+    codes = np.asarray(state["codes"]).copy()
+    scales = np.asarray(state["scales"], dtype=np.float64).copy()
+    plain = dict(state)
+    plain["cache"] = fp8_dequantize(codes, scales)
+    del plain["codes"], plain["scales"]
+    y, new = decode_step(plain, x, dt, A, Bm, C, Q, E, g, S, cache_bf16=False)
+    n_old = np.asarray(state["n_chunks"]).astype(np.int64)
+    for b in range(codes.shape[0]):
+        k = int(n_old[b])
+        if new["n_chunks"][b] == k + 1:  # this token closed chunk k
+            for h in range(codes.shape[1]):
+                codes[b, h, k], scales[b, h, k] = fp8_quantize_memory(new["cache"][b, h, k])
+    del new["cache"]
+    new["codes"], new["scales"] = codes, scales
+    return y, new

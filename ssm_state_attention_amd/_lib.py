@@ -47,6 +47,10 @@ _SIG = {
     "dart_sma_decode_workspace": [ctypes.POINTER(DartDecodeDims)],
     "dart_sma_decode": [ctypes.POINTER(DartDecodeDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F,
                         _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+    "dart_sma_decode_fp8": [ctypes.POINTER(DartDecodeDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                            _F, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+    "dart_cache_fp8_store": [ctypes.POINTER(DartDecodeDims), _VP, ctypes.c_int64, ctypes.c_int64,
+                             _VP, _VP, _VP],
     "dart_validate_dims": [ctypes.POINTER(DartDims)],
     "dart_validate_decode_dims": [ctypes.POINTER(DartDecodeDims)],
     "dart_status_str": [ctypes.c_int],

@@ -166,6 +166,44 @@ def dart_sma_decode(x, dt, A, Bm, C, Q, E, gate, cache, h, dH_cur, n_chunks, pos
                                 _stream()), "dart_sma_decode")
 
 
+def dart_sma_decode_fp8(x, dt, A, Bm, C, Q, E, gate, cache8, scale, h, dH_cur, n_chunks, pos,
+                        y, workspace, chunk):
+    """dart_sma_decode over the fp8 cache: cache8 [B,H,max_chunks,P,N] uint8
+    E4M3 codes and scale [B,H,max_chunks] f32 (see include/dart.h)."""
+    B, H, P = x.shape
+    G, N = Bm.shape[1], Bm.shape[2]
+    max_chunks = cache8.shape[2]
+    io, dev = x.dtype, x.device
+    d = decode_dims(B, H, G, N, P, chunk, max_chunks, io)
+    args = [_ptr(x, "x", io, (B, H, P), dev), _ptr(dt, "dt", torch.float32, (B, H), dev),
+            _ptr(A, "A", torch.float32, (H,), dev), _ptr(Bm, "Bm", io, (B, G, N), dev),
+            _ptr(C, "C", io, (B, G, N), dev), _ptr(Q, "Q", io, (B, G, N), dev),
+            _ptr(E, "E", io, (B, H, P), dev)]
+    state = [_ptr(cache8, "cache8", torch.uint8, (B, H, max_chunks, P, N), dev),
+             _ptr(scale, "scale", torch.float32, (B, H, max_chunks), dev),
+             _ptr(h, "h", torch.float32, (B, H, P, N), dev),
+             _ptr(dH_cur, "dH_cur", torch.float32, (B, H, P, N), dev),
+             _ptr(n_chunks, "n_chunks", torch.int32, (B,), dev),
+             _ptr(pos, "pos", torch.int32, (B,), dev), _ptr(y, "y", io, (B, H, P), dev)]
+    wsp = _ptr(workspace, "workspace", torch.uint8, None, dev)
+    check(lib().dart_sma_decode_fp8(d, *args, float(gate), *state, wsp, workspace.numel(),
+                                    _stream()), "dart_sma_decode_fp8")
+
+
+def dart_cache_fp8_store(dH_f32, first, cache8, scale, ngroups, chunk, io):
+    """Encode dH_f32 [B,H,n_mem,P,N] f32 into fp8 cache slots first ..
+    first + n_mem - 1 of cache8 [B,H,max_chunks,P,N] uint8 and scale
+    [B,H,max_chunks] f32.  ngroups, chunk and io are the decode dims the
+    cache serves (validated only)."""
+    B, H, n_mem, P, N = dH_f32.shape
+    max_chunks, dev = cache8.shape[2], dH_f32.device
+    d = decode_dims(B, H, ngroups, N, P, chunk, max_chunks, io)
+    args = [_ptr(dH_f32, "dH_f32", torch.float32, (B, H, n_mem, P, N), dev), int(n_mem),
+            int(first), _ptr(cache8, "cache8", torch.uint8, (B, H, max_chunks, P, N), dev),
+            _ptr(scale, "scale", torch.float32, (B, H, max_chunks), dev)]
+    check(lib().dart_cache_fp8_store(d, *args, _stream()), "dart_cache_fp8_store")
+
+
 # ----------------------------------------------------------------- helpers
 def prefill(x, dt, A, Bm, C, Q, E, gate, chunk, h0=None, decayed=False):
     """Whole prefill path; returns a dict of device tensors: y, y_ssd, dH
@@ -222,17 +260,27 @@ def prefill_continue(x, dt, A, Bm, C, Q, E, gate, chunk, cache, prior_chunks, h0
     return out
 
 
-def new_decode_state(batch, nheads, ngroups, dstate, headdim, chunk, max_chunks, dtype, device):
-    """Zeroed decode state: cache, h, dH_cur, n_chunks, pos and workspace."""
+def new_decode_state(batch, nheads, ngroups, dstate, headdim, chunk, max_chunks, dtype, device,
+                     fp8_cache=False):
+    """Zeroed decode state: the cache ("cache" in the io type, or with
+    fp8_cache "cache8" codes and "scale"), h, dH_cur, n_chunks, pos and
+    workspace."""
     dims = decode_dims(batch, nheads, ngroups, dstate, headdim, chunk, max_chunks, dtype)
     ws = dart_sma_decode_workspace(dims)
     if ws == 0:
         raise ValueError("unsupported decode dimensions")
     f32 = dict(dtype=torch.float32, device=device)
+    shape = (batch, nheads, max_chunks, headdim, dstate)
+    if fp8_cache:
+        cache = {"cache8": torch.zeros(shape, dtype=torch.uint8, device=device),
+                 "scale": torch.ones(batch, nheads, max_chunks, **f32)}
+    else:
+        cache = {"cache": torch.zeros(shape, dtype=dtype, device=device)}
     return {
         "chunk": int(chunk),
-        "cache": torch.zeros(batch, nheads, max_chunks, headdim, dstate, dtype=dtype,
-                             device=device),
+        "ngroups": int(ngroups),
+        "io": dtype,
+        **cache,
         "h": torch.zeros(batch, nheads, headdim, dstate, **f32),
         "dH_cur": torch.zeros(batch, nheads, headdim, dstate, **f32),
         "n_chunks": torch.zeros(batch, dtype=torch.int32, device=device),
@@ -246,6 +294,24 @@ def decode_step(state, x, dt, A, Bm, C, Q, E, gate, y=None):
     returns y [B,H,P]."""
     if y is None:
         y = torch.empty(x.shape, dtype=x.dtype, device=x.device)
-    dart_sma_decode(x, dt, A, Bm, C, Q, E, gate, state["cache"], state["h"], state["dH_cur"],
-                    state["n_chunks"], state["pos"], y, state["workspace"], state["chunk"])
+    if "cache8" in state:
+        dart_sma_decode_fp8(x, dt, A, Bm, C, Q, E, gate, state["cache8"], state["scale"],
+                            state["h"], state["dH_cur"], state["n_chunks"], state["pos"], y,
+                            state["workspace"], state["chunk"])
+    else:
+        dart_sma_decode(x, dt, A, Bm, C, Q, E, gate, state["cache"], state["h"],
+                        state["dH_cur"], state["n_chunks"], state["pos"], y, state["workspace"],
+                        state["chunk"])
     return y
+
+
+def store_memories(state, dH_f32, dH=None, first=0):
+    """Put memories into the decode cache at slots first, first + 1, ...:
+    the f32 memories dH_f32 [B,H,n,P,N] are encoded into an fp8 cache; an
+    io cache takes dH [B,H,n,P,N] (the io-typed memories of the prefill)."""
+    n = dH_f32.shape[2]
+    if "cache8" in state:
+        dart_cache_fp8_store(dH_f32, first, state["cache8"], state["scale"], state["ngroups"],
+                             state["chunk"], state["io"])
+    else:
+        state["cache"][:, :, first:first + n].copy_(dH)

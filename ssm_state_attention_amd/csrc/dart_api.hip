@@ -98,6 +98,8 @@ struct SmaDecodeFn {
   const float *dt, *A;
   float gate;
   void* cache;
+  uint8_t* cache8;
+  float* cscale;
   float *h, *dHc;
   int *nc, *pos;
   void *y, *ws;
@@ -106,10 +108,29 @@ struct SmaDecodeFn {
   hipError_t run() {
     return dart::launch_sma_decode<T, N, P>(
         sh, static_cast<const T*>(x), dt, A, static_cast<const T*>(Bm), static_cast<const T*>(C),
-        static_cast<const T*>(Q), static_cast<const T*>(E), gate, static_cast<T*>(cache), h, dHc,
-        nc, pos, static_cast<T*>(y), ws, st);
+        static_cast<const T*>(Q), static_cast<const T*>(E), gate, static_cast<T*>(cache), cache8,
+        cscale, h, dHc, nc, pos, static_cast<T*>(y), ws, st);
   }
 };
+
+struct Fp8StoreFn {
+  int B, H, n_mem, first, max_chunks;
+  const float* src;
+  uint8_t* cache8;
+  float* cscale;
+  hipStream_t st;
+  template <typename T, int N, int P>
+  hipError_t run() {
+    return dart::launch_fp8_store<T, N, P>(B, H, n_mem, first, max_chunks, src, cache8, cscale,
+                                           st);
+  }
+};
+
+dart::DecodeShape decode_shape(const dart_decode_dims* d) {
+  return {static_cast<int>(d->batch),      static_cast<int>(d->nheads),
+          static_cast<int>(d->ngroups),    static_cast<int>(d->chunk),
+          static_cast<int>(d->max_chunks), dart::decode_splits(*d)};
+}
 
 }  // namespace
 
@@ -189,10 +210,41 @@ extern "C" dart_status dart_sma_decode(const dart_decode_dims* dims, const void*
   if (!workspace || workspace_bytes < dart::decode_workspace_bytes(*dims))
     return DART_ERR_WORKSPACE;
   if (!aligned16(workspace)) return DART_ERR_ALIGN;
-  const dart::DecodeShape sh{static_cast<int>(dims->batch),      static_cast<int>(dims->nheads),
-                             static_cast<int>(dims->ngroups),    static_cast<int>(dims->chunk),
-                             static_cast<int>(dims->max_chunks), dart::decode_splits(*dims)};
-  SmaDecodeFn fn{sh, x, Bm, C, Q, E, dt, A, gate, cache, h, dH_cur, n_chunks, pos, y, workspace,
-       static_cast<hipStream_t>(stream)};
+  SmaDecodeFn fn{decode_shape(dims), x, Bm, C, Q, E, dt, A, gate, cache, nullptr, nullptr, h,
+                 dH_cur, n_chunks, pos, y, workspace, static_cast<hipStream_t>(stream)};
+  return dispatch(dims->io, dims->dstate, dims->headdim, fn);
+}
+
+extern "C" dart_status dart_sma_decode_fp8(const dart_decode_dims* dims, const void* x,
+                                           const float* dt, const float* A, const void* Bm,
+                                           const void* C, const void* Q, const void* E,
+                                           float gate, uint8_t* cache8, float* scale, float* h,
+                                           float* dH_cur, int32_t* n_chunks, int32_t* pos,
+                                           void* y, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  dart_status s = dart_validate_decode_dims(dims);
+  if (s != DART_OK) return s;
+  if ((s = check_ptrs(x, dt, A, Bm, C, Q, E, cache8, scale, h, dH_cur, n_chunks, pos, y)) !=
+      DART_OK)
+    return s;
+  if (!workspace || workspace_bytes < dart::decode_workspace_bytes(*dims))
+    return DART_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DART_ERR_ALIGN;
+  SmaDecodeFn fn{decode_shape(dims), x, Bm, C, Q, E, dt, A, gate, nullptr, cache8, scale, h,
+                 dH_cur, n_chunks, pos, y, workspace, static_cast<hipStream_t>(stream)};
+  return dispatch(dims->io, dims->dstate, dims->headdim, fn);
+}
+
+extern "C" dart_status dart_cache_fp8_store(const dart_decode_dims* dims, const float* dH_f32,
+                                            int64_t n_mem, int64_t first, uint8_t* cache8,
+                                            float* scale, void* stream) {
+  dart_status s = dart_validate_decode_dims(dims);
+  if (s != DART_OK) return s;
+  if (n_mem < 0 || first < 0 || first > dims->max_chunks - n_mem) return DART_ERR_BAD_DIMS;
+  if ((s = check_ptrs(dH_f32, cache8, scale)) != DART_OK) return s;
+  Fp8StoreFn fn{static_cast<int>(dims->batch), static_cast<int>(dims->nheads),
+                static_cast<int>(n_mem), static_cast<int>(first),
+                static_cast<int>(dims->max_chunks), dH_f32, cache8, scale,
+                static_cast<hipStream_t>(stream)};
   return dispatch(dims->io, dims->dstate, dims->headdim, fn);
 }

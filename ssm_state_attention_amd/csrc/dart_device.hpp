@@ -121,4 +121,33 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// online-softmax slack: weights may reach 2^kLazyLog2 before the running max
+// (and with it every accumulator) is rescaled
+constexpr float kLazyLog2 = 8.f;
+
+// Sum of v over lanes l and l^16, then over l and l^32 (gfx950 permlane
+// swaps: no LDS round trip).
+__device__ __forceinline__ float sum_lane_groups(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const unsigned u2 = __float_as_uint(v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
+// Sum over all 64 lanes without LDS: DPP within each quad and row of 16
+// lanes, then the two permlane swaps.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_mov<0x124>(v);  // row_ror 4: quads q and q+1 of the row
+  v += dpp_mov<0x128>(v);  // row_ror 8: the whole row of 16
+  return sum_lane_groups(v);
+}
+
 }  // namespace dart

@@ -33,11 +33,19 @@ hipError_t launch_sma_fwd(const PrefillShape& s, const T* Q, const T* E, const T
                           const T* dH, const T* y_ssd, const float* acum, float gate, T* y,
                           const T* prior, int k0, int pstride, hipStream_t st);
 
+// cache8 == nullptr: the cache is `cache` in the io type; otherwise it is
+// the fp8 code array cache8 with one scale per memory in cscale.
 template <typename T, int N, int P>
 hipError_t launch_sma_decode(const DecodeShape& s, const T* x, const float* dt, const float* A,
                              const T* Bm, const T* C, const T* Q, const T* E, float gate,
-                             T* cache, float* h, float* dH_cur, int* n_chunks, int* pos, T* y,
-                             void* workspace, hipStream_t st);
+                             T* cache, uint8_t* cache8, float* cscale, float* h, float* dH_cur,
+                             int* n_chunks, int* pos, T* y, void* workspace, hipStream_t st);
+
+// fp8 codes and scales of n_mem f32 memories per (batch, head), written to
+// cache slots first .. first + n_mem - 1 (T only selects the instantiation).
+template <typename T, int N, int P>
+hipError_t launch_fp8_store(int B, int H, int n_mem, int first, int max_chunks, const float* src,
+                            uint8_t* cache8, float* cscale, hipStream_t st);
 
 }  // namespace dart
 

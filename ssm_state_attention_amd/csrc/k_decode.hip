@@ -1,0 +1,618 @@
+// Single-token decode over the chunk-memory cache on gfx950, with the cache
+// held either in the io element type or as 8-bit floating point codes.
+//
+// Definitions (DART abstract: the length-dependent inference cache is the set
+// of chunk memories; Pith review of DART, "Core claim", minor comment 1 and
+// paper §4 Eq. 14): for the new token t of chunk k of a sequence
+//   h <- exp(dt·A)·h + dt·B_t x_tᵀ,  y_ssd = C_tᵀ·h    (the Mamba-2 recurrence)
+//   o_t = Σ_{c<k} softmax_c(Q_tᵀ·dH[c]·E_t / sqrt(N))·C_tᵀ·dH[c]
+//   y_t = y_ssd + gate·o_t
+// and the memory of chunk k, accumulated token by token in dH_cur, joins the
+// cache when its last token has been processed.
+//
+// The fp8 cache (Pith review, "Where Pith is reading between the lines":
+// SMA's reuse of the scan's dH invites cache quantisation) keeps memory c as
+// OCP FP8 E4M3 codes plus one power-of-two scale 2^e: the codes are the
+// round-to-nearest-even encodings of dH[c]·2^-e, with e = max(E - 8, -126)
+// for the memory's largest magnitude f·2^E (0.5 <= f < 1), so every scaled
+// magnitude is below 256 and no code saturates.
+#include "dart_launch.hpp"
+#include "dart_shapes.hpp"
+
+namespace dart {
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// Exponent e of the scale 2^e of a memory whose largest magnitude is amax:
+// with amax = f·2^E (0.5 <= f < 1), e = max(E - 8, -126); e = 0 when amax is 0.
+__device__ __forceinline__ int fp8_scale_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  const int field = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFFu);
+  return max(field - 134, -126);  // normal amax: E = field - 126
+}
+// 2^e for e in [-126, 127]
+__device__ __forceinline__ float pow2i(int e) {
+  return __uint_as_float(static_cast<unsigned>(e + 127) << 23);
+}
+// E4M3 codes of four values (round to nearest even), value i in byte i
+__device__ __forceinline__ unsigned pack_fp8x4(floatx4 v) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+  return static_cast<unsigned>(__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true));
+}
+
+// Largest value of m over a 256-thread workgroup (sh: 4 floats of LDS).
+__device__ __forceinline__ float block_max256(float m, float* sh) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
+  __syncthreads();
+  return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+}
+
+// Decode, step 1: one workgroup per (head, batch) advances the SSM state,
+// forms y_ssd = C·h into the workspace and, when the token closes its chunk,
+// appends the finished memory to the cache (at index n_chunks[b], which the
+// streaming kernel never reads): rounded to the io type, or (F8) encoded
+// with the scale taken from the memory's largest magnitude, which the
+// workgroup finds from the registers it already holds.  A launch of its
+// own: done by the first of the streaming workgroups it held every stream
+// back behind a latency-bound read-modify-write of 128 KB of state.
+template <typename T, int N, int P, bool F8>
+__global__ __launch_bounds__(256) void k_decode_state(
+    const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
+    const T* __restrict__ Bm, const T* __restrict__ C, T* __restrict__ cache,
+    uint8_t* __restrict__ cache8, float* __restrict__ cscale, float* __restrict__ hst,
+    float* __restrict__ dHc, const int* __restrict__ n_chunks, const int* __restrict__ pos,
+    int* __restrict__ ws_flag, float* __restrict__ ws_yssd, int H, int G, int S,
+    int max_chunks) {
+  constexpr int Q4 = N / 4;
+  static_assert((P * N / 4) % 64 == 0 && 64 % Q4 == 0, "decode state mapping");
+  __shared__ float sh_c[N], sh_b[N], sh_x[P], sh_y[P], sh_m[4];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (H / G);
+  const long pair = (long)b * H + h;
+  const int tid = threadIdx.x;
+  int kc = n_chunks[b];
+  kc = kc < 0 ? 0 : (kc > max_chunks ? max_chunks : kc);
+  const int ps = pos[b];
+  for (int i = tid; i < N; i += 256) {
+    const long o = ((long)b * G + g) * N + i;
+    sh_c[i] = to_f32(C[o]);
+    sh_b[i] = to_f32(Bm[o]);
+  }
+  for (int i = tid; i < P; i += 256) sh_x[i] = to_f32(x[pair * P + i]);
+  __syncthreads();
+  {
+    const float dtv = dt[pair];
+    const float a = exp_neg(dtv * A[h]);
+    const bool close = ps == S - 1;
+    const bool append = close && kc < max_chunks;  // uniform over the workgroup
+    floatx4* hp = reinterpret_cast<floatx4*>(hst + pair * (P * N));
+    floatx4* dp = reinterpret_cast<floatx4*>(dHc + pair * (P * N));
+    const long slot = pair * max_chunks + kc;
+    // all of this thread's state loads first, then the updates
+    // (P·N/4 is a multiple of 64, so the guard is uniform over each wave)
+    constexpr int SQ = P * N / 4, SV = (SQ + 255) / 256;
+    static_assert(SQ % 64 == 0 && (Q4 == 4 || Q4 == 8 || Q4 == 16 || Q4 == 32),
+                  "decode state split");
+    floatx4 hv[SV], dv[SV];
+#pragma unroll
+    for (int v = 0; v < SV; ++v) {
+      const int i = tid + v * 256;
+      if (SQ % 256 == 0 || i < SQ) {
+        hv[v] = hp[i];
+        dv[v] = dp[i];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < SV; ++v) {
+      const int i = tid + v * 256;
+      if (SQ % 256 != 0 && i >= SQ) break;
+      const int p = i / Q4, n = (i % Q4) * 4;
+      const float xd = dtv * sh_x[p];
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float u = xd * sh_b[n + e];
+        hv[v][e] = a * hv[v][e] + u;
+        dv[v][e] = a * dv[v][e] + u;
+        part += sh_c[n + e] * hv[v][e];
+      }
+      hp[i] = hv[v];
+      if constexpr (!F8) {
+        if (append) store4(cache + slot * (P * N) + (long)i * 4, dv[v]);
+      }
+      dp[i] = close ? floatx4{0.f, 0.f, 0.f, 0.f} : dv[v];
+      // sum over the Q4 lanes that share row p (the row rotations span 16
+      // lanes, so a group of 8 takes its last step by a lane exchange)
+      part += dpp_mov<0xB1>(part);
+      part += dpp_mov<0x4E>(part);
+      if (Q4 == 8) part += __shfl_xor(part, 4);
+      if (Q4 >= 16) {
+        part += dpp_mov<0x124>(part);
+        part += dpp_mov<0x128>(part);
+      }
+      if (Q4 >= 32) {
+        const unsigned u = __float_as_uint(part);
+        const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        part = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+      }
+      if ((i % Q4) == 0) sh_y[p] = part;
+    }
+    if constexpr (F8) {
+      if (append) {
+        float m = 0.f;
+#pragma unroll
+        for (int v = 0; v < SV; ++v) {
+          if (SQ % 256 != 0 && tid + v * 256 >= SQ) break;
+          m = fmaxf(m, fmaxf(fmaxf(fabsf(dv[v][0]), fabsf(dv[v][1])),
+                             fmaxf(fabsf(dv[v][2]), fabsf(dv[v][3]))));
+        }
+        const int e = fp8_scale_exp(block_max256(m, sh_m));
+        const float inv = pow2i(-e);
+        unsigned* dst = reinterpret_cast<unsigned*>(cache8 + slot * (P * N));
+#pragma unroll
+        for (int v = 0; v < SV; ++v) {
+          const int i = tid + v * 256;
+          if (SQ % 256 != 0 && i >= SQ) break;
+          dst[i] = pack_fp8x4(dv[v] * inv);
+        }
+        if (tid == 0) cscale[slot] = pow2i(e);
+      }
+    }
+    if (close && !append && tid == 0) atomicOr(ws_flag, 1);
+    __syncthreads();
+    for (int p = tid; p < P; p += 256) ws_yssd[pair * P + p] = sh_y[p];
+  }
+}
+
+// Merge of the per-wave online-softmax states of one workgroup into the
+// split's (max, denominator, numerator[P]) partial.  acc: this lane's value
+// sums for rows it·RP + pr, already reduced over the lanes of a row.
+template <int P, int NW, int NPASS, int RP>
+__device__ __forceinline__ void write_split_partial(const float (&acc)[NPASS], float mx, float ls,
+                                                    bool row_lead, int pr, float* ws_part,
+                                                    long pair, int splits, int split) {
+  __shared__ float sh_wm[NW], sh_wl[NW];
+  __shared__ float sh_wacc[NW][P];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (row_lead) {
+#pragma unroll
+    for (int it = 0; it < NPASS; ++it) sh_wacc[w][it * RP + pr] = acc[it];
+  }
+  if (lane == 0) {
+    sh_wm[w] = mx;
+    sh_wl[w] = ls;
+  }
+  __syncthreads();
+  float mall = -INFINITY;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) mall = fmaxf(mall, sh_wm[ww]);
+  for (int p = tid; p < P; p += 64 * NW) {
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      if (sh_wm[ww] > -INFINITY) {
+        const float f = exp2_fast(sh_wm[ww] - mall);
+        num += f * sh_wacc[ww][p];
+        den += f * sh_wl[ww];
+      }
+    }
+    float* part = ws_part + (pair * splits + split) * (P + 2);
+    part[2 + p] = num;
+    if (p == 0) {
+      part[0] = mall;
+      part[1] = den;
+    }
+  }
+}
+
+// Decode, step 2: one workgroup (4 waves) per (split, head, batch) streams
+// the cached memories of its split once from HBM.  Each wave takes whole
+// memories c = first + wave, first + wave + 4, ... (non-temporal 16-byte
+// loads): lane (nv, pr) holds key entries n in [nv·VE, nv·VE + VE) of rows
+// p = it·RP + pr, forms partial Q·dH[c] and C·dH[c] over its n-range,
+// reduces the score across the wave and keeps an online softmax whose value
+// accumulator stays partial over n until the end.  The (max, denominator,
+// numerator[P]) partial of the split goes to the workspace; k_decode_combine
+// merges the splits and adds y_ssd.
+template <typename T, int N, int P>
+__global__ __launch_bounds__(256) void k_sma_decode(
+    const T* __restrict__ C, const T* __restrict__ Q, const T* __restrict__ E,
+    const T* __restrict__ cache, const int* __restrict__ n_chunks, float* __restrict__ ws_part,
+    int H, int G, int max_chunks, int splits, int cps, float scale_log2) {
+  constexpr int VE = Vec16<T>::n;
+  constexpr int NV = N / VE;   // 16-byte vectors per memory row
+  constexpr int RP = 64 / NV;  // rows per wave pass
+  constexpr int NPASS = P / RP;
+  constexpr int NW = 4;
+  static_assert(64 % NV == 0 && P % RP == 0, "decode lane mapping");
+  typedef typename Vec16<T>::vec vec_t;
+  __shared__ float sh_q[N], sh_c[N], sh_e[P];
+
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (H / G);
+  const long pair = (long)b * H + h;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int kc = n_chunks[b];
+  kc = kc < 0 ? 0 : (kc > max_chunks ? max_chunks : kc);
+
+  for (int i = tid; i < N; i += 256) {
+    const long o = ((long)b * G + g) * N + i;
+    sh_q[i] = to_f32(Q[o]);
+    sh_c[i] = to_f32(C[o]);
+  }
+  for (int i = tid; i < P; i += 256) sh_e[i] = to_f32(E[pair * P + i]);
+  __syncthreads();
+
+  const int c_begin = split * cps;
+  const int c_end = min(kc, c_begin + cps);
+  const int nv = lane % NV, pr = lane / NV;
+  constexpr bool kDot2 = std::is_same<T, bf16>::value;
+  float qv[VE], cv[VE], ev[NPASS], acc[NPASS];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) {
+    qv[e] = sh_q[nv * VE + e];
+    cv[e] = sh_c[nv * VE + e];
+  }
+  // 16-bit io: Q and C stay packed (the widened values are exact copies)
+  // and each pair of key entries is one dot2 with fp32 accumulation
+  bf16x2 q2[VE / 2], c2[VE / 2];
+  if constexpr (kDot2) {
+#pragma unroll
+    for (int e = 0; e < VE / 2; ++e) {
+      q2[e] = bf16x2{from_f32<bf16>(qv[2 * e]), from_f32<bf16>(qv[2 * e + 1])};
+      c2[e] = bf16x2{from_f32<bf16>(cv[2 * e]), from_f32<bf16>(cv[2 * e + 1])};
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < NPASS; ++it) {
+    ev[it] = sh_e[it * RP + pr];
+    acc[it] = 0.f;
+  }
+  float mx = -INFINITY, ls = 0.f;
+  const T* base = cache + pair * (long)max_chunks * (P * N);
+  for (int c = c_begin + w; c < c_end; c += NW) {
+    const T* src = base + (long)c * (P * N);
+    vec_t raw[NPASS];
+#pragma unroll
+    for (int it = 0; it < NPASS; ++it) raw[it] = load16_nt(src + ((it * RP + pr) * NV + nv) * VE);
+    float s = 0.f, zc[NPASS];
+#pragma unroll
+    for (int it = 0; it < NPASS; ++it) {
+      float zq = 0.f, z2 = 0.f;
+      if constexpr (kDot2) {
+#pragma unroll
+        for (int e = 0; e < VE / 2; ++e) {
+          const bf16x2 v2 = bf16x2{raw[it][2 * e], raw[it][2 * e + 1]};
+          zq = __builtin_amdgcn_fdot2_f32_bf16(q2[e], v2, zq, false);
+          z2 = __builtin_amdgcn_fdot2_f32_bf16(c2[e], v2, z2, false);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          const float v = to_f32(raw[it][e]);
+          zq += qv[e] * v;
+          z2 += cv[e] * v;
+        }
+      }
+      zc[it] = z2;
+      s += ev[it] * zq;
+    }
+    s = wave_sum_dpp(s) * scale_log2;
+    // lazy rescale, as in the prefill kernel (s is uniform over the wave)
+    if (s > mx + kLazyLog2) {
+      const float al = exp2_fast(mx - s);  // 0 for the first memory
+      ls *= al;
+#pragma unroll
+      for (int it = 0; it < NPASS; ++it) acc[it] *= al;
+      mx = s;
+    }
+    const float pw = exp2_fast(s - mx);
+    ls += pw;
+#pragma unroll
+    for (int it = 0; it < NPASS; ++it) acc[it] += pw * zc[it];
+  }
+#pragma unroll
+  for (int it = 0; it < NPASS; ++it)
+#pragma unroll
+    for (int off = 1; off < NV; off <<= 1) acc[it] += __shfl_xor(acc[it], off);
+  write_split_partial<P, NW, NPASS, RP>(acc, mx, ls, nv == 0, pr, ws_part, pair, splits, split);
+}
+
+// Bytes of one fp8 cache row that a lane loads at a time: the widest of 16,
+// 8 and 4 for which whole rows tile the 64 lanes of a wave and the P rows
+// tile whole passes.
+template <int N, int P>
+struct F8Load {
+  static constexpr bool fits(int lb) {
+    return N % lb == 0 && 64 % (N / lb) == 0 && P % (64 / (N / lb)) == 0;
+  }
+  static constexpr int LB = fits(16) ? 16 : (fits(8) ? 8 : 4);
+  static constexpr int W = LB / 4;  // 32-bit words per load
+};
+template <int W>
+struct Words {
+  typedef unsigned v __attribute__((ext_vector_type(W)));
+};
+template <>
+struct Words<1> {
+  typedef unsigned v;
+};
+template <int W>
+__device__ __forceinline__ unsigned word(typename Words<W>::v r, int j) {
+  if constexpr (W == 1)
+    return r;
+  else
+    return r[j];
+}
+
+// Decode, step 2 over the fp8 cache: the streaming kernel above with LB-byte
+// code loads.  16-bit io decodes each pair of codes into a bf16 pair (exact:
+// every E4M3 value is a bfloat16 value) and contracts it with dot2; fp32 io
+// decodes into fp32.  The products are those of the codes, so the memory's
+// scale multiplies the reduced score and the softmax weight of its value.
+template <typename T, int N, int P>
+__global__ __launch_bounds__(256) void k_sma_decode_f8(
+    const T* __restrict__ C, const T* __restrict__ Q, const T* __restrict__ E,
+    const uint8_t* __restrict__ cache8, const float* __restrict__ cscale,
+    const int* __restrict__ n_chunks, float* __restrict__ ws_part, int H, int G, int max_chunks,
+    int splits, int cps, float scale_log2) {
+  constexpr int LB = F8Load<N, P>::LB, W = F8Load<N, P>::W;
+  constexpr int NV = N / LB;   // loads per memory row
+  constexpr int RP = 64 / NV;  // rows per wave pass
+  constexpr int NPASS = P / RP;
+  constexpr int NW = 4;
+  static_assert(64 % NV == 0 && P % RP == 0, "fp8 decode lane mapping");
+  typedef typename Words<W>::v load_t;
+  __shared__ float sh_q[N], sh_c[N], sh_e[P];
+
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (H / G);
+  const long pair = (long)b * H + h;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int kc = n_chunks[b];
+  kc = kc < 0 ? 0 : (kc > max_chunks ? max_chunks : kc);
+
+  for (int i = tid; i < N; i += 256) {
+    const long o = ((long)b * G + g) * N + i;
+    sh_q[i] = to_f32(Q[o]);
+    sh_c[i] = to_f32(C[o]);
+  }
+  for (int i = tid; i < P; i += 256) sh_e[i] = to_f32(E[pair * P + i]);
+  __syncthreads();
+
+  const int c_begin = split * cps;
+  const int c_end = min(kc, c_begin + cps);
+  const int nv = lane % NV, pr = lane / NV;
+  constexpr bool kDot2 = std::is_same<T, bf16>::value;
+  float qv[LB], cv[LB], ev[NPASS], acc[NPASS];
+#pragma unroll
+  for (int e = 0; e < LB; ++e) {
+    qv[e] = sh_q[nv * LB + e];
+    cv[e] = sh_c[nv * LB + e];
+  }
+  bf16x2 q2[LB / 2], c2[LB / 2];
+  if constexpr (kDot2) {
+#pragma unroll
+    for (int e = 0; e < LB / 2; ++e) {
+      q2[e] = bf16x2{from_f32<bf16>(qv[2 * e]), from_f32<bf16>(qv[2 * e + 1])};
+      c2[e] = bf16x2{from_f32<bf16>(cv[2 * e]), from_f32<bf16>(cv[2 * e + 1])};
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < NPASS; ++it) {
+    ev[it] = sh_e[it * RP + pr];
+    acc[it] = 0.f;
+  }
+  float mx = -INFINITY, ls = 0.f;
+  const uint8_t* base = cache8 + pair * (long)max_chunks * (P * N);
+  const float* sbase = cscale + pair * (long)max_chunks;
+  for (int c = c_begin + w; c < c_end; c += NW) {
+    const uint8_t* src = base + (long)c * (P * N);
+    load_t raw[NPASS];
+#pragma unroll
+    for (int it = 0; it < NPASS; ++it)
+      raw[it] = __builtin_nontemporal_load(
+          reinterpret_cast<const load_t*>(src + (it * RP + pr) * N + nv * LB));
+    const float sc = sbase[c];
+    float s = 0.f, zc[NPASS];
+#pragma unroll
+    for (int it = 0; it < NPASS; ++it) {
+      float zq = 0.f, z2 = 0.f;
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        const unsigned wd = word<W>(raw[it], j);
+        if constexpr (kDot2) {
+          const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd, 1.0f, false);
+          const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd, 1.0f, true);
+          zq = __builtin_amdgcn_fdot2_f32_bf16(q2[2 * j], lo, zq, false);
+          zq = __builtin_amdgcn_fdot2_f32_bf16(q2[2 * j + 1], hi, zq, false);
+          z2 = __builtin_amdgcn_fdot2_f32_bf16(c2[2 * j], lo, z2, false);
+          z2 = __builtin_amdgcn_fdot2_f32_bf16(c2[2 * j + 1], hi, z2, false);
+        } else {
+          const floatx2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd, false);
+          const floatx2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd, true);
+          zq += qv[4 * j] * lo[0] + qv[4 * j + 1] * lo[1] + qv[4 * j + 2] * hi[0] +
+                qv[4 * j + 3] * hi[1];
+          z2 += cv[4 * j] * lo[0] + cv[4 * j + 1] * lo[1] + cv[4 * j + 2] * hi[0] +
+                cv[4 * j + 3] * hi[1];
+        }
+      }
+      zc[it] = z2;
+      s += ev[it] * zq;
+    }
+    s = wave_sum_dpp(s) * (sc * scale_log2);
+    if (s > mx + kLazyLog2) {
+      const float al = exp2_fast(mx - s);  // 0 for the first memory
+      ls *= al;
+#pragma unroll
+      for (int it = 0; it < NPASS; ++it) acc[it] *= al;
+      mx = s;
+    }
+    const float pw = exp2_fast(s - mx);
+    ls += pw;
+    const float pv = pw * sc;
+#pragma unroll
+    for (int it = 0; it < NPASS; ++it) acc[it] += pv * zc[it];
+  }
+#pragma unroll
+  for (int it = 0; it < NPASS; ++it)
+#pragma unroll
+    for (int off = 1; off < NV; off <<= 1) acc[it] += __shfl_xor(acc[it], off);
+  write_split_partial<P, NW, NPASS, RP>(acc, mx, ls, nv == 0, pr, ws_part, pair, splits, split);
+}
+
+// Merge the per-split (max, denominator, numerator[P]) partials of one
+// (batch, head) and apply the gate.
+template <typename T>
+__global__ __launch_bounds__(128) void k_decode_combine(const float* __restrict__ ws_yssd,
+                                                        const float* __restrict__ ws_part,
+                                                        float gate, T* __restrict__ y, int P,
+                                                        int splits) {
+  const long pair = blockIdx.x;
+  const float* part = ws_part + pair * splits * (P + 2);
+  float mall = -INFINITY;
+  for (int s = 0; s < splits; ++s) mall = fmaxf(mall, part[s * (P + 2)]);
+  for (int p = threadIdx.x; p < P; p += blockDim.x) {
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float m = part[s * (P + 2)];
+      if (m > -INFINITY) {
+        const float f = exp2_fast(m - mall);
+        num += f * part[s * (P + 2) + 2 + p];
+        den += f * part[s * (P + 2) + 1];
+      }
+    }
+    const float o = den > 0.f ? num / den : 0.f;
+    y[pair * P + p] = from_f32<T>(ws_yssd[pair * P + p] + gate * o);
+  }
+}
+
+// Advance the per-sequence position after every head has read it.
+__global__ void k_decode_advance(int* __restrict__ n_chunks, int* __restrict__ pos, int B, int S,
+                                 int max_chunks) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  if (pos[b] == S - 1) {
+    const int k = n_chunks[b];
+    n_chunks[b] = k < max_chunks ? k + 1 : max_chunks;
+    pos[b] = 0;
+  } else {
+    pos[b] += 1;
+  }
+}
+
+// Store n_mem f32 memories per (batch, head) into fp8 cache slots first ..
+// first + n_mem - 1: one workgroup per memory finds its largest magnitude,
+// then writes the codes (one 32-bit word per four values) and the scale.
+template <int N, int P>
+__global__ __launch_bounds__(256) void k_fp8_store(const float* __restrict__ src, int n_mem,
+                                                   int first, uint8_t* __restrict__ cache8,
+                                                   float* __restrict__ cscale, int H,
+                                                   int max_chunks) {
+  constexpr int SQ = P * N / 4, SV = (SQ + 255) / 256;
+  __shared__ float sh_m[4];
+  const int mem = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const long pair = (long)b * H + h;
+  const int tid = threadIdx.x;
+  const floatx4* s4 = reinterpret_cast<const floatx4*>(src + (pair * n_mem + mem) * (long)(P * N));
+  floatx4 v[SV];
+  float m = 0.f;
+#pragma unroll
+  for (int k = 0; k < SV; ++k) {
+    const int i = tid + k * 256;
+    if (SQ % 256 == 0 || i < SQ) {
+      v[k] = __builtin_nontemporal_load(s4 + i);
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[k][0]), fabsf(v[k][1])),
+                         fmaxf(fabsf(v[k][2]), fabsf(v[k][3]))));
+    }
+  }
+  const int e = fp8_scale_exp(block_max256(m, sh_m));
+  const float inv = pow2i(-e);
+  const long slot = pair * max_chunks + first + mem;
+  unsigned* dst = reinterpret_cast<unsigned*>(cache8 + slot * (P * N));
+#pragma unroll
+  for (int k = 0; k < SV; ++k) {
+    const int i = tid + k * 256;
+    if (SQ % 256 == 0 || i < SQ) dst[i] = pack_fp8x4(v[k] * inv);
+  }
+  if (tid == 0) cscale[slot] = pow2i(e);
+}
+
+struct DecodeWs {
+  int* flag;
+  float* yssd;
+  float* part;
+};
+// Workspace layout: status flag (256 bytes), y_ssd [B·H, P] f32, then the
+// per-split partials [B·H, splits, P + 2] f32, each 256-byte aligned.
+DecodeWs decode_ws(void* workspace, long pairs, int P) {
+  char* ws = static_cast<char*>(workspace);
+  return {reinterpret_cast<int*>(ws), reinterpret_cast<float*>(ws + 256),
+          reinterpret_cast<float*>(ws + 256 + ((pairs * P * sizeof(float) + 255) / 256) * 256)};
+}
+
+}  // namespace
+
+template <typename T, int N, int P>
+hipError_t launch_sma_decode(const DecodeShape& s, const T* x, const float* dt, const float* A,
+                             const T* Bm, const T* C, const T* Q, const T* E, float gate,
+                             T* cache, uint8_t* cache8, float* cscale, float* h, float* dH_cur,
+                             int* n_chunks, int* pos, T* y, void* workspace, hipStream_t st) {
+  const long pairs = (long)s.B * s.H;
+  const DecodeWs ws = decode_ws(workspace, pairs, P);
+  const int cps = (s.max_chunks + s.splits - 1) / s.splits;
+  const float scale_log2 = kLog2e / sqrtf(static_cast<float>(N));
+  const bool f8 = cache8 != nullptr;
+  if (f8)
+    hipLaunchKernelGGL((k_decode_state<T, N, P, true>), dim3(1, s.H, s.B), dim3(256), 0, st, x,
+                       dt, A, Bm, C, nullptr, cache8, cscale, h, dH_cur, n_chunks, pos, ws.flag,
+                       ws.yssd, s.H, s.G, s.S, s.max_chunks);
+  else
+    hipLaunchKernelGGL((k_decode_state<T, N, P, false>), dim3(1, s.H, s.B), dim3(256), 0, st, x,
+                       dt, A, Bm, C, cache, nullptr, nullptr, h, dH_cur, n_chunks, pos, ws.flag,
+                       ws.yssd, s.H, s.G, s.S, s.max_chunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (f8)
+    hipLaunchKernelGGL((k_sma_decode_f8<T, N, P>), dim3(s.splits, s.H, s.B), dim3(256), 0, st, C,
+                       Q, E, cache8, cscale, n_chunks, ws.part, s.H, s.G, s.max_chunks, s.splits,
+                       cps, scale_log2);
+  else
+    hipLaunchKernelGGL((k_sma_decode<T, N, P>), dim3(s.splits, s.H, s.B), dim3(256), 0, st, C, Q,
+                       E, cache, n_chunks, ws.part, s.H, s.G, s.max_chunks, s.splits, cps,
+                       scale_log2);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_decode_combine<T>), dim3(pairs), dim3(128), 0, st, ws.yssd, ws.part, gate,
+                     y, P, s.splits);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_decode_advance, dim3((s.B + 255) / 256), dim3(256), 0, st, n_chunks, pos,
+                     s.B, s.S, s.max_chunks);
+  return hipGetLastError();
+}
+
+template <typename T, int N, int P>
+hipError_t launch_fp8_store(int B, int H, int n_mem, int first, int max_chunks, const float* src,
+                            uint8_t* cache8, float* cscale, hipStream_t st) {
+  if (n_mem == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_fp8_store<N, P>), dim3(n_mem, H, B), dim3(256), 0, st, src, n_mem, first,
+                     cache8, cscale, H, max_chunks);
+  return hipGetLastError();
+}
+
+#define DART_INST_DECODE(T, N, P)                                                               \
+  template hipError_t launch_sma_decode<T, N, P>(                                               \
+      const DecodeShape&, const T*, const float*, const float*, const T*, const T*, const T*,   \
+      const T*, float, T*, uint8_t*, float*, float*, float*, int*, int*, T*, void*,             \
+      hipStream_t);                                                                             \
+  template hipError_t launch_fp8_store<T, N, P>(int, int, int, int, int, const float*, uint8_t*, \
+                                                float*, hipStream_t);
+DART_FOR_EACH_SHAPE(DART_INST_DECODE)
+
+}  // namespace dart

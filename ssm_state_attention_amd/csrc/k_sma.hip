@@ -1,5 +1,5 @@
-// State-memory attention (SMA) on gfx950: prefill over all tokens and the
-// single-token decode step over the chunk-memory cache.
+// State-memory attention (SMA) on gfx950, prefill over all tokens (the
+// single-token decode step is in k_decode.hip).
 //
 // Definitions (Pith review of DART, "Core claim" and "What carries the
 // argument"; referee major comment 3, paper §3 Eq. 8; DART abstract): for a
@@ -28,23 +28,10 @@ struct SmaTile {
 // (batch, head) pairs per ordering group of one XCD (see k_sma_fwd)
 constexpr int kPairsPerGroup = 4;
 
-// online-softmax slack: weights may reach 2^kLazyLog2 before the running max
-// (and with it every accumulator) is rescaled
-constexpr float kLazyLog2 = 8.f;
 
 template <int V>
 using IC = std::integral_constant<int, V>;
 
-// Sum of v over lanes l and l^16, then over l and l^32 (gfx950 permlane
-// swaps: no LDS round trip).
-__device__ __forceinline__ float sum_lane_groups(float v) {
-  const unsigned u = __float_as_uint(v);
-  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
-  const unsigned u2 = __float_as_uint(v);
-  const auto r32 = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
-  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
-}
 
 // Per-wave tile arithmetic of the prefill kernel: a wave owns TW = 16·NTB
 // tokens of the workgroup's tile.  Each policy holds the wave's resident
@@ -184,19 +171,6 @@ struct SmaMath16 {
   }
 };
 
-// Sum over all 64 lanes without LDS: DPP within each quad and row of 16
-// lanes, then the two permlane swaps.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
-  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
-  v += dpp_mov<0x124>(v);  // row_ror 4: quads q and q+1 of the row
-  v += dpp_mov<0x128>(v);  // row_ror 8: the whole row of 16
-  return sum_lane_groups(v);
-}
 
 // Prefill SMA.  One workgroup = WAVES waves × 16·NTB tokens of ONE chunk k,
 // so every token of the workgroup sees the same memories c < k (no mask).
@@ -454,282 +428,6 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   }
 }
 
-// Decode, step 1: one workgroup per (head, batch) advances the SSM state,
-// forms y_ssd = C·h into the workspace and, when the token closes its chunk,
-// appends the finished memory to the cache (at index n_chunks[b], which the
-// streaming kernel never reads).  A launch of its own: done by the first of
-// the streaming workgroups it held every stream back behind a latency-bound
-// read-modify-write of 128 KB of state.
-template <typename T, int N, int P>
-__global__ __launch_bounds__(256) void k_decode_state(
-    const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
-    const T* __restrict__ Bm, const T* __restrict__ C, T* __restrict__ cache,
-    float* __restrict__ hst, float* __restrict__ dHc, const int* __restrict__ n_chunks,
-    const int* __restrict__ pos, int* __restrict__ ws_flag, float* __restrict__ ws_yssd, int H,
-    int G, int S, int max_chunks) {
-  constexpr int Q4 = N / 4;
-  static_assert((P * N / 4) % 64 == 0 && 64 % Q4 == 0, "decode state mapping");
-  __shared__ float sh_c[N], sh_b[N], sh_x[P], sh_y[P];
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int g = h / (H / G);
-  const long pair = (long)b * H + h;
-  const int tid = threadIdx.x;
-  int kc = n_chunks[b];
-  kc = kc < 0 ? 0 : (kc > max_chunks ? max_chunks : kc);
-  const int ps = pos[b];
-  for (int i = tid; i < N; i += 256) {
-    const long o = ((long)b * G + g) * N + i;
-    sh_c[i] = to_f32(C[o]);
-    sh_b[i] = to_f32(Bm[o]);
-  }
-  for (int i = tid; i < P; i += 256) sh_x[i] = to_f32(x[pair * P + i]);
-  __syncthreads();
-  {
-    const float dtv = dt[pair];
-    const float a = exp_neg(dtv * A[h]);
-    const bool close = ps == S - 1;
-    const bool append = close && kc < max_chunks;
-    floatx4* hp = reinterpret_cast<floatx4*>(hst + pair * (P * N));
-    floatx4* dp = reinterpret_cast<floatx4*>(dHc + pair * (P * N));
-    T* cdst = cache + (pair * max_chunks + kc) * (long)(P * N);
-    // all of this thread's state loads first, then the updates
-    // (P·N/4 is a multiple of 64, so the guard is uniform over each wave)
-    constexpr int SQ = P * N / 4, SV = (SQ + 255) / 256;
-    static_assert(SQ % 64 == 0 && (Q4 == 4 || Q4 == 8 || Q4 == 16 || Q4 == 32),
-                  "decode state split");
-    floatx4 hv[SV], dv[SV];
-#pragma unroll
-    for (int v = 0; v < SV; ++v) {
-      const int i = tid + v * 256;
-      if (SQ % 256 == 0 || i < SQ) {
-        hv[v] = hp[i];
-        dv[v] = dp[i];
-      }
-    }
-#pragma unroll
-    for (int v = 0; v < SV; ++v) {
-      const int i = tid + v * 256;
-      if (SQ % 256 != 0 && i >= SQ) break;
-      const int p = i / Q4, n = (i % Q4) * 4;
-      const float xd = dtv * sh_x[p];
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float u = xd * sh_b[n + e];
-        hv[v][e] = a * hv[v][e] + u;
-        dv[v][e] = a * dv[v][e] + u;
-        part += sh_c[n + e] * hv[v][e];
-      }
-      hp[i] = hv[v];
-      if (append) store4(cdst + (long)i * 4, dv[v]);
-      dp[i] = close ? floatx4{0.f, 0.f, 0.f, 0.f} : dv[v];
-      // sum over the Q4 lanes that share row p (the row rotations span 16
-      // lanes, so a group of 8 takes its last step by a lane exchange)
-      part += dpp_mov<0xB1>(part);
-      part += dpp_mov<0x4E>(part);
-      if (Q4 == 8) part += __shfl_xor(part, 4);
-      if (Q4 >= 16) {
-        part += dpp_mov<0x124>(part);
-        part += dpp_mov<0x128>(part);
-      }
-      if (Q4 >= 32) {
-        const unsigned u = __float_as_uint(part);
-        const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-        part = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
-      }
-      if ((i % Q4) == 0) sh_y[p] = part;
-    }
-    if (close && !append && tid == 0) atomicOr(ws_flag, 1);
-    __syncthreads();
-    for (int p = tid; p < P; p += 256) ws_yssd[pair * P + p] = sh_y[p];
-  }
-}
-
-// Decode, step 2: one workgroup (4 waves) per (split, head, batch) streams
-// the cached memories of its split once from HBM.  Each wave takes whole
-// memories c = first + wave, first + wave + 4, ... (non-temporal 16-byte
-// loads): lane (nv, pr) holds key entries n in [nv·VE, nv·VE + VE) of rows
-// p = it·RP + pr, forms partial Q·dH[c] and C·dH[c] over its n-range,
-// reduces the score across the wave and keeps an online softmax whose value
-// accumulator stays partial over n until the end.  The (max, denominator,
-// numerator[P]) partial of the split goes to the workspace; k_decode_combine
-// merges the splits and adds y_ssd.
-template <typename T, int N, int P>
-__global__ __launch_bounds__(256) void k_sma_decode(
-    const T* __restrict__ C, const T* __restrict__ Q, const T* __restrict__ E,
-    const T* __restrict__ cache, const int* __restrict__ n_chunks, float* __restrict__ ws_part,
-    int H, int G, int max_chunks, int splits, int cps, float scale_log2) {
-  constexpr int VE = Vec16<T>::n;
-  constexpr int NV = N / VE;   // 16-byte vectors per memory row
-  constexpr int RP = 64 / NV;  // rows per wave pass
-  constexpr int NPASS = P / RP;
-  constexpr int NW = 4;
-  static_assert(64 % NV == 0 && P % RP == 0, "decode lane mapping");
-  typedef typename Vec16<T>::vec vec_t;
-  __shared__ float sh_q[N], sh_c[N], sh_e[P];
-  __shared__ float sh_wm[NW], sh_wl[NW];
-  __shared__ float sh_wacc[NW][P];
-
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int g = h / (H / G);
-  const long pair = (long)b * H + h;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int kc = n_chunks[b];
-  kc = kc < 0 ? 0 : (kc > max_chunks ? max_chunks : kc);
-
-  for (int i = tid; i < N; i += 256) {
-    const long o = ((long)b * G + g) * N + i;
-    sh_q[i] = to_f32(Q[o]);
-    sh_c[i] = to_f32(C[o]);
-  }
-  for (int i = tid; i < P; i += 256) sh_e[i] = to_f32(E[pair * P + i]);
-  __syncthreads();
-
-  const int c_begin = split * cps;
-  const int c_end = min(kc, c_begin + cps);
-  const int nv = lane % NV, pr = lane / NV;
-  constexpr bool kDot2 = std::is_same<T, bf16>::value;
-  float qv[VE], cv[VE], ev[NPASS], acc[NPASS];
-#pragma unroll
-  for (int e = 0; e < VE; ++e) {
-    qv[e] = sh_q[nv * VE + e];
-    cv[e] = sh_c[nv * VE + e];
-  }
-  // 16-bit io: Q and C stay packed (the widened values are exact copies)
-  // and each pair of key entries is one dot2 with fp32 accumulation
-  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
-  b2_t q2[VE / 2], c2[VE / 2];
-  if constexpr (kDot2) {
-#pragma unroll
-    for (int e = 0; e < VE / 2; ++e) {
-      q2[e] = b2_t{from_f32<bf16>(qv[2 * e]), from_f32<bf16>(qv[2 * e + 1])};
-      c2[e] = b2_t{from_f32<bf16>(cv[2 * e]), from_f32<bf16>(cv[2 * e + 1])};
-    }
-  }
-#pragma unroll
-  for (int it = 0; it < NPASS; ++it) {
-    ev[it] = sh_e[it * RP + pr];
-    acc[it] = 0.f;
-  }
-  float mx = -INFINITY, ls = 0.f;
-  const T* base = cache + pair * (long)max_chunks * (P * N);
-  for (int c = c_begin + w; c < c_end; c += NW) {
-    const T* src = base + (long)c * (P * N);
-    vec_t raw[NPASS];
-#pragma unroll
-    for (int it = 0; it < NPASS; ++it) raw[it] = load16_nt(src + ((it * RP + pr) * NV + nv) * VE);
-    float s = 0.f, zc[NPASS];
-#pragma unroll
-    for (int it = 0; it < NPASS; ++it) {
-      float zq = 0.f, z2 = 0.f;
-      if constexpr (kDot2) {
-#pragma unroll
-        for (int e = 0; e < VE / 2; ++e) {
-          const b2_t v2 = b2_t{raw[it][2 * e], raw[it][2 * e + 1]};
-          zq = __builtin_amdgcn_fdot2_f32_bf16(q2[e], v2, zq, false);
-          z2 = __builtin_amdgcn_fdot2_f32_bf16(c2[e], v2, z2, false);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          const float v = to_f32(raw[it][e]);
-          zq += qv[e] * v;
-          z2 += cv[e] * v;
-        }
-      }
-      zc[it] = z2;
-      s += ev[it] * zq;
-    }
-    s = wave_sum_dpp(s) * scale_log2;
-    // lazy rescale, as in the prefill kernel (s is uniform over the wave)
-    if (s > mx + kLazyLog2) {
-      const float al = exp2_fast(mx - s);  // 0 for the first memory
-      ls *= al;
-#pragma unroll
-      for (int it = 0; it < NPASS; ++it) acc[it] *= al;
-      mx = s;
-    }
-    const float pw = exp2_fast(s - mx);
-    ls += pw;
-#pragma unroll
-    for (int it = 0; it < NPASS; ++it) acc[it] += pw * zc[it];
-  }
-#pragma unroll
-  for (int it = 0; it < NPASS; ++it)
-#pragma unroll
-    for (int off = 1; off < NV; off <<= 1) acc[it] += __shfl_xor(acc[it], off);
-  if (nv == 0) {
-#pragma unroll
-    for (int it = 0; it < NPASS; ++it) sh_wacc[w][it * RP + pr] = acc[it];
-  }
-  if (lane == 0) {
-    sh_wm[w] = mx;
-    sh_wl[w] = ls;
-  }
-  __syncthreads();
-
-  float mall = -INFINITY;
-#pragma unroll
-  for (int ww = 0; ww < NW; ++ww) mall = fmaxf(mall, sh_wm[ww]);
-  for (int p = tid; p < P; p += 256) {
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      if (sh_wm[ww] > -INFINITY) {
-        const float f = exp2_fast(sh_wm[ww] - mall);
-        num += f * sh_wacc[ww][p];
-        den += f * sh_wl[ww];
-      }
-    }
-    float* part = ws_part + (pair * splits + split) * (P + 2);
-    part[2 + p] = num;
-    if (p == 0) {
-      part[0] = mall;
-      part[1] = den;
-    }
-  }
-}
-
-// Merge the per-split (max, denominator, numerator[P]) partials of one
-// (batch, head) and apply the gate.
-template <typename T>
-__global__ __launch_bounds__(128) void k_decode_combine(const float* __restrict__ ws_yssd,
-                                                        const float* __restrict__ ws_part,
-                                                        float gate, T* __restrict__ y, int P,
-                                                        int splits) {
-  const long pair = blockIdx.x;
-  const float* part = ws_part + pair * splits * (P + 2);
-  float mall = -INFINITY;
-  for (int s = 0; s < splits; ++s) mall = fmaxf(mall, part[s * (P + 2)]);
-  for (int p = threadIdx.x; p < P; p += blockDim.x) {
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float m = part[s * (P + 2)];
-      if (m > -INFINITY) {
-        const float f = exp2_fast(m - mall);
-        num += f * part[s * (P + 2) + 2 + p];
-        den += f * part[s * (P + 2) + 1];
-      }
-    }
-    const float o = den > 0.f ? num / den : 0.f;
-    y[pair * P + p] = from_f32<T>(ws_yssd[pair * P + p] + gate * o);
-  }
-}
-
-// Advance the per-sequence position after every head has read it.
-__global__ void k_decode_advance(int* __restrict__ n_chunks, int* __restrict__ pos, int B, int S,
-                                 int max_chunks) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= B) return;
-  if (pos[b] == S - 1) {
-    const int k = n_chunks[b];
-    n_chunks[b] = k < max_chunks ? k + 1 : max_chunks;
-    pos[b] = 0;
-  } else {
-    pos[b] += 1;
-  }
-}
-
 template <typename T, int N, int P, int NTB, int WAVES>
 hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T* C, const T* dH,
                          const T* y_ssd, const float* acum, float gate, T* y, const T* prior,
@@ -775,45 +473,11 @@ hipError_t launch_sma_fwd(const PrefillShape& s, const T* Q, const T* E, const T
                                         st);
 }
 
-template <typename T, int N, int P>
-hipError_t launch_sma_decode(const DecodeShape& s, const T* x, const float* dt, const float* A,
-                             const T* Bm, const T* C, const T* Q, const T* E, float gate,
-                             T* cache, float* h, float* dH_cur, int* n_chunks, int* pos, T* y,
-                             void* workspace, hipStream_t st) {
-  const long pairs = (long)s.B * s.H;
-  char* ws = static_cast<char*>(workspace);
-  int* flag = reinterpret_cast<int*>(ws);
-  float* ws_yssd = reinterpret_cast<float*>(ws + 256);
-  float* ws_part = reinterpret_cast<float*>(
-      ws + 256 + ((pairs * P * sizeof(float) + 255) / 256) * 256);
-  const int cps = (s.max_chunks + s.splits - 1) / s.splits;
-  const float scale_log2 = kLog2e / sqrtf(static_cast<float>(N));
-  hipLaunchKernelGGL((k_decode_state<T, N, P>), dim3(1, s.H, s.B), dim3(256), 0, st, x, dt, A, Bm,
-                     C, cache, h, dH_cur, n_chunks, pos, flag, ws_yssd, s.H, s.G, s.S,
-                     s.max_chunks);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_sma_decode<T, N, P>), dim3(s.splits, s.H, s.B), dim3(256), 0, st, C, Q,
-                     E, cache, n_chunks, ws_part, s.H, s.G, s.max_chunks, s.splits, cps,
-                     scale_log2);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_decode_combine<T>), dim3(pairs), dim3(128), 0, st, ws_yssd, ws_part,
-                     gate, y, P, s.splits);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_decode_advance, dim3((s.B + 255) / 256), dim3(256), 0, st, n_chunks, pos,
-                     s.B, s.S, s.max_chunks);
-  return hipGetLastError();
-}
 
 #define DART_INST_SMA(T, N, P)                                                                 \
   template hipError_t launch_sma_fwd<T, N, P>(const PrefillShape&, const T*, const T*, const T*, \
                                               const T*, const T*, const float*, float, T*,   \
-                                              const T*, int, int, hipStream_t);              \
-  template hipError_t launch_sma_decode<T, N, P>(                                                \
-      const DecodeShape&, const T*, const float*, const float*, const T*, const T*, const T*,    \
-      const T*, float, T*, float*, float*, int*, int*, T*, void*, hipStream_t);
+                                              const T*, int, int, hipStream_t);
 DART_FOR_EACH_SHAPE(DART_INST_SMA)
 
 }  // namespace dart

@@ -422,4 +422,106 @@ def pin_sma_decayed_from_recurrence(orc):
     _close(got, ref, tol=1e-9, what="decayed SMA vs recurrence states")
 
 
+
+# ------------------------------------------------------------ fp8 cache
+# The E4M3 format is fixed by the OCP 8-bit floating point specification;
+# torch's float8_e4m3fn dtype implements it (conversion from float32 rounds
+# to nearest, ties to even) and serves as the library routine.
+def _torch_e4m3_values(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(
+        torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def pin_fp8_decode_all_codes(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    got = orc.fp8_e4m3_decode(codes)
+    ref = _torch_e4m3_values(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), "fp8 NaN codes"
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and np.isnan(got).sum() == 2
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin]), "fp8 decode differs from the library"
+    # format facts: 1.0, the largest finite value, the smallest subnormal and
+    # normal, the largest subnormal, a negative value, negative zero
+    for c, v in ((0x38, 1.0), (0x7E, 448.0), (0x01, 2.0 ** -9), (0x08, 2.0 ** -6),
+                 (0x07, 7 * 2.0 ** -9), (0xB8, -1.0), (0xC4, -3.0)):
+        assert got[c] == v, (hex(c), got[c], v)
+    assert got[0x80] == 0.0 and np.signbit(got[0x80])
+
+
+def pin_fp8_encode_matches_library(orc):
+    rng = np.random.default_rng(81)
+    # magnitudes across every binade, the subnormals included
+    v = rng.standard_normal(60000) * np.exp2(rng.uniform(-13.0, 8.7, 60000))
+    # every midpoint between neighbouring finite values (ties), and the
+    # values themselves
+    fin = np.sort(np.unique(_torch_e4m3_values(np.arange(0x7F, dtype=np.uint8))))
+    mids = 0.5 * (fin[1:] + fin[:-1])
+    v = np.concatenate([v, fin, -fin, mids, -mids, [0.0, -0.0, 2.0 ** -11, -(2.0 ** -11)]])
+    v = v[np.abs(v) <= 448.0].astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = orc.fp8_e4m3_encode(v.astype(np.float64))
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, f"fp8 encode differs at {v[bad[:4]]}: {got[bad[:4]]} vs {ref[bad[:4]]}"
+    # ties go to the even mantissa
+    assert orc.fp8_e4m3_encode(np.array([1.0625, 1.1875, 1.5 * 2.0 ** -9])).tolist() == [
+        0x38, 0x3A, 0x02]
+
+
+def pin_fp8_memory_scale(orc):
+    rng = np.random.default_rng(82)
+    for mag in (1e-30, 3e-7, 0.02, 1.0, 7.5, 4e5, 1e30):
+        mem = rng.standard_normal((6, 5)) * mag
+        s = orc.fp8_memory_scale(mem)
+        m, e = math.frexp(s)
+        assert m == 0.5, "scale is not a power of two"
+        top = np.max(np.abs(mem)) / s
+        assert 128.0 <= top < 256.0, (mag, top)
+        codes, s2 = orc.fp8_quantize_memory(mem)
+        assert s2 == s and codes.shape == mem.shape and codes.dtype == np.uint8
+        deq = _torch_e4m3_values(codes) * s
+        # half a grid step: 1/16 of the magnitude in the normal range,
+        # 2^-10 of the scale among the subnormals
+        assert np.all(np.abs(deq - mem) <= np.maximum(np.abs(mem) / 16.0, s * 2.0 ** -10))
+    pow2 = np.zeros((3, 3))
+    pow2[1, 2] = -2.0 ** 5
+    assert orc.fp8_memory_scale(pow2) * 128.0 == 2.0 ** 5
+    assert orc.fp8_memory_scale(np.zeros((4, 4))) == 1.0
+
+
+def pin_decode_step_fp8_reads_the_dequantised_cache(orc):
+    """The fp8 decode step equals the float decode step over the memories the
+    codes stand for (dequantised here with the library), and a memory it
+    appends is its f64 counterpart within the rounding bound."""
+    rng = np.random.default_rng(83)
+    B, H, G, N, P, S, Mx = 2, 2, 1, 4, 3, 5, 4
+    codes = rng.integers(0, 256, (B, H, Mx, N, P)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x30  # no NaN codes
+    scales = np.exp2(rng.integers(-9, 4, (B, H, Mx))).astype(np.float64)
+    cache = _torch_e4m3_values(codes) * scales[..., None, None]
+    h = rng.standard_normal((B, H, N, P))
+    dHc = rng.standard_normal((B, H, N, P))
+    state = {"h": h, "dH_cur": dHc, "n_chunks": np.array([3, 2]), "pos": np.array([S - 1, 1])}
+    x, E = rng.standard_normal((B, H, P)), rng.standard_normal((B, H, P))
+    dt = np.full((B, H), 0.1)
+    A = -np.ones(H)
+    Bm, C, Q = (rng.standard_normal((B, G, N)) for _ in range(3))
+    y8, new8 = orc.decode_step_fp8(dict(state, codes=codes, scales=scales), x, dt, A, Bm, C, Q,
+                                   E, 0.7, S)
+    yf, newf = orc.decode_step(dict(state, cache=cache), x, dt, A, Bm, C, Q, E, 0.7, S,
+                               cache_bf16=False)
+    _close(y8, yf, 1e-12, "fp8 decode y")
+    _close(new8["h"], newf["h"], 1e-12, "fp8 decode h")
+    assert list(new8["n_chunks"]) == [4, 2] and list(new8["pos"]) == [0, 2]
+    # sequence 0 appended memory 3; everything else is untouched
+    app = _torch_e4m3_values(new8["codes"][0, :, 3]) * new8["scales"][0, :, 3, None, None]
+    ref = newf["cache"][0, :, 3]
+    assert np.all(np.abs(app - ref) <= np.abs(ref) / 16.0 + 2.0 ** -10 * np.max(np.abs(ref)))
+    for hh in range(H):
+        top = np.max(np.abs(ref[hh])) / new8["scales"][0, hh, 3]
+        assert 128.0 <= top < 256.0
+    keep = np.ones((B, H, Mx), dtype=bool)
+    keep[0, :, 3] = False
+    assert np.array_equal(new8["codes"][keep], codes[keep])
+    assert np.array_equal(new8["scales"][keep], scales[keep])
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

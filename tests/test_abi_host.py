@@ -152,6 +152,34 @@ def test_decode_rejects_small_workspace():
     assert lib.dart_sma_decode(d, *args, 0.5, *state, MIS, need, None) == ALIGN
 
 
+def test_fp8_cache_entry_points_validate_on_host():
+    lib = dart.lib()
+    d = ddims(2, 4, 4, 128, 64, 256, 8)
+    need = api.dart_sma_decode_workspace(d)
+    args = [A16] * 7
+    # cache8, scale, h, dH_cur, n_chunks, pos, y
+    for i in range(7):
+        state = [A16] * 7
+        state[i] = None
+        assert lib.dart_sma_decode_fp8(d, *args, 0.5, *state, A16, need, None) == NULLP
+    state = [A16] * 7
+    assert lib.dart_sma_decode_fp8(d, *args, 0.5, *state, A16, need - 256, None) == WS
+    state[1] = MIS
+    assert lib.dart_sma_decode_fp8(d, *args, 0.5, *state, A16, need, None) == ALIGN
+    assert lib.dart_sma_decode_fp8(ddims(N=96), *args, 0.5, *([A16] * 7), A16, need,
+                                   None) == UNSUP
+    # store: 0 <= n_mem, 0 <= first <= max_chunks - n_mem
+    st = lib.dart_cache_fp8_store
+    assert st(d, A16, -1, 0, A16, A16, None) == BAD
+    assert st(d, A16, 2, -1, A16, A16, None) == BAD
+    assert st(d, A16, 9, 0, A16, A16, None) == BAD
+    assert st(d, A16, 4, 5, A16, A16, None) == BAD
+    assert st(d, None, 8, 0, A16, A16, None) == NULLP
+    assert st(d, A16, 8, 0, A16, None, None) == NULLP
+    assert st(d, A16, 8, 0, MIS, A16, None) == ALIGN
+    assert st(ddims(mx=0), A16, 0, 0, A16, A16, None) == BAD
+
+
 def test_binding_checks_tensors_before_calling():
     x = torch.zeros(1, 64, 1, 16)
     with pytest.raises(ValueError, match="GPU"):

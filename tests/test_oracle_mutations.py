@@ -68,6 +68,18 @@ MUTATIONS = [
      "if pos[b] == S - 1:", "if pos[b] == S:"),
     ("decode skips the SSM decay of the chunk memory",
      "dHc = a[:, :, None, None] * dHc + inp", "dHc = dHc + inp"),
+    ("fp8 exponent bias 8",
+     "normal = (1.0 + mant / 8.0) * np.exp2(field - 7.0)",
+     "normal = (1.0 + mant / 8.0) * np.exp2(field - 8.0)"),
+    ("fp8 encoding truncates",
+     "r = np.round(a / step) * step", "r = np.floor(a / step) * step"),
+    ("fp8 subnormal grid too fine",
+     "e = np.maximum(E - 1, -6)", "e = np.maximum(E - 1, -7)"),
+    ("fp8 scale one binade too high",
+     "return math.ldexp(1.0, max(E - 8, -126))", "return math.ldexp(1.0, max(E - 7, -126))"),
+    ("fp8 decode step ignores the scales",
+     'plain["cache"] = fp8_dequantize(codes, scales)',
+     'plain["cache"] = fp8_e4m3_decode(codes)'),
     ("cache ratio counts keys only",
      "return (L // S) * N * P, 2 * L * P", "return (L // S) * N * P, L * P"),
 ]

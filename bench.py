@@ -6,7 +6,8 @@ Mamba-2 ~370M layer shape: batch 4, 32 heads, groups of 8 heads sharing
 B/C/Q, L = 8192, S = 256, N = 128, P = 64, bfloat16 inputs with fp32
 accumulation.  `value` is prefill tokens/s (batch·L / step time).  The
 decode step over a 4 GiB chunk-memory cache (batch 64, 32 heads, 128
-cached chunks) is timed in the same run and reported under "decode".
+cached chunks) is timed in the same run and reported under "decode", and
+the same step over the fp8 (E4M3) cache under "decode_fp8".
 
 Prints one JSON line.  `python bench.py --steps K --warmup W`.
 """
@@ -196,6 +197,61 @@ def bench_decode(args, torch, api, synth):
     }
 
 
+def bench_decode_fp8(args, torch, api, synth):
+    """The decode step of bench_decode over the fp8 (E4M3 + one scale per
+    memory) cache: same shape, same token; the cache is encoded from f32
+    memories drawn on the device, 16 chunks at a time."""
+    c = DECODE
+    B, H, G, N, P, S, k = c["B"], c["H"], c["G"], c["N"], c["P"], c["S"], c["chunks"]
+    st = api.new_decode_state(B, H, G, N, P, S, k, torch.bfloat16, "cuda:0", fp8_cache=True)
+    for blk in range(0, k, 16):
+        n = min(16, k - blk)
+        mem = synth.draw_state(50 + blk, (B, H, n, P, N), 0.01, torch.float32, device="cuda:0")
+        api.store_memories(st, mem, first=blk)
+        del mem
+    st["h"].copy_(synth.draw_state(51, (B, H, P, N), 0.01, torch.float32, device="cuda:0"))
+    st["n_chunks"].fill_(k)
+    tok = {kk: v.to("cuda:0") for kk, v in
+           synth.draw_decode_token(53, B, H, G, N, P, io=torch.bfloat16).items()}
+    y = torch.empty(B, H, P, dtype=torch.bfloat16, device="cuda:0")
+
+    def step():
+        api.decode_step(st, tok["x"], tok["dt"], tok["A"], tok["Bm"], tok["C"], tok["Q"],
+                        tok["E"], 0.5, y=y)
+
+    steps = max(1, min(args.steps, S - 2))
+    warm = max(0, min(args.warmup, S - 2 - steps))
+    for _ in range(warm):
+        step()
+    st["pos"].zero_()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    cache_bytes = B * H * k * N * P + 4 * B * H * k  # codes + scales
+    state_bytes = 2 * 2 * B * H * N * P * 4
+    tot = (cache_bytes + state_bytes) / (ms / 1e3) / 1e9
+    return {
+        "metric": "decode chunk-memory HBM GB/s, fp8 cache",
+        "value": cache_bytes / (ms / 1e3) / 1e9,
+        "unit": "GB/s",
+        "ms_per_step": ms,
+        "steps": steps,
+        "chunk_memory_bytes": cache_bytes,
+        "total_bytes_incl_state": cache_bytes + state_bytes,
+        "config": {"workload": "DART decode over the fp8 (E4M3) chunk-memory cache",
+                   "batch": B, "heads": H, "dstate": N, "headdim": P, "chunk": S,
+                   "cached_chunks": k, "io": "bf16", "cache": "e4m3 + f32 scale per memory"},
+        "roofline": {"kernel": "dart_sma_decode_fp8", "bound": "hbm", "achieved": tot,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": tot / PEAK_HBM_GBS,
+                     "traffic": None},
+    }
+
+
 def cpu_baseline(inp, seconds):
     """The fp64 oracle, unmodified, on whole (batch, head) pairs of the same
     workload until about `seconds` of CPU time; the full-layer rate follows
@@ -278,6 +334,8 @@ def main():
     if not args.no_decode:
         torch.cuda.empty_cache()
         result["decode"] = bench_decode(args, torch, api, synth)
+        torch.cuda.empty_cache()
+        result["decode_fp8"] = bench_decode_fp8(args, torch, api, synth)
     if not args.no_cpu_baseline and pre is not None:
         result["cpu_baseline"] = cpu_baseline(pre["inputs"], args.cpu_seconds)
     print(json.dumps(result), flush=True)

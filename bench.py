@@ -25,22 +25,29 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "SMA+scan prefill tokens/s & MFMA% at L=8K; decode chunk-memory HBM GB/s"
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this
-# benchmark, calibrated against a 1 GiB copy (profiles/); valid only for the
-# kernel source they were measured on.
-KERNEL_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                             "ssm_state_attention_amd", "csrc", "k_sma.hip")
-PROFILED_TRAFFIC = {"source_sha1": "a129ac176de3d5c12b62837c2e2736023407da33",
-                    "k_sma_fwd": (547.8 + 134.2) * 1e6,
-                    # the four launches of one decode call
-                    "dart_sma_decode": (4296.4 + 0.6 + 135.7 + 134.7 + 1.6 + 0.3) * 1e6}
+# benchmark, calibrated against a 1 GiB copy (profiles/); each figure is valid
+# only for the kernel source it was measured on (SHA-1 of that file).
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "ssm_state_attention_amd", "csrc")
+PROFILED_TRAFFIC = {
+    "k_sma_fwd": ("k_sma.hip", "4b76f137bc708b83e5b9f2f604c61a25b6e8736c",
+                  (548.03 + 134.22) * 1e6),
+    # the four launches of one decode call (state, stream, combine, advance)
+    "dart_sma_decode": ("k_decode.hip", "1edf2954b0ac30901f6e19755b249602c54386d1",
+                        (135.75 + 134.74 + 4296.39 + 0.59 + 1.57 + 0.26) * 1e6),
+    "dart_sma_decode_fp8": ("k_decode.hip", "1edf2954b0ac30901f6e19755b249602c54386d1",
+                            (135.76 + 134.74 + 2150.98 + 0.59 + 1.57 + 0.26) * 1e6),
+}
 
 
 def profiled_traffic(kernel):
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
-        if hashlib.sha1(f.read()).hexdigest() != PROFILED_TRAFFIC["source_sha1"]:
+    src, sha1, nbytes = PROFILED_TRAFFIC[kernel]
+    if sha1 is None:
+        return None
+    with open(os.path.join(CSRC, src), "rb") as f:
+        if hashlib.sha1(f.read()).hexdigest() != sha1:
             return None
-    return PROFILED_TRAFFIC[kernel]
+    return nbytes
 
 
 def sma_flops(c):
@@ -248,7 +255,7 @@ def bench_decode_fp8(args, torch, api, synth):
                    "cached_chunks": k, "io": "bf16", "cache": "e4m3 + f32 scale per memory"},
         "roofline": {"kernel": "dart_sma_decode_fp8", "bound": "hbm", "achieved": tot,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": tot / PEAK_HBM_GBS,
-                     "traffic": None},
+                     "traffic": profiled_traffic("dart_sma_decode_fp8")},
     }
 
 

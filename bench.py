@@ -129,10 +129,27 @@ def bench_prefill(args, torch, api, synth):
     wall = time.perf_counter() - t0
     ms = wall * 1e3 / args.steps
     split = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(3)]
+    per_step = sorted(e[0].elapsed_time(e[3]) for e in evs)
+    per_sma = sorted(e[2].elapsed_time(e[3]) for e in evs)
     flops_sma, flops_scan = sma_flops(c), scan_flops(c)
     sma_ms = split[2]
+    # cold inputs: 512 MB touched between repetitions evicts them from L2 and MALL
+    junk = torch.empty(128 << 20, dtype=torch.float32, device="cuda:0")
+    cold = []
+    for _ in range(max(3, min(args.steps, 10))):
+        junk.add_(1.0)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        step(ev)
+        torch.cuda.synchronize()
+        cold.append(ev[0].elapsed_time(ev[3]))
+    del junk
     return {
         "ms_per_step": ms,
+        "step_ms_median": per_step[len(per_step) // 2],
+        "step_ms_min": per_step[0],
+        "step_ms_cold_median": sorted(cold)[len(cold) // 2],
+        "sma_ms_median": per_sma[len(per_sma) // 2],
+        "sma_ms_min": per_sma[0],
         "tokens_per_s": B * L / (ms / 1e3),
         "kernel_ms": {"chunk_state": split[0], "state_pass+chunk_out": split[1],
                       "sma_fwd": sma_ms},
@@ -151,6 +168,27 @@ def bench_prefill(args, torch, api, synth):
     }
 
 
+def timed_steps(torch, step, steps):
+    """Mean over `steps` back-to-back calls (one pair of events around all
+    of them), then median and min of `steps` calls timed one by one."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    mean = e0.elapsed_time(e1) / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    each = sorted(a.elapsed_time(b) for a, b in evs)
+    return mean, each[len(each) // 2], each[0]
+
+
 def bench_decode(args, torch, api, synth):
     c = DECODE
     B, H, G, N, P, S, k = c["B"], c["H"], c["G"], c["N"], c["P"], c["S"], c["chunks"]
@@ -167,19 +205,14 @@ def bench_decode(args, torch, api, synth):
         api.decode_step(st, tok["x"], tok["dt"], tok["A"], tok["Bm"], tok["C"], tok["Q"],
                         tok["E"], 0.5, y=y)
 
-    steps = max(1, min(args.steps, S - 2))  # stay inside one chunk: no append in the loop
-    warm = max(0, min(args.warmup, S - 2 - steps))
+    # stay inside one chunk (no append): timed_steps makes 2·steps calls
+    steps = max(1, min(args.steps, (S - 2) // 2))
+    warm = max(0, min(args.warmup, S - 2 - 2 * steps))
     for _ in range(warm):
         step()
     st["pos"].zero_()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms, med, mn = timed_steps(torch, step, steps)
     cache_bytes = B * H * k * N * P * 2
     state_bytes = 2 * 2 * B * H * N * P * 4  # h and dH_cur read + written
     gbs = cache_bytes / (ms / 1e3) / 1e9
@@ -189,6 +222,8 @@ def bench_decode(args, torch, api, synth):
         "value": gbs,
         "unit": "GB/s",
         "ms_per_step": ms,
+        "ms_median": med,
+        "ms_min": mn,
         "steps": steps,
         "chunk_memory_bytes": cache_bytes,
         "total_bytes_incl_state": cache_bytes + state_bytes,
@@ -226,19 +261,13 @@ def bench_decode_fp8(args, torch, api, synth):
         api.decode_step(st, tok["x"], tok["dt"], tok["A"], tok["Bm"], tok["C"], tok["Q"],
                         tok["E"], 0.5, y=y)
 
-    steps = max(1, min(args.steps, S - 2))
-    warm = max(0, min(args.warmup, S - 2 - steps))
+    steps = max(1, min(args.steps, (S - 2) // 2))
+    warm = max(0, min(args.warmup, S - 2 - 2 * steps))
     for _ in range(warm):
         step()
     st["pos"].zero_()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms, med, mn = timed_steps(torch, step, steps)
     cache_bytes = B * H * k * N * P + 4 * B * H * k  # codes + scales
     state_bytes = 2 * 2 * B * H * N * P * 4
     tot = (cache_bytes + state_bytes) / (ms / 1e3) / 1e9
@@ -247,6 +276,8 @@ def bench_decode_fp8(args, torch, api, synth):
         "value": cache_bytes / (ms / 1e3) / 1e9,
         "unit": "GB/s",
         "ms_per_step": ms,
+        "ms_median": med,
+        "ms_min": mn,
         "steps": steps,
         "chunk_memory_bytes": cache_bytes,
         "total_bytes_incl_state": cache_bytes + state_bytes,
@@ -301,6 +332,14 @@ def cpu_baseline(inp, seconds):
     }
 
 
+def environment(torch):
+    """ROCm build and device identification."""
+    prop = torch.cuda.get_device_properties(0)
+    return {"hip": torch.version.hip, "torch": torch.__version__,
+            "arch": getattr(prop, "gcnArchName", None), "compute_units": prop.multi_processor_count,
+            "hbm_bytes": prop.total_memory}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -323,6 +362,7 @@ def main():
                          "groups": BASE["G"], "dstate": BASE["N"], "headdim": BASE["P"],
                          "chunk": BASE["S"], "io": "bf16", "accumulate": "fp32",
                          "parallelism": "single GPU"}}
+    result["env"] = environment(torch)
     if args.copy_probe:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
@@ -336,6 +376,9 @@ def main():
         result["ms_per_step"] = pre["ms_per_step"]
         result["roofline"] = pre["roofline"]
         result["kernel_ms"] = pre["kernel_ms"]
+        result["timing_ms"] = {k: pre[k] for k in ("step_ms_median", "step_ms_min",
+                                                   "step_ms_cold_median", "sma_ms_median",
+                                                   "sma_ms_min")}
         result["mfma_frac_whole_prefill"] = pre["mfma_frac_whole_prefill"]
         result["algorithmic_gflop_per_step"] = {k: v / 1e9 for k, v in pre["flops"].items()}
     if not args.no_decode:

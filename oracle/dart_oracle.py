@@ -77,6 +77,8 @@ __all__ = [
     "fp8_quantize_memory",
     "fp8_dequantize",
     "decode_step_fp8",
+    "sma_backward",
+    "gated_backward",
 ]
 
 
@@ -238,6 +240,68 @@ def sma(Q, E, C, dH, S, tokens=None):
                 vals = np.einsum("tn,cnp->tcp", Ch[b, ts, h], mem)
                 o[b, ts, h] = np.einsum("tc,tcp->tp", _softmax(scores), vals)
     return o
+
+
+def sma_backward(Q, E, C, dH, S, do):
+    """Gradients of a loss through the SMA readout, given do = ∂loss/∂o
+    [B,L,H,P] (reverse-mode chain rule through the steps of :func:`sma`).
+    For token t of chunk k, memory c < k, with K, V, s as in :func:`sma` and
+    α the softmax weights over c:
+
+        dV_{t,c} = α_{t,c}·do_t
+        dα_{t,c} = do_t·V_{t,c}
+        ds_{t,c} = α_{t,c}·(dα_{t,c} − Σ_c' α_{t,c'}·dα_{t,c'})
+        dK_{t,c} = ds_{t,c}·Q_t / sqrt(N)
+        dQ_t  += Σ_c ds_{t,c}·K_{t,c} / sqrt(N)
+        dE_t  += Σ_c ΔH[c]ᵀ·dK_{t,c}
+        dC_t  += Σ_c ΔH[c]·dV_{t,c}
+        dΔH[c] += Σ_t dK_{t,c}·E_tᵀ + C_t·dV_{t,c}ᵀ
+
+    Q and C are shared by the heads of a group, so their gradients are
+    summed over those heads.  Returns (dQ [B,L,G,N], dE [B,L,H,P],
+    dC [B,L,G,N], ddH [B,H,M,N,P])."""
+    E, dH, do = _f64(E), _f64(dH), _f64(do)
+    Bsz, L, H, P = E.shape
+    G = np.shape(Q)[2]
+    Qh, Ch = _per_head(Q, H), _per_head(C, H)
+    N = Qh.shape[-1]
+    dQh = np.zeros((Bsz, L, H, N))
+    dCh = np.zeros((Bsz, L, H, N))
+    dE = np.zeros((Bsz, L, H, P))
+    ddH = np.zeros_like(dH)
+    rs = 1.0 / math.sqrt(N)
+    for b in range(Bsz):
+        for h in range(H):
+            for k in range(1, L // S):
+                ts = np.arange(k * S, (k + 1) * S)
+                mem = dH[b, h, :k]  # the memories token ts read, [k,N,P]
+                Qt, Ct, Et, dot = Qh[b, ts, h], Ch[b, ts, h], E[b, ts, h], do[b, ts, h]
+                K = np.einsum("cnp,tp->tcn", mem, Et)               # [t,c,N]
+                V = np.einsum("tn,cnp->tcp", Ct, mem)               # [t,c,P]
+                alpha = _softmax(np.einsum("tn,tcn->tc", Qt, K) * rs)
+                dV = alpha[:, :, None] * dot[:, None, :]
+                dalpha = np.einsum("tp,tcp->tc", dot, V)
+                ds = alpha * (dalpha - np.sum(alpha * dalpha, axis=1, keepdims=True))
+                dK = ds[:, :, None] * Qt[:, None, :] * rs           # [t,c,N]
+                dQh[b, ts, h] += np.einsum("tc,tcn->tn", ds, K) * rs
+                dE[b, ts, h] += np.einsum("cnp,tcn->tp", mem, dK)
+                dCh[b, ts, h] += np.einsum("cnp,tcp->tn", mem, dV)
+                ddH[b, h, :k] += (np.einsum("tcn,tp->cnp", dK, Et)
+                                  + np.einsum("tn,tcp->cnp", Ct, dV))
+    gmap = group_of_head(H, G)
+    dQ = np.zeros((Bsz, L, G, N))
+    dC = np.zeros((Bsz, L, G, N))
+    for h in range(H):
+        dQ[:, :, gmap[h]] += dQh[:, :, h]
+        dC[:, :, gmap[h]] += dCh[:, :, h]
+    return dQ, dE, dC, ddH
+
+
+def gated_backward(dy, o, g):
+    """Backward of y = y_ssd + g·o [pith-core]: returns (dy_ssd, do, dg) =
+    (dy, g·dy, Σ dy·o) for an upstream gradient dy."""
+    dy, o = _f64(dy), _f64(o)
+    return dy.copy(), float(g) * dy, float(np.sum(dy * o))
 
 
 def sma_bruteforce(Q, E, C, dH, S):

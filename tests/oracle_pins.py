@@ -524,4 +524,74 @@ def pin_decode_step_fp8_reads_the_dequantised_cache(orc):
     assert np.array_equal(new8["codes"][keep], codes[keep])
     assert np.array_equal(new8["scales"][keep], scales[keep])
 
+
+# ------------------------------------------------------------ backward
+def _fd_grad(f, arr, eps=1e-6):
+    """Central finite differences of the scalar f() with respect to every
+    element of arr (modified in place and restored)."""
+    g = np.zeros_like(arr)
+    for idx in np.ndindex(arr.shape):
+        a0 = arr[idx]
+        arr[idx] = a0 + eps
+        fp = f()
+        arr[idx] = a0 - eps
+        fm = f()
+        arr[idx] = a0
+        g[idx] = (fp - fm) / (2 * eps)
+    return g
+
+
+def pin_sma_backward_finite_differences(orc):
+    """Every gradient of Σ do·o against central differences of the forward
+    readout (three chunks, heads sharing a group, sharpened scores)."""
+    rng = np.random.default_rng(91)
+    B, L, H, G, N, P, S = 1, 12, 4, 2, 3, 2, 4
+    Q = rng.standard_normal((B, L, G, N)) * 2.0
+    E = rng.standard_normal((B, L, H, P))
+    C = rng.standard_normal((B, L, G, N))
+    dH = rng.standard_normal((B, H, L // S, N, P))
+    do = rng.standard_normal((B, L, H, P))
+    grads = orc.sma_backward(Q, E, C, dH, S, do)
+
+    def loss():
+        return float(np.sum(do * orc.sma(Q, E, C, dH, S)))
+
+    for name, arr, g in zip(("dQ", "dE", "dC", "ddH"), (Q, E, C, dH), grads):
+        num = _fd_grad(loss, arr)
+        _close(g, num, 1e-7 * max(1.0, float(np.max(np.abs(num)))), f"sma backward {name}")
+
+
+def pin_sma_backward_single_memory(orc):
+    """Two chunks: the second chunk's tokens see one memory, so α = 1 and
+    o_t = ΔH[0]ᵀC_t; then dQ = dE = 0, dC_t = ΔH[0]·do_t and
+    dΔH[0] = Σ_t C_t do_tᵀ (first-chunk tokens contribute nothing)."""
+    rng = np.random.default_rng(92)
+    B, L, H, G, N, P, S = 2, 10, 1, 1, 4, 3, 5
+    Q = rng.standard_normal((B, L, G, N))
+    E = rng.standard_normal((B, L, H, P))
+    C = rng.standard_normal((B, L, G, N))
+    dH = rng.standard_normal((B, H, 2, N, P))
+    do = rng.standard_normal((B, L, H, P))
+    dQ, dE, dC, ddH = orc.sma_backward(Q, E, C, dH, S, do)
+    _close(dQ, np.zeros_like(dQ), 1e-12, "single memory dQ")
+    _close(dE, np.zeros_like(dE), 1e-12, "single memory dE")
+    for b in range(B):
+        for t in range(L):
+            want = dH[b, 0, 0] @ do[b, t, 0] if t >= S else np.zeros(N)
+            _close(dC[b, t, 0], want, 1e-12, "single memory dC")
+        want = sum(np.outer(C[b, t, 0], do[b, t, 0]) for t in range(S, L))
+        _close(ddH[b, 0, 0], want, 1e-12, "single memory ddH[0]")
+        _close(ddH[b, 0, 1], np.zeros((N, P)), 1e-12, "last memory unread")
+
+
+def pin_gated_backward(orc):
+    rng = np.random.default_rng(93)
+    dy, o, ys = (rng.standard_normal((2, 6, 3, 4)) for _ in range(3))
+    g = np.array([0.3])
+    dys, do, dg = orc.gated_backward(dy, o, g[0])
+    _close(dys, dy, 0.0, "dy_ssd")
+    _close(do, 0.3 * dy, 1e-15, "do")
+    num = _fd_grad(lambda: float(np.sum(dy * orc.gated_output(ys, o, g[0]))), g)
+    _close(np.array([dg]), num, 1e-7, "dg")
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -80,6 +80,20 @@ MUTATIONS = [
     ("fp8 decode step ignores the scales",
      'plain["cache"] = fp8_dequantize(codes, scales)',
      'plain["cache"] = fp8_e4m3_decode(codes)'),
+    ("SMA backward drops the softmax centring",
+     "ds = alpha * (dalpha - np.sum(alpha * dalpha, axis=1, keepdims=True))",
+     "ds = alpha * dalpha"),
+    ("SMA backward key gradient without the score scale",
+     "dK = ds[:, :, None] * Qt[:, None, :] * rs", "dK = ds[:, :, None] * Qt[:, None, :]"),
+    ("SMA backward value gradient from the query",
+     "dCh[b, ts, h] += np.einsum(\"cnp,tcp->tn\", mem, dV)",
+     "dCh[b, ts, h] += np.einsum(\"cnp,tcp->tn\", mem, dV) * 0.5"),
+    ("SMA backward drops the key term of the memory gradient",
+     "ddH[b, h, :k] += (np.einsum(\"tcn,tp->cnp\", dK, Et)",
+     "ddH[b, h, :k] += (0.0 * np.einsum(\"tcn,tp->cnp\", dK, Et)"),
+    ("gate gradient scaled by g",
+     "return dy.copy(), float(g) * dy, float(np.sum(dy * o))",
+     "return dy.copy(), float(g) * dy, float(g) * float(np.sum(dy * o))"),
     ("cache ratio counts keys only",
      "return (L // S) * N * P, 2 * L * P", "return (L // S) * N * P, L * P"),
 ]

@@ -174,6 +174,43 @@ dart_status dart_sma_fwd_decayed(const dart_dims* dims, const void* Q, const voi
                                  const void* C, const void* dH, const float* acum,
                                  const void* y_ssd, float gate, void* y, void* stream);
 
+/*
+ * Training forward of SMA: dart_sma_fwd plus the statistics the backward
+ * reads.  Same formulas and arguments as dart_sma_fwd, and
+ * out: o [B,L,H,P] f32, the readout before the gate (0 for chunk-0 tokens);
+ *      lse [B,H,L] f32, the softmax log-normaliser of each token in base-2
+ *      units of the scaled score, log2 Σ_c 2^(s_{t,c}·log2(e)) (0 for
+ *      chunk-0 tokens).
+ */
+dart_status dart_sma_fwd_train(const dart_dims* dims, const void* Q, const void* E,
+                               const void* C, const void* dH, const void* y_ssd, float gate,
+                               void* y, void* o, float* lse, void* stream);
+
+/*
+ * Backward of SMA and the gated add (the reverse-mode derivative of
+ * dart_sma_fwd; Pith review of DART, "Core claim": the path is trained end
+ * to end).  With do_t = gate·dy_t, α the softmax weights (recomputed from
+ * lse) and D_t = do_t·o_t, for token t of chunk k and memory c < k:
+ *   ds      = α·(do_t·(C_tᵀ·dH[c]) − D_t)
+ *   dE_t    = Σ_c ds·dH[c]ᵀ·Q_t / sqrt(N)
+ *   dQ_t    = Σ_c ds·dH[c]·E_t / sqrt(N)      (summed over the group's heads)
+ *   dC_t    = Σ_c α·dH[c]·do_t                (SMA part; summed likewise)
+ *   ddH[c]  = Σ_t ds·Q_t E_tᵀ / sqrt(N) + α·C_t do_tᵀ
+ *   dgate   = Σ dy·o;   the gradient of y_ssd is dy itself (not written).
+ * in:  Q, C [B,L,G,N], E [B,L,H,P], dH [B,H,M,P,N] (io), o [B,L,H,P] f32 and
+ *      lse [B,H,L] f32 (both from dart_sma_fwd_train), dy [B,L,H,P] io, gate
+ * out: dQ, dC [B,L,G,N] f32; dE [B,L,H,P] f32; ddH [B,H,M,P,N] f32;
+ *      dgate: one f32 (device memory)
+ * workspace: device memory of at least dart_sma_bwd_workspace(dims) bytes.
+ * Compiled for bf16 io with P <= 64 and chunks that are multiples of 64;
+ * other dims return DART_ERR_UNSUPPORTED.
+ */
+size_t dart_sma_bwd_workspace(const dart_dims* dims);
+dart_status dart_sma_bwd(const dart_dims* dims, const void* Q, const void* E, const void* C,
+                         const void* dH, const void* o, const float* lse, const void* dy,
+                         float gate, float* dQ, float* dE, float* dC, float* ddH, float* dgate,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace dart_sma_decode needs for these dims (a
  * multiple of 256; 0 if the dims are invalid). */
 size_t dart_sma_decode_workspace(const dart_decode_dims* dims);

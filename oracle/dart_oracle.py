@@ -79,6 +79,7 @@ __all__ = [
     "decode_step_fp8",
     "sma_backward",
     "gated_backward",
+    "sma_logsumexp",
 ]
 
 
@@ -295,6 +296,25 @@ def sma_backward(Q, E, C, dH, S, do):
         dQ[:, :, gmap[h]] += dQh[:, :, h]
         dC[:, :, gmap[h]] += dCh[:, :, h]
     return dQ, dE, dC, ddH
+
+
+def sma_logsumexp(Q, E, C, dH, S):
+    """log Σ_{c<k} exp(s_{t,c}) per token (natural log; the softmax
+    normaliser of :func:`sma`), [B,H,L]; 0 for chunk-0 tokens."""
+    E, dH = _f64(E), _f64(dH)
+    Bsz, L, H, P = E.shape
+    Qh = _per_head(Q, H)
+    N = Qh.shape[-1]
+    out = np.zeros((Bsz, H, L))
+    for b in range(Bsz):
+        for h in range(H):
+            for k in range(1, L // S):
+                ts = np.arange(k * S, (k + 1) * S)
+                keys = np.einsum("cnp,tp->tcn", dH[b, h, :k], E[b, ts, h])
+                sc = np.einsum("tn,tcn->tc", Qh[b, ts, h], keys) / math.sqrt(N)
+                m = np.max(sc, axis=1)
+                out[b, h, ts] = m + np.log(np.sum(np.exp(sc - m[:, None]), axis=1))
+    return out
 
 
 def gated_backward(dy, o, g):

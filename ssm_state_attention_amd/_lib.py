@@ -51,11 +51,17 @@ _SIG = {
                             _F, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "dart_cache_fp8_store": [ctypes.POINTER(DartDecodeDims), _VP, ctypes.c_int64, ctypes.c_int64,
                              _VP, _VP, _VP],
+    "dart_sma_fwd_train": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _F, _VP, _VP, _VP,
+                           _VP],
+    "dart_sma_bwd_workspace": [ctypes.POINTER(DartDims)],
+    "dart_sma_bwd": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F, _VP, _VP,
+                     _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "dart_validate_dims": [ctypes.POINTER(DartDims)],
     "dart_validate_decode_dims": [ctypes.POINTER(DartDecodeDims)],
     "dart_status_str": [ctypes.c_int],
 }
-_RES = {"dart_sma_decode_workspace": ctypes.c_size_t, "dart_status_str": ctypes.c_char_p}
+_RES = {"dart_sma_decode_workspace": ctypes.c_size_t, "dart_sma_bwd_workspace": ctypes.c_size_t,
+        "dart_status_str": ctypes.c_char_p}
 
 _lib = None
 

@@ -132,6 +132,60 @@ def dart_sma_fwd_decayed(Q, E, C, dH, acum, y_ssd, gate, y, chunk):
           "dart_sma_fwd_decayed")
 
 
+def dart_sma_fwd_train(Q, E, C, dH, y_ssd, gate, y, o, lse, chunk):
+    """SMA + gated add that also writes o [B,L,H,P] f32 and lse [B,H,L] f32
+    for the backward (see include/dart.h)."""
+    B, L, H, P = E.shape
+    G, N = Q.shape[2], Q.shape[3]
+    d = DartDims(B, L, H, G, N, P, int(chunk), _io_code(E.dtype))
+    M, io, dev = L // chunk, E.dtype, E.device
+    args = [_ptr(Q, "Q", io, (B, L, G, N), dev), _ptr(E, "E", io, (B, L, H, P), dev),
+            _ptr(C, "C", io, (B, L, G, N), dev), _ptr(dH, "dH", io, (B, H, M, P, N), dev),
+            _ptr(y_ssd, "y_ssd", io, (B, L, H, P), dev)]
+    outs = [_ptr(y, "y", io, (B, L, H, P), dev), _ptr(o, "o", torch.float32, (B, L, H, P), dev),
+            _ptr(lse, "lse", torch.float32, (B, H, L), dev)]
+    check(lib().dart_sma_fwd_train(d, *args, float(gate), *outs, _stream()),
+          "dart_sma_fwd_train")
+
+
+def dart_sma_bwd_workspace(dims):
+    """Workspace bytes for dart_sma_bwd (0 for unsupported dims)."""
+    return int(lib().dart_sma_bwd_workspace(dims))
+
+
+def dart_sma_bwd(Q, E, C, dH, o, lse, dy, gate, chunk, out=None):
+    """Backward of SMA + gated add (see include/dart.h).  Returns a dict of
+    f32 device tensors dQ, dC [B,L,G,N], dE [B,L,H,P], ddH [B,H,M,P,N] and
+    dgate [1]; ``out`` may hold preallocated ones plus "workspace"."""
+    B, L, H, P = E.shape
+    G, N = Q.shape[2], Q.shape[3]
+    d = DartDims(B, L, H, G, N, P, int(chunk), _io_code(E.dtype))
+    M, io, dev = L // chunk, E.dtype, E.device
+    ws = dart_sma_bwd_workspace(d)
+    if ws == 0:
+        raise ValueError("dart_sma_bwd: unsupported dimensions")
+    f32 = dict(dtype=torch.float32, device=dev)
+    if out is None:
+        out = {"dQ": torch.empty(B, L, G, N, **f32), "dC": torch.empty(B, L, G, N, **f32),
+               "dE": torch.empty(B, L, H, P, **f32), "ddH": torch.empty(B, H, M, P, N, **f32),
+               "dgate": torch.empty(1, **f32),
+               "workspace": torch.empty(ws, dtype=torch.uint8, device=dev)}
+    args = [_ptr(Q, "Q", io, (B, L, G, N), dev), _ptr(E, "E", io, (B, L, H, P), dev),
+            _ptr(C, "C", io, (B, L, G, N), dev), _ptr(dH, "dH", io, (B, H, M, P, N), dev),
+            _ptr(o, "o", torch.float32, (B, L, H, P), dev),
+            _ptr(lse, "lse", torch.float32, (B, H, L), dev),
+            _ptr(dy, "dy", io, (B, L, H, P), dev)]
+    outs = [_ptr(out["dQ"], "dQ", torch.float32, (B, L, G, N), dev),
+            _ptr(out["dE"], "dE", torch.float32, (B, L, H, P), dev),
+            _ptr(out["dC"], "dC", torch.float32, (B, L, G, N), dev),
+            _ptr(out["ddH"], "ddH", torch.float32, (B, H, M, P, N), dev),
+            _ptr(out["dgate"], "dgate", torch.float32, (1,), dev)]
+    wsp = _ptr(out["workspace"], "workspace", torch.uint8, None, dev)
+    check(lib().dart_sma_bwd(d, *args, float(gate), *outs, wsp, out["workspace"].numel(),
+                             _stream()), "dart_sma_bwd")
+    return out
+
+
 def decode_dims(batch, nheads, ngroups, dstate, headdim, chunk, max_chunks, dtype):
     return DartDecodeDims(batch, nheads, ngroups, dstate, headdim, int(chunk), int(max_chunks),
                           _io_code(dtype))

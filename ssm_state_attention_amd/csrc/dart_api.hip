@@ -82,13 +82,15 @@ struct SmaFwdFn {
   const void* prior;
   int k0, pstride;
   hipStream_t st;
+  void* o = nullptr;
+  float* lse = nullptr;
   template <typename T, int N, int P>
   hipError_t run() {
     return dart::launch_sma_fwd<T, N, P>(sh, static_cast<const T*>(Q), static_cast<const T*>(E),
                                          static_cast<const T*>(C), static_cast<const T*>(dH),
                                          static_cast<const T*>(y_ssd), acum, gate,
                                          static_cast<T*>(y), static_cast<const T*>(prior), k0,
-                                         pstride, st);
+                                         pstride, static_cast<float*>(o), lse, st);
   }
 };
 
@@ -125,6 +127,30 @@ struct Fp8StoreFn {
                                            st);
   }
 };
+
+struct SmaBwdFn {
+  dart::PrefillShape sh;
+  const void *Q, *E, *C, *dH, *o;
+  const float* lse;
+  const void* dy;
+  float gate;
+  float *dQ, *dE, *dC, *ddH, *dgate;
+  void* ws;
+  hipStream_t st;
+  template <typename T, int N, int P>
+  hipError_t run() {
+    return dart::launch_sma_bwd<T, N, P>(
+        sh, static_cast<const T*>(Q), static_cast<const T*>(E), static_cast<const T*>(C),
+        static_cast<const T*>(dH), static_cast<const float*>(o), lse, static_cast<const T*>(dy), gate,
+        dQ, dE, dC, ddH, dgate, ws, st);
+  }
+};
+
+// The backward is compiled for 16-bit io with P <= 64 and chunks of whole
+// 64-token tiles.
+bool bwd_supported(const dart_dims* d) {
+  return d->io == DART_BF16 && d->headdim <= 64 && d->chunk % 64 == 0;
+}
 
 dart::DecodeShape decode_shape(const dart_decode_dims* d) {
   return {static_cast<int>(d->batch),      static_cast<int>(d->nheads),
@@ -165,6 +191,18 @@ extern "C" dart_status dart_sma_fwd(const dart_dims* dims, const void* Q, const 
   if ((s = check_ptrs(Q, E, C, dH, y_ssd, y)) != DART_OK) return s;
   SmaFwdFn fn{prefill_shape(dims), Q, E, C, dH, y_ssd, nullptr, gate, y, nullptr, 0, 0,
               static_cast<hipStream_t>(stream)};
+  return dispatch(dims->io, dims->dstate, dims->headdim, fn);
+}
+
+extern "C" dart_status dart_sma_fwd_train(const dart_dims* dims, const void* Q, const void* E,
+                                          const void* C, const void* dH, const void* y_ssd,
+                                          float gate, void* y, void* o, float* lse,
+                                          void* stream) {
+  dart_status s = dart_validate_dims(dims);
+  if (s != DART_OK) return s;
+  if ((s = check_ptrs(Q, E, C, dH, y_ssd, y, o, lse)) != DART_OK) return s;
+  SmaFwdFn fn{prefill_shape(dims), Q, E, C, dH, y_ssd, nullptr, gate, y, nullptr, 0, 0,
+              static_cast<hipStream_t>(stream), o, lse};
   return dispatch(dims->io, dims->dstate, dims->headdim, fn);
 }
 
@@ -246,5 +284,27 @@ extern "C" dart_status dart_cache_fp8_store(const dart_decode_dims* dims, const 
                 static_cast<int>(n_mem), static_cast<int>(first),
                 static_cast<int>(dims->max_chunks), dH_f32, cache8, scale,
                 static_cast<hipStream_t>(stream)};
+  return dispatch(dims->io, dims->dstate, dims->headdim, fn);
+}
+
+extern "C" size_t dart_sma_bwd_workspace(const dart_dims* dims) {
+  if (dart_validate_dims(dims) != DART_OK || !bwd_supported(dims)) return 0;
+  return (dart::sma_bwd_workspace_bytes(dims->batch, dims->seqlen, dims->nheads) + 255) / 256 *
+         256;
+}
+
+extern "C" dart_status dart_sma_bwd(const dart_dims* dims, const void* Q, const void* E,
+                                    const void* C, const void* dH, const void* o,
+                                    const float* lse, const void* dy, float gate, float* dQ,
+                                    float* dE, float* dC, float* ddH, float* dgate,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  dart_status s = dart_validate_dims(dims);
+  if (s != DART_OK) return s;
+  if (!bwd_supported(dims)) return DART_ERR_UNSUPPORTED;
+  if ((s = check_ptrs(Q, E, C, dH, o, lse, dy, dQ, dE, dC, ddH, dgate)) != DART_OK) return s;
+  if (!workspace || workspace_bytes < dart_sma_bwd_workspace(dims)) return DART_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DART_ERR_ALIGN;
+  SmaBwdFn fn{prefill_shape(dims), Q, E, C, dH, o, lse, dy, gate, dQ, dE, dC, ddH, dgate,
+              workspace, static_cast<hipStream_t>(stream)};
   return dispatch(dims->io, dims->dstate, dims->headdim, fn);
 }

@@ -25,13 +25,15 @@ hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt,
                              const float* h0, T* H_in, float* h_final, T* y_ssd,
                              hipStream_t st);
 
-template <typename T, int N, int P>
 // acum == nullptr: the SMA of the pages; otherwise the decay-included variant.
 // k0 > 0: the tokens continue sequences whose first k0 memories are in prior
-// (pstride memories per (batch, head)).
+// (pstride memories per (batch, head)).  o != nullptr: also write the readout
+// o [B,L,H,P] (f32) and the base-2 log-normaliser lse [B,H,L] for the backward.
+template <typename T, int N, int P>
 hipError_t launch_sma_fwd(const PrefillShape& s, const T* Q, const T* E, const T* C,
                           const T* dH, const T* y_ssd, const float* acum, float gate, T* y,
-                          const T* prior, int k0, int pstride, hipStream_t st);
+                          const T* prior, int k0, int pstride, float* o, float* lse,
+                          hipStream_t st);
 
 // cache8 == nullptr: the cache is `cache` in the io type; otherwise it is
 // the fp8 code array cache8 with one scale per memory in cscale.
@@ -46,6 +48,16 @@ hipError_t launch_sma_decode(const DecodeShape& s, const T* x, const float* dt, 
 template <typename T, int N, int P>
 hipError_t launch_fp8_store(int B, int H, int n_mem, int first, int max_chunks, const float* src,
                             uint8_t* cache8, float* cscale, hipStream_t st);
+
+// SMA backward (16-bit io, P <= 64): dQ, dC [B,L,G,N], dE [B,L,H,P], ddH
+// [B,H,M,P,N] and dgate (all f32) from the training forward's o and lse and
+// the upstream gradient dy; workspace of sma_bwd_workspace_bytes().
+template <typename T, int N, int P>
+hipError_t launch_sma_bwd(const PrefillShape& s, const T* Q, const T* E, const T* C,
+                          const T* dH, const float* o, const float* lse, const T* dy, float gate,
+                          float* dQ, float* dE, float* dC, float* ddH, float* dgate,
+                          void* workspace, hipStream_t st);
+size_t sma_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H);
 
 }  // namespace dart
 

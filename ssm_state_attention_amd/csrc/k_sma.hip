@@ -157,6 +157,21 @@ struct SmaMath16 {
       for (int pb = 0; pb < NPB; ++pb) acc[tb][pb] += pv * zc[tb][pb];
     }
   }
+  // Training statistics of the tile's tokens: the readout o_t (before the
+  // gate) to o rows [t][stride] and the softmax log-normaliser in the
+  // kernel's base-2 score units, lse_t = mx + log2(ls), to lse[t]; both 0
+  // for tokens that see no memory.
+  __device__ __forceinline__ void stats(float* o, long ostride, float* lse, bool any) {
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+      const float inv = any ? 1.f / ls[tb] : 0.f;
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb)
+        *reinterpret_cast<floatx4*>(o + lrow(tb) * ostride + pb * 16 + 4 * grp) =
+            inv * acc[tb][pb];
+      if (grp == 0) lse[lrow(tb)] = any ? mx[tb] + __builtin_amdgcn_logf(ls[tb]) : 0.f;
+    }
+  }
   // y = y_ssd + gate·o in the LDS rows [t][p] that hold y_ssd
   __device__ __forceinline__ void finish(T* ty, int ld, float gate, bool any) {
 #pragma unroll
@@ -209,7 +224,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     const T* __restrict__ Q, const T* __restrict__ E, const T* __restrict__ C,
     const T* __restrict__ dH, const T* __restrict__ y_ssd, const float* __restrict__ acum,
     float gate, T* __restrict__ y, int BH, int L, int H, int G, int S, int npq, int bg_major,
-    float scale_log2, const T* __restrict__ prior, int k0, int pstride) {
+    float scale_log2, const T* __restrict__ prior, int k0, int pstride,
+    float* __restrict__ o_out, float* __restrict__ lse_out) {
   using MM = Mma<T>;
   constexpr int K = MM::K, KL = MM::KL, VE = Vec16<T>::n;
   // LDS row strides (elements): a 32-byte pad keeps the 16-byte fragment reads
@@ -418,6 +434,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   }
 
   // ---- epilogue: y = y_ssd + gate·o in LDS, then whole-row stores ----
+  if (o_out)
+    tm.stats(o_out + (row0 * H + h) * P, (long)H * P,
+             lse_out + (long)pair * L + (long)kl * S + sub * TWG, k > 0);
   tm.finish(sh_ty, LDE, gate, k > 0);
   __syncthreads();
 #pragma unroll
@@ -431,7 +450,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
 template <typename T, int N, int P, int NTB, int WAVES>
 hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T* C, const T* dH,
                          const T* y_ssd, const float* acum, float gate, T* y, const T* prior,
-                         int k0, int pstride, hipStream_t st) {
+                         int k0, int pstride, float* o, float* lse, hipStream_t st) {
   const int M = s.L / s.S;
   const int BH = s.B * s.H;
   const int hpg = s.H / s.G;
@@ -444,11 +463,11 @@ hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T*
   if (acum)
     hipLaunchKernelGGL((k_sma_fwd<T, N, P, NTB, WAVES, true>), dim3(blocks), dim3(64 * WAVES), 0,
                        st, Q, E, C, dH, y_ssd, acum, gate, y, BH, s.L, s.H, s.G, s.S, npq,
-                       bg_major, scale_log2, prior, k0, pstride);
+                       bg_major, scale_log2, prior, k0, pstride, o, lse);
   else
     hipLaunchKernelGGL((k_sma_fwd<T, N, P, NTB, WAVES, false>), dim3(blocks), dim3(64 * WAVES), 0,
                        st, Q, E, C, dH, y_ssd, acum, gate, y, BH, s.L, s.H, s.G, s.S, npq,
-                       bg_major, scale_log2, prior, k0, pstride);
+                       bg_major, scale_log2, prior, k0, pstride, o, lse);
   return hipGetLastError();
 }
 
@@ -457,27 +476,28 @@ hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T*
 template <typename T, int N, int P>
 hipError_t launch_sma_fwd(const PrefillShape& s, const T* Q, const T* E, const T* C,
                           const T* dH, const T* y_ssd, const float* acum, float gate, T* y,
-                          const T* prior, int k0, int pstride, hipStream_t st) {
+                          const T* prior, int k0, int pstride, float* o, float* lse,
+                          hipStream_t st) {
   constexpr int NTB = SmaTile<N, P>::NTB;
   const int r = s.S / (16 * NTB);  // S % 32 == 0, so r >= 1
   if (r % 8 == 0)
     return sma_fwd_waves<T, N, P, NTB, 8>(s, Q, E, C, dH, y_ssd, acum, gate, y, prior, k0,
-                                           pstride, st);
+                                           pstride, o, lse, st);
   if (r % 4 == 0)
     return sma_fwd_waves<T, N, P, NTB, 4>(s, Q, E, C, dH, y_ssd, acum, gate, y, prior, k0,
-                                           pstride, st);
+                                           pstride, o, lse, st);
   if (r % 2 == 0)
     return sma_fwd_waves<T, N, P, NTB, 2>(s, Q, E, C, dH, y_ssd, acum, gate, y, prior, k0,
-                                           pstride, st);
+                                           pstride, o, lse, st);
   return sma_fwd_waves<T, N, P, NTB, 1>(s, Q, E, C, dH, y_ssd, acum, gate, y, prior, k0, pstride,
-                                        st);
+                                        o, lse, st);
 }
 
 
 #define DART_INST_SMA(T, N, P)                                                                 \
   template hipError_t launch_sma_fwd<T, N, P>(const PrefillShape&, const T*, const T*, const T*, \
                                               const T*, const T*, const float*, float, T*,   \
-                                              const T*, int, int, hipStream_t);
+                                              const T*, int, int, float*, float*, hipStream_t);
 DART_FOR_EACH_SHAPE(DART_INST_SMA)
 
 }  // namespace dart

@@ -594,4 +594,24 @@ def pin_gated_backward(orc):
     num = _fd_grad(lambda: float(np.sum(dy * orc.gated_output(ys, o, g[0]))), g)
     _close(np.array([dg]), num, 1e-7, "dg")
 
+
+def pin_sma_logsumexp(orc):
+    """One visible memory: the normaliser is the score itself; Q = 0 (all
+    scores 0): it is log k for chunk k."""
+    rng = np.random.default_rng(94)
+    B, L, H, G, N, P, S = 1, 12, 2, 1, 3, 2, 4
+    Q = rng.standard_normal((B, L, G, N))
+    E = rng.standard_normal((B, L, H, P))
+    C = rng.standard_normal((B, L, G, N))
+    dH = rng.standard_normal((B, H, 3, N, P))
+    lse = orc.sma_logsumexp(Q, E, C, dH, S)
+    for h in range(H):
+        for t in range(S, 2 * S):
+            want = Q[0, t, 0] @ (dH[0, h, 0] @ E[0, t, h]) / math.sqrt(N)
+            _close(lse[0, h, t], want, 1e-12, "one-memory normaliser")
+    lse0 = orc.sma_logsumexp(np.zeros_like(Q), E, C, dH, S)
+    for t in range(L):
+        want = 0.0 if t < S else math.log(t // S)
+        _close(lse0[0, :, t], np.full(H, want), 1e-12, "uniform normaliser")
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

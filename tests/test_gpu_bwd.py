@@ -1,0 +1,142 @@
+"""GPU parity of the SMA backward (and of the training forward's statistics)
+against the fp64 oracle on the same seeded inputs.
+
+Bar: bfloat16 inputs with fp32 accumulation, so every output tensor meets
+max|gpu - ref| <= 2e-2 * max|ref| (the gradients are f32 tensors, but the
+kernels round their MFMA operands to bf16 as the forward does); the gate
+gradient is a scalar and meets |gpu - ref| <= 2e-2 * |ref| (the readout o
+it sums is kept in f32 by the training forward, so the cancellation in
+Σ dy·o does not amplify a bf16 rounding).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ssm_state_attention_amd import api, synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+BF = torch.bfloat16
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def assert_parity(gpu, ref, what):
+    g = gpu if isinstance(gpu, np.ndarray) else synth.as_f64(gpu)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert g.shape == ref.shape, f"{what}: shape {g.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = float(np.max(np.abs(g - ref))) if g.size else 0.0
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    bound = 2e-2 * scale
+    print(f"{what}: max err {err:.3e} bound {bound:.3e} (max|ref| {scale:.3e})", flush=True)
+    assert err <= bound, f"{what}: max err {err:.3e} > bound {bound:.3e}"
+
+
+def _pn_to_np(t):
+    """Library layout [..., P, N] -> oracle layout [..., N, P]."""
+    return np.swapaxes(synth.as_f64(t), -1, -2)
+
+
+def _inputs(seed, B, L, H, G, N, P, S, qscale, mem_std):
+    """Prefill token inputs (synth recipe), memories N(0, mem_std²) and an
+    upstream gradient dy ~ N(0, 1), all bf16."""
+    inp = synth.draw_prefill(seed, B, L, H, G, N, P, io=BF, qscale=qscale)
+    inp["dH"] = synth.draw_state(seed + 1, (B, H, L // S, P, N), mem_std, BF)
+    inp["dy"] = synth.draw_state(seed + 2, (B, L, H, P), 1.0, BF)
+    inp["y_ssd"] = synth.draw_state(seed + 3, (B, L, H, P), 1.0, BF)
+    return inp
+
+
+def _gpu_train(d, gate, S):
+    B, L, H, P = d["E"].shape
+    y = torch.empty(B, L, H, P, dtype=BF, device=DEV)
+    o = torch.empty(B, L, H, P, dtype=torch.float32, device=DEV)
+    lse = torch.empty(B, H, L, dtype=torch.float32, device=DEV)
+    api.dart_sma_fwd_train(d["Q"], d["E"], d["C"], d["dH"], d["y_ssd"], gate, y, o, lse, S)
+    grads = api.dart_sma_bwd(d["Q"], d["E"], d["C"], d["dH"], o, lse, d["dy"], gate, S)
+    torch.cuda.synchronize()
+    return y, o, lse, grads
+
+
+@pytest.mark.parametrize("B,L,H,G,N,P,S,qscale,mem_std", [
+    (1, 256, 2, 1, 32, 32, 64, 1.0, 0.05),      # heads share a group; 4 chunks
+    (2, 384, 4, 2, 64, 64, 128, 30.0, 0.05),    # sharpened softmax
+    (1, 768, 3, 3, 128, 64, 256, 1.0, 0.05),    # the layer's N, P, S
+    (2, 512, 8, 1, 128, 64, 128, 100.0, 0.02),  # one group of 8 heads, sharpened
+])
+def test_sma_backward(B, L, H, G, N, P, S, qscale, mem_std):
+    _need_gpu()
+    print(f"sma backward case B{B} L{L} H{H} G{G} N{N} P{P} S{S} qscale{qscale}", flush=True)
+    gate = 0.7
+    inp = _inputs(11, B, L, H, G, N, P, S, qscale, mem_std)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    y, o, lse, gr = _gpu_train(d, gate, S)
+    # the training forward's y is the plain forward's, bit for bit
+    y_plain = torch.empty_like(y)
+    api.dart_sma_fwd(d["Q"], d["E"], d["C"], d["dH"], d["y_ssd"], gate, y_plain, S)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_plain)
+    n = {k: synth.as_f64(v) for k, v in inp.items()}
+    dHo = np.swapaxes(n["dH"], -1, -2)
+    o_ref = oracle.sma(n["Q"], n["E"], n["C"], dHo, S)
+    lse_ref = oracle.sma_logsumexp(n["Q"], n["E"], n["C"], dHo, S)
+    assert_parity(o, o_ref, "o")
+    assert_parity(synth.as_f64(lse) * math.log(2.0), lse_ref, "lse")
+    _, do, dg = oracle.gated_backward(n["dy"], o_ref, gate)
+    dQ, dE, dC, ddH = oracle.sma_backward(n["Q"], n["E"], n["C"], dHo, S, do)
+    assert_parity(gr["dQ"], dQ, "dQ")
+    assert_parity(gr["dE"], dE, "dE")
+    assert_parity(gr["dC"], dC, "dC")
+    assert_parity(_pn_to_np(gr["ddH"]), ddH, "ddH")
+    dg_gpu = float(gr["dgate"].item())
+    print(f"dgate {dg_gpu:.6e} ref {dg:.6e}", flush=True)
+    assert abs(dg_gpu - dg) <= 2e-2 * abs(dg)
+
+
+def test_sma_backward_rejects_unsupported():
+    _need_gpu()
+    d = {k: v.to(DEV) for k, v in _inputs(12, 1, 64, 1, 1, 32, 32, 32, 1.0, 0.05).items()}
+    with pytest.raises(ValueError, match="unsupported"):
+        _gpu_train(d, 0.5, 32)  # chunk of 32 tokens: not a whole 64-token tile
+
+
+def test_sma_backward_full_size_sampled_group():
+    """The Mamba-2 ~370M layer shape (batch 4, 32 heads in groups of 8,
+    L=8192, S=256, N=128, P=64): the whole backward on the GPU; the oracle
+    computes one (batch, group) in full (its 8 heads, so dQ and dC are the
+    group sums) and the GPU's tensors for it are compared."""
+    _need_gpu()
+    B, L, H, G, N, P, S, gate = 4, 8192, 32, 4, 128, 64, 256, 0.5
+    inp = _inputs(13, B, L, H, G, N, P, S, 1.0, 0.05)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    y, o, lse, gr = _gpu_train(d, gate, S)
+    b, g = 2, 1
+    hs = slice(g * 8, g * 8 + 8)
+    sl = {"Q": inp["Q"][b:b + 1, :, g:g + 1], "C": inp["C"][b:b + 1, :, g:g + 1],
+          "E": inp["E"][b:b + 1, :, hs], "dy": inp["dy"][b:b + 1, :, hs],
+          "dH": inp["dH"][b:b + 1, hs]}
+    n = {k: synth.as_f64(v) for k, v in sl.items()}
+    dHo = np.swapaxes(n["dH"], -1, -2)
+    o_ref = oracle.sma(n["Q"], n["E"], n["C"], dHo, S)
+    assert_parity(o[b:b + 1, :, hs], o_ref, "full-size o (one group)")
+    _, do, _ = oracle.gated_backward(n["dy"], o_ref, gate)
+    dQ, dE, dC, ddH = oracle.sma_backward(n["Q"], n["E"], n["C"], dHo, S, do)
+    assert_parity(gr["dQ"][b:b + 1, :, g:g + 1], dQ, "full-size dQ (one group)")
+    assert_parity(gr["dC"][b:b + 1, :, g:g + 1], dC, "full-size dC (one group)")
+    assert_parity(gr["dE"][b:b + 1, :, hs], dE, "full-size dE (one group)")
+    assert_parity(_pn_to_np(gr["ddH"][b:b + 1, hs]), ddH, "full-size ddH (one group)")
+    # the gate gradient over the whole layer, from the GPU's own o (a
+    # property: dgate = Σ dy·o, whatever o is)
+    prod = synth.as_f64(d["dy"]) * synth.as_f64(o)
+    dg_prop, l1 = float(np.sum(prod)), float(np.sum(np.abs(prod)))
+    # f32 summation of the 33.5 M products in the kernels' order: within
+    # 1e-4 of the sum of their magnitudes
+    assert abs(float(gr["dgate"].item()) - dg_prop) <= 1e-4 * l1

@@ -7,7 +7,8 @@ B/C/Q, L = 8192, S = 256, N = 128, P = 64, bfloat16 inputs with fp32
 accumulation.  `value` is prefill tokens/s (batch·L / step time).  The
 decode step over a 4 GiB chunk-memory cache (batch 64, 32 heads, 128
 cached chunks) is timed in the same run and reported under "decode", and
-the same step over the fp8 (E4M3) cache under "decode_fp8".
+the same step over the fp8 (E4M3) cache under "decode_fp8"; the SMA backward at
+the prefill shape is reported under "backward".
 
 Prints one JSON line.  `python bench.py --steps K --warmup W`.
 """
@@ -76,6 +77,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
@@ -165,6 +167,54 @@ def bench_prefill(args, torch, api, synth):
         },
         "mfma_frac_whole_prefill": (flops_sma + flops_scan) / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
         "inputs": inp,
+    }
+
+
+def sma_bwd_flops(c):
+    """Algorithmic SMA backward FLOPs per visible (token, memory) pair:
+    Zq and Zc again (4·N·P, the softmax weights are not stored), dQ and dC
+    (2·N·P each) and the two outer products of dDeltaH (4·N·P): 12·N·P."""
+    return 3.0 * sma_flops(c)
+
+
+def bench_backward(args, torch, api, synth, inp):
+    """The SMA backward at the prefill shape: dart_sma_fwd_train once, then
+    dart_sma_bwd timed (memories from the prefill, dy ~ N(0, 1))."""
+    c = BASE
+    B, L, H, G, N, P, S = c["B"], c["L"], c["H"], c["G"], c["N"], c["P"], c["S"]
+    d = {k: v.to("cuda:0") for k, v in inp.items()}
+    pre = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], c["gate"], S)
+    dy = synth.draw_state(60, (B, L, H, P), 1.0, torch.bfloat16, device="cuda:0")
+    f32 = dict(dtype=torch.float32, device="cuda:0")
+    y = torch.empty(B, L, H, P, dtype=torch.bfloat16, device="cuda:0")
+    o, lse = torch.empty(B, L, H, P, **f32), torch.empty(B, H, L, **f32)
+    api.dart_sma_fwd_train(d["Q"], d["E"], d["C"], pre["dH"], pre["y_ssd"], c["gate"], y, o, lse,
+                           S)
+    out = api.dart_sma_bwd(d["Q"], d["E"], d["C"], pre["dH"], o, lse, dy, c["gate"], S)
+
+    def step():
+        api.dart_sma_bwd(d["Q"], d["E"], d["C"], pre["dH"], o, lse, dy, c["gate"], S, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms, med, mn = timed_steps(torch, step, args.steps)
+    fl = sma_bwd_flops(c)
+    return {
+        "metric": "SMA backward TFLOP/s (algorithmic)",
+        "value": fl / (ms / 1e3) / 1e12,
+        "unit": "TFLOP/s",
+        "ms_per_step": ms,
+        "ms_median": med,
+        "ms_min": mn,
+        "algorithmic_gflop": fl / 1e9,
+        "config": {"workload": "DART SMA backward at the prefill shape", "batch": B,
+                   "seqlen": L, "heads": H, "groups": G, "dstate": N, "headdim": P, "chunk": S,
+                   "io": "bf16", "gradients": "f32"},
+        "roofline": {"kernel": "dart_sma_bwd", "bound": "mfma",
+                     "achieved": fl / (ms / 1e3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": fl / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                     "traffic": None},
     }
 
 
@@ -381,6 +431,9 @@ def main():
                                                    "sma_ms_min")}
         result["mfma_frac_whole_prefill"] = pre["mfma_frac_whole_prefill"]
         result["algorithmic_gflop_per_step"] = {k: v / 1e9 for k, v in pre["flops"].items()}
+    if not args.no_backward and pre is not None:
+        torch.cuda.empty_cache()
+        result["backward"] = bench_backward(args, torch, api, synth, pre["inputs"])
     if not args.no_decode:
         torch.cuda.empty_cache()
         result["decode"] = bench_decode(args, torch, api, synth)

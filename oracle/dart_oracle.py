@@ -80,6 +80,7 @@ __all__ = [
     "sma_backward",
     "gated_backward",
     "sma_logsumexp",
+    "ssd_backward",
 ]
 
 
@@ -202,6 +203,97 @@ def chunk_output(x, dt, A, Bm, C, H_in, S):
         inter = np.einsum("bthn,bhnp->bthp", Ch[:, sl], H_in[:, :, k])
         y[:, sl] = intra + np.exp(cs * A)[..., None] * inter
     return y
+
+
+def ssd_backward(x, dt, A, Bm, C, S, dy, ddH=None, dh_final=None, h0=None):
+    """Gradients through the chunked scan (reverse of :func:`chunk_states`,
+    :func:`state_pass` and :func:`chunk_output`) [pith-axioms;
+    pith-carries].  Upstream gradients: dy of y_ssd [B,L,H,P], ddH of the
+    chunk memories [B,H,M,N,P] (e.g. from SMA) and dh_final of the final
+    state [B,H,N,P]; the last two default to zero.
+
+    With u_t = A·Σ_{l=kS}^{t} dt_l (the log-decay from the start of token
+    t's chunk k to t) and U_c = u at the last token of chunk c:
+      intra  y_t += Σ_{j<=t} (C_t·B_j)·exp(u_t − u_j)·dt_j·x_j
+      inter  y_t += exp(u_t)·C_tᵀH_in[k]
+      state  H_in[c+1] = exp(U_c)·H_in[c] + ΔH[c]
+      memory ΔH[c] = Σ_i exp(U_c − u_i)·dt_i·B_i x_iᵀ
+    each term is differentiated in turn, the state recursion last chunk
+    first, and the log-decays u pass their gradient to dt and A at the end.
+    B and C are shared by the heads of a group, so dB and dC are summed over
+    them.  Returns a dict with dx [B,L,H,P], ddt [B,L,H], dA [H],
+    dB [B,L,G,N], dC [B,L,G,N] and dh0 [B,H,N,P]."""
+    x, dt, A, dy = _f64(x), _f64(dt), _f64(A), _f64(dy)
+    Bsz, L, H, P = x.shape
+    M = L // S
+    G = np.shape(Bm)[2]
+    Bh, Ch = _per_head(Bm, H), _per_head(C, H)
+    N = Bh.shape[-1]
+    H_in = state_pass(chunk_states(x, dt, A, Bm, S), dt, A, S, h0)
+    dx, ddt, dA = np.zeros_like(x), np.zeros_like(dt), np.zeros(H)
+    dBh, dCh = np.zeros((Bsz, L, H, N)), np.zeros((Bsz, L, H, N))
+    dh0 = np.zeros((Bsz, H, N, P))
+    causal = np.tril(np.ones((S, S), dtype=bool))                   # j <= t
+    for b in range(Bsz):
+        for h in range(H):
+            a = A[h]
+            du = np.zeros(L)                    # ∂loss/∂u_t
+            dHin = np.zeros((M + 1, N, P))      # ∂loss/∂H_in[c] through the outputs
+            if dh_final is not None:
+                dHin[M] = _f64(dh_final)[b, h]
+            chunks = []
+            for k in range(M):
+                ts = np.arange(k * S, (k + 1) * S)
+                xk, Bk, Ck = x[b, ts, h], Bh[b, ts, h], Ch[b, ts, h]
+                dyk, dtk = dy[b, ts, h], dt[b, ts, h]
+                u = a * np.cumsum(dtk)
+                chunks.append((ts, xk, Bk, dtk, u))
+                # intra-chunk term
+                dec = np.where(causal, np.exp(np.where(causal, u[:, None] - u[None, :], 0.0)), 0.0)
+                cb = Ck @ Bk.T                                      # [t,j]
+                dx[b, ts, h] += (cb * dec * dtk[None, :]).T @ dyk
+                dw = np.where(causal, dyk @ xk.T, 0.0)              # ∂/∂ of each product term
+                dcb = dw * dec * dtk[None, :]
+                dCh[b, ts, h] += dcb @ Bk
+                dBh[b, ts, h] += dcb.T @ Ck
+                ddt[b, ts, h] += np.sum(dw * cb * dec, axis=0)
+                g = dw * cb * dtk[None, :] * dec                    # ∂/∂(u_t − u_j)
+                du[ts] += g.sum(axis=1) - g.sum(axis=0)
+                # inter-chunk term
+                eu = np.exp(u)
+                dCh[b, ts, h] += eu[:, None] * (dyk @ H_in[b, h, k].T)
+                dHin[k] += (eu[:, None] * Ck).T @ dyk
+                du[ts] += eu * np.sum(dyk * (Ck @ H_in[b, h, k]), axis=1)
+            # state passing, last chunk first
+            dmem = np.zeros((M, N, P))
+            Gs = dHin[M].copy()
+            for c in range(M - 1, -1, -1):
+                ts, _, _, _, u = chunks[c]
+                dmem[c] = Gs + (0.0 if ddH is None else _f64(ddH)[b, h, c])
+                du[ts[-1]] += np.sum(Gs * np.exp(u[-1]) * H_in[b, h, c])
+                Gs = np.exp(u[-1]) * Gs + dHin[c]
+            dh0[b, h] = Gs
+            # chunk memories
+            for c in range(M):
+                ts, xk, Bk, dtk, u = chunks[c]
+                wd = np.exp(u[-1] - u)
+                dx[b, ts, h] += (wd * dtk)[:, None] * (Bk @ dmem[c])
+                dBh[b, ts, h] += (wd * dtk)[:, None] * (xk @ dmem[c].T)
+                dwi = np.einsum("in,np,ip->i", Bk, dmem[c], xk)
+                ddt[b, ts, h] += wd * dwi
+                gw = dwi * wd * dtk                                 # ∂/∂(U_c − u_i)
+                du[ts[-1]] += gw.sum()
+                du[ts] -= gw
+            # u_t = a·Σ_{l=kS}^{t} dt_l
+            for ts, _, _, dtk, _ in chunks:
+                ddt[b, ts, h] += a * np.cumsum(du[ts][::-1])[::-1]
+                dA[h] += np.sum(du[ts] * np.cumsum(dtk))
+    gmap = group_of_head(H, G)
+    dB, dC = np.zeros((Bsz, L, G, N)), np.zeros((Bsz, L, G, N))
+    for h in range(H):
+        dB[:, :, gmap[h]] += dBh[:, :, h]
+        dC[:, :, gmap[h]] += dCh[:, :, h]
+    return {"dx": dx, "ddt": ddt, "dA": dA, "dB": dB, "dC": dC, "dh0": dh0}
 
 
 # --------------------------------------------------------------------------

@@ -27,6 +27,10 @@ namespace dart {
 namespace {
 
 
+// (batch, token) rows per workgroup of the dy·o pass (each workgroup leaves
+// one partial of the gate gradient)
+constexpr int kPrepRows = 4;
+
 // Eight values -> an MFMA operand fragment.
 __device__ __forceinline__ bf16x8 pack8(const float (&v)[8]) {
   bf16x8 r;
@@ -38,32 +42,40 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// dy·o for every (batch, token, head): one workgroup per (batch, token)
-// row of H·P values, 16-byte vectors, the P/8 lanes of a head summed by lane
-// exchanges.  The row's Σ dy·o goes to part[row] for the gate gradient.
+// dy·o for every (batch, token, head): each workgroup takes kPrepRows
+// consecutive (batch, token) rows of H·P values (all their loads issued
+// before the first use), 16-byte vectors, the P/8 lanes of a head summed by
+// lane exchanges.  Each workgroup's Σ dy·o goes to part[blockIdx] for the
+// gate gradient.
 template <int P>
 __global__ __launch_bounds__(256) void k_sma_bwd_prep(const bf16* __restrict__ dy,
                                                       const float* __restrict__ o,
                                                       float* __restrict__ dyo,
-                                                      float* __restrict__ part, int L, int H) {
+                                                      float* __restrict__ part, long rows, int L,
+                                                      int H) {
   constexpr int LPH = P / 8;  // lanes per head
   static_assert(LPH <= 64 && 64 % LPH == 0, "prep lanes");
   __shared__ float sh[4];
-  const long row = blockIdx.x;  // b·L + t
-  const int b = static_cast<int>(row / L), t = static_cast<int>(row % L);
+  const int HL = H * LPH;  // 16-byte vectors of dy per row
   float tot = 0.f;
-  for (int i = threadIdx.x; i < H * LPH; i += 256) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(dy + row * H * P + i * 8);
-    const floatx4 c0 = *reinterpret_cast<const floatx4*>(o + row * H * P + i * 8);
-    const floatx4 c1 = *reinterpret_cast<const floatx4*>(o + row * H * P + i * 8 + 4);
+  for (int i = threadIdx.x; i < kPrepRows * HL; i += 256) {
+    const long row = blockIdx.x * kPrepRows + i / HL;
+    const int v = i % HL;
+    bf16x8 a = bf16x8{};
+    floatx4 c0 = floatx4{0.f, 0.f, 0.f, 0.f}, c1 = c0;
+    if (row < rows) {
+      a = *reinterpret_cast<const bf16x8*>(dy + row * H * P + v * 8);
+      c0 = *reinterpret_cast<const floatx4*>(o + row * H * P + v * 8);
+      c1 = *reinterpret_cast<const floatx4*>(o + row * H * P + v * 8 + 4);
+    }
     float d = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) d += to_f32(a[e]) * c0[e] + to_f32(a[4 + e]) * c1[e];
 #pragma unroll
     for (int off = 1; off < LPH; off <<= 1) d += __shfl_xor(d, off);
-    const int h = i / LPH;
-    if (i % LPH == 0) {
-      dyo[((long)b * H + h) * L + t] = d;
+    if (v % LPH == 0 && row < rows) {
+      const int b = static_cast<int>(row / L), t = static_cast<int>(row % L);
+      dyo[((long)b * H + v / LPH) * L + t] = d;
       tot += d;
     }
   }
@@ -71,7 +83,7 @@ __global__ __launch_bounds__(256) void k_sma_bwd_prep(const bf16* __restrict__ d
   for (int off = 1; off < 64; off <<= 1) tot += __shfl_xor(tot, off);
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = tot;
   __syncthreads();
-  if (threadIdx.x == 0) part[row] = sh[0] + sh[1] + sh[2] + sh[3];
+  if (threadIdx.x == 0) part[blockIdx.x] = sh[0] + sh[1] + sh[2] + sh[3];
 }
 
 // Σ part[0 .. n) -> *out (one workgroup, fixed order).
@@ -279,9 +291,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_bwd_tok(
 //            (Q·ds/sqrt(N)) E^T + (C·g·α) dy^T with MFMAs whose K axis is the
 //            token: both operands are token columns of the LDS tiles, read
 //            by transpose reads; the A side is scaled per token in registers.
-// The next tile's rows are in flight (registers) during both phases.
+// Two workgroups share a CU (at most 256 VGPRs), so one's tile loads and
+// barriers overlap the other's MFMAs.
 template <int N, int P>
-__global__ __launch_bounds__(256) void k_sma_bwd_mem(
+__global__ __launch_bounds__(256, 2) void k_sma_bwd_mem(
     const bf16* __restrict__ Q, const bf16* __restrict__ E, const bf16* __restrict__ C,
     const bf16* __restrict__ dH, const bf16* __restrict__ dy, const float* __restrict__ lse,
     const float* __restrict__ dyo, float gate, float* __restrict__ ddH, int B, int L, int H,
@@ -350,9 +363,9 @@ __global__ __launch_bounds__(256) void k_sma_bwd_mem(
         rd[v] = *reinterpret_cast<const bf16x8*>(dy + ((r0 + t) * H + h) * P + pv * 8);
       }
     };
-    fetch(0);
     for (int i = 0; i < ntile; ++i) {
       const int t0 = tok0(i);
+      fetch(i);
 #pragma unroll
       for (int v = 0; v < QV; ++v) {
         const int vi = tid + v * 256, t = vi / (N / 8), nv = vi % (N / 8);
@@ -366,7 +379,6 @@ __global__ __launch_bounds__(256) void k_sma_bwd_mem(
         *reinterpret_cast<bf16x8*>(&sD[t * LDP + pv * 8]) = rd[v];
       }
       __syncthreads();
-      if (i + 1 < ntile) fetch(i + 1);
       // phase 1: this wave's 16 tokens
       {
         const int tl = w * 16 + col;
@@ -473,11 +485,12 @@ hipError_t launch_sma_bwd(const PrefillShape& s, const T* Q, const T* E, const T
     float* part = dyo + ((rows * s.H + 63) / 64) * 64;
     const float scale_log2 = kLog2e / sqrtf(static_cast<float>(N));
     const float rsn = 1.f / sqrtf(static_cast<float>(N));
-    hipLaunchKernelGGL((k_sma_bwd_prep<P>), dim3(rows), dim3(256), 0, st, dy, o, dyo, part, s.L,
-                       s.H);
+    const long pblocks = (rows + kPrepRows - 1) / kPrepRows;
+    hipLaunchKernelGGL((k_sma_bwd_prep<P>), dim3(pblocks), dim3(256), 0, st, dy, o, dyo, part,
+                       rows, s.L, s.H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_sum, dim3(1), dim3(256), 0, st, part, rows, dgate);
+    hipLaunchKernelGGL(k_sum, dim3(1), dim3(256), 0, st, part, pblocks, dgate);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int waves = s.S % 128 == 0 ? 8 : 4;  // S is a multiple of 64
     const long tblocks = (long)s.B * s.G * M * (s.S / (16 * waves));
@@ -496,7 +509,7 @@ hipError_t launch_sma_bwd(const PrefillShape& s, const T* Q, const T* E, const T
 
 size_t sma_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H) {
   const size_t rows = static_cast<size_t>(B * L);
-  return (((rows * H + 63) / 64) * 64 + rows) * sizeof(float);
+  return (((rows * H + 63) / 64) * 64 + (rows + kPrepRows - 1) / kPrepRows) * sizeof(float);
 }
 
 #define DART_INST_SMA_BWD(T, N, P)                                                              \

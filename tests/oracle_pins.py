@@ -614,4 +614,33 @@ def pin_sma_logsumexp(orc):
         want = 0.0 if t < S else math.log(t // S)
         _close(lse0[0, :, t], np.full(H, want), 1e-12, "uniform normaliser")
 
+
+def pin_ssd_backward_finite_differences(orc):
+    """Every gradient of the scan (dx, ddt, dA, dB, dC, dh0) against central
+    differences of Σ dy·y_ssd + Σ ddH·ΔH + Σ dh_final·h_final computed with
+    the forward functions (two chunks, two heads sharing B/C, initial
+    state)."""
+    rng = np.random.default_rng(95)
+    B, L, H, G, N, P, S = 1, 8, 2, 1, 3, 2, 4
+    M = L // S
+    x = rng.standard_normal((B, L, H, P))
+    dt = rng.uniform(0.1, 0.6, (B, L, H))
+    A = -rng.uniform(0.5, 2.0, H)
+    Bm, C = rng.standard_normal((B, L, G, N)), rng.standard_normal((B, L, G, N))
+    h0 = rng.standard_normal((B, H, N, P))
+    dy = rng.standard_normal((B, L, H, P))
+    ddH = rng.standard_normal((B, H, M, N, P))
+    dhf = rng.standard_normal((B, H, N, P))
+    g = orc.ssd_backward(x, dt, A, Bm, C, S, dy, ddH, dhf, h0)
+
+    def loss():
+        dH = orc.chunk_states(x, dt, A, Bm, S)
+        H_in = orc.state_pass(dH, dt, A, S, h0)
+        y = orc.chunk_output(x, dt, A, Bm, C, H_in, S)
+        return float(np.sum(dy * y) + np.sum(ddH * dH) + np.sum(dhf * H_in[:, :, M]))
+
+    for name, arr in (("dx", x), ("ddt", dt), ("dA", A), ("dB", Bm), ("dC", C), ("dh0", h0)):
+        num = _fd_grad(loss, arr)
+        _close(g[name], num, 1e-7 * max(1.0, float(np.max(np.abs(num)))), f"ssd backward {name}")
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

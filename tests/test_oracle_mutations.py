@@ -94,6 +94,14 @@ MUTATIONS = [
     ("gate gradient scaled by g",
      "return dy.copy(), float(g) * dy, float(np.sum(dy * o))",
      "return dy.copy(), float(g) * dy, float(g) * float(np.sum(dy * o))"),
+    ("scan backward: state gradient passed back without the chunk decay",
+     "Gs = np.exp(u[-1]) * Gs + dHin[c]", "Gs = Gs + dHin[c]"),
+    ("scan backward: intra term misses the dt factor's own gradient",
+     "ddt[b, ts, h] += np.sum(dw * cb * dec, axis=0)", "ddt[b, ts, h] += 0.0"),
+    ("scan backward: log-decay gradient summed over earlier tokens",
+     "ddt[b, ts, h] += a * np.cumsum(du[ts][::-1])[::-1]", "ddt[b, ts, h] += a * np.cumsum(du[ts])"),
+    ("scan backward: state gradient of the output without exp(u)",
+     "dHin[k] += (eu[:, None] * Ck).T @ dyk", "dHin[k] += Ck.T @ dyk"),
     ("cache ratio counts keys only",
      "return (L // S) * N * P, 2 * L * P", "return (L // S) * N * P, L * P"),
 ]

@@ -233,7 +233,7 @@ def ssd_backward(x, dt, A, Bm, C, S, dy, ddH=None, dh_final=None, h0=None):
     dx, ddt, dA = np.zeros_like(x), np.zeros_like(dt), np.zeros(H)
     dBh, dCh = np.zeros((Bsz, L, H, N)), np.zeros((Bsz, L, H, N))
     dh0 = np.zeros((Bsz, H, N, P))
-    causal = np.tril(np.ones((S, S), dtype=bool))                   # j <= t
+    lower = np.tril(np.ones((S, S), dtype=bool))        # pairs j <= t of a chunk
     for b in range(Bsz):
         for h in range(H):
             a = A[h]
@@ -249,10 +249,10 @@ def ssd_backward(x, dt, A, Bm, C, S, dy, ddH=None, dh_final=None, h0=None):
                 u = a * np.cumsum(dtk)
                 chunks.append((ts, xk, Bk, dtk, u))
                 # intra-chunk term
-                dec = np.where(causal, np.exp(np.where(causal, u[:, None] - u[None, :], 0.0)), 0.0)
+                dec = np.where(lower, np.exp(np.where(lower, u[:, None] - u[None, :], 0.0)), 0.0)
                 cb = Ck @ Bk.T                                      # [t,j]
                 dx[b, ts, h] += (cb * dec * dtk[None, :]).T @ dyk
-                dw = np.where(causal, dyk @ xk.T, 0.0)              # ∂/∂ of each product term
+                dw = np.where(lower, dyk @ xk.T, 0.0)              # ∂/∂ of each product term
                 dcb = dw * dec * dtk[None, :]
                 dCh[b, ts, h] += dcb @ Bk
                 dBh[b, ts, h] += dcb.T @ Ck

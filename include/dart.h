@@ -211,6 +211,36 @@ dart_status dart_sma_bwd(const dart_dims* dims, const void* Q, const void* E, co
                          float gate, float* dQ, float* dE, float* dC, float* ddH, float* dgate,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Backward of the chunked scan (dart_chunk_state + dart_state_pass; the
+ * Mamba-2 SSD that the Pith review's axiom ledger and "What carries the
+ * argument" describe).  With u_t = acum (the log-decay from the start of
+ * token t's chunk) and U_c its value at the chunk's last token:
+ *   dH[c]      = Σ_i exp(U_c − u_i)·dt_i·B_i x_iᵀ
+ *   H_in[c+1]  = exp(U_c)·H_in[c] + dH[c]
+ *   y_ssd_t    = Σ_{j<=t} (C_t·B_j)·exp(u_t − u_j)·dt_j·x_j + exp(u_t)·C_tᵀH_in[k]
+ * and the upstream gradients dy (of y_ssd; the gated add passes dy through
+ * unchanged), ddH (of the memories, e.g. from dart_sma_bwd; may be NULL)
+ * and dh_final (of the final state; may be NULL), this returns the
+ * gradients of x, dt, A, B, C and of the initial state.
+ * in:  x, dy [B,L,H,P] io; dt [B,L,H] f32; A [H] f32; Bm, C [B,L,G,N] io;
+ *      acum [B,H,M,S] f32 (dart_chunk_state); H_in [B,H,M,P,N] io
+ *      (dart_state_pass); ddH [B,H,M,P,N] f32; dh_final [B,H,P,N] f32;
+ *      dC_sma [B,L,G,N] f32 or NULL: added to dC (dC_sma may be dC itself)
+ * out: dx [B,L,H,P], ddt [B,L,H], dA [H], dB, dC [B,L,G,N], dh0 [B,H,P,N],
+ *      all f32 (dB and dC summed over the heads of each group)
+ * workspace: at least dart_scan_bwd_workspace(dims) bytes of device memory.
+ * Compiled for bf16 io with P <= 64 and chunks that are multiples of 64;
+ * other dims return DART_ERR_UNSUPPORTED.
+ */
+size_t dart_scan_bwd_workspace(const dart_dims* dims);
+dart_status dart_scan_bwd(const dart_dims* dims, const void* x, const float* dt, const float* A,
+                          const void* Bm, const void* C, const float* acum, const void* H_in,
+                          const void* dy, const float* ddH, const float* dh_final,
+                          const float* dC_sma, float* dx, float* ddt, float* dA, float* dB,
+                          float* dC, float* dh0, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Bytes of device workspace dart_sma_decode needs for these dims (a
  * multiple of 256; 0 if the dims are invalid). */
 size_t dart_sma_decode_workspace(const dart_decode_dims* dims);

@@ -56,11 +56,15 @@ _SIG = {
     "dart_sma_bwd_workspace": [ctypes.POINTER(DartDims)],
     "dart_sma_bwd": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F, _VP, _VP,
                      _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+    "dart_scan_bwd_workspace": [ctypes.POINTER(DartDims)],
+    "dart_scan_bwd": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                      _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "dart_validate_dims": [ctypes.POINTER(DartDims)],
     "dart_validate_decode_dims": [ctypes.POINTER(DartDecodeDims)],
     "dart_status_str": [ctypes.c_int],
 }
 _RES = {"dart_sma_decode_workspace": ctypes.c_size_t, "dart_sma_bwd_workspace": ctypes.c_size_t,
+        "dart_scan_bwd_workspace": ctypes.c_size_t,
         "dart_status_str": ctypes.c_char_p}
 
 _lib = None

@@ -186,6 +186,45 @@ def dart_sma_bwd(Q, E, C, dH, o, lse, dy, gate, chunk, out=None):
     return out
 
 
+def dart_scan_bwd(x, dt, A, Bm, C, acum, H_in, dy, chunk, ddH=None, dh_final=None,
+                  dC_sma=None, out=None):
+    """Backward of the chunked scan (see include/dart.h).  Returns a dict of
+    f32 device tensors dx [B,L,H,P], ddt [B,L,H], dA [H], dB, dC [B,L,G,N]
+    (dC includes dC_sma when given) and dh0 [B,H,P,N]; ``out`` may hold
+    preallocated ones plus "workspace"."""
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    d = DartDims(B, L, H, G, N, P, int(chunk), _io_code(x.dtype))
+    M, io, dev = L // chunk, x.dtype, x.device
+    ws = int(lib().dart_scan_bwd_workspace(d))
+    if ws == 0:
+        raise ValueError("dart_scan_bwd: unsupported dimensions")
+    f32 = dict(dtype=torch.float32, device=dev)
+    if out is None:
+        out = {"dx": torch.empty(B, L, H, P, **f32), "ddt": torch.empty(B, L, H, **f32),
+               "dA": torch.empty(H, **f32), "dB": torch.empty(B, L, G, N, **f32),
+               "dC": torch.empty(B, L, G, N, **f32), "dh0": torch.empty(B, H, P, N, **f32),
+               "workspace": torch.empty(ws, dtype=torch.uint8, device=dev)}
+    args = [_ptr(x, "x", io, (B, L, H, P), dev), _ptr(dt, "dt", torch.float32, (B, L, H), dev),
+            _ptr(A, "A", torch.float32, (H,), dev), _ptr(Bm, "Bm", io, (B, L, G, N), dev),
+            _ptr(C, "C", io, (B, L, G, N), dev),
+            _ptr(acum, "acum", torch.float32, (B, H, M, chunk), dev),
+            _ptr(H_in, "H_in", io, (B, H, M, P, N), dev), _ptr(dy, "dy", io, (B, L, H, P), dev),
+            _ptr(ddH, "ddH", torch.float32, (B, H, M, P, N), dev),
+            _ptr(dh_final, "dh_final", torch.float32, (B, H, P, N), dev),
+            _ptr(dC_sma, "dC_sma", torch.float32, (B, L, G, N), dev)]
+    outs = [_ptr(out["dx"], "dx", torch.float32, (B, L, H, P), dev),
+            _ptr(out["ddt"], "ddt", torch.float32, (B, L, H), dev),
+            _ptr(out["dA"], "dA", torch.float32, (H,), dev),
+            _ptr(out["dB"], "dB", torch.float32, (B, L, G, N), dev),
+            _ptr(out["dC"], "dC", torch.float32, (B, L, G, N), dev),
+            _ptr(out["dh0"], "dh0", torch.float32, (B, H, P, N), dev)]
+    wsp = _ptr(out["workspace"], "workspace", torch.uint8, None, dev)
+    check(lib().dart_scan_bwd(d, *args, *outs, wsp, out["workspace"].numel(), _stream()),
+          "dart_scan_bwd")
+    return out
+
+
 def decode_dims(batch, nheads, ngroups, dstate, headdim, chunk, max_chunks, dtype):
     return DartDecodeDims(batch, nheads, ngroups, dstate, headdim, int(chunk), int(max_chunks),
                           _io_code(dtype))
@@ -285,6 +324,44 @@ def prefill(x, dt, A, Bm, C, Q, E, gate, chunk, h0=None, decayed=False):
     else:
         dart_sma_fwd(Q, E, C, out["dH"], out["y_ssd"], gate, out["y"], chunk)
     return out
+
+
+def prefill_train(x, dt, A, Bm, C, Q, E, gate, chunk, h0=None):
+    """:func:`prefill` that also keeps what the backward reads: o [B,L,H,P]
+    f32 and lse [B,H,L] f32 (dart_sma_fwd_train)."""
+    B, L, H, P = x.shape
+    N = Bm.shape[3]
+    M, dev = L // chunk, x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {
+        "acum": torch.empty(B, H, M, chunk, **f32),
+        "dH": torch.empty(B, H, M, P, N, dtype=x.dtype, device=dev),
+        "dH_f32": torch.empty(B, H, M, P, N, **f32),
+        "H_in": torch.empty(B, H, M, P, N, dtype=x.dtype, device=dev),
+        "h_final": torch.empty(B, H, P, N, **f32),
+        "y_ssd": torch.empty(B, L, H, P, dtype=x.dtype, device=dev),
+        "y": torch.empty(B, L, H, P, dtype=x.dtype, device=dev),
+        "o": torch.empty(B, L, H, P, **f32),
+        "lse": torch.empty(B, H, L, **f32),
+    }
+    dart_chunk_state(x, dt, A, Bm, out["acum"], out["dH"], out["dH_f32"], chunk)
+    dart_state_pass(x, dt, Bm, C, out["acum"], out["dH_f32"], h0, out["H_in"], out["h_final"],
+                    out["y_ssd"], chunk)
+    dart_sma_fwd_train(Q, E, C, out["dH"], out["y_ssd"], gate, out["y"], out["o"], out["lse"],
+                       chunk)
+    return out
+
+
+def prefill_backward(fwd, x, dt, A, Bm, C, Q, E, gate, chunk, dy, dh_final=None):
+    """Gradients of the whole prefill (SMA, gated add and the chunked scan)
+    for an upstream gradient dy [B,L,H,P] of y (and optionally dh_final of
+    the final state), from the tensors :func:`prefill_train` returned.
+    Returns f32 tensors dx, ddt, dA, dB, dC, dQ, dE, dgate and dh0."""
+    sm = dart_sma_bwd(Q, E, C, fwd["dH"], fwd["o"], fwd["lse"], dy, gate, chunk)
+    sc = dart_scan_bwd(x, dt, A, Bm, C, fwd["acum"], fwd["H_in"], dy, chunk, ddH=sm["ddH"],
+                       dh_final=dh_final, dC_sma=sm["dC"])
+    return {"dx": sc["dx"], "ddt": sc["ddt"], "dA": sc["dA"], "dB": sc["dB"], "dC": sc["dC"],
+            "dQ": sm["dQ"], "dE": sm["dE"], "dgate": sm["dgate"], "dh0": sc["dh0"]}
 
 
 def prefill_continue(x, dt, A, Bm, C, Q, E, gate, chunk, cache, prior_chunks, h0):

@@ -146,6 +146,22 @@ struct SmaBwdFn {
   }
 };
 
+struct ScanBwdFn {
+  dart::PrefillShape sh;
+  const void *x, *Bm, *C, *H_in, *dy;
+  const float *dt, *A, *acum, *ddH, *dhf, *dC_sma;
+  float *dx, *ddt, *dA, *dB, *dC, *dh0;
+  void* ws;
+  hipStream_t st;
+  template <typename T, int N, int P>
+  hipError_t run() {
+    return dart::launch_scan_bwd<T, N, P>(
+        sh, static_cast<const T*>(x), dt, A, static_cast<const T*>(Bm), static_cast<const T*>(C),
+        acum, static_cast<const T*>(H_in), static_cast<const T*>(dy), ddH, dhf, dC_sma, dx, ddt,
+        dA, dB, dC, dh0, ws, st);
+  }
+};
+
 // The backward is compiled for 16-bit io with P <= 64 and chunks of whole
 // 64-token tiles.
 bool bwd_supported(const dart_dims* d) {
@@ -306,5 +322,33 @@ extern "C" dart_status dart_sma_bwd(const dart_dims* dims, const void* Q, const 
   if (!aligned16(workspace)) return DART_ERR_ALIGN;
   SmaBwdFn fn{prefill_shape(dims), Q, E, C, dH, o, lse, dy, gate, dQ, dE, dC, ddH, dgate,
               workspace, static_cast<hipStream_t>(stream)};
+  return dispatch(dims->io, dims->dstate, dims->headdim, fn);
+}
+
+extern "C" size_t dart_scan_bwd_workspace(const dart_dims* dims) {
+  if (dart_validate_dims(dims) != DART_OK || !bwd_supported(dims)) return 0;
+  return dart::scan_bwd_workspace_bytes(dims->batch, dims->seqlen, dims->nheads, dims->dstate,
+                                        dims->headdim, dims->chunk);
+}
+
+extern "C" dart_status dart_scan_bwd(const dart_dims* dims, const void* x, const float* dt,
+                                     const float* A, const void* Bm, const void* C,
+                                     const float* acum, const void* H_in, const void* dy,
+                                     const float* ddH, const float* dh_final,
+                                     const float* dC_sma, float* dx, float* ddt, float* dA,
+                                     float* dB, float* dC, float* dh0, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  dart_status s = dart_validate_dims(dims);
+  if (s != DART_OK) return s;
+  if (!bwd_supported(dims)) return DART_ERR_UNSUPPORTED;
+  if ((s = check_ptrs(x, dt, A, Bm, C, acum, H_in, dy, dx, ddt, dA, dB, dC, dh0)) != DART_OK)
+    return s;
+  for (const void* p : {static_cast<const void*>(ddH), static_cast<const void*>(dh_final),
+                        static_cast<const void*>(dC_sma)})
+    if (p && !aligned16(p)) return DART_ERR_ALIGN;
+  if (!workspace || workspace_bytes < dart_scan_bwd_workspace(dims)) return DART_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DART_ERR_ALIGN;
+  ScanBwdFn fn{prefill_shape(dims), x, Bm, C, H_in, dy, dt, A, acum, ddH, dh_final, dC_sma,
+               dx, ddt, dA, dB, dC, dh0, workspace, static_cast<hipStream_t>(stream)};
   return dispatch(dims->io, dims->dstate, dims->headdim, fn);
 }

@@ -59,6 +59,17 @@ hipError_t launch_sma_bwd(const PrefillShape& s, const T* Q, const T* E, const T
                           void* workspace, hipStream_t st);
 size_t sma_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H);
 
+// Scan backward (16-bit io, P <= 64, S a multiple of 64): dx, ddt, dA, dB,
+// dC (+ dC_sma), dh0 (all f32) from dy, ddH and dh_final (both may be null).
+template <typename T, int N, int P>
+hipError_t launch_scan_bwd(const PrefillShape& s, const T* x, const float* dt, const float* A,
+                           const T* Bm, const T* C, const float* acum, const T* H_in, const T* dy,
+                           const float* ddH, const float* dh_final, const float* dC_sma,
+                           float* dx, float* ddt, float* dA, float* dB, float* dC, float* dh0,
+                           void* workspace, hipStream_t st);
+size_t scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t N, int64_t P,
+                                int64_t S);
+
 }  // namespace dart
 
 // (T, N, P) combinations compiled into the library; must match

@@ -140,3 +140,108 @@ def test_sma_backward_full_size_sampled_group():
     # f32 summation of the 33.5 M products in the kernels' order: within
     # 1e-4 of the sum of their magnitudes
     assert abs(float(gr["dgate"].item()) - dg_prop) <= 1e-4 * l1
+
+
+# ------------------------------------------------------------ scan backward
+def _scan_case(seed, B, L, H, G, N, P, S, with_extra=True):
+    inp = synth.draw_prefill(seed, B, L, H, G, N, P, io=BF)
+    M = L // S
+    extra = {
+        "dy": synth.draw_state(seed + 5, (B, L, H, P), 1.0, BF),
+        "ddH": synth.draw_state(seed + 6, (B, H, M, P, N), 1.0, torch.float32),
+        "dhf": synth.draw_state(seed + 7, (B, H, P, N), 1.0, torch.float32),
+        "dCs": synth.draw_state(seed + 8, (B, L, G, N), 1.0, torch.float32),
+    }
+    return inp, extra
+
+
+def _oracle_scan(inp, extra, S, with_extra):
+    n = {k: synth.as_f64(v) for k, v in inp.items()}
+    ddH = np.swapaxes(synth.as_f64(extra["ddH"]), -1, -2) if with_extra else None
+    dhf = np.swapaxes(synth.as_f64(extra["dhf"]), -1, -2) if with_extra else None
+    ref = oracle.ssd_backward(n["x"], n["dt"], n["A"], n["Bm"], n["C"], S,
+                              synth.as_f64(extra["dy"]), ddH, dhf)
+    if with_extra:
+        ref["dC"] = ref["dC"] + synth.as_f64(extra["dCs"])
+    return ref
+
+
+def _check_scan(gr, ref, what):
+    for k in ("dx", "ddt", "dA", "dB", "dC"):
+        assert_parity(gr[k], ref[k], f"{what} {k}")
+    assert_parity(_pn_to_np(gr["dh0"]), ref["dh0"], f"{what} dh0")
+
+
+@pytest.mark.parametrize("B,L,H,G,N,P,S,with_extra", [
+    (1, 256, 2, 1, 32, 32, 64, True),      # heads share B/C; one key block per chunk
+    (2, 384, 4, 2, 64, 64, 128, True),     # two blocks per chunk
+    (1, 768, 3, 3, 128, 64, 256, True),    # the layer's N, P, S
+    (2, 512, 8, 1, 128, 64, 128, False),   # one group of 8 heads; dy only
+])
+def test_scan_backward(B, L, H, G, N, P, S, with_extra):
+    _need_gpu()
+    print(f"scan backward case B{B} L{L} H{H} G{G} N{N} P{P} S{S} extra{with_extra}", flush=True)
+    inp, extra = _scan_case(21, B, L, H, G, N, P, S)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    e = {k: v.to(DEV) for k, v in extra.items()}
+    fwd = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], 0.5, S)
+    gr = api.dart_scan_bwd(d["x"], d["dt"], d["A"], d["Bm"], d["C"], fwd["acum"], fwd["H_in"],
+                           e["dy"], S, ddH=e["ddH"] if with_extra else None,
+                           dh_final=e["dhf"] if with_extra else None,
+                           dC_sma=e["dCs"] if with_extra else None)
+    torch.cuda.synchronize()
+    _check_scan(gr, _oracle_scan(inp, extra, S, with_extra), "scan")
+
+
+def test_prefill_backward_end_to_end():
+    """SMA backward feeding the scan backward (ddH and the SMA part of dC),
+    against the oracle's chain: sma_backward, then ssd_backward with the
+    SMA's memory gradient."""
+    _need_gpu()
+    B, L, H, G, N, P, S, gate = 2, 512, 4, 2, 128, 64, 128, 0.7
+    inp = synth.draw_prefill(31, B, L, H, G, N, P, io=BF, qscale=30.0)
+    dy = synth.draw_state(32, (B, L, H, P), 1.0, BF)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    fwd = api.prefill_train(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate, S)
+    gr = api.prefill_backward(fwd, d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"],
+                              gate, S, dy.to(DEV))
+    torch.cuda.synchronize()
+    n = {k: synth.as_f64(v) for k, v in inp.items()}
+    dH = oracle.chunk_states(n["x"], n["dt"], n["A"], n["Bm"], S)
+    o = oracle.sma(n["Q"], n["E"], n["C"], dH, S)
+    _, do, dg = oracle.gated_backward(synth.as_f64(dy), o, gate)
+    dQ, dE, dC_s, ddH = oracle.sma_backward(n["Q"], n["E"], n["C"], dH, S, do)
+    ref = oracle.ssd_backward(n["x"], n["dt"], n["A"], n["Bm"], n["C"], S, synth.as_f64(dy), ddH)
+    ref["dC"] = ref["dC"] + dC_s
+    for k in ("dx", "ddt", "dA", "dB", "dC"):
+        assert_parity(gr[k], ref[k], f"end-to-end {k}")
+    assert_parity(gr["dQ"], dQ, "end-to-end dQ")
+    assert_parity(gr["dE"], dE, "end-to-end dE")
+    assert abs(float(gr["dgate"].item()) - dg) <= 2e-2 * abs(dg)
+
+
+def test_scan_backward_full_size_sampled_group():
+    """The ~370M layer shape: the whole scan backward on the GPU; one
+    (batch, group) (8 heads, so dB and dC are complete group sums) against
+    the oracle; dA sums over the batch and is checked at the small shapes."""
+    _need_gpu()
+    B, L, H, G, N, P, S = 4, 8192, 32, 4, 128, 64, 256
+    inp, extra = _scan_case(41, B, L, H, G, N, P, S)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    e = {k: v.to(DEV) for k, v in extra.items()}
+    fwd = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], 0.5, S)
+    gr = api.dart_scan_bwd(d["x"], d["dt"], d["A"], d["Bm"], d["C"], fwd["acum"], fwd["H_in"],
+                           e["dy"], S, ddH=e["ddH"], dh_final=e["dhf"], dC_sma=e["dCs"])
+    torch.cuda.synchronize()
+    b, g = 1, 3
+    hs = slice(g * 8, g * 8 + 8)
+    sl = {"x": inp["x"][b:b + 1, :, hs], "dt": inp["dt"][b:b + 1, :, hs], "A": inp["A"][hs],
+          "Bm": inp["Bm"][b:b + 1, :, g:g + 1], "C": inp["C"][b:b + 1, :, g:g + 1]}
+    ex = {"dy": extra["dy"][b:b + 1, :, hs], "ddH": extra["ddH"][b:b + 1, hs],
+          "dhf": extra["dhf"][b:b + 1, hs], "dCs": extra["dCs"][b:b + 1, :, g:g + 1]}
+    ref = _oracle_scan(sl, ex, S, True)
+    assert_parity(gr["dx"][b:b + 1, :, hs], ref["dx"], "full-size dx (one group)")
+    assert_parity(gr["ddt"][b:b + 1, :, hs], ref["ddt"], "full-size ddt (one group)")
+    assert_parity(gr["dB"][b:b + 1, :, g:g + 1], ref["dB"], "full-size dB (one group)")
+    assert_parity(gr["dC"][b:b + 1, :, g:g + 1], ref["dC"], "full-size dC (one group)")
+    assert_parity(_pn_to_np(gr["dh0"][b:b + 1, hs]), ref["dh0"], "full-size dh0 (one group)")

@@ -7,8 +7,8 @@ B/C/Q, L = 8192, S = 256, N = 128, P = 64, bfloat16 inputs with fp32
 accumulation.  `value` is prefill tokens/s (batch·L / step time).  The
 decode step over a 4 GiB chunk-memory cache (batch 64, 32 heads, 128
 cached chunks) is timed in the same run and reported under "decode", and
-the same step over the fp8 (E4M3) cache under "decode_fp8"; the SMA backward at
-the prefill shape is reported under "backward".
+the same step over the fp8 (E4M3) cache under "decode_fp8"; the backward of the
+prefill (SMA and scan) at the prefill shape is reported under "backward".
 
 Prints one JSON line.  `python bench.py --steps K --warmup W`.
 """
@@ -177,44 +177,73 @@ def sma_bwd_flops(c):
     return 3.0 * sma_flops(c)
 
 
+def scan_bwd_flops(c):
+    """Algorithmic scan backward FLOPs: per (batch, head, chunk) the
+    N×P-sized products (the outputs' state gradient, the memory term's dx
+    and dB and its dt dot, the inter term's dC and its log-decay dot:
+    5 × 2·S·N·P) and the causal S×S products dy·xᵀ, dx, dB, dC (2 FLOPs per
+    token pair and feature, S(S+1)/2 pairs); C·Bᵀ once per group."""
+    M = c["L"] // c["S"]
+    S, N, P = c["S"], c["N"], c["P"]
+    pairs = S * (S + 1) / 2
+    per_head = 10 * S * N * P + 2 * pairs * (P + P + N + N)
+    per_group = 2 * pairs * N
+    return M * c["B"] * (per_head * c["H"] + per_group * c["G"])
+
+
 def bench_backward(args, torch, api, synth, inp):
-    """The SMA backward at the prefill shape: dart_sma_fwd_train once, then
-    dart_sma_bwd timed (memories from the prefill, dy ~ N(0, 1))."""
+    """The backward of the whole prefill at the prefill shape: the training
+    forward once, then dart_sma_bwd + dart_scan_bwd timed (dy ~ N(0, 1))."""
     c = BASE
     B, L, H, G, N, P, S = c["B"], c["L"], c["H"], c["G"], c["N"], c["P"], c["S"]
     d = {k: v.to("cuda:0") for k, v in inp.items()}
-    pre = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], c["gate"], S)
+    fwd = api.prefill_train(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], c["gate"],
+                            S)
     dy = synth.draw_state(60, (B, L, H, P), 1.0, torch.bfloat16, device="cuda:0")
-    f32 = dict(dtype=torch.float32, device="cuda:0")
-    y = torch.empty(B, L, H, P, dtype=torch.bfloat16, device="cuda:0")
-    o, lse = torch.empty(B, L, H, P, **f32), torch.empty(B, H, L, **f32)
-    api.dart_sma_fwd_train(d["Q"], d["E"], d["C"], pre["dH"], pre["y_ssd"], c["gate"], y, o, lse,
-                           S)
-    out = api.dart_sma_bwd(d["Q"], d["E"], d["C"], pre["dH"], o, lse, dy, c["gate"], S)
+    sm = api.dart_sma_bwd(d["Q"], d["E"], d["C"], fwd["dH"], fwd["o"], fwd["lse"], dy,
+                          c["gate"], S)
+    sc = api.dart_scan_bwd(d["x"], d["dt"], d["A"], d["Bm"], d["C"], fwd["acum"], fwd["H_in"],
+                           dy, S, ddH=sm["ddH"], dC_sma=sm["dC"])
 
-    def step():
-        api.dart_sma_bwd(d["Q"], d["E"], d["C"], pre["dH"], o, lse, dy, c["gate"], S, out=out)
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        api.dart_sma_bwd(d["Q"], d["E"], d["C"], fwd["dH"], fwd["o"], fwd["lse"], dy, c["gate"],
+                         S, out=sm)
+        if ev:
+            ev[1].record()
+        api.dart_scan_bwd(d["x"], d["dt"], d["A"], d["Bm"], d["C"], fwd["acum"], fwd["H_in"],
+                          dy, S, ddH=sm["ddH"], dC_sma=sm["dC"], out=sc)
+        if ev:
+            ev[2].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ms, med, mn = timed_steps(torch, step, args.steps)
-    fl = sma_bwd_flops(c)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    sma_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)[args.steps // 2]
+    scan_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)[args.steps // 2]
+    tot_ms = sorted(e[0].elapsed_time(e[2]) for e in evs)[args.steps // 2]
+    f_sma, f_scan = sma_bwd_flops(c), scan_bwd_flops(c)
     return {
-        "metric": "SMA backward TFLOP/s (algorithmic)",
-        "value": fl / (ms / 1e3) / 1e12,
-        "unit": "TFLOP/s",
-        "ms_per_step": ms,
-        "ms_median": med,
-        "ms_min": mn,
-        "algorithmic_gflop": fl / 1e9,
-        "config": {"workload": "DART SMA backward at the prefill shape", "batch": B,
-                   "seqlen": L, "heads": H, "groups": G, "dstate": N, "headdim": P, "chunk": S,
-                   "io": "bf16", "gradients": "f32"},
+        "metric": "prefill backward tokens/s",
+        "value": B * L / (tot_ms / 1e3),
+        "unit": "tokens/s",
+        "ms_median": tot_ms,
+        "kernel_ms_median": {"dart_sma_bwd": sma_ms, "dart_scan_bwd": scan_ms},
+        "algorithmic_gflop": {"sma_bwd": f_sma / 1e9, "scan_bwd": f_scan / 1e9},
+        "mfma_frac_whole_backward": (f_sma + f_scan) / (tot_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+        "config": {"workload": "DART prefill backward (SMA + chunked scan) at the prefill shape",
+                   "batch": B, "seqlen": L, "heads": H, "groups": G, "dstate": N, "headdim": P,
+                   "chunk": S, "io": "bf16", "gradients": "f32"},
         "roofline": {"kernel": "dart_sma_bwd", "bound": "mfma",
-                     "achieved": fl / (ms / 1e3) / 1e12, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": fl / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                     "achieved": f_sma / (sma_ms / 1e3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": f_sma / (sma_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
                      "traffic": None},
+        "scan_bwd_frac": f_scan / (scan_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
     }
 
 

@@ -15,15 +15,16 @@
 //   k_ssd_bwd_pass: last chunk first, G = dh_final; dmem[c] = G + ddH[c];
 //                   the log-decay gradient <G, exp(U_c)·H_in[c]>;
 //                   G = exp(U_c)·G + Yc[c]; dh0 = G
-//   k_ssd_bwd_j:    per 64-token key block j: dx, dB (per head), the direct
-//                   dt gradient and the log-decay gradients of the memory
-//                   term and of the intra term's keys
-//   k_ssd_bwd_t:    per 64-token query block t: dC (per head) of the intra
-//                   and inter terms and the queries' log-decay gradients
+//   k_ssd_bwd_j:    per 64-token key block j: dx, dB, the direct dt
+//                   gradient and the log-decay gradients of the memory term
+//                   and of the intra term's keys
+//   k_ssd_bwd_t:    per 64-token query block t: dC of the intra and inter
+//                   terms and the queries' log-decay gradients
 //   k_ssd_bwd_fin:  log-decay gradients -> dt (reverse cumulative sum inside
 //                   the chunk, times A) and partial dA
-//   k_group_sum, k_head_sum: dB, dC summed over the heads of a group (plus
-//                   the SMA part of dC), dA summed over batch and chunks.
+//   k_head_sum:     dA summed over batch and chunks.
+// The key- and query-block kernels walk the heads of a group, so dB and dC
+// (shared by those heads) are summed in registers.
 // Intra-chunk products run on MFMA tiles of 16 tokens × 16 tokens whose D
 // registers are fed back as the next product's B operand (K = tokens), the
 // token-axis A operands read by LDS transpose reads.
@@ -104,7 +105,8 @@ __global__ __launch_bounds__(256) void k_ssd_bwd_yc(const bf16* __restrict__ C,
     __syncthreads();
     stage_rows<N, LDN>(sC, C + (t0 * G + g) * N, (long)G * N);
     stage_rows<P, LDP>(sDy, dy + (t0 * H + h) * P, (long)H * P);
-    if (threadIdx.x < kT) se[threadIdx.x] = exp_neg(acum[(pair * M + c) * S + tile * kT + threadIdx.x]);
+    if (threadIdx.x < kT)
+      se[threadIdx.x] = exp_neg(acum[(pair * M + c) * S + tile * kT + threadIdx.x]);
     __syncthreads();
     if (w < AW) {
 #pragma unroll
@@ -169,17 +171,20 @@ __global__ __launch_bounds__(256) void k_ssd_bwd_pass(
 }
 
 // Key-block backward: one workgroup (4 waves) per (64-token block j of
-// chunk c, head, batch); wave w owns key columns 16w .. 16w+15.
+// chunk c, head group, batch); it walks the heads of the group (B, and so
+// dB, is shared by them) and wave w owns key columns 16w .. 16w+15.  Per
+// head:
 //   memory term: BD = dmem[c]ᵀ-products give dx and dB of the keys, scaled
 //                by w_j = exp(U_c − u_j)·dt_j, and Σ_p BD·x for dt and u;
 //   intra term: for every query block t >= j, the 16×16 tiles cb = C·Bᵀ and
 //                dw = dy·xᵀ (rows t), masked decay, then dx += dyᵀ(cb∘dec·dt)
 //                and dB += Cᵀ(dw∘dec·dt) with the tiles as B operands.
+// dB accumulates over the heads in registers and is written once.
 template <int N, int P>
 __global__ __launch_bounds__(256, 2) void k_ssd_bwd_j(
     const bf16* __restrict__ x, const float* __restrict__ dt, const bf16* __restrict__ Bm,
     const bf16* __restrict__ C, const bf16* __restrict__ dy, const float* __restrict__ acum,
-    const bf16* __restrict__ dmem, float* __restrict__ dx, float* __restrict__ dBh,
+    const bf16* __restrict__ dmem, float* __restrict__ dx, float* __restrict__ dB,
     float* __restrict__ ddtd, float* __restrict__ duj, float* __restrict__ gwj, int L, int H,
     int G, int S) {
   constexpr int LDN = N + 16, LDP = P + 16, NKK = N / 32, NK2 = P / 32, NNB = N / 16,
@@ -188,147 +193,160 @@ __global__ __launch_bounds__(256, 2) void k_ssd_bwd_j(
       sD[P * LDN];
   __shared__ __align__(16) float su[kT];
   const int nblk = S / kT, c = blockIdx.x / nblk, jb = blockIdx.x % nblk;
-  const int h = blockIdx.y, b = blockIdx.z, g = h / (H / G), M = L / S;
-  const long pair = (long)b * H + h;
+  const int g = blockIdx.y, b = blockIdx.z, hpg = H / G, M = L / S;
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const float* ac = acum + (pair * M + c) * S;
   const int jw = 16 * w + col;  // key within the block
   const int jl = jb * kT + jw;  // key within the chunk
   const long rowj = (long)b * L + (long)c * S + jl;
   const long r0j = (long)b * L + (long)c * S + jb * kT;
-  stage_rows<P, LDP>(sX, x + (r0j * H + h) * P, (long)H * P);
   stage_rows<N, LDN>(sB, Bm + (r0j * G + g) * N, (long)G * N);
-  {
-    const bf16* src = dmem + (pair * M + c) * (long)(P * N);
-    for (int vi = threadIdx.x; vi < P * N / 8; vi += 256) {
-      const int p = vi / (N / 8), v = vi % (N / 8);
-      *reinterpret_cast<bf16x8*>(&sD[p * LDN + v * 8]) =
-          *reinterpret_cast<const bf16x8*>(src + p * N + v * 8);
-    }
-  }
   __syncthreads();
-  const float uj = ac[jl], dtj = dt[rowj * H + h], U = ac[S - 1];
-  bf16x8 bj[NKK], xj[NK2];
+  bf16x8 bj[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk)
     bj[kk] = *reinterpret_cast<const bf16x8*>(&sB[jw * LDN + kk * 32 + grp * 8]);
+  floatx4 dBT[NNB];
 #pragma unroll
-  for (int k2 = 0; k2 < NK2; ++k2)
-    xj[k2] = *reinterpret_cast<const bf16x8*>(&sX[jw * LDP + k2 * 32 + grp * 8]);
+  for (int nb = 0; nb < NNB; ++nb) dBT[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // memory term
-  floatx4 dxT[NPB], dBT[NNB];
-  float ddt_mem, gw;
-  {
-    float s = 0.f;
-#pragma unroll
-    for (int pb = 0; pb < NPB; ++pb) {
-      floatx4 a4 = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        a4 = Mma<bf16>::mma(
-            *reinterpret_cast<const bf16x8*>(&sD[(pb * 16 + col) * LDN + kk * 32 + grp * 8]),
-            bj[kk], a4);
-      const bf16x4 xv = *reinterpret_cast<const bf16x4*>(&sX[jw * LDP + pb * 16 + 4 * grp]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s += a4[i] * to_f32(xv[i]);
-      dxT[pb] = a4;
+  for (int hh = 0; hh < hpg; ++hh) {
+    const int h = g * hpg + hh;
+    const long pair = (long)b * H + h;
+    const float* ac = acum + (pair * M + c) * S;
+    __syncthreads();  // the previous head's reads of sX and sD are done
+    stage_rows<P, LDP>(sX, x + (r0j * H + h) * P, (long)H * P);
+    {
+      const bf16* src = dmem + (pair * M + c) * (long)(P * N);
+      for (int vi = threadIdx.x; vi < P * N / 8; vi += 256) {
+        const int p = vi / (N / 8), v = vi % (N / 8);
+        *reinterpret_cast<bf16x8*>(&sD[p * LDN + v * 8]) =
+            *reinterpret_cast<const bf16x8*>(src + p * N + v * 8);
+      }
     }
-    const float dwi = sum_lane_groups(s);
-    const float wd = exp_neg(U - uj), wj = wd * dtj;
-#pragma unroll
-    for (int pb = 0; pb < NPB; ++pb) dxT[pb] *= wj;
-    ddt_mem = wd * dwi;
-    gw = dwi * wj;
-#pragma unroll
-    for (int nb = 0; nb < NNB; ++nb) {
-      floatx4 a4 = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k2 = 0; k2 < NK2; ++k2)
-        a4 = Mma<bf16>::mma(tr_frag<LDN>(sD, k2, nb, col, grp),
-                            row_frag_split(&sX[jw * LDP], k2, grp), a4);
-      dBT[nb] = wj * a4;
-    }
-  }
-  // intra term, query blocks t >= j
-  float ddt_in = 0.f, du_in = 0.f;
-  for (int tb = jb; tb < nblk; ++tb) {
-    const long r0t = (long)b * L + (long)c * S + tb * kT;
     __syncthreads();
-    stage_rows<N, LDN>(sC, C + (r0t * G + g) * N, (long)G * N);
-    stage_rows<P, LDP>(sDy, dy + (r0t * H + h) * P, (long)H * P);
-    if (threadIdx.x < kT) su[threadIdx.x] = ac[tb * kT + threadIdx.x];
-    __syncthreads();
+    const float uj = ac[jl], dtj = dt[rowj * H + h], U = ac[S - 1];
+    bf16x8 xj[NK2];
 #pragma unroll
-    for (int ks = 0; ks < kT / 32; ++ks) {
-      if (tb == jb && 2 * ks + 1 < w) continue;  // every query of the pair precedes the keys
-      floatx4 cb[2], dw[2];
+    for (int k2 = 0; k2 < NK2; ++k2)
+      xj[k2] = *reinterpret_cast<const bf16x8*>(&sX[jw * LDP + k2 * 32 + grp * 8]);
+
+    // memory term
+    floatx4 dxT[NPB];
+    float ddt_mem, gw;
+    {
+      float s = 0.f;
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int rb = 2 * ks + r;
-        cb[r] = floatx4{0.f, 0.f, 0.f, 0.f};
-        dw[r] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int pb = 0; pb < NPB; ++pb) {
+        floatx4 a4 = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk)
-          cb[r] = Mma<bf16>::mma(
-              *reinterpret_cast<const bf16x8*>(&sC[(16 * rb + col) * LDN + kk * 32 + grp * 8]),
-              bj[kk], cb[r]);
+          a4 = Mma<bf16>::mma(
+              *reinterpret_cast<const bf16x8*>(&sD[(pb * 16 + col) * LDN + kk * 32 + grp * 8]),
+              bj[kk], a4);
+        const bf16x4 xv = *reinterpret_cast<const bf16x4*>(&sX[jw * LDP + pb * 16 + 4 * grp]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s += a4[i] * to_f32(xv[i]);
+        dxT[pb] = a4;
+      }
+      const float dwi = sum_lane_groups(s);
+      const float wd = exp_neg(U - uj), wj = wd * dtj;
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb) dxT[pb] *= wj;
+      ddt_mem = wd * dwi;
+      gw = dwi * wj;
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb) {
+        floatx4 a4 = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k2 = 0; k2 < NK2; ++k2)
-          dw[r] = Mma<bf16>::mma(
-              *reinterpret_cast<const bf16x8*>(&sDy[(16 * rb + col) * LDP + k2 * 32 + grp * 8]),
-              xj[k2], dw[r]);
+          a4 = Mma<bf16>::mma(tr_frag<LDN>(sD, k2, nb, col, grp),
+                              row_frag_split(&sX[jw * LDP], k2, grp), a4);
+        dBT[nb] += wj * a4;
       }
-      float g1[8], g2[8];
+    }
+    // intra term, query blocks t >= j
+    float ddt_in = 0.f;
+    for (int tb = jb; tb < nblk; ++tb) {
+      const long r0t = (long)b * L + (long)c * S + tb * kT;
+      __syncthreads();
+      stage_rows<N, LDN>(sC, C + (r0t * G + g) * N, (long)G * N);
+      stage_rows<P, LDP>(sDy, dy + (r0t * H + h) * P, (long)H * P);
+      if (threadIdx.x < kT) su[threadIdx.x] = ac[tb * kT + threadIdx.x];
+      __syncthreads();
 #pragma unroll
-      for (int r = 0; r < 2; ++r)
+      for (int ks = 0; ks < kT / 32; ++ks) {
+        if (tb == jb && 2 * ks + 1 < w) continue;  // every query of the pair precedes the keys
+        floatx4 cb[2], dw[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tw = 16 * (2 * ks + r) + 4 * grp + i;  // query within the block
-          const bool ok = tb > jb || tw >= jw;
-          const float dec = ok ? exp_neg(su[tw] - uj) : 0.f;
-          const float cd = cb[r][i] * dec, wdc = dw[r][i] * dec;
-          g1[4 * r + i] = cd * dtj;
-          g2[4 * r + i] = wdc * dtj;
-          ddt_in += wdc * cb[r][i];
+        for (int r = 0; r < 2; ++r) {
+          const int rb = 2 * ks + r;
+          cb[r] = floatx4{0.f, 0.f, 0.f, 0.f};
+          dw[r] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk)
+            cb[r] = Mma<bf16>::mma(
+                *reinterpret_cast<const bf16x8*>(&sC[(16 * rb + col) * LDN + kk * 32 + grp * 8]),
+                bj[kk], cb[r]);
+#pragma unroll
+          for (int k2 = 0; k2 < NK2; ++k2)
+            dw[r] = Mma<bf16>::mma(
+                *reinterpret_cast<const bf16x8*>(&sDy[(16 * rb + col) * LDP + k2 * 32 + grp * 8]),
+                xj[k2], dw[r]);
         }
-      const bf16x8 f1 = pack8f(g1), f2 = pack8f(g2);
+        float g1[8], g2[8];
 #pragma unroll
-      for (int pb = 0; pb < NPB; ++pb)
-        dxT[pb] = Mma<bf16>::mma(tr_frag<LDP>(sDy, ks, pb, col, grp), f1, dxT[pb]);
+        for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int nb = 0; nb < NNB; ++nb)
-        dBT[nb] = Mma<bf16>::mma(tr_frag<LDN>(sC, ks, nb, col, grp), f2, dBT[nb]);
+          for (int i = 0; i < 4; ++i) {
+            const int tw = 16 * (2 * ks + r) + 4 * grp + i;  // query within the block
+            const bool ok = tb > jb || tw >= jw;
+            const float dec = ok ? exp_neg(su[tw] - uj) : 0.f;
+            const float cd = cb[r][i] * dec, wdc = dw[r][i] * dec;
+            g1[4 * r + i] = cd * dtj;
+            g2[4 * r + i] = wdc * dtj;
+            ddt_in += wdc * cb[r][i];
+          }
+        const bf16x8 f1 = pack8f(g1), f2 = pack8f(g2);
+#pragma unroll
+        for (int pb = 0; pb < NPB; ++pb)
+          dxT[pb] = Mma<bf16>::mma(tr_frag<LDP>(sDy, ks, pb, col, grp), f1, dxT[pb]);
+#pragma unroll
+        for (int nb = 0; nb < NNB; ++nb)
+          dBT[nb] = Mma<bf16>::mma(tr_frag<LDN>(sC, ks, nb, col, grp), f2, dBT[nb]);
+      }
+    }
+    ddt_in = sum_lane_groups(ddt_in);
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb)
+      *reinterpret_cast<floatx4*>(dx + (rowj * H + h) * P + pb * 16 + 4 * grp) = dxT[pb];
+    if (grp == 0) {
+      ddtd[rowj * H + h] = ddt_mem + ddt_in;
+      // Σ_t dw·cb·dec·dt_j: the keys' log-decay enters with a minus
+      duj[pair * L + (long)c * S + jl] = -gw - ddt_in * dtj;
+      gwj[pair * L + (long)c * S + jl] = gw;
     }
   }
-  ddt_in = sum_lane_groups(ddt_in);
-  du_in = ddt_in * dtj;  // Σ_t dw·cb·dec·dt_j: the keys' log-decay enters with a minus
-#pragma unroll
-  for (int pb = 0; pb < NPB; ++pb)
-    *reinterpret_cast<floatx4*>(dx + (rowj * H + h) * P + pb * 16 + 4 * grp) = dxT[pb];
 #pragma unroll
   for (int nb = 0; nb < NNB; ++nb)
-    *reinterpret_cast<floatx4*>(dBh + (rowj * H + h) * N + nb * 16 + 4 * grp) = dBT[nb];
-  if (grp == 0) {
-    ddtd[rowj * H + h] = ddt_mem + ddt_in;
-    duj[pair * L + (long)c * S + jl] = -gw - du_in;
-    gwj[pair * L + (long)c * S + jl] = gw;
-  }
+    *reinterpret_cast<floatx4*>(dB + (rowj * G + g) * N + nb * 16 + 4 * grp) = dBT[nb];
 }
 
 // Query-block backward: one workgroup (4 waves) per (64-token block t of
-// chunk c, head, batch); wave w owns query columns 16w .. 16w+15.
-//   inter term: dC = exp(u_t)·H_in[c]·dy_t and the log-decay gradient
+// chunk c, head group, batch); it walks the heads of the group (C, and so
+// dC, is shared by them) and wave w owns query columns 16w .. 16w+15.  Per
+// head:
+//   inter term: dC += exp(u_t)·H_in[c]·dy_t and the log-decay gradient
 //               exp(u_t)·dy_t·(C_tᵀH_in[c]);
 //   intra term: for every key block j <= t, the tiles cbᵀ = B·Cᵀ and
 //               dwᵀ = x·dyᵀ (rows j), masked decay, dC += Bᵀ(dwᵀ∘dec·dt),
 //               and the queries' log-decay gradient Σ_j dw·cb·dec·dt.
+// dC (plus dC_in, the SMA part, when given) is written once.
 template <int N, int P>
 __global__ __launch_bounds__(256, 2) void k_ssd_bwd_t(
     const bf16* __restrict__ x, const float* __restrict__ dt, const bf16* __restrict__ Bm,
     const bf16* __restrict__ C, const bf16* __restrict__ dy, const float* __restrict__ acum,
-    const bf16* __restrict__ H_in, float* __restrict__ dCh, float* __restrict__ dut, int L,
+    const bf16* __restrict__ H_in, const float* dC_in, float* dC, float* __restrict__ dut, int L,
     int H, int G, int S) {
   constexpr int LDN = N + 16, LDP = P + 16, NKK = N / 32, NK2 = P / 32, NNB = N / 16,
                 NPB = P / 16;
@@ -336,117 +354,130 @@ __global__ __launch_bounds__(256, 2) void k_ssd_bwd_t(
       sH[P * LDN];
   __shared__ __align__(16) float su[kT], sdt[kT];
   const int nblk = S / kT, c = blockIdx.x / nblk, tb = blockIdx.x % nblk;
-  const int h = blockIdx.y, b = blockIdx.z, g = h / (H / G), M = L / S;
-  const long pair = (long)b * H + h;
+  const int g = blockIdx.y, b = blockIdx.z, hpg = H / G, M = L / S;
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const float* ac = acum + (pair * M + c) * S;
   const int tw = 16 * w + col;
   const int tl = tb * kT + tw;
   const long rowt = (long)b * L + (long)c * S + tl;
   const long r0t = (long)b * L + (long)c * S + tb * kT;
   stage_rows<N, LDN>(sC, C + (r0t * G + g) * N, (long)G * N);
-  stage_rows<P, LDP>(sDy, dy + (r0t * H + h) * P, (long)H * P);
-  {
-    const bf16* src = H_in + (pair * M + c) * (long)(P * N);
-    for (int vi = threadIdx.x; vi < P * N / 8; vi += 256) {
-      const int p = vi / (N / 8), v = vi % (N / 8);
-      *reinterpret_cast<bf16x8*>(&sH[p * LDN + v * 8]) =
-          *reinterpret_cast<const bf16x8*>(src + p * N + v * 8);
-    }
-  }
   __syncthreads();
-  const float ut = ac[tl], eu = exp_neg(ut);
-  bf16x8 ct[NKK], dyf[NK2];
+  bf16x8 ct[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk)
     ct[kk] = *reinterpret_cast<const bf16x8*>(&sC[tw * LDN + kk * 32 + grp * 8]);
-#pragma unroll
-  for (int k2 = 0; k2 < NK2; ++k2)
-    dyf[k2] = *reinterpret_cast<const bf16x8*>(&sDy[tw * LDP + k2 * 32 + grp * 8]);
-  // inter term
   floatx4 dCT[NNB];
 #pragma unroll
-  for (int nb = 0; nb < NNB; ++nb) {
-    floatx4 a4 = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < NNB; ++nb) dCT[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int hh = 0; hh < hpg; ++hh) {
+    const int h = g * hpg + hh;
+    const long pair = (long)b * H + h;
+    const float* ac = acum + (pair * M + c) * S;
+    __syncthreads();  // the previous head's reads of sDy and sH are done
+    stage_rows<P, LDP>(sDy, dy + (r0t * H + h) * P, (long)H * P);
+    {
+      const bf16* src = H_in + (pair * M + c) * (long)(P * N);
+      for (int vi = threadIdx.x; vi < P * N / 8; vi += 256) {
+        const int p = vi / (N / 8), v = vi % (N / 8);
+        *reinterpret_cast<bf16x8*>(&sH[p * LDN + v * 8]) =
+            *reinterpret_cast<const bf16x8*>(src + p * N + v * 8);
+      }
+    }
+    __syncthreads();
+    const float ut = ac[tl], eu = exp_neg(ut);
+    bf16x8 dyf[NK2];
 #pragma unroll
     for (int k2 = 0; k2 < NK2; ++k2)
-      a4 = Mma<bf16>::mma(tr_frag<LDN>(sH, k2, nb, col, grp), row_frag_split(&sDy[tw * LDP], k2, grp),
-                          a4);
-    dCT[nb] = eu * a4;
-  }
-  float du;
-  {
-    float s = 0.f;
+      dyf[k2] = *reinterpret_cast<const bf16x8*>(&sDy[tw * LDP + k2 * 32 + grp * 8]);
+    // inter term
 #pragma unroll
-    for (int pb = 0; pb < NPB; ++pb) {
+    for (int nb = 0; nb < NNB; ++nb) {
       floatx4 a4 = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        a4 = Mma<bf16>::mma(
-            *reinterpret_cast<const bf16x8*>(&sH[(pb * 16 + col) * LDN + kk * 32 + grp * 8]),
-            ct[kk], a4);
-      const bf16x4 dv = *reinterpret_cast<const bf16x4*>(&sDy[tw * LDP + pb * 16 + 4 * grp]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s += a4[i] * to_f32(dv[i]);
+      for (int k2 = 0; k2 < NK2; ++k2)
+        a4 = Mma<bf16>::mma(tr_frag<LDN>(sH, k2, nb, col, grp),
+                            row_frag_split(&sDy[tw * LDP], k2, grp), a4);
+      dCT[nb] += eu * a4;
     }
-    du = eu * sum_lane_groups(s);
-  }
-  // intra term, key blocks j <= t
-  float du_in = 0.f;
-  for (int jb = 0; jb <= tb; ++jb) {
-    const long r0j = (long)b * L + (long)c * S + jb * kT;
-    __syncthreads();
-    stage_rows<P, LDP>(sX, x + (r0j * H + h) * P, (long)H * P);
-    stage_rows<N, LDN>(sB, Bm + (r0j * G + g) * N, (long)G * N);
-    if (threadIdx.x < kT) {
-      su[threadIdx.x] = ac[jb * kT + threadIdx.x];
-      sdt[threadIdx.x] = dt[(r0j + threadIdx.x) * H + h];
-    }
-    __syncthreads();
+    float du;
+    {
+      float s = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < kT / 32; ++ks) {
-      if (jb == tb && 2 * ks > w) continue;  // every key of the pair follows the queries
-      floatx4 cb[2], dw[2];
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int rb = 2 * ks + r;
-        cb[r] = floatx4{0.f, 0.f, 0.f, 0.f};
-        dw[r] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int pb = 0; pb < NPB; ++pb) {
+        floatx4 a4 = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk)
-          cb[r] = Mma<bf16>::mma(
-              *reinterpret_cast<const bf16x8*>(&sB[(16 * rb + col) * LDN + kk * 32 + grp * 8]),
-              ct[kk], cb[r]);
+          a4 = Mma<bf16>::mma(
+              *reinterpret_cast<const bf16x8*>(&sH[(pb * 16 + col) * LDN + kk * 32 + grp * 8]),
+              ct[kk], a4);
+        const bf16x4 dv = *reinterpret_cast<const bf16x4*>(&sDy[tw * LDP + pb * 16 + 4 * grp]);
 #pragma unroll
-        for (int k2 = 0; k2 < NK2; ++k2)
-          dw[r] = Mma<bf16>::mma(
-              *reinterpret_cast<const bf16x8*>(&sX[(16 * rb + col) * LDP + k2 * 32 + grp * 8]),
-              dyf[k2], dw[r]);
+        for (int i = 0; i < 4; ++i) s += a4[i] * to_f32(dv[i]);
       }
-      float g2[8];
-#pragma unroll
-      for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int jw = 16 * (2 * ks + r) + 4 * grp + i;  // key within the block
-          const bool ok = jb < tb || jw <= tw;
-          const float dec = ok ? exp_neg(ut - su[jw]) : 0.f;
-          const float v = dw[r][i] * dec * sdt[jw];
-          g2[4 * r + i] = v;
-          du_in += v * cb[r][i];
-        }
-      const bf16x8 f2 = pack8f(g2);
-#pragma unroll
-      for (int nb = 0; nb < NNB; ++nb)
-        dCT[nb] = Mma<bf16>::mma(tr_frag<LDN>(sB, ks, nb, col, grp), f2, dCT[nb]);
+      du = eu * sum_lane_groups(s);
     }
-  }
-  du += sum_lane_groups(du_in);
+    // intra term, key blocks j <= t
+    float du_in = 0.f;
+    for (int jb = 0; jb <= tb; ++jb) {
+      const long r0j = (long)b * L + (long)c * S + jb * kT;
+      __syncthreads();
+      stage_rows<P, LDP>(sX, x + (r0j * H + h) * P, (long)H * P);
+      stage_rows<N, LDN>(sB, Bm + (r0j * G + g) * N, (long)G * N);
+      if (threadIdx.x < kT) {
+        su[threadIdx.x] = ac[jb * kT + threadIdx.x];
+        sdt[threadIdx.x] = dt[(r0j + threadIdx.x) * H + h];
+      }
+      __syncthreads();
 #pragma unroll
-  for (int nb = 0; nb < NNB; ++nb)
-    *reinterpret_cast<floatx4*>(dCh + (rowt * H + h) * N + nb * 16 + 4 * grp) = dCT[nb];
-  if (grp == 0) dut[pair * L + (long)c * S + tl] = du;
+      for (int ks = 0; ks < kT / 32; ++ks) {
+        if (jb == tb && 2 * ks > w) continue;  // every key of the pair follows the queries
+        floatx4 cb[2], dw[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int rb = 2 * ks + r;
+          cb[r] = floatx4{0.f, 0.f, 0.f, 0.f};
+          dw[r] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk)
+            cb[r] = Mma<bf16>::mma(
+                *reinterpret_cast<const bf16x8*>(&sB[(16 * rb + col) * LDN + kk * 32 + grp * 8]),
+                ct[kk], cb[r]);
+#pragma unroll
+          for (int k2 = 0; k2 < NK2; ++k2)
+            dw[r] = Mma<bf16>::mma(
+                *reinterpret_cast<const bf16x8*>(&sX[(16 * rb + col) * LDP + k2 * 32 + grp * 8]),
+                dyf[k2], dw[r]);
+        }
+        float g2[8];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int jw = 16 * (2 * ks + r) + 4 * grp + i;  // key within the block
+            const bool ok = jb < tb || jw <= tw;
+            const float dec = ok ? exp_neg(ut - su[jw]) : 0.f;
+            const float v = dw[r][i] * dec * sdt[jw];
+            g2[4 * r + i] = v;
+            du_in += v * cb[r][i];
+          }
+        const bf16x8 f2 = pack8f(g2);
+#pragma unroll
+        for (int nb = 0; nb < NNB; ++nb)
+          dCT[nb] = Mma<bf16>::mma(tr_frag<LDN>(sB, ks, nb, col, grp), f2, dCT[nb]);
+      }
+    }
+    du += sum_lane_groups(du_in);
+    if (grp == 0) dut[pair * L + (long)c * S + tl] = du;
+  }
+#pragma unroll
+  for (int nb = 0; nb < NNB; ++nb) {
+    const long o = (rowt * G + g) * N + nb * 16 + 4 * grp;
+    floatx4 v = dCT[nb];
+    if (dC_in) v += *reinterpret_cast<const floatx4*>(dC_in + o);
+    *reinterpret_cast<floatx4*>(dC + o) = v;
+  }
 }
 
 // Log-decay gradients of one (chunk, head, batch) -> dt and A: du_t = duj +
@@ -485,30 +516,6 @@ __global__ __launch_bounds__(256) void k_ssd_bwd_fin(
   if (i == 0) dApart[pair * M + c] = part;
 }
 
-// dB[b,t,g] = Σ_{h in g} dBh[b,t,h]; dC[b,t,g] = dC_in[b,t,g] + Σ_h dCh[b,t,h]
-// (dC_in may be dC itself: each element is read before it is written by the
-// same thread).
-__global__ __launch_bounds__(256) void k_group_sum(const float* __restrict__ dBh,
-                                                   const float* __restrict__ dCh,
-                                                   const float* dC_in, float* __restrict__ dB,
-                                                   float* dC, long rows, int H, int G, int N) {
-  const int hpg = H / G, q = N / 4;
-  const long total = rows * G * q;
-  for (long i = blockIdx.x * 256L + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
-    const long row = i / (G * q);
-    const int g = static_cast<int>((i / q) % G), v = static_cast<int>(i % q);
-    floatx4 sb = floatx4{0.f, 0.f, 0.f, 0.f}, sc = sb;
-    for (int hh = 0; hh < hpg; ++hh) {
-      const long src = ((row * H + g * hpg + hh) * N) / 4 + v;
-      sb += reinterpret_cast<const floatx4*>(dBh)[src];
-      sc += reinterpret_cast<const floatx4*>(dCh)[src];
-    }
-    if (dC_in) sc += reinterpret_cast<const floatx4*>(dC_in)[i];
-    reinterpret_cast<floatx4*>(dB)[i] = sb;
-    reinterpret_cast<floatx4*>(dC)[i] = sc;
-  }
-}
-
 // dA[h] = Σ_{b, c} dApart[b, h, c]
 __global__ __launch_bounds__(256) void k_head_sum(const float* __restrict__ dApart,
                                                   float* __restrict__ dA, int B, int H, int M) {
@@ -523,7 +530,7 @@ __global__ __launch_bounds__(256) void k_head_sum(const float* __restrict__ dApa
 struct ScanBwdWs {
   float* Yc;
   bf16* dmem;
-  float *dus, *dBh, *dCh, *ddtd, *duj, *dut, *gwj, *dApart;
+  float *dus, *ddtd, *duj, *dut, *gwj, *dApart;
 };
 
 ScanBwdWs scan_bwd_ws(void* base, int64_t B, int64_t L, int64_t H, int64_t N, int64_t P,
@@ -540,8 +547,6 @@ ScanBwdWs scan_bwd_ws(void* base, int64_t B, int64_t L, int64_t H, int64_t N, in
   ws.Yc = reinterpret_cast<float*>(take(size_t(B * H * M) * PN * 4));
   ws.dmem = reinterpret_cast<bf16*>(take(size_t(B * H * M) * PN * 2));
   ws.dus = reinterpret_cast<float*>(take(size_t(B * H * M * ntile) * 4));
-  ws.dBh = reinterpret_cast<float*>(take(size_t(B * L * H) * N * 4));
-  ws.dCh = reinterpret_cast<float*>(take(size_t(B * L * H) * N * 4));
   ws.ddtd = reinterpret_cast<float*>(take(size_t(B * L * H) * 4));
   ws.duj = reinterpret_cast<float*>(take(size_t(B * L * H) * 4));
   ws.dut = reinterpret_cast<float*>(take(size_t(B * L * H) * 4));
@@ -578,21 +583,14 @@ hipError_t launch_scan_bwd(const PrefillShape& s, const T* x, const float* dt, c
     hipLaunchKernelGGL(k_ssd_bwd_pass, dim3(ntile, s.H, s.B), dim3(256), 0, st, acum, H_in,
                        ws.Yc, ddH, dh_final, ws.dmem, ws.dus, dh0, s.H, M, s.S, PN);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_ssd_bwd_j<N, P>), dim3(M * nblk, s.H, s.B), dim3(256), 0, st, x, dt, Bm,
-                       C, dy, acum, ws.dmem, dx, ws.dBh, ws.ddtd, ws.duj, ws.gwj, s.L, s.H, s.G,
-                       s.S);
+    hipLaunchKernelGGL((k_ssd_bwd_j<N, P>), dim3(M * nblk, s.G, s.B), dim3(256), 0, st, x, dt, Bm,
+                       C, dy, acum, ws.dmem, dx, dB, ws.ddtd, ws.duj, ws.gwj, s.L, s.H, s.G, s.S);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_ssd_bwd_t<N, P>), dim3(M * nblk, s.H, s.B), dim3(256), 0, st, x, dt, Bm,
-                       C, dy, acum, H_in, ws.dCh, ws.dut, s.L, s.H, s.G, s.S);
+    hipLaunchKernelGGL((k_ssd_bwd_t<N, P>), dim3(M * nblk, s.G, s.B), dim3(256), 0, st, x, dt, Bm,
+                       C, dy, acum, H_in, dC_sma, dC, ws.dut, s.L, s.H, s.G, s.S);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_ssd_bwd_fin, dim3(M, s.H, s.B), dim3(256), 0, st, dt, A, ws.duj, ws.dut,
                        ws.gwj, ws.dus, ws.ddtd, ddt, ws.dApart, s.L, s.H, s.S, ntile);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    const long rows = (long)s.B * s.L;
-    const long items = rows * s.G * (N / 4);
-    const long gblocks = (items + 255) / 256 < 8192 ? (items + 255) / 256 : 8192;
-    hipLaunchKernelGGL(k_group_sum, dim3(gblocks), dim3(256), 0, st, ws.dBh, ws.dCh, dC_sma, dB,
-                       dC, rows, s.H, s.G, N);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_head_sum, dim3(s.H), dim3(256), 0, st, ws.dApart, dA, s.B, s.H, M);
     return hipGetLastError();

@@ -54,29 +54,43 @@ __global__ __launch_bounds__(256) void k_sma_bwd_prep(const bf16* __restrict__ d
                                                       float* __restrict__ part, long rows, int L,
                                                       int H) {
   constexpr int LPH = P / 8;  // lanes per head
+  constexpr int IT = 4;  // 16-byte items per thread and pass (all loads of a pass in flight)
   static_assert(LPH <= 64 && 64 % LPH == 0, "prep lanes");
   __shared__ float sh[4];
   const int HL = H * LPH;  // 16-byte vectors of dy per row
+  const int items = kPrepRows * HL;
   float tot = 0.f;
-  for (int i = threadIdx.x; i < kPrepRows * HL; i += 256) {
-    const long row = blockIdx.x * kPrepRows + i / HL;
-    const int v = i % HL;
-    bf16x8 a = bf16x8{};
-    floatx4 c0 = floatx4{0.f, 0.f, 0.f, 0.f}, c1 = c0;
-    if (row < rows) {
-      a = *reinterpret_cast<const bf16x8*>(dy + row * H * P + v * 8);
-      c0 = *reinterpret_cast<const floatx4*>(o + row * H * P + v * 8);
-      c1 = *reinterpret_cast<const floatx4*>(o + row * H * P + v * 8 + 4);
+  for (int base = 0; base < items; base += IT * 256) {
+    bf16x8 a[IT];
+    floatx4 c0[IT], c1[IT];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {  // every load of the pass in flight first
+      const int i = base + k * 256 + threadIdx.x;
+      const long row = blockIdx.x * kPrepRows + i / HL;
+      const int v = i % HL;
+      a[k] = bf16x8{};
+      c0[k] = c1[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (i < items && row < rows) {
+        a[k] = *reinterpret_cast<const bf16x8*>(dy + row * H * P + v * 8);
+        c0[k] = *reinterpret_cast<const floatx4*>(o + row * H * P + v * 8);
+        c1[k] = *reinterpret_cast<const floatx4*>(o + row * H * P + v * 8 + 4);
+      }
     }
-    float d = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) d += to_f32(a[e]) * c0[e] + to_f32(a[4 + e]) * c1[e];
+    for (int k = 0; k < IT; ++k) {
+      const int i = base + k * 256 + threadIdx.x;
+      const long row = blockIdx.x * kPrepRows + i / HL;
+      const int v = i % HL;
+      float d = 0.f;
 #pragma unroll
-    for (int off = 1; off < LPH; off <<= 1) d += __shfl_xor(d, off);
-    if (v % LPH == 0 && row < rows) {
-      const int b = static_cast<int>(row / L), t = static_cast<int>(row % L);
-      dyo[((long)b * H + v / LPH) * L + t] = d;
-      tot += d;
+      for (int e = 0; e < 4; ++e) d += to_f32(a[k][e]) * c0[k][e] + to_f32(a[k][4 + e]) * c1[k][e];
+#pragma unroll
+      for (int off = 1; off < LPH; off <<= 1) d += __shfl_xor(d, off);
+      if (v % LPH == 0 && i < items && row < rows) {
+        const int b = static_cast<int>(row / L), t = static_cast<int>(row % L);
+        dyo[((long)b * H + v / LPH) * L + t] = d;
+        tot += d;
+      }
     }
   }
 #pragma unroll

@@ -180,6 +180,38 @@ def test_fp8_cache_entry_points_validate_on_host():
     assert st(ddims(mx=0), A16, 0, 0, A16, A16, None) == BAD
 
 
+def test_backward_entry_points_validate_on_host():
+    lib = dart.lib()
+    d = dims(2, 512, 4, 2, 128, 64, 128, BF16)
+    ws_sma, ws_scan = lib.dart_sma_bwd_workspace(d), lib.dart_scan_bwd_workspace(d)
+    assert ws_sma > 0 and ws_sma % 256 == 0 and ws_scan > 0
+    # unsupported: fp32 io, P = 128, 32-token chunks
+    for bad in (dims(1, 1024, 1, 1, 16, 16, 64, F32), dims(1, 512, 2, 2, 128, 128, 256, BF16),
+                dims(1, 1024, 2, 2, 128, 64, 32, BF16)):
+        assert lib.dart_sma_bwd_workspace(bad) == 0 and lib.dart_scan_bwd_workspace(bad) == 0
+        assert lib.dart_sma_bwd(bad, *([A16] * 7), 0.5, *([A16] * 5), A16, 1 << 30,
+                                None) == UNSUP
+        assert lib.dart_scan_bwd(bad, *([A16] * 8), None, None, None, *([A16] * 6), A16,
+                                 1 << 30, None) == UNSUP
+    # Q, E, C, dH, o, lse, dy, then dQ, dE, dC, ddH, dgate
+    for i in range(12):
+        p = [A16] * 12
+        p[i] = None
+        assert lib.dart_sma_bwd(d, *p[:7], 0.5, *p[7:], A16, ws_sma, None) == NULLP
+    assert lib.dart_sma_bwd(d, *([A16] * 7), 0.5, *([A16] * 5), A16, ws_sma - 256, None) == WS
+    assert lib.dart_sma_bwd(d, *([A16] * 7), 0.5, *([A16] * 5), MIS, ws_sma, None) == ALIGN
+    # x, dt, A, Bm, C, acum, H_in, dy, (ddH, dh_final, dC_sma optional), dx .. dh0
+    for i in range(14):
+        p = [A16] * 14
+        p[i] = None
+        assert lib.dart_scan_bwd(d, *p[:8], None, None, None, *p[8:], A16, ws_scan,
+                                 None) == NULLP
+    assert lib.dart_scan_bwd(d, *([A16] * 8), MIS, None, None, *([A16] * 6), A16, ws_scan,
+                             None) == ALIGN
+    assert lib.dart_scan_bwd(d, *([A16] * 8), None, None, None, *([A16] * 6), A16,
+                             ws_scan - 256, None) == WS
+
+
 def test_binding_checks_tensors_before_calling():
     x = torch.zeros(1, 64, 1, 16)
     with pytest.raises(ValueError, match="GPU"):

@@ -245,3 +245,27 @@ def test_scan_backward_full_size_sampled_group():
     assert_parity(gr["dB"][b:b + 1, :, g:g + 1], ref["dB"], "full-size dB (one group)")
     assert_parity(gr["dC"][b:b + 1, :, g:g + 1], ref["dC"], "full-size dC (one group)")
     assert_parity(_pn_to_np(gr["dh0"][b:b + 1, hs]), ref["dh0"], "full-size dh0 (one group)")
+
+
+def test_backward_single_chunk():
+    """One chunk: no memory is visible, so every SMA gradient and dgate are
+    zero and the scan backward is the intra-chunk term plus the state
+    gradients of one chunk."""
+    _need_gpu()
+    B, L, H, G, N, P, S, gate = 2, 128, 2, 1, 64, 64, 128, 0.5
+    inp = synth.draw_prefill(51, B, L, H, G, N, P, io=BF)
+    dy = synth.draw_state(52, (B, L, H, P), 1.0, BF)
+    dhf = synth.draw_state(53, (B, H, P, N), 1.0, torch.float32)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    fwd = api.prefill_train(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate, S)
+    gr = api.prefill_backward(fwd, d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"],
+                              gate, S, dy.to(DEV), dh_final=dhf.to(DEV))
+    torch.cuda.synchronize()
+    assert float(gr["dgate"].item()) == 0.0
+    assert not bool(gr["dQ"].any()) and not bool(gr["dE"].any())
+    n = {k: synth.as_f64(v) for k, v in inp.items()}
+    ref = oracle.ssd_backward(n["x"], n["dt"], n["A"], n["Bm"], n["C"], S, synth.as_f64(dy),
+                              None, np.swapaxes(synth.as_f64(dhf), -1, -2))
+    for k in ("dx", "ddt", "dA", "dB", "dC"):
+        assert_parity(gr[k], ref[k], f"single chunk {k}")
+    assert_parity(_pn_to_np(gr["dh0"]), ref["dh0"], "single chunk dh0")

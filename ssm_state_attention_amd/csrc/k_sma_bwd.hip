@@ -306,7 +306,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_bwd_tok(
 //            token: both operands are token columns of the LDS tiles, read
 //            by transpose reads; the A side is scaled per token in registers.
 // Two workgroups share a CU (at most 256 VGPRs), so one's tile loads and
-// barriers overlap the other's MFMAs.
+// barriers overlap the other's MFMAs; the next tile's Q and C rows are
+// fetched into registers during phase 2.
 template <int N, int P>
 __global__ __launch_bounds__(256, 2) void k_sma_bwd_mem(
     const bf16* __restrict__ Q, const bf16* __restrict__ E, const bf16* __restrict__ C,
@@ -362,7 +363,7 @@ __global__ __launch_bounds__(256, 2) void k_sma_bwd_mem(
       return kc * S + (i % (S / T)) * T;
     };
     bf16x8 rq[QV], rc[QV], re[EV], rd[EV];
-    auto fetch = [&](int i) __attribute__((always_inline)) {
+    auto fetch_qc = [&](int i) __attribute__((always_inline)) {
       const long r0 = (long)b * L + tok0(i);
 #pragma unroll
       for (int v = 0; v < QV; ++v) {
@@ -370,6 +371,9 @@ __global__ __launch_bounds__(256, 2) void k_sma_bwd_mem(
         rq[v] = *reinterpret_cast<const bf16x8*>(Q + ((r0 + t) * G + g) * N + nv * 8);
         rc[v] = *reinterpret_cast<const bf16x8*>(C + ((r0 + t) * G + g) * N + nv * 8);
       }
+    };
+    auto fetch_ed = [&](int i) __attribute__((always_inline)) {
+      const long r0 = (long)b * L + tok0(i);
 #pragma unroll
       for (int v = 0; v < EV; ++v) {
         const int vi = tid + v * 256, t = vi / (P / 8), pv = vi % (P / 8);
@@ -377,9 +381,10 @@ __global__ __launch_bounds__(256, 2) void k_sma_bwd_mem(
         rd[v] = *reinterpret_cast<const bf16x8*>(dy + ((r0 + t) * H + h) * P + pv * 8);
       }
     };
+    fetch_qc(0);
     for (int i = 0; i < ntile; ++i) {
       const int t0 = tok0(i);
-      fetch(i);
+      fetch_ed(i);
 #pragma unroll
       for (int v = 0; v < QV; ++v) {
         const int vi = tid + v * 256, t = vi / (N / 8), nv = vi % (N / 8);
@@ -430,6 +435,9 @@ __global__ __launch_bounds__(256, 2) void k_sma_bwd_mem(
         }
       }
       __syncthreads();
+      // the next tile's Q and C rows are in flight during phase 2 (more would
+      // push the registers past 256)
+      if (i + 1 < ntile) fetch_qc(i + 1);
       // phase 2: ddH rows n of this wave, K = the tile's 64 tokens
       if (w < AW) {
 #pragma unroll

@@ -69,6 +69,30 @@ __device__ __forceinline__ void stage_rows(bf16* dst, const bf16* src, long gs) 
         *reinterpret_cast<const bf16x8*>(src + t * gs + v * 8);
   }
 }
+// The same 64 rows held in registers between their global loads and the LDS
+// write (so the loads of the next block can be in flight during a block's
+// products).
+template <int F>
+struct RowRegs {
+  static constexpr int RV = kT * F / 8 / 256;
+  static_assert(RV >= 1 && RV * 256 * 8 == kT * F, "row split");
+  bf16x8 v[RV];
+  __device__ __forceinline__ void fetch(const bf16* src, long gs) {
+#pragma unroll
+    for (int r = 0; r < RV; ++r) {
+      const int vi = threadIdx.x + r * 256, t = vi / (F / 8), c = vi % (F / 8);
+      v[r] = *reinterpret_cast<const bf16x8*>(src + t * gs + c * 8);
+    }
+  }
+  template <int LD>
+  __device__ __forceinline__ void store(bf16* dst) const {
+#pragma unroll
+    for (int r = 0; r < RV; ++r) {
+      const int vi = threadIdx.x + r * 256, t = vi / (F / 8), c = vi % (F / 8);
+      *reinterpret_cast<bf16x8*>(dst + t * LD + c * 8) = v[r];
+    }
+  }
+};
 __device__ __forceinline__ float block_sum256(float v, float* sh) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
@@ -267,13 +291,21 @@ __global__ __launch_bounds__(256, 2) void k_ssd_bwd_j(
     }
     // intra term, query blocks t >= j
     float ddt_in = 0.f;
-    for (int tb = jb; tb < nblk; ++tb) {
+    RowRegs<N> rc;
+    RowRegs<P> rd;
+    auto fetch_t = [&](int tb) __attribute__((always_inline)) {
       const long r0t = (long)b * L + (long)c * S + tb * kT;
+      rc.fetch(C + (r0t * G + g) * N, (long)G * N);
+      rd.fetch(dy + (r0t * H + h) * P, (long)H * P);
+    };
+    fetch_t(jb);
+    for (int tb = jb; tb < nblk; ++tb) {
       __syncthreads();
-      stage_rows<N, LDN>(sC, C + (r0t * G + g) * N, (long)G * N);
-      stage_rows<P, LDP>(sDy, dy + (r0t * H + h) * P, (long)H * P);
+      rc.template store<LDN>(sC);
+      rd.template store<LDP>(sDy);
       if (threadIdx.x < kT) su[threadIdx.x] = ac[tb * kT + threadIdx.x];
       __syncthreads();
+      if (tb + 1 < nblk) fetch_t(tb + 1);
 #pragma unroll
       for (int ks = 0; ks < kT / 32; ++ks) {
         if (tb == jb && 2 * ks + 1 < w) continue;  // every query of the pair precedes the keys
@@ -420,16 +452,25 @@ __global__ __launch_bounds__(256, 2) void k_ssd_bwd_t(
     }
     // intra term, key blocks j <= t
     float du_in = 0.f;
+    RowRegs<P> rx;
+    RowRegs<N> rb;
+    auto fetch_j = [&](int jb) __attribute__((always_inline)) {
+      const long r0j = (long)b * L + (long)c * S + jb * kT;
+      rx.fetch(x + (r0j * H + h) * P, (long)H * P);
+      rb.fetch(Bm + (r0j * G + g) * N, (long)G * N);
+    };
+    fetch_j(0);
     for (int jb = 0; jb <= tb; ++jb) {
       const long r0j = (long)b * L + (long)c * S + jb * kT;
       __syncthreads();
-      stage_rows<P, LDP>(sX, x + (r0j * H + h) * P, (long)H * P);
-      stage_rows<N, LDN>(sB, Bm + (r0j * G + g) * N, (long)G * N);
+      rx.template store<LDP>(sX);
+      rb.template store<LDN>(sB);
       if (threadIdx.x < kT) {
         su[threadIdx.x] = ac[jb * kT + threadIdx.x];
         sdt[threadIdx.x] = dt[(r0j + threadIdx.x) * H + h];
       }
       __syncthreads();
+      if (jb + 1 <= tb) fetch_j(jb + 1);
 #pragma unroll
       for (int ks = 0; ks < kT / 32; ++ks) {
         if (jb == tb && 2 * ks > w) continue;  // every key of the pair follows the queries

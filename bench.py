@@ -30,13 +30,17 @@ METRIC = "SMA+scan prefill tokens/s & MFMA% at L=8K; decode chunk-memory HBM GB/
 # only for the kernel source it was measured on (SHA-1 of that file).
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "ssm_state_attention_amd", "csrc")
 PROFILED_TRAFFIC = {
-    "k_sma_fwd": ("k_sma.hip", "4b76f137bc708b83e5b9f2f604c61a25b6e8736c",
-                  (548.03 + 134.22) * 1e6),
+    "k_sma_fwd": ("k_sma.hip", "d2c74d7f6ffb66e1aff59911d102532d1387c826",
+                  (548.41 + 134.22) * 1e6),
     # the four launches of one decode call (state, stream, combine, advance)
     "dart_sma_decode": ("k_decode.hip", "1edf2954b0ac30901f6e19755b249602c54386d1",
                         (135.75 + 134.74 + 4296.39 + 0.59 + 1.57 + 0.26) * 1e6),
     "dart_sma_decode_fp8": ("k_decode.hip", "1edf2954b0ac30901f6e19755b249602c54386d1",
                             (135.76 + 134.74 + 2150.98 + 0.59 + 1.57 + 0.26) * 1e6),
+    # the launches of one SMA backward call (dy·o pass, gate sum, token- and
+    # memory-major kernels)
+    "dart_sma_bwd": ("k_sma_bwd.hip", "078b88f12c52944eb035411837c76711d43ec120",
+                     (402.77 + 8.87 + 499.19 + 402.65 + 2482.47 + 134.26 + 0.05) * 1e6),
 }
 
 
@@ -242,7 +246,7 @@ def bench_backward(args, torch, api, synth, inp):
         "roofline": {"kernel": "dart_sma_bwd", "bound": "mfma",
                      "achieved": f_sma / (sma_ms / 1e3) / 1e12, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": f_sma / (sma_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
-                     "traffic": None},
+                     "traffic": profiled_traffic("dart_sma_bwd")},
         "scan_bwd_frac": f_scan / (scan_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
     }
 

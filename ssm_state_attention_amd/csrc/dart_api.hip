@@ -165,7 +165,9 @@ struct ScanBwdFn {
 // The backward is compiled for 16-bit io with P <= 64 and chunks of whole
 // 64-token tiles.
 bool bwd_supported(const dart_dims* d) {
-  return d->io == DART_BF16 && d->headdim <= 64 && d->chunk % 64 == 0;
+  // the dy·o pass launches one workgroup per four (batch, token) rows
+  return d->io == DART_BF16 && d->headdim <= 64 && d->chunk % 64 == 0 &&
+         d->batch * d->seqlen / 4 < (int64_t(1) << 31);
 }
 
 dart::DecodeShape decode_shape(const dart_decode_dims* d) {

@@ -13,6 +13,14 @@
  * Prefill is three calls on one stream, in this order:
  *   dart_chunk_state -> dart_state_pass -> dart_sma_fwd
  * Decode is one call per generated token: dart_sma_decode.
+ * Extensions of the same path:
+ *   training: dart_sma_fwd_train in place of dart_sma_fwd, then the backward
+ *             dart_sma_bwd -> dart_scan_bwd (its memory gradient and the SMA
+ *             part of dC feed the scan backward);
+ *   the decay-included SMA variant: dart_sma_fwd_decayed;
+ *   chunked prefill from a decode cache: dart_sma_fwd_cont (with h0 given to
+ *             dart_state_pass);
+ *   an fp8 chunk-memory cache: dart_cache_fp8_store, dart_sma_decode_fp8.
  *
  * Conventions for every call
  * --------------------------
@@ -25,7 +33,8 @@
  *   non-OK status means nothing was enqueued.  DART_ERR_HIP reports a launch
  *   failure; a fault inside a kernel surfaces at the caller's next
  *   synchronisation.
- * - Outputs never alias inputs (decode state arguments are in/out).
+ * - Outputs never alias inputs (decode state arguments are in/out; the one
+ *   documented exception is dart_scan_bwd's dC_sma, which may be dC).
  * - Symbols: B batch, L sequence length, H heads, G groups (B, C and Q are
  *   shared by H/G consecutive heads), N state size (key axis), P head dim
  *   (value axis), S chunk size, M = L/S chunks, k = floor(t/S) the chunk of

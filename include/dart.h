@@ -20,7 +20,8 @@
  *   the decay-included SMA variant: dart_sma_fwd_decayed;
  *   chunked prefill from a decode cache: dart_sma_fwd_cont (with h0 given to
  *             dart_state_pass);
- *   an fp8 chunk-memory cache: dart_cache_fp8_store, dart_sma_decode_fp8.
+ *   an fp8 chunk-memory cache: dart_cache_fp8_store, dart_sma_decode_fp8,
+ *             dart_sma_fwd_cont_fp8.
  *
  * Conventions for every call
  * --------------------------
@@ -332,6 +333,23 @@ dart_status dart_sma_decode_fp8(const dart_decode_dims* dims, const void* x, con
                                 const void* E, float gate, uint8_t* cache8, float* scale,
                                 float* h, float* dH_cur, int32_t* n_chunks, int32_t* pos, void* y,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dart_sma_fwd_cont over the fp8 cache: identical steps and arguments except
+ * that prior memory c < prior_chunks of (b, h) is decode(cache8[b,h,c])·
+ * scale[b,h,c] (the format above; cache8 [B,H,cache_chunks,P,N],
+ * scale [B,H,cache_chunks]).  The product is taken in bfloat16, where it is
+ * exact for memories of normal magnitude.  io must be DART_BF16.
+ *
+ * errors: DART_ERR_UNSUPPORTED for io = DART_F32; DART_ERR_BAD_DIMS unless
+ *         0 <= prior_chunks <= cache_chunks; cache8 and scale may be NULL
+ *         when prior_chunks = 0.
+ */
+dart_status dart_sma_fwd_cont_fp8(const dart_dims* dims, int64_t prior_chunks,
+                                  int64_t cache_chunks, const void* Q, const void* E,
+                                  const void* C, const uint8_t* cache8, const float* scale,
+                                  const void* dH, const void* y_ssd, float gate, void* y,
+                                  void* stream);
 
 /* Host-only checks (no HIP call; usable without a GPU). */
 dart_status dart_validate_dims(const dart_dims* dims);

@@ -44,6 +44,8 @@ _SIG = {
                              _VP],
     "dart_sma_fwd_cont": [ctypes.POINTER(DartDims), ctypes.c_int64, ctypes.c_int64, _VP, _VP,
                           _VP, _VP, _VP, _VP, _F, _VP, _VP],
+    "dart_sma_fwd_cont_fp8": [ctypes.POINTER(DartDims), ctypes.c_int64, ctypes.c_int64, _VP,
+                              _VP, _VP, _VP, _VP, _VP, _VP, _F, _VP, _VP],
     "dart_sma_decode_workspace": [ctypes.POINTER(DartDecodeDims)],
     "dart_sma_decode": [ctypes.POINTER(DartDecodeDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F,
                         _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],

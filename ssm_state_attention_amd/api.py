@@ -116,6 +116,26 @@ def dart_sma_fwd_cont(Q, E, C, cache, prior_chunks, dH, y_ssd, gate, y, chunk):
                                   yp, _stream()), "dart_sma_fwd_cont")
 
 
+def dart_sma_fwd_cont_fp8(Q, E, C, cache8, scale, prior_chunks, dH, y_ssd, gate, y, chunk):
+    """dart_sma_fwd_cont with the prior memories in the fp8 cache: codes
+    cache8 [B,H,max_chunks,P,N] uint8 and scales [B,H,max_chunks] f32 (see
+    include/dart.h); bfloat16 io only."""
+    B, L, H, P = E.shape
+    G, N = Q.shape[2], Q.shape[3]
+    d = DartDims(B, L, H, G, N, P, int(chunk), _io_code(E.dtype))
+    M, io, dev = L // chunk, E.dtype, E.device
+    cache_chunks = cache8.shape[2]
+    args = [_ptr(Q, "Q", io, (B, L, G, N), dev), _ptr(E, "E", io, (B, L, H, P), dev),
+            _ptr(C, "C", io, (B, L, G, N), dev),
+            _ptr(cache8, "cache8", torch.uint8, (B, H, cache_chunks, P, N), dev),
+            _ptr(scale, "scale", torch.float32, (B, H, cache_chunks), dev),
+            _ptr(dH, "dH", io, (B, H, M, P, N), dev),
+            _ptr(y_ssd, "y_ssd", io, (B, L, H, P), dev)]
+    yp = _ptr(y, "y", io, (B, L, H, P), dev)
+    check(lib().dart_sma_fwd_cont_fp8(d, int(prior_chunks), int(cache_chunks), *args,
+                                      float(gate), yp, _stream()), "dart_sma_fwd_cont_fp8")
+
+
 def dart_sma_fwd_decayed(Q, E, C, dH, acum, y_ssd, gate, y, chunk):
     """Decay-included SMA + gated add (see include/dart.h): acum [B,H,M,S]
     f32 from dart_chunk_state; y [B,L,H,P] io."""
@@ -364,12 +384,15 @@ def prefill_backward(fwd, x, dt, A, Bm, C, Q, E, gate, chunk, dy, dh_final=None)
             "dQ": sm["dQ"], "dE": sm["dE"], "dgate": sm["dgate"], "dh0": sc["dh0"]}
 
 
-def prefill_continue(x, dt, A, Bm, C, Q, E, gate, chunk, cache, prior_chunks, h0):
+def prefill_continue(x, dt, A, Bm, C, Q, E, gate, chunk, cache, prior_chunks, h0, scale=None):
     """Chunked prefill: the tokens are chunks prior_chunks, prior_chunks+1, ...
     of sequences whose first prior_chunks memories are in ``cache``
-    [B,H,max_chunks,P,N] (the decode cache) and whose state after them is
-    ``h0`` [B,H,P,N] f32.  Returns the dict of :func:`prefill` for the new
-    tokens; the new memories (out["dH"]) are not written into the cache."""
+    [B,H,max_chunks,P,N] (the decode cache: io-typed, or uint8 fp8 codes with
+    their ``scale`` [B,H,max_chunks]) and whose state after them is ``h0``
+    [B,H,P,N] f32.  Returns the dict of :func:`prefill` for the new tokens;
+    the new memories (out["dH"]) are not written into the cache."""
+    if (cache.dtype == torch.uint8) != (scale is not None):
+        raise ValueError("an fp8 cache (uint8) needs its scale, and only it takes one")
     B, L, H, P = x.shape
     N = Bm.shape[3]
     M, dev = L // chunk, x.device
@@ -386,8 +409,12 @@ def prefill_continue(x, dt, A, Bm, C, Q, E, gate, chunk, cache, prior_chunks, h0
     dart_chunk_state(x, dt, A, Bm, out["acum"], out["dH"], out["dH_f32"], chunk)
     dart_state_pass(x, dt, Bm, C, out["acum"], out["dH_f32"], h0, out["H_in"], out["h_final"],
                     out["y_ssd"], chunk)
-    dart_sma_fwd_cont(Q, E, C, cache, prior_chunks, out["dH"], out["y_ssd"], gate, out["y"],
-                      chunk)
+    if scale is not None:
+        dart_sma_fwd_cont_fp8(Q, E, C, cache, scale, prior_chunks, out["dH"], out["y_ssd"], gate,
+                              out["y"], chunk)
+    else:
+        dart_sma_fwd_cont(Q, E, C, cache, prior_chunks, out["dH"], out["y_ssd"], gate, out["y"],
+                          chunk)
     return out
 
 

@@ -84,13 +84,16 @@ struct SmaFwdFn {
   hipStream_t st;
   void* o = nullptr;
   float* lse = nullptr;
+  const uint8_t* prior8 = nullptr;
+  const float* pscale = nullptr;
   template <typename T, int N, int P>
   hipError_t run() {
     return dart::launch_sma_fwd<T, N, P>(sh, static_cast<const T*>(Q), static_cast<const T*>(E),
                                          static_cast<const T*>(C), static_cast<const T*>(dH),
                                          static_cast<const T*>(y_ssd), acum, gate,
                                          static_cast<T*>(y), static_cast<const T*>(prior), k0,
-                                         pstride, static_cast<float*>(o), lse, st);
+                                         pstride, static_cast<float*>(o), lse, prior8, pscale,
+                                         st);
   }
 };
 
@@ -238,6 +241,32 @@ extern "C" dart_status dart_sma_fwd_cont(const dart_dims* dims, int64_t prior_ch
   SmaFwdFn fn{prefill_shape(dims), Q, E, C, dH, y_ssd, nullptr, gate, y,
               prior_chunks > 0 ? cache : nullptr, static_cast<int>(prior_chunks),
               static_cast<int>(cache_chunks), static_cast<hipStream_t>(stream)};
+  return dispatch(dims->io, dims->dstate, dims->headdim, fn);
+}
+
+extern "C" dart_status dart_sma_fwd_cont_fp8(const dart_dims* dims, int64_t prior_chunks,
+                                             int64_t cache_chunks, const void* Q, const void* E,
+                                             const void* C, const uint8_t* cache8,
+                                             const float* scale, const void* dH,
+                                             const void* y_ssd, float gate, void* y,
+                                             void* stream) {
+  dart_status s = dart_validate_dims(dims);
+  if (s != DART_OK) return s;
+  if (dims->io != DART_BF16) return DART_ERR_UNSUPPORTED;
+  if (prior_chunks < 0 || cache_chunks < prior_chunks || prior_chunks > INT32_MAX ||
+      cache_chunks > INT32_MAX || prior_chunks + dims->seqlen / dims->chunk > INT32_MAX)
+    return DART_ERR_BAD_DIMS;
+  if ((s = check_ptrs(Q, E, C, dH, y_ssd, y)) != DART_OK) return s;
+  if (prior_chunks > 0 && (s = check_ptrs(cache8, scale)) != DART_OK) return s;
+  SmaFwdFn fn{prefill_shape(dims), Q, E, C, dH, y_ssd, nullptr, gate, y, nullptr,
+              static_cast<int>(prior_chunks), static_cast<int>(cache_chunks),
+              static_cast<hipStream_t>(stream)};
+  if (prior_chunks > 0) {
+    fn.prior8 = cache8;
+    fn.pscale = scale;
+  } else {
+    fn.k0 = 0;
+  }
   return dispatch(dims->io, dims->dstate, dims->headdim, fn);
 }
 

@@ -27,13 +27,15 @@ hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt,
 
 // acum == nullptr: the SMA of the pages; otherwise the decay-included variant.
 // k0 > 0: the tokens continue sequences whose first k0 memories are in prior
-// (pstride memories per (batch, head)).  o != nullptr: also write the readout
-// o [B,L,H,P] (f32) and the base-2 log-normaliser lse [B,H,L] for the backward.
+// (pstride memories per (batch, head)), or, with prior8 != nullptr, in the fp8
+// cache prior8 with one scale per memory in pscale (bf16 only; acum must be
+// nullptr).  o != nullptr: also write the readout o [B,L,H,P] (f32) and the
+// base-2 log-normaliser lse [B,H,L] for the backward.
 template <typename T, int N, int P>
 hipError_t launch_sma_fwd(const PrefillShape& s, const T* Q, const T* E, const T* C,
                           const T* dH, const T* y_ssd, const float* acum, float gate, T* y,
                           const T* prior, int k0, int pstride, float* o, float* lse,
-                          hipStream_t st);
+                          const uint8_t* prior8, const float* pscale, hipStream_t st);
 
 // cache8 == nullptr: the cache is `cache` in the io type; otherwise it is
 // the fp8 code array cache8 with one scale per memory in cscale.

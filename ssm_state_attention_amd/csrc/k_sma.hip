@@ -219,13 +219,19 @@ struct SmaMath16 {
 // sequences; memories c < k0 come from `prior` (one row of `pstride`
 // memories per (batch, head), the decode cache layout), memories c >= k0
 // from dH (chunk c - k0).
-template <typename T, int N, int P, int NTB, int WAVES, bool DECAY>
+//
+// PRIOR8 (continuation from an fp8 cache): the prior memories are E4M3 codes
+// (prior8, one power-of-two scale each in pscale); each is decoded while it
+// is staged into LDS (code·scale is exact in bfloat16), so the rest of the
+// kernel is unchanged and the loads stay one step ahead.
+template <typename T, int N, int P, int NTB, int WAVES, bool DECAY, bool PRIOR8 = false>
 __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     const T* __restrict__ Q, const T* __restrict__ E, const T* __restrict__ C,
     const T* __restrict__ dH, const T* __restrict__ y_ssd, const float* __restrict__ acum,
     float gate, T* __restrict__ y, int BH, int L, int H, int G, int S, int npq, int bg_major,
     float scale_log2, const T* __restrict__ prior, int k0, int pstride,
-    float* __restrict__ o_out, float* __restrict__ lse_out) {
+    float* __restrict__ o_out, float* __restrict__ lse_out, const uint8_t* __restrict__ prior8,
+    const float* __restrict__ pscale) {
   using MM = Mma<T>;
   constexpr int K = MM::K, KL = MM::KL, VE = Vec16<T>::n;
   // LDS row strides (elements): a 32-byte pad keeps the 16-byte fragment reads
@@ -306,24 +312,62 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   const T* pmem = k0 > 0 ? prior + (long)pair * pstride * (P * N) : nullptr;
   // loop step i multiplies memory mi(i): oldest first, or newest first with DECAY
   auto mi = [&](int i) __attribute__((always_inline)) { return DECAY ? k - 1 - i : i; };
-  vec_t stg0[VPT], stg[VPT];
-  auto gload = [&](int i, vec_t (&dst)[VPT]) __attribute__((always_inline)) {
+  // a staged memory: 16-byte vectors of the io type, or (PRIOR8) the codes
+  // of a prior memory with its scale (scale 0 marks an io-type memory)
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  struct Staged {
+    vec_t v[VPT];
+    u32x2 raw[PRIOR8 ? VPT : 1];
+    float sc;
+  };
+  const uint8_t* pmem8 = PRIOR8 && k0 > 0 ? prior8 + (long)pair * pstride * (P * N) : nullptr;
+  const float* psc = PRIOR8 && k0 > 0 ? pscale + (long)pair * pstride : nullptr;
+  Staged stg0, stg;
+  auto gload = [&](int i, Staged& dst) __attribute__((always_inline)) {
     const int c = mi(i);
+    if constexpr (PRIOR8) {
+      dst.sc = 0.f;
+      if (c < k0) {  // uniform over the workgroup
+        const u32x2* s8 = reinterpret_cast<const u32x2*>(pmem8 + (long)c * (P * N));
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+          const int vi = tid + v * NTHR;
+          if (NVEC % NTHR == 0 || vi < NVEC) dst.raw[v] = s8[vi];
+        }
+        dst.sc = psc[c];
+        return;
+      }
+    }
     const vec_t* src = reinterpret_cast<const vec_t*>(
         c < k0 ? pmem + (long)c * (P * N) : mem + (long)(c - k0) * (P * N));
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
       const int vi = tid + v * NTHR;
-      if (NVEC % NTHR == 0 || vi < NVEC) dst[v] = src[vi];
+      if (NVEC % NTHR == 0 || vi < NVEC) dst.v[v] = src[vi];
     }
   };
-  auto swrite = [&](int buf, const vec_t (&src)[VPT]) __attribute__((always_inline)) {
+  auto swrite = [&](int buf, const Staged& src) __attribute__((always_inline)) {
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
       const int vi = tid + v * NTHR;
       if (NVEC % NTHR == 0 || vi < NVEC) {
         const int p = vi / (N / VE), nv = vi % (N / VE);
-        *reinterpret_cast<vec_t*>(&sh_mem[buf][p * LDN + nv * VE]) = src[v];
+        vec_t val = src.v[v];
+        if constexpr (PRIOR8) {
+          if (src.sc != 0.f) {  // an E4M3 prior memory: decode and scale (exact)
+            typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+            for (int wd = 0; wd < 2; ++wd) {
+              const b2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src.raw[v][wd], 1.0f, false);
+              const b2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src.raw[v][wd], 1.0f, true);
+              val[4 * wd + 0] = from_f32<T>(to_f32(lo[0]) * src.sc);
+              val[4 * wd + 1] = from_f32<T>(to_f32(lo[1]) * src.sc);
+              val[4 * wd + 2] = from_f32<T>(to_f32(hi[0]) * src.sc);
+              val[4 * wd + 3] = from_f32<T>(to_f32(hi[1]) * src.sc);
+            }
+          }
+        }
+        *reinterpret_cast<vec_t*>(&sh_mem[buf][p * LDN + nv * VE]) = val;
       }
     }
   };
@@ -450,7 +494,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
 template <typename T, int N, int P, int NTB, int WAVES>
 hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T* C, const T* dH,
                          const T* y_ssd, const float* acum, float gate, T* y, const T* prior,
-                         int k0, int pstride, float* o, float* lse, hipStream_t st) {
+                         int k0, int pstride, float* o, float* lse, const uint8_t* prior8,
+                         const float* pscale, hipStream_t st) {
   const int M = s.L / s.S;
   const int BH = s.B * s.H;
   const int hpg = s.H / s.G;
@@ -460,14 +505,25 @@ hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T*
   const int ngrp = (npq + kPairsPerGroup - 1) / kPairsPerGroup;
   const long blocks = 8L * ngrp * kPairsPerGroup * M * tpc;
   const float scale_log2 = kLog2e / sqrtf(static_cast<float>(N));
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (prior8) {
+      hipLaunchKernelGGL((k_sma_fwd<T, N, P, NTB, WAVES, false, true>), dim3(blocks),
+                         dim3(64 * WAVES), 0, st, Q, E, C, dH, y_ssd, acum, gate, y, BH, s.L, s.H,
+                         s.G, s.S, npq, bg_major, scale_log2, prior, k0, pstride, o, lse, prior8,
+                         pscale);
+      return hipGetLastError();
+    }
+  } else if (prior8) {
+    return hipErrorNotSupported;
+  }
   if (acum)
     hipLaunchKernelGGL((k_sma_fwd<T, N, P, NTB, WAVES, true>), dim3(blocks), dim3(64 * WAVES), 0,
                        st, Q, E, C, dH, y_ssd, acum, gate, y, BH, s.L, s.H, s.G, s.S, npq,
-                       bg_major, scale_log2, prior, k0, pstride, o, lse);
+                       bg_major, scale_log2, prior, k0, pstride, o, lse, nullptr, nullptr);
   else
     hipLaunchKernelGGL((k_sma_fwd<T, N, P, NTB, WAVES, false>), dim3(blocks), dim3(64 * WAVES), 0,
                        st, Q, E, C, dH, y_ssd, acum, gate, y, BH, s.L, s.H, s.G, s.S, npq,
-                       bg_major, scale_log2, prior, k0, pstride, o, lse);
+                       bg_major, scale_log2, prior, k0, pstride, o, lse, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -477,27 +533,28 @@ template <typename T, int N, int P>
 hipError_t launch_sma_fwd(const PrefillShape& s, const T* Q, const T* E, const T* C,
                           const T* dH, const T* y_ssd, const float* acum, float gate, T* y,
                           const T* prior, int k0, int pstride, float* o, float* lse,
-                          hipStream_t st) {
+                          const uint8_t* prior8, const float* pscale, hipStream_t st) {
   constexpr int NTB = SmaTile<N, P>::NTB;
   const int r = s.S / (16 * NTB);  // S % 32 == 0, so r >= 1
   if (r % 8 == 0)
     return sma_fwd_waves<T, N, P, NTB, 8>(s, Q, E, C, dH, y_ssd, acum, gate, y, prior, k0,
-                                           pstride, o, lse, st);
+                                           pstride, o, lse, prior8, pscale, st);
   if (r % 4 == 0)
     return sma_fwd_waves<T, N, P, NTB, 4>(s, Q, E, C, dH, y_ssd, acum, gate, y, prior, k0,
-                                           pstride, o, lse, st);
+                                           pstride, o, lse, prior8, pscale, st);
   if (r % 2 == 0)
     return sma_fwd_waves<T, N, P, NTB, 2>(s, Q, E, C, dH, y_ssd, acum, gate, y, prior, k0,
-                                           pstride, o, lse, st);
+                                           pstride, o, lse, prior8, pscale, st);
   return sma_fwd_waves<T, N, P, NTB, 1>(s, Q, E, C, dH, y_ssd, acum, gate, y, prior, k0, pstride,
-                                        o, lse, st);
+                                        o, lse, prior8, pscale, st);
 }
 
 
 #define DART_INST_SMA(T, N, P)                                                                 \
   template hipError_t launch_sma_fwd<T, N, P>(const PrefillShape&, const T*, const T*, const T*, \
                                               const T*, const T*, const float*, float, T*,   \
-                                              const T*, int, int, float*, float*, hipStream_t);
+                                              const T*, int, int, float*, float*,           \
+                                              const uint8_t*, const float*, hipStream_t);
 DART_FOR_EACH_SHAPE(DART_INST_SMA)
 
 }  // namespace dart

@@ -180,6 +180,28 @@ def test_fp8_cache_entry_points_validate_on_host():
     assert st(ddims(mx=0), A16, 0, 0, A16, A16, None) == BAD
 
 
+def test_fp8_continuation_validates_on_host():
+    lib = dart.lib()
+    cont = lib.dart_sma_fwd_cont_fp8
+    d = dims(2, 512, 4, 2, 128, 64, 128, BF16)
+    # Q, E, C, cache8, scale, dH, y_ssd, gate, y
+    for i in range(8):
+        p = [A16] * 8
+        p[i] = None
+        assert cont(d, 3, 5, *p[:7], 0.5, p[7], None) == NULLP
+    p = [A16] * 8
+    p[3] = p[4] = MIS
+    assert cont(d, 3, 5, *p[:7], 0.5, p[7], None) == ALIGN
+    # (a NULL cache with prior_chunks = 0 passes validation and would launch:
+    # not called here)
+    assert cont(d, 6, 5, *([A16] * 7), 0.5, A16, None) == BAD
+    assert cont(d, -1, 5, *([A16] * 7), 0.5, A16, None) == BAD
+    assert cont(dims(2, 512, 4, 2, 32, 32, 128, F32), 1, 5, *([A16] * 7), 0.5, A16,
+                None) == UNSUP
+    assert cont(dims(2, 512, 4, 2, 96, 64, 128, BF16), 1, 5, *([A16] * 7), 0.5, A16,
+                None) == UNSUP
+
+
 def test_backward_entry_points_validate_on_host():
     lib = dart.lib()
     d = dims(2, 512, 4, 2, 128, 64, 128, BF16)

@@ -297,3 +297,80 @@ def test_decode_fp8_full_size_sampled():
                                             sl["C"], sl["Q"], sl["E"], 0.5, S)
         assert_parity(y[b:b + 1], y_ref, io, f"fp8 decode y b{b}")
         assert_parity(_pn_to_np(st["h"][b:b + 1]), new["h"], io, f"fp8 decode h b{b}")
+
+
+# ------------------------------------------- chunked prefill from the cache
+def _spread_memories(seed, shape, std):
+    """f64 memories in the oracle layout [..., N, P]: N(0, std²) values, each
+    memory times 2^U with U uniform in [-3, 3], so that the scales differ."""
+    rng = np.random.default_rng(seed)
+    m = rng.standard_normal(shape) * std
+    return m * np.exp2(rng.uniform(-3.0, 3.0, shape[:-2]))[..., None, None]
+
+
+@pytest.mark.parametrize("N,P,S,k0,M", [(128, 64, 64, 3, 2), (64, 64, 64, 5, 3),
+                                        (128, 128, 64, 2, 2), (32, 32, 32, 7, 2),
+                                        (128, 64, 256, 1, 2), (128, 64, 64, 0, 2)])
+def test_sma_continuation_fp8_cache(N, P, S, k0, M):
+    """dart_sma_fwd_cont_fp8 on seeded inputs: prior memories encoded by the
+    oracle (codes and scales uploaded as the cache, spare slots holding NaN
+    codes that must never be read), new memories drawn directly, y_ssd = 0
+    and gate 1, so y is the SMA readout itself; against the oracle's
+    sma_continue over the decoded priors."""
+    _need_gpu()
+    io, B, H, G = torch.bfloat16, 2, 4, 2
+    L, cap = M * S, k0 + 2
+    print(f"fp8 continuation N{N} P{P} S{S} k0={k0} M={M}", flush=True)
+    inp = synth.draw_prefill(120 + k0, B, L, H, G, N, P, io=io, qscale=10.0)
+    prior = _spread_memories(121 + k0, (B, H, k0, N, P), 0.05)
+    codes = np.full((B, H, cap, N, P), 0x7F, dtype=np.uint8)
+    scales = np.full((B, H, cap), np.nan)
+    if k0:
+        codes[:, :, :k0], scales[:, :, :k0] = _oracle_quantize(prior)
+    dH = synth.draw_state(122 + k0, (B, H, M, P, N), 0.05, io)
+    cache8 = torch.from_numpy(np.ascontiguousarray(np.swapaxes(codes, -1, -2))).to(DEV)
+    scale = torch.from_numpy(scales.astype(np.float32)).to(DEV)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    y_ssd = torch.zeros(B, L, H, P, dtype=io, device=DEV)
+    y = torch.full((B, L, H, P), float("nan"), dtype=io, device=DEV)
+    api.dart_sma_fwd_cont_fp8(d["Q"], d["E"], d["C"], cache8, scale, k0, dH.to(DEV), y_ssd, 1.0,
+                              y, S)
+    torch.cuda.synchronize()
+    n = {k: synth.as_f64(v) for k, v in inp.items()}
+    deq = oracle.fp8_dequantize(codes[:, :, :k0], scales[:, :, :k0])
+    o_ref = oracle.sma_continue(n["Q"], n["E"], n["C"], deq, _pn_to_np(dH), S)
+    assert_parity(y, o_ref, io, "SMA readout over the fp8 cache")
+
+
+def test_prefill_continuation_fp8_cache():
+    """Chunked prefill over the fp8 cache, end to end: prefill k0 chunks,
+    encode their f32 memories (dart_cache_fp8_store), continue the next M
+    chunks from the fp8 cache and the final state.  Reference: the oracle's
+    whole-sequence prefill for y_ssd and the new memories, with the SMA over
+    the oracle's own encoding of its first k0 memories.  The two encodings
+    start from memories that differ by rounding, so a code may differ by one
+    step where a value sits near a midpoint; the bar on y absorbs that."""
+    _need_gpu()
+    io, N, P, S, k0, M = torch.bfloat16, 128, 64, 64, 3, 2
+    B, H, G, gate = 2, 4, 2, 0.5
+    L = (k0 + M) * S
+    inp = synth.draw_prefill(130, B, L, H, G, N, P, io=io, qscale=10.0)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    part = lambda lo, hi: {k: (v if k == "A" else v[:, lo:hi].contiguous()) for k, v in d.items()}
+    pre, tail = part(0, k0 * S), part(k0 * S, L)
+    head = api.prefill(pre["x"], pre["dt"], pre["A"], pre["Bm"], pre["C"], pre["Q"], pre["E"],
+                       gate, S)
+    st = api.new_decode_state(B, H, G, N, P, S, k0 + M, io, DEV, fp8_cache=True)
+    api.store_memories(st, head["dH_f32"])
+    cont = api.prefill_continue(tail["x"], tail["dt"], tail["A"], tail["Bm"], tail["C"],
+                                tail["Q"], tail["E"], gate, S, st["cache8"], k0, head["h_final"],
+                                scale=st["scale"])
+    torch.cuda.synchronize()
+    n = {k: synth.as_f64(v) for k, v in inp.items()}
+    ref = oracle.prefill(n["x"], n["dt"], n["A"], n["Bm"], n["C"], n["Q"], n["E"], gate, S)
+    codes, scales = _oracle_quantize(ref["dH"][:, :, :k0])
+    sl = slice(k0 * S, L)
+    o_ref = oracle.sma_continue(n["Q"][:, sl], n["E"][:, sl], n["C"][:, sl],
+                                oracle.fp8_dequantize(codes, scales), ref["dH"][:, :, k0:], S)
+    assert_parity(cont["y"], ref["y_ssd"][:, sl] + gate * o_ref, io, "continued y (fp8 cache)")
+    assert_parity(_pn_to_np(cont["h_final"]), ref["h_final"], io, "continued final state")

@@ -211,7 +211,9 @@ dart_status dart_sma_fwd_train(const dart_dims* dims, const void* Q, const void*
  *      lse [B,H,L] f32 (both from dart_sma_fwd_train), dy [B,L,H,P] io, gate
  * out: dQ, dC [B,L,G,N] f32; dE [B,L,H,P] f32; ddH [B,H,M,P,N] f32;
  *      dgate: one f32 (device memory)
- * workspace: device memory of at least dart_sma_bwd_workspace(dims) bytes.
+ * workspace: device memory of at least dart_sma_bwd_workspace(dims) bytes:
+ *      about 4·B·H·L bytes plus 8 bytes per visible (token, memory) pair,
+ *      B·H·L·(M-1)/2 of them (~130 MB at B=4, H=32, L=8192, S=256).
  * Compiled for bf16 io with P <= 64 and chunks that are multiples of 64;
  * other dims return DART_ERR_UNSUPPORTED.
  */

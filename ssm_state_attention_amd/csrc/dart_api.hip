@@ -336,7 +336,8 @@ extern "C" dart_status dart_cache_fp8_store(const dart_decode_dims* dims, const 
 
 extern "C" size_t dart_sma_bwd_workspace(const dart_dims* dims) {
   if (dart_validate_dims(dims) != DART_OK || !bwd_supported(dims)) return 0;
-  return (dart::sma_bwd_workspace_bytes(dims->batch, dims->seqlen, dims->nheads) + 255) / 256 *
+  return (dart::sma_bwd_workspace_bytes(dims->batch, dims->seqlen, dims->nheads,
+                                        dims->chunk) + 255) / 256 *
          256;
 }
 

@@ -59,7 +59,7 @@ hipError_t launch_sma_bwd(const PrefillShape& s, const T* Q, const T* E, const T
                           const T* dH, const float* o, const float* lse, const T* dy, float gate,
                           float* dQ, float* dE, float* dC, float* ddH, float* dgate,
                           void* workspace, hipStream_t st);
-size_t sma_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H);
+size_t sma_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t S);
 
 // Scan backward (16-bit io, P <= 64, S a multiple of 64): dx, ddt, dA, dB,
 // dC (+ dC_sma), dh0 (all f32) from dy, ddH and dh_final (both may be null).

@@ -15,11 +15,14 @@
 // per-(token, memory) value is stored.
 //
 // k_sma_bwd_prep: dy·o per (token, head) and the gate gradient.
-// k_sma_bwd_tok:  token-major (as the forward): dQ, dC, dE.
-// k_sma_bwd_mem:  memory-major: ddH[c] from every later token.
-// Both recompute Zq and Zc with the forward's MFMA tiles; the products with
-// dH[c] taken along P (dQ, dC) and the token sums (ddH) read their operands
-// with gfx950's LDS transpose reads.
+// k_sma_bwd_tok:  token-major (as the forward): dQ, dC, dE; it also leaves
+//                 ds/sqrt(N) and g·α of every visible (token, memory) pair
+//                 in the workspace.
+// k_sma_bwd_mem:  memory-major: ddH[c] from every later token, from those
+//                 factors (no recomputation).
+// The token kernel recomputes Zq and Zc with the forward's MFMA tiles; the
+// products with dH[c] taken along P (dQ, dC) and the token sums (ddH) read
+// their operands with gfx950's LDS transpose reads.
 #include "dart_launch.hpp"
 #include "dart_shapes.hpp"
 
@@ -100,6 +103,13 @@ __global__ __launch_bounds__(256) void k_sma_bwd_prep(const bf16* __restrict__ d
   if (threadIdx.x == 0) part[blockIdx.x] = sh[0] + sh[1] + sh[2] + sh[3];
 }
 
+// Offset of memory c's factors within the backward workspace's factor
+// array: (batch, head) pairs one after another, each holding, for c = 0 ..
+// M-2, the S·(M-1-c) tokens of chunks c+1 .. M-1 in order.
+__host__ __device__ __forceinline__ long dsga_offset(long pair, int c, int M, int S) {
+  return (pair * M * (M - 1) / 2 + (long)c * (M - 1) - (long)c * (c - 1) / 2) * S;
+}
+
 // Σ part[0 .. n) -> *out (one workgroup, fixed order).
 __global__ __launch_bounds__(256) void k_sum(const float* __restrict__ part, long n,
                                              float* __restrict__ out) {
@@ -128,12 +138,17 @@ __global__ __launch_bounds__(256) void k_sum(const float* __restrict__ part, lon
 //     already holds (p = (2kk + e/4)·16 + 4·grp + e%4), so no exchange is needed.
 // Grid: (batch, group) pairs dealt to the 8 XCDs (blockIdx % 8) when their
 // count allows, heaviest chunks first.
+//
+// dsga: for each (batch, head) the factors (ds/sqrt(N), g·α) of memory c
+// for the tokens of chunks c+1 .. M-1, memories one after another (see
+// dsga_offset).
 template <int N, int P, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_sma_bwd_tok(
     const bf16* __restrict__ Q, const bf16* __restrict__ E, const bf16* __restrict__ C,
     const bf16* __restrict__ dH, const bf16* __restrict__ dy, const float* __restrict__ lse,
     const float* __restrict__ dyo, float gate, float* __restrict__ dQ, float* __restrict__ dE,
-    float* __restrict__ dC, int B, int L, int H, int G, int S, float scale_log2, float rsn) {
+    float* __restrict__ dC, float2* __restrict__ dsga, int B, int L, int H, int G, int S,
+    float scale_log2, float rsn) {
   constexpr int NKK = N / 32, NPB = P / 16, NNB = N / 16, NK2 = P / 32;
   constexpr int LDN = N + 16;
   constexpr int NTHR = 64 * WAVES, NVEC = P * N / 8;
@@ -222,6 +237,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_bwd_tok(
     }
     const float lse_t = lse[pair * L + tok];
     const float D_t = gate * dyo[pair * L + tok];
+    float2* fac = dsga + dsga_offset(pair, 0, M, S) + tok - S;  // memory 0's entry of tok
     floatx4 de[NPB];
 #pragma unroll
     for (int pb = 0; pb < NPB; ++pb) de[pb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -256,6 +272,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_bwd_tok(
       const float al = exp2_fast(s - lse_t);
       const float dsr = al * (da - D_t) * rsn;
       const float ga = gate * al;
+      if (grp == 0) fac[0] = float2{dsr, ga};
+      fac += (long)(M - 2 - c) * S;  // to memory c+1's entry of tok
 #pragma unroll
       for (int pb = 0; pb < NPB; ++pb) de[pb] += dsr * zq[pb];
       bf16x8 b1[NK2], b2[NK2];
@@ -295,34 +313,39 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_bwd_tok(
 }
 
 // Memory-major backward: one workgroup (4 waves) per (batch, head, memory c)
-// accumulates ddH[c] over the 64-token tiles of chunks M-1 down to c+1 (the
-// workgroups of one (batch, head) start on the same tiles, which they then
-// share through L2).  Per tile:
-//   phase 1: wave w recomputes Zq, Zc of tokens 16w .. 16w+15 (the memory's
-//            A fragments stay in registers, Q/C rows come from LDS), then
-//            α and ds, and leaves ds/sqrt(N) and g·α per token in LDS;
-//   phase 2: wave w owns n rows of ddH[c] and sums, over the 64 tokens,
-//            (Q·ds/sqrt(N)) E^T + (C·g·α) dy^T with MFMAs whose K axis is the
-//            token: both operands are token columns of the LDS tiles, read
-//            by transpose reads; the A side is scaled per token in registers.
-// Two workgroups share a CU (at most 256 VGPRs), so one's tile loads and
-// barriers overlap the other's MFMAs; the next tile's Q and C rows are
-// fetched into registers during phase 2.
+// sums ddH[c] = Σ_t (Q_t·ds/sqrt(N)) E_tᵀ + (C_t·g·α) dy_tᵀ over the 64-token
+// tiles of chunks M-1 down to c+1 (the workgroups of one (batch, head) start
+// on the same tiles, which they then share through L2).  The factors
+// ds/sqrt(N) and g·α come from the token-major kernel, so a tile needs no
+// recomputation: its Q, C, E and dy rows and its 64 factor pairs go to LDS,
+// and the sums are MFMAs whose K axis is the token, both operands read as
+// token columns by transpose reads, the A side scaled per token in
+// registers.  Wave w takes tokens 32·(w/2) .. +31 of each tile and the rows
+// n of half w%2 of ddH[c] (each E/dy column is read by two waves, each Q/C
+// column by one); the two token halves are added once at the end.  Two
+// workgroups share a CU, so one's tile stores and barriers overlap the
+// other's MFMAs, and the next tile is fetched into registers while the
+// current one is multiplied.
 template <int N, int P>
 __global__ __launch_bounds__(256, 2) void k_sma_bwd_mem(
     const bf16* __restrict__ Q, const bf16* __restrict__ E, const bf16* __restrict__ C,
-    const bf16* __restrict__ dH, const bf16* __restrict__ dy, const float* __restrict__ lse,
-    const float* __restrict__ dyo, float gate, float* __restrict__ ddH, int B, int L, int H,
-    int G, int S, float scale_log2, float rsn) {
-  constexpr int NKK = N / 32, NPB = P / 16, NNB = N / 16;
-  constexpr int NBW = NNB >= 8 ? NNB / 4 : 1;  // n blocks per wave in phase 2
-  constexpr int AW = NNB / NBW;                // waves active in phase 2
+    const bf16* __restrict__ dy, const float2* __restrict__ dsga, float* __restrict__ ddH,
+    int B, int L, int H, int G, int S) {
+  constexpr int NPB = P / 16, NNB = N / 16;
+  constexpr int NBW = NNB / 2;  // n blocks per wave
   constexpr int LDN = N + 16, LDP = P + 16, T = 64;
   constexpr int QV = T * N / 8 / 256, EV = T * P / 8 / 256;  // 16-byte vectors per thread
   static_assert(QV >= 1 && EV >= 1 && QV * 256 * 8 == T * N && EV * 256 * 8 == T * P,
                 "tile split");
-  __shared__ __align__(16) bf16 sQ[T * LDN], sC[T * LDN], sE[T * LDP], sD[T * LDP];
+  constexpr int TILE = 2 * T * LDN + 2 * T * LDP;  // bf16 elements
+  constexpr int RED = 2 * NBW * NPB * 64 * 4;       // floats of the final exchange
+  static_assert(RED * 4 <= TILE * 2, "exchange fits the tile buffers");
+  __shared__ __align__(16) bf16 sh[TILE];
   __shared__ __align__(16) float s_ds[T], s_ga[T];
+  bf16* sQ = sh;
+  bf16* sC = sQ + T * LDN;
+  bf16* sE = sC + T * LDN;
+  bf16* sD = sE + T * LDP;
 
   const int M = L / S, BH = B * H, hpg = H / G;
   int pair, c;
@@ -338,7 +361,9 @@ __global__ __launch_bounds__(256, 2) void k_sma_bwd_mem(
   const int b = pair / H, h = pair % H, g = h / hpg;
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tg = w >> 1, nh = w & 1;
   float* out = ddH + ((long)pair * M + c) * (P * N);
+  const float2* fac = dsga + dsga_offset(pair, c, M, S);  // tokens of chunks c+1 ..
 
   floatx4 acc[NBW][NPB];
 #pragma unroll
@@ -347,147 +372,109 @@ __global__ __launch_bounds__(256, 2) void k_sma_bwd_mem(
     for (int pb = 0; pb < NPB; ++pb) acc[i][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int ntile = (M - 1 - c) * (S / T);
-  if (ntile > 0) {
-    // the memory's A fragments (rows p, K = n), resident for every tile
-    bf16x8 ma[NPB][NKK];
-    const bf16* mem = dH + ((long)pair * M + c) * (P * N);
+  // tile i covers tokens tok0(i) .. +63, chunks from the last one down
+  auto tok0 = [&](int i) __attribute__((always_inline)) {
+    const int kc = M - 1 - i / (S / T);
+    return kc * S + (i % (S / T)) * T;
+  };
+  bf16x8 rq[QV], rc[QV], re[EV], rd[EV];
+  float2 rf = float2{0.f, 0.f};
+  auto fetch = [&](int i) __attribute__((always_inline)) {
+    const int t0 = tok0(i);
+    const long r0 = (long)b * L + t0;
 #pragma unroll
-    for (int pb = 0; pb < NPB; ++pb)
+    for (int v = 0; v < QV; ++v) {
+      const int vi = tid + v * 256, t = vi / (N / 8), nv = vi % (N / 8);
+      rq[v] = *reinterpret_cast<const bf16x8*>(Q + ((r0 + t) * G + g) * N + nv * 8);
+      rc[v] = *reinterpret_cast<const bf16x8*>(C + ((r0 + t) * G + g) * N + nv * 8);
+    }
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        ma[pb][kk] =
-            *reinterpret_cast<const bf16x8*>(mem + (pb * 16 + col) * N + kk * 32 + grp * 8);
-    // tile i covers tokens tok0(i) .. +63, chunks from the last one down
-    auto tok0 = [&](int i) __attribute__((always_inline)) {
-      const int kc = M - 1 - i / (S / T);
-      return kc * S + (i % (S / T)) * T;
-    };
-    bf16x8 rq[QV], rc[QV], re[EV], rd[EV];
-    auto fetch_qc = [&](int i) __attribute__((always_inline)) {
-      const long r0 = (long)b * L + tok0(i);
+    for (int v = 0; v < EV; ++v) {
+      const int vi = tid + v * 256, t = vi / (P / 8), pv = vi % (P / 8);
+      re[v] = *reinterpret_cast<const bf16x8*>(E + ((r0 + t) * H + h) * P + pv * 8);
+      rd[v] = *reinterpret_cast<const bf16x8*>(dy + ((r0 + t) * H + h) * P + pv * 8);
+    }
+    if (w == 0) rf = fac[t0 - (c + 1) * S + lane];
+  };
+  if (ntile > 0) fetch(0);
+  for (int i = 0; i < ntile; ++i) {
 #pragma unroll
-      for (int v = 0; v < QV; ++v) {
-        const int vi = tid + v * 256, t = vi / (N / 8), nv = vi % (N / 8);
-        rq[v] = *reinterpret_cast<const bf16x8*>(Q + ((r0 + t) * G + g) * N + nv * 8);
-        rc[v] = *reinterpret_cast<const bf16x8*>(C + ((r0 + t) * G + g) * N + nv * 8);
+    for (int v = 0; v < QV; ++v) {
+      const int vi = tid + v * 256, t = vi / (N / 8), nv = vi % (N / 8);
+      *reinterpret_cast<bf16x8*>(&sQ[t * LDN + nv * 8]) = rq[v];
+      *reinterpret_cast<bf16x8*>(&sC[t * LDN + nv * 8]) = rc[v];
+    }
+#pragma unroll
+    for (int v = 0; v < EV; ++v) {
+      const int vi = tid + v * 256, t = vi / (P / 8), pv = vi % (P / 8);
+      *reinterpret_cast<bf16x8*>(&sE[t * LDP + pv * 8]) = re[v];
+      *reinterpret_cast<bf16x8*>(&sD[t * LDP + pv * 8]) = rd[v];
+    }
+    if (w == 0) {
+      s_ds[lane] = rf.x;
+      s_ga[lane] = rf.y;
+    }
+    __syncthreads();
+    if (i + 1 < ntile) fetch(i + 1);
+    {
+      const int r0 = tg * 32 + 4 * grp;  // this lane's token runs r0.., r0+16..
+      const floatx4 f1a = *reinterpret_cast<const floatx4*>(&s_ds[r0]);
+      const floatx4 f1b = *reinterpret_cast<const floatx4*>(&s_ds[r0 + 16]);
+      const floatx4 f2a = *reinterpret_cast<const floatx4*>(&s_ga[r0]);
+      const floatx4 f2b = *reinterpret_cast<const floatx4*>(&s_ga[r0 + 16]);
+      bf16x8 be[NPB], bd[NPB];
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb) {
+        const int o = (r0 + col / 4) * LDP + pb * 16 + 4 * (col % 4);
+        be[pb] = cat8(lds_read_tr4(&sE[o]), lds_read_tr4(&sE[o + 16 * LDP]));
+        bd[pb] = cat8(lds_read_tr4(&sD[o]), lds_read_tr4(&sD[o + 16 * LDP]));
       }
-    };
-    auto fetch_ed = [&](int i) __attribute__((always_inline)) {
-      const long r0 = (long)b * L + tok0(i);
 #pragma unroll
-      for (int v = 0; v < EV; ++v) {
-        const int vi = tid + v * 256, t = vi / (P / 8), pv = vi % (P / 8);
-        re[v] = *reinterpret_cast<const bf16x8*>(E + ((r0 + t) * H + h) * P + pv * 8);
-        rd[v] = *reinterpret_cast<const bf16x8*>(dy + ((r0 + t) * H + h) * P + pv * 8);
-      }
-    };
-    fetch_qc(0);
-    for (int i = 0; i < ntile; ++i) {
-      const int t0 = tok0(i);
-      fetch_ed(i);
+      for (int i2 = 0; i2 < NBW; ++i2) {
+        const int nb = nh * NBW + i2;
+        const int o = (r0 + col / 4) * LDN + nb * 16 + 4 * (col % 4);
+        const bf16x4 q0 = lds_read_tr4(&sQ[o]), q1 = lds_read_tr4(&sQ[o + 16 * LDN]);
+        const bf16x4 c0 = lds_read_tr4(&sC[o]), c1 = lds_read_tr4(&sC[o + 16 * LDN]);
+        float vq[8], vc[8];
 #pragma unroll
-      for (int v = 0; v < QV; ++v) {
-        const int vi = tid + v * 256, t = vi / (N / 8), nv = vi % (N / 8);
-        *reinterpret_cast<bf16x8*>(&sQ[t * LDN + nv * 8]) = rq[v];
-        *reinterpret_cast<bf16x8*>(&sC[t * LDN + nv * 8]) = rc[v];
-      }
-#pragma unroll
-      for (int v = 0; v < EV; ++v) {
-        const int vi = tid + v * 256, t = vi / (P / 8), pv = vi % (P / 8);
-        *reinterpret_cast<bf16x8*>(&sE[t * LDP + pv * 8]) = re[v];
-        *reinterpret_cast<bf16x8*>(&sD[t * LDP + pv * 8]) = rd[v];
-      }
-      __syncthreads();
-      // phase 1: this wave's 16 tokens
-      {
-        const int tl = w * 16 + col;
-        const int tok = t0 + tl;
-        bf16x8 qf[NKK], cf[NKK];
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          qf[kk] = *reinterpret_cast<const bf16x8*>(&sQ[tl * LDN + kk * 32 + grp * 8]);
-          cf[kk] = *reinterpret_cast<const bf16x8*>(&sC[tl * LDN + kk * 32 + grp * 8]);
+        for (int e = 0; e < 4; ++e) {
+          vq[e] = to_f32(q0[e]) * f1a[e];
+          vq[4 + e] = to_f32(q1[e]) * f1b[e];
+          vc[e] = to_f32(c0[e]) * f2a[e];
+          vc[4 + e] = to_f32(c1[e]) * f2b[e];
         }
-        float s = 0.f, da = 0.f;
+        const bf16x8 aq = pack8(vq), ac = pack8(vc);
 #pragma unroll
         for (int pb = 0; pb < NPB; ++pb) {
-          floatx4 zq = floatx4{0.f, 0.f, 0.f, 0.f}, zc = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kk = 0; kk < NKK; ++kk) {
-            zq = Mma<bf16>::mma(ma[pb][kk], qf[kk], zq);
-            zc = Mma<bf16>::mma(ma[pb][kk], cf[kk], zc);
-          }
-          const bf16x4 ev = *reinterpret_cast<const bf16x4*>(&sE[tl * LDP + pb * 16 + 4 * grp]);
-          const bf16x4 dv = *reinterpret_cast<const bf16x4*>(&sD[tl * LDP + pb * 16 + 4 * grp]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            s += zq[e] * to_f32(ev[e]);
-            da += zc[e] * to_f32(dv[e]);
-          }
-        }
-        s = sum_lane_groups(s) * scale_log2;
-        da = sum_lane_groups(da) * gate;
-        const long lt = (long)pair * L + tok;
-        const float al = exp2_fast(s - lse[lt]);
-        if (grp == 0) {
-          s_ds[tl] = al * (da - gate * dyo[lt]) * rsn;
-          s_ga[tl] = gate * al;
+          acc[i2][pb] = Mma<bf16>::mma(aq, be[pb], acc[i2][pb]);
+          acc[i2][pb] = Mma<bf16>::mma(ac, bd[pb], acc[i2][pb]);
         }
       }
-      __syncthreads();
-      // the next tile's Q and C rows are in flight during phase 2 (more would
-      // push the registers past 256)
-      if (i + 1 < ntile) fetch_qc(i + 1);
-      // phase 2: ddH rows n of this wave, K = the tile's 64 tokens
-      if (w < AW) {
-#pragma unroll
-        for (int ks = 0; ks < T / 32; ++ks) {
-          const int r0 = ks * 32 + 4 * grp;  // this lane's token runs r0.., r0+16..
-          const floatx4 f1a = *reinterpret_cast<const floatx4*>(&s_ds[r0]);
-          const floatx4 f1b = *reinterpret_cast<const floatx4*>(&s_ds[r0 + 16]);
-          const floatx4 f2a = *reinterpret_cast<const floatx4*>(&s_ga[r0]);
-          const floatx4 f2b = *reinterpret_cast<const floatx4*>(&s_ga[r0 + 16]);
-          bf16x8 be[NPB], bd[NPB];
-#pragma unroll
-          for (int pb = 0; pb < NPB; ++pb) {
-            const int o = (r0 + col / 4) * LDP + pb * 16 + 4 * (col % 4);
-            be[pb] = cat8(lds_read_tr4(&sE[o]), lds_read_tr4(&sE[o + 16 * LDP]));
-            bd[pb] = cat8(lds_read_tr4(&sD[o]), lds_read_tr4(&sD[o + 16 * LDP]));
-          }
-#pragma unroll
-          for (int i2 = 0; i2 < NBW; ++i2) {
-            const int nb = w * NBW + i2;
-            const int o = (r0 + col / 4) * LDN + nb * 16 + 4 * (col % 4);
-            const bf16x4 q0 = lds_read_tr4(&sQ[o]), q1 = lds_read_tr4(&sQ[o + 16 * LDN]);
-            const bf16x4 c0 = lds_read_tr4(&sC[o]), c1 = lds_read_tr4(&sC[o + 16 * LDN]);
-            float vq[8], vc[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              vq[e] = to_f32(q0[e]) * f1a[e];
-              vq[4 + e] = to_f32(q1[e]) * f1b[e];
-              vc[e] = to_f32(c0[e]) * f2a[e];
-              vc[4 + e] = to_f32(c1[e]) * f2b[e];
-            }
-            const bf16x8 aq = pack8(vq), ac = pack8(vc);
-#pragma unroll
-            for (int pb = 0; pb < NPB; ++pb) {
-              acc[i2][pb] = Mma<bf16>::mma(aq, be[pb], acc[i2][pb]);
-              acc[i2][pb] = Mma<bf16>::mma(ac, bd[pb], acc[i2][pb]);
-            }
-          }
-        }
-      }
-      __syncthreads();
     }
+    __syncthreads();
   }
-  // ddH[c] rows [p][n]: lane holds n = nb·16 + 4·grp .. +3 of column p = pb·16 + col
-  if (w < AW) {
+  // the second token half hands its sums to the first through LDS
+  float* red = reinterpret_cast<float*>(sh);
+  if (tg == 1) {
 #pragma unroll
     for (int i2 = 0; i2 < NBW; ++i2)
 #pragma unroll
       for (int pb = 0; pb < NPB; ++pb)
-        *reinterpret_cast<floatx4*>(out + (pb * 16 + col) * N + (w * NBW + i2) * 16 + 4 * grp) =
+        *reinterpret_cast<floatx4*>(&red[(((nh * NBW + i2) * NPB + pb) * 64 + lane) * 4]) =
             acc[i2][pb];
+  }
+  __syncthreads();
+  // ddH[c] rows [p][n]: lane holds n = nb·16 + 4·grp .. +3 of column p = pb·16 + col
+  if (tg == 0) {
+#pragma unroll
+    for (int i2 = 0; i2 < NBW; ++i2)
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb) {
+        const int nb = nh * NBW + i2;
+        *reinterpret_cast<floatx4*>(out + (pb * 16 + col) * N + nb * 16 + 4 * grp) =
+            acc[i2][pb] +
+            *reinterpret_cast<const floatx4*>(&red[((nb * NPB + pb) * 64 + lane) * 4]);
+      }
   }
 }
 
@@ -503,11 +490,12 @@ hipError_t launch_sma_bwd(const PrefillShape& s, const T* Q, const T* E, const T
   } else {
     const int M = s.L / s.S;
     const long rows = (long)s.B * s.L;
+    const long pblocks = (rows + kPrepRows - 1) / kPrepRows;
     float* dyo = static_cast<float*>(workspace);
     float* part = dyo + ((rows * s.H + 63) / 64) * 64;
+    float2* dsga = reinterpret_cast<float2*>(part + (pblocks + 63) / 64 * 64);
     const float scale_log2 = kLog2e / sqrtf(static_cast<float>(N));
     const float rsn = 1.f / sqrtf(static_cast<float>(N));
-    const long pblocks = (rows + kPrepRows - 1) / kPrepRows;
     hipLaunchKernelGGL((k_sma_bwd_prep<P>), dim3(pblocks), dim3(256), 0, st, dy, o, dyo, part,
                        rows, s.L, s.H);
     hipError_t e = hipGetLastError();
@@ -518,20 +506,26 @@ hipError_t launch_sma_bwd(const PrefillShape& s, const T* Q, const T* E, const T
     const long tblocks = (long)s.B * s.G * M * (s.S / (16 * waves));
     if (waves == 8)
       hipLaunchKernelGGL((k_sma_bwd_tok<N, P, 8>), dim3(tblocks), dim3(512), 0, st, Q, E, C, dH,
-                         dy, lse, dyo, gate, dQ, dE, dC, s.B, s.L, s.H, s.G, s.S, scale_log2, rsn);
+                         dy, lse, dyo, gate, dQ, dE, dC, dsga, s.B, s.L, s.H, s.G, s.S,
+                         scale_log2, rsn);
     else
       hipLaunchKernelGGL((k_sma_bwd_tok<N, P, 4>), dim3(tblocks), dim3(256), 0, st, Q, E, C, dH,
-                         dy, lse, dyo, gate, dQ, dE, dC, s.B, s.L, s.H, s.G, s.S, scale_log2, rsn);
+                         dy, lse, dyo, gate, dQ, dE, dC, dsga, s.B, s.L, s.H, s.G, s.S,
+                         scale_log2, rsn);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((k_sma_bwd_mem<N, P>), dim3((long)s.B * s.H * M), dim3(256), 0, st, Q, E,
-                       C, dH, dy, lse, dyo, gate, ddH, s.B, s.L, s.H, s.G, s.S, scale_log2, rsn);
+                       C, dy, dsga, ddH, s.B, s.L, s.H, s.G, s.S);
     return hipGetLastError();
   }
 }
 
-size_t sma_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H) {
-  const size_t rows = static_cast<size_t>(B * L);
-  return (((rows * H + 63) / 64) * 64 + (rows + kPrepRows - 1) / kPrepRows) * sizeof(float);
+// dy·o [B,H,L] and the gate partials (f32, each padded to 64 values), then
+// the factor pairs of every visible (token, memory): B·H·L·(M-1)/2 float2.
+size_t sma_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t S) {
+  const size_t rows = static_cast<size_t>(B * L), M = static_cast<size_t>(L / S);
+  const size_t pblocks = (rows + kPrepRows - 1) / kPrepRows;
+  return (((rows * H + 63) / 64) * 64 + (pblocks + 63) / 64 * 64) * sizeof(float) +
+         static_cast<size_t>(B * H * S) * (M * (M - 1) / 2) * sizeof(float2);
 }
 
 #define DART_INST_SMA_BWD(T, N, P)                                                              \

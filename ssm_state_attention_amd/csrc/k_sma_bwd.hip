@@ -312,58 +312,54 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_bwd_tok(
   }
 }
 
-// Memory-major backward: one workgroup (4 waves) per (batch, head, memory c)
-// sums ddH[c] = Σ_t (Q_t·ds/sqrt(N)) E_tᵀ + (C_t·g·α) dy_tᵀ over the 64-token
-// tiles of chunks M-1 down to c+1 (the workgroups of one (batch, head) start
-// on the same tiles, which they then share through L2).  The factors
-// ds/sqrt(N) and g·α come from the token-major kernel, so a tile needs no
-// recomputation: its Q, C, E and dy rows and its 64 factor pairs go to LDS,
-// and the sums are MFMAs whose K axis is the token, both operands read as
-// token columns by transpose reads, the A side scaled per token in
-// registers.  Wave w takes tokens 32·(w/2) .. +31 of each tile and the rows
-// n of half w%2 of ddH[c] (each E/dy column is read by two waves, each Q/C
-// column by one); the two token halves are added once at the end.  Two
-// workgroups share a CU, so one's tile stores and barriers overlap the
-// other's MFMAs, and the next tile is fetched into registers while the
-// current one is multiplied.
+// Memory-major backward: one workgroup (8 waves) per (batch, head) and pair
+// of memories c0 = 2j, c1 = 2j+1, summing ddH[c] = Σ_t (Q_t·ds/sqrt(N)) E_tᵀ +
+// (C_t·g·α) dy_tᵀ over the 64-token tiles of chunks M-1 down to c0+1 (the
+// tiles of chunk c1 count for c0 only).  The factors ds/sqrt(N) and g·α come
+// from the token-major kernel, so a tile needs no recomputation: its Q and
+// C rows are staged in LDS once for both memories, its E and dy rows once
+// per memory, already scaled by that memory's factors (double-buffered, one
+// barrier per tile; the next tile and its factors are fetched into
+// registers while the current one is multiplied), and the sums are MFMAs
+// whose K axis is the token, both operands read as token columns by
+// transpose reads straight into the MFMAs.
+// Waves 4m .. 4m+3 take memory c0 + m; among them wave w takes tokens
+// 32·(w/2 % 2) .. +31 of each tile and the rows n of half w%2 of ddH[c]
+// (each E/dy column is read by two waves of a memory, each Q/C column by
+// one); the two token halves are added once at the end.  The workgroups of
+// one (batch, head) start on the same tiles and share them through L2.
 template <int N, int P>
-__global__ __launch_bounds__(256, 2) void k_sma_bwd_mem(
+__global__ __launch_bounds__(512) void k_sma_bwd_mem(
     const bf16* __restrict__ Q, const bf16* __restrict__ E, const bf16* __restrict__ C,
     const bf16* __restrict__ dy, const float2* __restrict__ dsga, float* __restrict__ ddH,
     int B, int L, int H, int G, int S) {
   constexpr int NPB = P / 16, NNB = N / 16;
   constexpr int NBW = NNB / 2;  // n blocks per wave
-  constexpr int LDN = N + 16, LDP = P + 16, T = 64;
-  constexpr int QV = T * N / 8 / 256, EV = T * P / 8 / 256;  // 16-byte vectors per thread
-  static_assert(QV >= 1 && EV >= 1 && QV * 256 * 8 == T * N && EV * 256 * 8 == T * P,
-                "tile split");
-  constexpr int TILE = 2 * T * LDN + 2 * T * LDP;  // bf16 elements
-  constexpr int RED = 2 * NBW * NPB * 64 * 4;       // floats of the final exchange
-  static_assert(RED * 4 <= TILE * 2, "exchange fits the tile buffers");
-  __shared__ __align__(16) bf16 sh[TILE];
-  __shared__ __align__(16) float s_ds[T], s_ga[T];
-  bf16* sQ = sh;
-  bf16* sC = sQ + T * LDN;
-  bf16* sE = sC + T * LDN;
-  bf16* sD = sE + T * LDP;
+  constexpr int LDN = N + 16, LDP = P + 16, T = 64, NT = 512;
+  constexpr int QN = T * N / 8, EN = T * P / 8;  // 16-byte vectors of a Q (C) and an E (dy) tile
+  constexpr int QV = (QN + NT - 1) / NT, EV = (EN + NT - 1) / NT;
+  constexpr int TILE = 2 * T * LDN + 4 * T * LDP;  // bf16: Q, C, then E·ds, dy·gα per memory
+  constexpr int RED = 2 * NBW * NPB * 64 * 4;       // floats of one memory's final exchange
+  constexpr int SH = 2 * TILE > RED * 4 ? 2 * TILE : RED * 4;  // RED * 4 bf16 = 2·RED floats
+  __shared__ __align__(16) bf16 sh[SH];
 
   const int M = L / S, BH = B * H, hpg = H / G;
-  int pair, c;
+  int pair, j;
   if ((B * G) % 8 == 0) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per = BH / 8;
-    const int j = slot % per;
-    c = slot / per;
-    pair = ((j / hpg) * 8 + xcd) * hpg + j % hpg;
+    const int jj = slot % per;
+    j = slot / per;
+    pair = ((jj / hpg) * 8 + xcd) * hpg + jj % hpg;
   } else {
     pair = blockIdx.x % BH;
-    c = blockIdx.x / BH;
+    j = blockIdx.x / BH;
   }
   const int b = pair / H, h = pair % H, g = h / hpg;
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tg = w >> 1, nh = w & 1;
-  float* out = ddH + ((long)pair * M + c) * (P * N);
-  const float2* fac = dsga + dsga_offset(pair, c, M, S);  // tokens of chunks c+1 ..
+  const int mw = w >> 2, tg = (w >> 1) & 1, nh = w & 1;
+  const int c0 = 2 * j, c = c0 + mw;
+  const bool live = c < M;  // c1 = M when M is odd: no memory
 
   floatx4 acc[NBW][NPB];
 #pragma unroll
@@ -371,90 +367,112 @@ __global__ __launch_bounds__(256, 2) void k_sma_bwd_mem(
 #pragma unroll
     for (int pb = 0; pb < NPB; ++pb) acc[i][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const int ntile = (M - 1 - c) * (S / T);
-  // tile i covers tokens tok0(i) .. +63, chunks from the last one down
+  const int ntile = (M - 1 - c0) * (S / T);
+  // tile i covers tokens tok0(i) .. +63 of chunk kc(i), chunks from the last one down
+  auto kc = [&](int i) __attribute__((always_inline)) { return M - 1 - i / (S / T); };
   auto tok0 = [&](int i) __attribute__((always_inline)) {
-    const int kc = M - 1 - i / (S / T);
-    return kc * S + (i % (S / T)) * T;
+    return kc(i) * S + (i % (S / T)) * T;
   };
   bf16x8 rq[QV], rc[QV], re[EV], rd[EV];
-  float2 rf = float2{0.f, 0.f};
+  float2 rf[2][EV];  // factors (ds/sqrt(N), g·α) of the token of re[v], per memory
+  const bool live1 = c0 + 1 < M;
+  const long f0 = dsga_offset(pair, c0, M, S) - (long)(c0 + 1) * S;
+  const long f1 = live1 ? dsga_offset(pair, c0 + 1, M, S) - (long)(c0 + 2) * S : 0;
   auto fetch = [&](int i) __attribute__((always_inline)) {
     const int t0 = tok0(i);
     const long r0 = (long)b * L + t0;
 #pragma unroll
     for (int v = 0; v < QV; ++v) {
-      const int vi = tid + v * 256, t = vi / (N / 8), nv = vi % (N / 8);
-      rq[v] = *reinterpret_cast<const bf16x8*>(Q + ((r0 + t) * G + g) * N + nv * 8);
-      rc[v] = *reinterpret_cast<const bf16x8*>(C + ((r0 + t) * G + g) * N + nv * 8);
+      const int vi = tid + v * NT, t = vi / (N / 8), nv = vi % (N / 8);
+      if (QN % NT == 0 || vi < QN) {
+        rq[v] = *reinterpret_cast<const bf16x8*>(Q + ((r0 + t) * G + g) * N + nv * 8);
+        rc[v] = *reinterpret_cast<const bf16x8*>(C + ((r0 + t) * G + g) * N + nv * 8);
+      }
     }
 #pragma unroll
     for (int v = 0; v < EV; ++v) {
-      const int vi = tid + v * 256, t = vi / (P / 8), pv = vi % (P / 8);
-      re[v] = *reinterpret_cast<const bf16x8*>(E + ((r0 + t) * H + h) * P + pv * 8);
-      rd[v] = *reinterpret_cast<const bf16x8*>(dy + ((r0 + t) * H + h) * P + pv * 8);
+      const int vi = tid + v * NT, t = vi / (P / 8), pv = vi % (P / 8);
+      if (EN % NT == 0 || vi < EN) {
+        re[v] = *reinterpret_cast<const bf16x8*>(E + ((r0 + t) * H + h) * P + pv * 8);
+        rd[v] = *reinterpret_cast<const bf16x8*>(dy + ((r0 + t) * H + h) * P + pv * 8);
+        rf[0][v] = dsga[f0 + t0 + t];
+        // memory c1 takes no part in the tiles of its own chunk
+        rf[1][v] = live1 && kc(i) > c0 + 1 ? dsga[f1 + t0 + t] : float2{0.f, 0.f};
+      }
     }
-    if (w == 0) rf = fac[t0 - (c + 1) * S + lane];
   };
-  if (ntile > 0) fetch(0);
-  for (int i = 0; i < ntile; ++i) {
+  auto stage = [&](int buf) __attribute__((always_inline)) {
+    bf16* sQ = sh + buf * TILE;
+    bf16* sC = sQ + T * LDN;
+    bf16* sE = sC + T * LDN;  // [memory][t][p], then sD likewise
+    bf16* sD = sE + 2 * T * LDP;
 #pragma unroll
     for (int v = 0; v < QV; ++v) {
-      const int vi = tid + v * 256, t = vi / (N / 8), nv = vi % (N / 8);
-      *reinterpret_cast<bf16x8*>(&sQ[t * LDN + nv * 8]) = rq[v];
-      *reinterpret_cast<bf16x8*>(&sC[t * LDN + nv * 8]) = rc[v];
+      const int vi = tid + v * NT, t = vi / (N / 8), nv = vi % (N / 8);
+      if (QN % NT == 0 || vi < QN) {
+        *reinterpret_cast<bf16x8*>(&sQ[t * LDN + nv * 8]) = rq[v];
+        *reinterpret_cast<bf16x8*>(&sC[t * LDN + nv * 8]) = rc[v];
+      }
     }
 #pragma unroll
     for (int v = 0; v < EV; ++v) {
-      const int vi = tid + v * 256, t = vi / (P / 8), pv = vi % (P / 8);
-      *reinterpret_cast<bf16x8*>(&sE[t * LDP + pv * 8]) = re[v];
-      *reinterpret_cast<bf16x8*>(&sD[t * LDP + pv * 8]) = rd[v];
+      const int vi = tid + v * NT, t = vi / (P / 8), pv = vi % (P / 8);
+      if (EN % NT == 0 || vi < EN) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          float ve[8], vd[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            ve[e] = to_f32(re[v][e]) * rf[m][v].x;
+            vd[e] = to_f32(rd[v][e]) * rf[m][v].y;
+          }
+          *reinterpret_cast<bf16x8*>(&sE[(m * T + t) * LDP + pv * 8]) = pack8(ve);
+          *reinterpret_cast<bf16x8*>(&sD[(m * T + t) * LDP + pv * 8]) = pack8(vd);
+        }
+      }
     }
-    if (w == 0) {
-      s_ds[lane] = rf.x;
-      s_ga[lane] = rf.y;
+  };
+  auto multiply = [&](int buf) __attribute__((always_inline)) {
+    const bf16* sQ = sh + buf * TILE;
+    const bf16* sC = sQ + T * LDN;
+    const bf16* sE = sC + T * LDN + mw * T * LDP;  // this wave's memory
+    const bf16* sD = sE + 2 * T * LDP;
+    const int r0 = tg * 32 + 4 * grp;  // this lane's token runs r0.., r0+16..
+    bf16x8 be[NPB], bd[NPB];
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb) {
+      const int o = (r0 + col / 4) * LDP + pb * 16 + 4 * (col % 4);
+      be[pb] = cat8(lds_read_tr4(&sE[o]), lds_read_tr4(&sE[o + 16 * LDP]));
+      bd[pb] = cat8(lds_read_tr4(&sD[o]), lds_read_tr4(&sD[o + 16 * LDP]));
     }
-    __syncthreads();
-    if (i + 1 < ntile) fetch(i + 1);
-    {
-      const int r0 = tg * 32 + 4 * grp;  // this lane's token runs r0.., r0+16..
-      const floatx4 f1a = *reinterpret_cast<const floatx4*>(&s_ds[r0]);
-      const floatx4 f1b = *reinterpret_cast<const floatx4*>(&s_ds[r0 + 16]);
-      const floatx4 f2a = *reinterpret_cast<const floatx4*>(&s_ga[r0]);
-      const floatx4 f2b = *reinterpret_cast<const floatx4*>(&s_ga[r0 + 16]);
-      bf16x8 be[NPB], bd[NPB];
+#pragma unroll
+    for (int i2 = 0; i2 < NBW; ++i2) {
+      const int nb = nh * NBW + i2;
+      const int o = (r0 + col / 4) * LDN + nb * 16 + 4 * (col % 4);
+      const bf16x8 aq = cat8(lds_read_tr4(&sQ[o]), lds_read_tr4(&sQ[o + 16 * LDN]));
+      const bf16x8 ac = cat8(lds_read_tr4(&sC[o]), lds_read_tr4(&sC[o + 16 * LDN]));
 #pragma unroll
       for (int pb = 0; pb < NPB; ++pb) {
-        const int o = (r0 + col / 4) * LDP + pb * 16 + 4 * (col % 4);
-        be[pb] = cat8(lds_read_tr4(&sE[o]), lds_read_tr4(&sE[o + 16 * LDP]));
-        bd[pb] = cat8(lds_read_tr4(&sD[o]), lds_read_tr4(&sD[o + 16 * LDP]));
-      }
-#pragma unroll
-      for (int i2 = 0; i2 < NBW; ++i2) {
-        const int nb = nh * NBW + i2;
-        const int o = (r0 + col / 4) * LDN + nb * 16 + 4 * (col % 4);
-        const bf16x4 q0 = lds_read_tr4(&sQ[o]), q1 = lds_read_tr4(&sQ[o + 16 * LDN]);
-        const bf16x4 c0 = lds_read_tr4(&sC[o]), c1 = lds_read_tr4(&sC[o + 16 * LDN]);
-        float vq[8], vc[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vq[e] = to_f32(q0[e]) * f1a[e];
-          vq[4 + e] = to_f32(q1[e]) * f1b[e];
-          vc[e] = to_f32(c0[e]) * f2a[e];
-          vc[4 + e] = to_f32(c1[e]) * f2b[e];
-        }
-        const bf16x8 aq = pack8(vq), ac = pack8(vc);
-#pragma unroll
-        for (int pb = 0; pb < NPB; ++pb) {
-          acc[i2][pb] = Mma<bf16>::mma(aq, be[pb], acc[i2][pb]);
-          acc[i2][pb] = Mma<bf16>::mma(ac, bd[pb], acc[i2][pb]);
-        }
+        acc[i2][pb] = Mma<bf16>::mma(aq, be[pb], acc[i2][pb]);
+        acc[i2][pb] = Mma<bf16>::mma(ac, bd[pb], acc[i2][pb]);
       }
     }
+  };
+  if (ntile > 0) {
+    fetch(0);
+    stage(0);
+  }
+  __syncthreads();
+  for (int i = 0; i < ntile; ++i) {
+    // buffer i&1 holds tile i; buffer (i+1)&1 was last read before the
+    // previous barrier
+    if (i + 1 < ntile) fetch(i + 1);
+    if (live && kc(i) > c) multiply(i & 1);  // uniform over the wave
+    if (i + 1 < ntile) stage((i + 1) & 1);
     __syncthreads();
   }
-  // the second token half hands its sums to the first through LDS
-  float* red = reinterpret_cast<float*>(sh);
+  // the second token half of each memory hands its sums to the first
+  float* red = reinterpret_cast<float*>(sh) + mw * RED;
   if (tg == 1) {
 #pragma unroll
     for (int i2 = 0; i2 < NBW; ++i2)
@@ -465,7 +483,8 @@ __global__ __launch_bounds__(256, 2) void k_sma_bwd_mem(
   }
   __syncthreads();
   // ddH[c] rows [p][n]: lane holds n = nb·16 + 4·grp .. +3 of column p = pb·16 + col
-  if (tg == 0) {
+  if (tg == 0 && live) {
+    float* out = ddH + ((long)pair * M + c) * (P * N);
 #pragma unroll
     for (int i2 = 0; i2 < NBW; ++i2)
 #pragma unroll
@@ -513,8 +532,8 @@ hipError_t launch_sma_bwd(const PrefillShape& s, const T* Q, const T* E, const T
                          dy, lse, dyo, gate, dQ, dE, dC, dsga, s.B, s.L, s.H, s.G, s.S,
                          scale_log2, rsn);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_sma_bwd_mem<N, P>), dim3((long)s.B * s.H * M), dim3(256), 0, st, Q, E,
-                       C, dy, dsga, ddH, s.B, s.L, s.H, s.G, s.S);
+    hipLaunchKernelGGL((k_sma_bwd_mem<N, P>), dim3((long)s.B * s.H * ((M + 1) / 2)), dim3(512),
+                       0, st, Q, E, C, dy, dsga, ddH, s.B, s.L, s.H, s.G, s.S);
     return hipGetLastError();
   }
 }

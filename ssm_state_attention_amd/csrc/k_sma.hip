@@ -251,11 +251,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   constexpr int QV = TWG * (N / VE) / NTHR;  // vectors per thread, Q or C tile
   constexpr int EV = TWG * (P / VE) / NTHR;  // vectors per thread, E or y tile
   static_assert(QV * NTHR == TWG * (N / VE) && EV * NTHR == TWG * (P / VE), "tile split");
-  constexpr int R1A = TWG * LDN > TWG * LDE ? TWG * LDN : TWG * LDE;
+  constexpr int R1A = TWG * LDN + TWG * LDE;
   constexpr int R1 = R1A > 2 * P * LDN ? R1A : 2 * P * LDN;
   typedef typename Vec16<T>::vec vec_t;
-  // sh_r1: the Q, C and E tiles in turn during the prologue, then the two
-  // memory buffers; sh_ty: y_ssd, overwritten by y in the epilogue
+  // sh_r1: the Q and E tiles side by side, then the C tile, during the
+  // prologue, then the two memory buffers; sh_ty: y_ssd, overwritten by y in
+  // the epilogue
   __shared__ __align__(16) T sh_r1[R1];
   __shared__ __align__(16) T sh_ty[TWG * LDE];
   T(*sh_mem)[P * LDN] = reinterpret_cast<T(*)[P * LDN]>(sh_r1);
@@ -286,7 +287,26 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   const int col = lane & 15, grp = lane >> 4;
   const long row0 = (long)b * L + (long)kl * S + sub * TWG;  // first token of the tile
 
-  // ---- prologue: every load in flight before the first wait ----
+  if (k == 0) {  // no memory is visible: y = y_ssd, o = 0, lse = 0
+#pragma unroll
+    for (int v = 0; v < EV; ++v) {
+      const int i = tid + v * NTHR, t = i / (P / VE), pv = i % (P / VE);
+      *reinterpret_cast<vec_t*>(y + ((row0 + t) * H + h) * P + pv * VE) =
+          load16(y_ssd + ((row0 + t) * H + h) * P + pv * VE);
+    }
+    if (o_out) {
+      for (int i = tid; i < TWG * (P / 4); i += NTHR) {
+        const int t = i / (P / 4), p4 = i % (P / 4);
+        *reinterpret_cast<floatx4*>(o_out + ((row0 + t) * H + h) * P + 4 * p4) =
+            floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+      for (int t = tid; t < TWG; t += NTHR)
+        lse_out[(long)pair * L + (long)kl * S + sub * TWG + t] = 0.f;
+    }
+    return;
+  }
+  // ---- prologue: every load in flight before the first wait, in the
+  // order they are staged ----
   vec_t qs[QV], cs[QV], es[EV], ys[EV];
 #pragma unroll
   for (int v = 0; v < QV; ++v) {
@@ -296,7 +316,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
 #pragma unroll
   for (int v = 0; v < EV; ++v) {
     const int i = tid + v * NTHR, t = i / (P / VE), pv = i % (P / VE);
-    ys[v] = load16(y_ssd + ((row0 + t) * H + h) * P + pv * VE);
+    es[v] = load16(E + ((row0 + t) * H + h) * P + pv * VE);
   }
 #pragma unroll
   for (int v = 0; v < QV; ++v) {
@@ -306,7 +326,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
 #pragma unroll
   for (int v = 0; v < EV; ++v) {
     const int i = tid + v * NTHR, t = i / (P / VE), pv = i % (P / VE);
-    es[v] = load16(E + ((row0 + t) * H + h) * P + pv * VE);
+    ys[v] = load16(y_ssd + ((row0 + t) * H + h) * P + pv * VE);
   }
   const T* mem = dH + (long)pair * M * (P * N);
   const T* pmem = k0 > 0 ? prior + (long)pair * pstride * (P * N) : nullptr;
@@ -375,7 +395,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
     gload(0, stg0);
     gload(min(1, k - 1), stg);
   }
-  // Q tile -> fragments; y_ssd parked for the epilogue
+  // Q tile -> fragments; E tile -> this lane's p rows, kept in the input
+  // type (bf16 pairs halve the registers) and widened when the score is
+  // formed
+  T* sh_e = sh_r1 + TWG * LDN;
 #pragma unroll
   for (int v = 0; v < QV; ++v) {
     const int i = tid + v * NTHR, t = i / (N / VE), nv = i % (N / VE);
@@ -384,36 +407,32 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
 #pragma unroll
   for (int v = 0; v < EV; ++v) {
     const int i = tid + v * NTHR, t = i / (P / VE), pv = i % (P / VE);
-    *reinterpret_cast<vec_t*>(&sh_ty[t * LDE + pv * VE]) = ys[v];
+    *reinterpret_cast<vec_t*>(&sh_e[t * LDE + pv * VE]) = es[v];
   }
   __syncthreads();
   SmaMath16<T, N, P, NTB> tm;
   tm.init(w, lane);
   tm.load_q(sh_r1, LDN);
+  tm.load_e(sh_e, LDE);
   const float* acum_pair = DECAY ? acum + (long)pair * M * S : nullptr;
   if (DECAY) {
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) tm.at[tb] = acum_pair[(long)kl * S + sub * TWG + tm.lrow(tb)];
   }
   __syncthreads();
-  // C tile -> fragments
+  // C tile -> fragments; y_ssd parked for the epilogue
 #pragma unroll
   for (int v = 0; v < QV; ++v) {
     const int i = tid + v * NTHR, t = i / (N / VE), nv = i % (N / VE);
     *reinterpret_cast<vec_t*>(&sh_r1[t * LDN + nv * VE]) = cs[v];
   }
-  __syncthreads();
-  tm.load_c(sh_r1, LDN);
-  __syncthreads();
-  // E tile -> this lane's p rows, kept in the input type (bf16 pairs halve
-  // the registers) and widened when the score is formed
 #pragma unroll
   for (int v = 0; v < EV; ++v) {
     const int i = tid + v * NTHR, t = i / (P / VE), pv = i % (P / VE);
-    *reinterpret_cast<vec_t*>(&sh_r1[t * LDE + pv * VE]) = es[v];
+    *reinterpret_cast<vec_t*>(&sh_ty[t * LDE + pv * VE]) = ys[v];
   }
   __syncthreads();
-  tm.load_e(sh_r1, LDE);
+  tm.load_c(sh_r1, LDN);
   __syncthreads();  // sh_r1 becomes the memory buffers
 
   // DECAY: dlog is the log-decay over the chunks after the memory being

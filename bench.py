@@ -30,17 +30,17 @@ METRIC = "SMA+scan prefill tokens/s & MFMA% at L=8K; decode chunk-memory HBM GB/
 # only for the kernel source it was measured on (SHA-1 of that file).
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "ssm_state_attention_amd", "csrc")
 PROFILED_TRAFFIC = {
-    "k_sma_fwd": ("k_sma.hip", "d2c74d7f6ffb66e1aff59911d102532d1387c826",
-                  (548.41 + 134.22) * 1e6),
+    "k_sma_fwd": ("k_sma.hip", "f6f9434729a4e2da041c040785b1ddc12d04969a",
+                  (541.44 + 134.22) * 1e6),
     # the four launches of one decode call (state, stream, combine, advance)
     "dart_sma_decode": ("k_decode.hip", "1edf2954b0ac30901f6e19755b249602c54386d1",
-                        (135.75 + 134.74 + 4296.39 + 0.59 + 1.57 + 0.26) * 1e6),
+                        (135.75 + 134.74 + 4296.37 + 0.59 + 1.57 + 0.26) * 1e6),
     "dart_sma_decode_fp8": ("k_decode.hip", "1edf2954b0ac30901f6e19755b249602c54386d1",
-                            (135.76 + 134.74 + 2150.98 + 0.59 + 1.57 + 0.26) * 1e6),
+                            (135.75 + 134.74 + 2150.97 + 0.59 + 1.57 + 0.26) * 1e6),
     # the launches of one SMA backward call (dy·o pass, gate sum, token- and
     # memory-major kernels)
-    "dart_sma_bwd": ("k_sma_bwd.hip", "078b88f12c52944eb035411837c76711d43ec120",
-                     (402.77 + 8.87 + 499.19 + 402.65 + 2482.47 + 134.26 + 0.05) * 1e6),
+    "dart_sma_bwd": ("k_sma_bwd.hip", "06886dd2840539233c3b3aa764f7abb9a7d1c8a6",
+                     (402.77 + 8.85 + 0.04 + 501.35 + 532.68 + 1789.51 + 135.51) * 1e6),
 }
 
 

@@ -71,6 +71,7 @@ def _gpu_train(d, gate, S):
     (2, 384, 4, 2, 64, 64, 128, 30.0, 0.05),    # sharpened softmax
     (1, 768, 3, 3, 128, 64, 256, 1.0, 0.05),    # the layer's N, P, S
     (2, 512, 8, 1, 128, 64, 128, 100.0, 0.02),  # one group of 8 heads, sharpened
+    (2, 640, 8, 4, 128, 64, 128, 30.0, 0.05),   # 8 (batch, group) pairs: the XCD-dealt grid; 5 chunks
 ])
 def test_sma_backward(B, L, H, G, N, P, S, qscale, mem_std):
     _need_gpu()

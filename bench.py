@@ -439,7 +439,7 @@ def main():
         sys.exit(1)
     result = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
               "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
-              "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, BASE recipe)",
+              "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded: x ~ N(0,1); B, C, Q ~ N(0,1)/sqrt(N); E ~ N(0,1)/sqrt(P); dt log-uniform)",
               "config": {"workload": "DART prefill at the Mamba-2 ~370M layer shape",
                          "batch": BASE["B"], "seqlen": BASE["L"], "heads": BASE["H"],
                          "groups": BASE["G"], "dstate": BASE["N"], "headdim": BASE["P"],

@@ -415,12 +415,36 @@ def cpu_baseline(inp, seconds):
     }
 
 
+def shader_clock_levels():
+    """The shader clock's DPM levels (MHz) and the level marked current, read
+    from the amdgpu sysfs table (a file read: no tool is started); None where
+    the table is not readable."""
+    import glob
+    import re
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                lines = f.read().splitlines()
+        except OSError:
+            continue
+        levels, current = [], None
+        for line in lines:
+            m = re.search(r"(\d+)\s*Mhz", line, re.I)
+            if m:
+                levels.append(int(m.group(1)))
+                if "*" in line:
+                    current = int(m.group(1))
+        if levels:
+            return {"levels_mhz": levels, "current_mhz": current}
+    return None
+
+
 def environment(torch):
     """ROCm build and device identification."""
     prop = torch.cuda.get_device_properties(0)
     return {"hip": torch.version.hip, "torch": torch.__version__,
             "arch": getattr(prop, "gcnArchName", None), "compute_units": prop.multi_processor_count,
-            "hbm_bytes": prop.total_memory}
+            "hbm_bytes": prop.total_memory, "sclk": shader_clock_levels()}
 
 
 def main():
@@ -455,6 +479,8 @@ def main():
     pre = None
     if not args.no_prefill:
         pre = bench_prefill(args, torch, api, synth)
+        levels = shader_clock_levels()
+        result["env"]["sclk_current_after_prefill_mhz"] = levels and levels["current_mhz"]
         result["value"] = pre["tokens_per_s"]
         result["ms_per_step"] = pre["ms_per_step"]
         result["roofline"] = pre["roofline"]

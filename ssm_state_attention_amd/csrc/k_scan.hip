@@ -364,9 +364,12 @@ struct ChunkOutLds {
 //   with W[j][t] = exp(acum_t - acum_j)·dt_j for j <= t, 0 above.  W is
 //   factored per tile through the end of its key block, e(jb):
 //   u = 2^(A_t - A_e(jb)) (one exp per lane and tile) and
-//   v_j = 2^(A_e(jb) - A_j + log2 dt_j) (per key, once per head), A = acum·log2(e).
-//   Both factors stay in range (u <= 1 below the diagonal, v_j <= dt_j·2^|block|);
+//   v_j = 2^(A_e(jb) - A_j + log2 dt_j) (per key, once per head), A = acum·log2(e),
+//   for key blocks below the token's own block, where u <= 1 and v_j <= dt_j;
 //   an underflowing u means a weight far below fp32 resolution of the sum.
+//   On the diagonal block u would be a growth factor (up to the log-decay of
+//   15 tokens, which overflows for large dt·|A|), so there each weight is
+//   formed directly as 2^(A_t - A_j + log2 dt_j).
 // The weighted tile stays in registers: its D layout (rows j = 16·jb +
 // 4·grp + i of column t) is the B operand of the second product, with the
 // k-slots of xᵀ's A operand assigned the same j's.
@@ -385,6 +388,7 @@ __global__ __launch_bounds__(kOutThreads) void k_chunk_out(
   __shared__ __align__(16) unsigned char sh_raw[Lds::bytes];
   __shared__ __align__(16) float sh_at[kMaxChunk];  // A_s = acum_s·log2(e)
   __shared__ __align__(16) float sh_v[kMaxChunk];   // v_j
+  __shared__ __align__(16) float sh_ld[kMaxChunk];  // log2 dt_j
   __shared__ float sh_ae[kMaxBlk];                  // A at the end of each block
   T* sh_b = reinterpret_cast<T*>(sh_raw);
   T* sh_xt = reinterpret_cast<T*>(sh_raw);
@@ -479,8 +483,10 @@ __global__ __launch_bounds__(kOutThreads) void k_chunk_out(
     }
     if (tid < S) {
       const float a2 = ar * kLog2e, e2 = ae * kLog2e;
+      const float ld = __builtin_amdgcn_logf(dr);
       sh_at[tid] = a2;
-      sh_v[tid] = exp2_fast(e2 - a2 + __builtin_amdgcn_logf(dr));
+      sh_ld[tid] = ld;
+      sh_v[tid] = exp2_fast(e2 - a2 + ld);
       if ((tid & 15) == 15) sh_ae[tid >> 4] = a2;
     }
 #pragma unroll
@@ -524,14 +530,24 @@ __global__ __launch_bounds__(kOutThreads) void k_chunk_out(
           yin[pb] = MM::mma(MM::load(&sh_ht[(pb * 16 + col) * LDH + kk * K + grp * KL]), cf[kk],
                             yin[pb]);
       const float at_t = sh_at[t];
-      // weighted tile jb (rows j = jb*16 + 4*grp + i, column t)
+      // weighted tile jb (rows j = jb*16 + 4*grp + i, column t).  Below the
+      // diagonal block both factors are <= 1·dt_j; on it u would exceed 1
+      // (by up to the log-decay of 15 tokens), so each weight is formed
+      // directly as 2^(A_t - A_j + log2 dt_j) with A_t - A_j <= 0.
       auto weights = [&](int jb, floatx4 tile) {
-        const float u = exp2_fast(at_t - sh_ae[jb]);
-        const floatx4 vj = *reinterpret_cast<const floatx4*>(&sh_v[jb * 16 + 4 * grp]);
         floatx4 wv;
+        if (jb < tb) {
+          const float u = exp2_fast(at_t - sh_ae[jb]);
+          const floatx4 vj = *reinterpret_cast<const floatx4*>(&sh_v[jb * 16 + 4 * grp]);
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-          wv[i4] = (jb * 16 + 4 * grp + i4 <= t) ? tile[i4] * (u * vj[i4]) : 0.f;
+          for (int i4 = 0; i4 < 4; ++i4) wv[i4] = tile[i4] * (u * vj[i4]);
+        } else {
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int j = jb * 16 + 4 * grp + i4;
+            wv[i4] = j <= t ? tile[i4] * exp2_fast((at_t - sh_at[j]) + sh_ld[j]) : 0.f;
+          }
+        }
         return wv;
       };
       if constexpr (std::is_same<T, float>::value) {
@@ -632,6 +648,7 @@ __global__ __launch_bounds__(kOutThreads) void k_chunk_out_tr(
   __shared__ __align__(16) unsigned char sh_raw[Lds::bytes];
   __shared__ __align__(16) float sh_at[kMaxChunk];  // A_s = acum_s·log2(e)
   __shared__ __align__(16) float sh_v[kMaxChunk];   // v_j
+  __shared__ __align__(16) float sh_ld[kMaxChunk];  // log2 dt_j
   bf16* sh_b = reinterpret_cast<bf16*>(sh_raw);
   bf16* sh_c = sh_b + kMaxChunk * LDC;
   bf16* sh_x = reinterpret_cast<bf16*>(sh_raw);
@@ -748,8 +765,10 @@ __global__ __launch_bounds__(kOutThreads) void k_chunk_out_tr(
       const float a2 = ar * kLog2e;
       const float e2 = __shfl(a2, lane | 15);
       if (tid < S) {
+        const float ld = __builtin_amdgcn_logf(dr);
         sh_at[tid] = a2;
-        sh_v[tid] = exp2_fast(e2 - a2 + __builtin_amdgcn_logf(dr));
+        sh_ld[tid] = ld;
+        sh_v[tid] = exp2_fast(e2 - a2 + ld);
       }
     }
     __syncthreads();
@@ -776,15 +795,25 @@ __global__ __launch_bounds__(kOutThreads) void k_chunk_out_tr(
                            yin[q]);
       }
       // weighted tile jb (rows j = jb*16 + 4*grp + i, column t).  The tiles
-      // are causally masked already and zero above the diagonal block; the
-      // clamp keeps u finite there (u <= 1 below the diagonal), so a zero
-      // tile stays zero.
+      // are causally masked already.  Below the diagonal block the factored
+      // weight u·v_j has both factors <= 1·dt_j; on the diagonal block each
+      // weight is 2^(A_t - A_j + log2 dt_j) with A_t - A_j <= 0 for the
+      // unmasked keys; above it (the second block of a pair) it is zero.
+      // tb is wave-uniform, so these are scalar branches.
       auto weights = [&](int jb, floatx4 tile) __attribute__((always_inline)) {
-        const float u = exp2_fast(fminf(at_t - sh_at[jb * 16 + 15], 126.f));
-        const floatx4 vj = *reinterpret_cast<const floatx4*>(&sh_v[jb * 16 + 4 * grp]);
-        floatx4 wv;
+        floatx4 wv = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (jb < tb) {
+          const float u = exp2_fast(at_t - sh_at[jb * 16 + 15]);
+          const floatx4 vj = *reinterpret_cast<const floatx4*>(&sh_v[jb * 16 + 4 * grp]);
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) wv[i4] = (tile[i4] * u) * vj[i4];
+          for (int i4 = 0; i4 < 4; ++i4) wv[i4] = (tile[i4] * u) * vj[i4];
+        } else if (jb == tb) {
+          const floatx4 aj = *reinterpret_cast<const floatx4*>(&sh_at[jb * 16 + 4 * grp]);
+          const floatx4 lj = *reinterpret_cast<const floatx4*>(&sh_ld[jb * 16 + 4 * grp]);
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4)
+            wv[i4] = 4 * grp + i4 <= col ? tile[i4] * exp2_fast((at_t - aj[i4]) + lj[i4]) : 0.f;
+        }
         return wv;
       };
 #pragma unroll

@@ -538,10 +538,19 @@ def prefill(x, dt, A, Bm, C, Q, E, g, S, h0=None, decayed=False):
 # --------------------------------------------------------------------------
 def round_bf16(a):
     """Round fp64 values to the nearest bfloat16 (ties to even), returned as
-    fp64.  Used where the cache is kept in bfloat16."""
-    import torch  # library conversion primitive, CPU only
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)).to(
-        torch.bfloat16).to(torch.float64).numpy()
+    fp64.  Used where the cache is kept in bfloat16.
+
+    bfloat16 is binary32 with the significand cut to 8 bits (1 implicit + 7
+    stored), so a finite x = m·2^e (0.5 <= |m| < 1, numpy frexp) lies on the
+    grid 2^(e-8); below the smallest normal 2^-126 the grid stays at the
+    subnormal step 2^-133.  x is rounded once, straight from fp64, to the
+    nearest grid point, an exact tie going to the even multiple (numpy rint);
+    magnitudes that round to 2^128 or beyond overflow to infinity."""
+    a = np.asarray(a, dtype=np.float64)
+    _, e = np.frexp(a)
+    step = np.ldexp(1.0, np.maximum(e - 8, -133))
+    r = np.rint(a / step) * step
+    return np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, a), r)
 
 
 def decode_step(state, x, dt, A, Bm, C, Q, E, g, S, cache_bf16=True):

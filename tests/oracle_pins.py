@@ -345,6 +345,42 @@ def pin_decode_equals_prefill(orc):
     assert list(state["n_chunks"]) == [M] * B and list(state["pos"]) == [0] * B
 
 
+def pin_round_bf16(orc):
+    """round_bf16 is round-to-nearest-even onto the bfloat16 grid (8
+    significant bits; subnormal step 2^-133), taken once from fp64.
+    Exact midpoints: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 and goes
+    to the even significand 1; 1 + 3·2^-8 lies halfway between 1 + 2^-7
+    (odd) and 1 + 2^-6 (even).  A value above a midpoint by less than half
+    an fp32 step must round up (a conversion through fp32 first would meet
+    a tie there and round down).  On fp32 values, where a single rounding
+    from fp32 is the same rounding, it agrees with torch's float32 ->
+    bfloat16 conversion."""
+    cases = [
+        (1 + 2.0 ** -8, 1.0),
+        (1 + 3 * 2.0 ** -8, 1 + 2.0 ** -6),
+        (-(1 + 2.0 ** -8), -1.0),
+        (-(1 + 3 * 2.0 ** -8), -(1 + 2.0 ** -6)),
+        (1 + 2.0 ** -8 + 2.0 ** -40, 1 + 2.0 ** -7),
+        (1 + 2.0 ** -8 - 2.0 ** -40, 1.0),
+        (3 * 2.0 ** 20 + 2.0 ** 13, 3 * 2.0 ** 20),          # tie above 1.5·2^21 (step 2^14): even
+        (3 * 2.0 ** 20 + 3 * 2.0 ** 13, 3 * 2.0 ** 20 + 2.0 ** 15),  # tie above an odd multiple
+        (2.0 ** -126 * (1 + 2.0 ** -8), 2.0 ** -126),        # tie at the smallest normal
+        (2.0 ** -134, 0.0),                                  # half the smallest subnormal: tie to 0
+        (3 * 2.0 ** -134, 2.0 ** -132),                      # tie between 1 and 2 subnormal steps
+        (0.0, 0.0),
+        (2.0 ** 128 * (1 - 2.0 ** -9), np.inf),              # midpoint above the largest finite
+        (2.0 ** 128 * (1 - 2.0 ** -8), 2.0 ** 128 * (1 - 2.0 ** -8)),
+    ]
+    for x, want in cases:
+        got = float(orc.round_bf16(np.array([x]))[0])
+        assert got == want, f"round_bf16({x!r}) = {got!r}, want {want!r}"
+    rng = np.random.default_rng(40)
+    v = (rng.standard_normal(20000) * np.exp2(rng.integers(-130, 120, 20000))).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    got = orc.round_bf16(v.astype(np.float64))
+    assert np.array_equal(got, ref), "round_bf16 differs from torch's fp32 -> bf16 conversion"
+
+
 # ------------------------------------------------------------ cache ratio
 def pin_cache_ratio_golden(orc):
     """The printed figure: at S=256, N=128 the DART cache is 25% of the

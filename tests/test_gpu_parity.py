@@ -94,11 +94,60 @@ def test_config1_bf16_prefill():
     (1, 384, 4, 2, 64, 64, 128, torch.bfloat16),      # 4-wave tiles, grouped B/C/Q
     (2, 512, 2, 2, 128, 128, 256, torch.bfloat16),    # largest shape, one token block/wave
     (1, 768, 3, 3, 128, 64, 256, torch.bfloat16),     # M = 3
-    (2, 96, 3, 3, 32, 32, 96, torch.float32),         # S not a power of two
+    (2, 288, 3, 3, 32, 32, 96, torch.float32),        # S not a power of two, M = 3
+    (1, 384, 2, 2, 64, 64, 96, torch.bfloat16),       # S = 96 (three 1-wave tiles), M = 4
     (1, 320, 2, 1, 16, 16, 32, torch.float32),
 ])
 def test_prefill_shapes(B, L, H, G, N, P, S, io):
     run_prefill_case(B, L, H, G, N, P, S, io, seed=B * 100 + L + H)
+
+
+@pytest.mark.parametrize("B,L,H,G,N,P,S,io,qscale", [
+    (2, 288, 3, 3, 32, 32, 96, torch.float32, 1e2),   # S = 96, M = 3
+    (1, 384, 2, 2, 64, 64, 96, torch.bfloat16, 1e3),  # S = 96, M = 4, 1-wave tiles
+])
+def test_prefill_sharpened_chunk96(B, L, H, G, N, P, S, io, qscale):
+    """Chunks of 96 tokens (not a power of two) with memories visible and a
+    sharpened softmax: the SMA readout o alone against the oracle."""
+    out, ref = run_prefill_case(B, L, H, G, N, P, S, io, seed=5 + L, qscale=qscale, gate=1.0)
+    o_gpu = synth.as_f64(out["y"]) - synth.as_f64(out["y_ssd"])
+    assert_parity(o_gpu, ref["o"], io, "o (sharpened, S=96)")
+
+
+@pytest.mark.parametrize("qscale", [1e2, 1e4])
+def test_prefill_sharpened_grouped_xcd_mapping(qscale):
+    """Batch x groups a multiple of 8 with several heads per group: the SMA
+    launch places the heads of one (batch, group) side by side on one XCD
+    (the mapping the ~370M-layer benchmark shape uses).  Sharpened scores
+    make the readout o sensitive to the score path; o is checked alone."""
+    out, ref = run_prefill_case(2, 2048, 16, 4, 128, 64, 256, torch.bfloat16, seed=13,
+                                qscale=qscale, gate=1.0)
+    o_gpu = synth.as_f64(out["y"]) - synth.as_f64(out["y_ssd"])
+    assert_parity(o_gpu, ref["o"], torch.bfloat16, "o (sharpened, grouped XCD mapping)")
+
+
+@pytest.mark.parametrize("io,N,P,S", [(torch.bfloat16, 128, 64, 256), (torch.float32, 16, 16, 64),
+                                      (torch.bfloat16, 64, 64, 64)])
+def test_prefill_large_decay(io, N, P, S):
+    """Per-token decays dt·|A| of 8 to 16 (far outside the synthetic recipe):
+    inside a 16-token block the log-decay spans more than 2^7, so the
+    intra-chunk weights must be formed without factors that overflow."""
+    _need_gpu()
+    B, H, G, L = 1, 4, 2, 4 * S
+    inp = synth.draw_prefill(17, B, L, H, G, N, P, io=io, qscale=10.0)
+    rng = np.random.default_rng(18)
+    inp["dt"] = torch.from_numpy(rng.uniform(0.5, 1.0, (B, L, H))).to(torch.float32)
+    inp["A"] = torch.full((H,), -16.0, dtype=torch.float32)
+    d = _to_dev(inp)
+    gate = 0.5
+    out = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate, S)
+    torch.cuda.synchronize()
+    n = _np(inp)
+    ref = oracle.prefill(n["x"], n["dt"], n["A"], n["Bm"], n["C"], n["Q"], n["E"], gate, S)
+    assert_parity(_pn_to_np(out["dH_f32"]), ref["dH"], io, "dH_f32 (large decay)")
+    assert_parity(_pn_to_np(out["h_final"]), ref["h_final"], io, "h_final (large decay)")
+    assert_parity(out["y_ssd"], ref["y_ssd"], io, "y_ssd (large decay)")
+    assert_parity(out["y"], ref["y"], io, "y (large decay)")
 
 
 @pytest.mark.parametrize("qscale", [1e2, 1e4])
@@ -116,7 +165,7 @@ def test_prefill_sharpened_softmax(qscale):
     (2, 512, 2, 2, 128, 128, 256, torch.bfloat16, 1.0),  # one token block per wave
     (1, 384, 4, 2, 64, 64, 128, torch.bfloat16, 1e2),    # sharpened, grouped B/C/Q
     (2, 64, 3, 1, 32, 32, 32, torch.bfloat16, 1.0),      # M = 2
-    (2, 96, 3, 3, 32, 32, 96, torch.float32, 1e2),       # S not a power of two
+    (2, 288, 3, 3, 32, 32, 96, torch.float32, 1e2),      # S not a power of two, M = 3
     (1, 320, 2, 1, 16, 16, 32, torch.float32, 1.0),      # M = 10: old memories decay to ~0
 ])
 def test_prefill_decayed(B, L, H, G, N, P, S, io, qscale):
@@ -178,6 +227,15 @@ def _decode_case(B, H, G, N, P, S, max_chunks, n_chunks, pos, io, seed, gate=0.5
     y_ref, new = oracle.decode_step(ostate, n["x"], n["dt"], n["A"], n["Bm"], n["C"], n["Q"],
                                     n["E"], gate, S, cache_bf16=io == torch.bfloat16)
     assert_parity(y, y_ref, io, "decode y")
+    if qscale != 1.0:
+        # the SMA readout alone: y - C·h over the updated state, against the
+        # oracle's readout (its y at gate g minus its y at gate 0, over g)
+        y0_ref, _ = oracle.decode_step(ostate, n["x"], n["dt"], n["A"], n["Bm"], n["C"], n["Q"],
+                                       n["E"], 0.0, S, cache_bf16=io == torch.bfloat16)
+        Ch = n["C"][:, oracle.group_of_head(H, G)]
+        y_ssd_gpu = np.einsum("bhn,bhnp->bhp", Ch, _pn_to_np(st["h"]))
+        assert_parity((synth.as_f64(y) - y_ssd_gpu) / gate, (y_ref - y0_ref) / gate, io,
+                      "decode o (sharpened)")
     assert_parity(_pn_to_np(st["h"]), new["h"], io, "decode h")
     assert_parity(_pn_to_np(st["dH_cur"]), new["dH_cur"], io, "decode dH_cur")
     assert_parity(_pn_to_np(st["cache"]), new["cache"], io, "decode cache")
@@ -201,10 +259,12 @@ def test_decode_sharpened():
                  qscale=1e4)
 
 
-def test_decode_many_pairs_single_split():
-    """Enough pairs that each workgroup streams its whole cache (no combine)."""
+@pytest.mark.parametrize("qscale", [1.0, 1e4])
+def test_decode_many_pairs_single_split(qscale):
+    """Enough pairs that each workgroup streams its whole cache (no combine);
+    with sharpened scores the readout is checked alone."""
     _decode_case(32, 32, 32, 128, 64, 256, 8, list(range(1, 9)) * 4, [255, 0] * 16,
-                 torch.bfloat16, seed=22)
+                 torch.bfloat16, seed=22, qscale=qscale, gate=1.0 if qscale != 1.0 else 0.5)
 
 
 def test_decode_cache_full_sets_flag():
@@ -218,10 +278,14 @@ def test_decode_cache_full_sets_flag():
     st["n_chunks"].fill_(mx)
     st["pos"].fill_(S - 1)
     d = _to_dev(synth.draw_decode_token(31, B, H, H, N, P, io=torch.bfloat16))
-    api.decode_step(st, d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], 0.5)
+    assert not api.cache_overflowed(st)
+    with pytest.raises(RuntimeError, match="decode cache full"):
+        api.decode_step(st, d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], 0.5,
+                        check_overflow=True)
     torch.cuda.synchronize()
     assert torch.equal(st["cache"], before)
     assert int(st["workspace"][:4].view(torch.int32).item()) == 1
+    assert api.cache_overflowed(st)
     assert st["n_chunks"].tolist() == [mx] * B and st["pos"].tolist() == [0] * B
 
 
@@ -331,32 +395,41 @@ def _oracle_pair(n, b, h, H, G, S, gate, tokens=None):
         oracle.gated_output(y_ssd, o, gate)[0, :, 0]
 
 
-def test_config2_full_size_sampled_pairs():
+@pytest.mark.parametrize("qscale", [1.0, 1e3])
+def test_config2_full_size_sampled_pairs(qscale):
     """Prefill bf16 at the Mamba-2 ~370M layer shape (batch 4, 32 heads,
     groups of 8 heads, L=8192, S=256, N=128, P=64), the configuration the
-    benchmark times; every output of three sampled (batch, head) pairs is
-    checked against the oracle."""
+    benchmark times, in the launch configuration it times (heads of one
+    (batch, group) side by side on one XCD); every output of three sampled
+    (batch, head) pairs is checked against the oracle.  With sharpened
+    queries (gate 1) the SMA readout o = y - y_ssd is also checked alone."""
     _need_gpu()
-    B, L, H, G, N, P, S, gate = 4, 8192, 32, 4, 128, 64, 256, 0.5
-    inp = synth.draw_prefill(0, B, L, H, G, N, P, io=torch.bfloat16)
+    B, L, H, G, N, P, S = 4, 8192, 32, 4, 128, 64, 256
+    gate = 0.5 if qscale == 1.0 else 1.0
+    print(f"c2 full size qscale {qscale}", flush=True)
+    inp = synth.draw_prefill(0, B, L, H, G, N, P, io=torch.bfloat16, qscale=qscale)
     d = _to_dev(inp)
     out = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate, S)
     torch.cuda.synchronize()
     n = _np(inp)
+    io = torch.bfloat16
     for b, h in [(0, 0), (1, 13), (3, 31)]:
         dH, H_in, y_ssd, o, y = _oracle_pair(n, b, h, H, G, S, gate)
-        io = torch.bfloat16
         assert_parity(_pn_to_np(out["dH"][b, h]), dH, io, f"c2 dH b{b} h{h}")
         assert_parity(_pn_to_np(out["H_in"][b, h]), H_in[:-1], io, f"c2 H_in b{b} h{h}")
         assert_parity(_pn_to_np(out["h_final"][b, h]), H_in[-1], io, f"c2 h_final b{b} h{h}")
         assert_parity(out["y_ssd"][b, :, h], y_ssd, io, f"c2 y_ssd b{b} h{h}")
         assert_parity(out["y"][b, :, h], y, io, f"c2 y b{b} h{h}")
+        if qscale != 1.0:
+            o_gpu = synth.as_f64(out["y"][b, :, h]) - synth.as_f64(out["y_ssd"][b, :, h])
+            assert_parity(o_gpu, o, io, f"c2 o (sharpened) b{b} h{h}")
 
 
-def test_config4_full_size_decode_sampled_pairs():
+def test_config4_full_size_decode_all_pairs():
     """Decode bf16: batch 64, 32 heads, N=128, P=64, S=256, 128 cached chunks
-    per sequence (4 GiB cache), one new token at the start of chunk 128; the
-    outputs of sampled sequences (all heads) against the oracle."""
+    per sequence (4 GiB cache), one new token at the start of chunk 128;
+    every (sequence, head) pair against the oracle, which is run one
+    sequence at a time (its 64 MB slice of the cache)."""
     _need_gpu()
     B, H, N, P, S, mx = 64, 32, 128, 64, 256, 128
     io = torch.bfloat16
@@ -365,33 +438,45 @@ def test_config4_full_size_decode_sampled_pairs():
     st["h"].copy_(synth.draw_state(51, (B, H, P, N), 0.01, torch.float32, device=DEV))
     st["dH_cur"].copy_(synth.draw_state(52, (B, H, P, N), 0.01, torch.float32, device=DEV))
     st["n_chunks"].fill_(mx)
-    samples = (0, 17, 63)
-    pre = {b: {"cache": _pn_to_np(st["cache"][b:b + 1]), "h": _pn_to_np(st["h"][b:b + 1]),
-               "dH_cur": _pn_to_np(st["dH_cur"][b:b + 1]), "n_chunks": np.array([mx]),
-               "pos": np.array([0])} for b in samples}
+    h_before, dHc_before = st["h"].clone(), st["dH_cur"].clone()
     tok = synth.draw_decode_token(53, B, H, H, N, P, io=io)
     d = _to_dev(tok)
     y = api.decode_step(st, d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], 0.5)
     torch.cuda.synchronize()
+    # pos 0 appends nothing: the cache after the step is the cache the step read
     n = _np(tok)
-    for b in samples:
+    y_ref = np.empty((B, H, P))
+    h_ref = np.empty((B, H, N, P))
+    for b in range(B):
+        pre = {"cache": _pn_to_np(st["cache"][b:b + 1]), "h": _pn_to_np(h_before[b:b + 1]),
+               "dH_cur": _pn_to_np(dHc_before[b:b + 1]), "n_chunks": np.array([mx]),
+               "pos": np.array([0])}
         sl = {k: v[b:b + 1] for k, v in n.items() if k != "A"}
-        y_ref, new = oracle.decode_step(pre[b], sl["x"], sl["dt"], n["A"], sl["Bm"], sl["C"],
-                                        sl["Q"], sl["E"], 0.5, S)
-        assert_parity(y[b:b + 1], y_ref, io, f"c4 decode y b{b}")
-        assert_parity(_pn_to_np(st["h"][b:b + 1]), new["h"], io, f"c4 decode h b{b}")
+        yr, new = oracle.decode_step(pre, sl["x"], sl["dt"], n["A"], sl["Bm"], sl["C"], sl["Q"],
+                                     sl["E"], 0.5, S)
+        y_ref[b], h_ref[b] = yr[0], new["h"][0]
+        if b % 16 == 15:
+            print(f"c4 oracle: {b + 1} of {B} sequences", flush=True)
+    assert_parity(y, y_ref, io, "c4 decode y (all pairs)")
+    assert_parity(_pn_to_np(st["h"]), h_ref, io, "c4 decode h (all pairs)")
+    assert st["n_chunks"].tolist() == [mx] * B and st["pos"].tolist() == [1] * B
 
 
-def test_config3_long_context_sampled_tokens():
+@pytest.mark.parametrize("qscale", [1.0, 1e3])
+def test_config3_long_context_sampled_tokens(qscale):
     """Long-context prefill bf16 (batch 1, 32 heads, L=65536, S=256, N=128,
     P=64: 256 chunk memories per head).  For three heads the oracle computes
-    every memory, the boundary states and y_ssd, and the SMA readout of 64
-    tokens spread over all chunk indices (first, middle and last chunks
-    included)."""
+    every memory and the SMA readout of 64 tokens spread over all chunk
+    indices (first, middle and last chunks included: the last chunk's
+    tokens attend 255 memories).  At qscale 1 the boundary states, y_ssd and
+    y are checked too; with sharpened queries (gate 1) the readout
+    o = y - y_ssd of the sampled tokens is checked alone."""
     _need_gpu()
-    B, L, H, G, N, P, S, gate = 1, 65536, 32, 32, 128, 64, 256, 0.5
+    B, L, H, G, N, P, S = 1, 65536, 32, 32, 128, 64, 256
+    gate = 0.5 if qscale == 1.0 else 1.0
     M = L // S
-    inp = synth.draw_prefill(3, B, L, H, G, N, P, io=torch.bfloat16)
+    print(f"c3 long context qscale {qscale}", flush=True)
+    inp = synth.draw_prefill(3, B, L, H, G, N, P, io=torch.bfloat16, qscale=qscale)
     d = _to_dev(inp)
     out = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate, S)
     torch.cuda.synchronize()
@@ -399,17 +484,23 @@ def test_config3_long_context_sampled_tokens():
     chunks = np.unique(np.concatenate([[0, 1, 2, M // 2, M - 2, M - 1],
                                        rng.integers(0, M, 58)]))
     tokens = np.sort(chunks * S + rng.integers(0, S, chunks.size))
+    tokens = np.unique(np.concatenate([tokens, [L - 1]]))
     io = torch.bfloat16
     for h in (0, 17, 31):
         sl = {k: synth.as_f64(v[:, :, h:h + 1]) for k, v in inp.items() if k != "A"}
         A = synth.as_f64(inp["A"][h:h + 1])
         dH = oracle.chunk_states(sl["x"], sl["dt"], A, sl["Bm"], S)
-        H_in = oracle.state_pass(dH, sl["dt"], A, S)
-        y_ssd = oracle.chunk_output(sl["x"], sl["dt"], A, sl["Bm"], sl["C"], H_in, S)
         o = oracle.sma(sl["Q"], sl["E"], sl["C"], dH, S, tokens=tokens)
-        y = oracle.gated_output(y_ssd, o, gate)
         assert_parity(_pn_to_np(out["dH"][0, h]), dH[0, 0], io, f"c3 dH h{h}")
-        assert_parity(_pn_to_np(out["H_in"][0, h]), H_in[0, 0, :-1], io, f"c3 H_in h{h}")
-        assert_parity(_pn_to_np(out["h_final"][0, h]), H_in[0, 0, -1], io, f"c3 h_final h{h}")
-        assert_parity(out["y_ssd"][0, :, h], y_ssd[0, :, 0], io, f"c3 y_ssd h{h}")
-        assert_parity(out["y"][0, tokens, h], y[0, tokens, 0], io, f"c3 y (sampled) h{h}")
+        if qscale == 1.0:
+            H_in = oracle.state_pass(dH, sl["dt"], A, S)
+            y_ssd = oracle.chunk_output(sl["x"], sl["dt"], A, sl["Bm"], sl["C"], H_in, S)
+            y = oracle.gated_output(y_ssd, o, gate)
+            assert_parity(_pn_to_np(out["H_in"][0, h]), H_in[0, 0, :-1], io, f"c3 H_in h{h}")
+            assert_parity(_pn_to_np(out["h_final"][0, h]), H_in[0, 0, -1], io,
+                          f"c3 h_final h{h}")
+            assert_parity(out["y_ssd"][0, :, h], y_ssd[0, :, 0], io, f"c3 y_ssd h{h}")
+            assert_parity(out["y"][0, tokens, h], y[0, tokens, 0], io, f"c3 y (sampled) h{h}")
+        else:
+            o_gpu = synth.as_f64(out["y"][0, tokens, h]) - synth.as_f64(out["y_ssd"][0, tokens, h])
+            assert_parity(o_gpu, o[0, tokens, 0], io, f"c3 o (sharpened, sampled) h{h}")

@@ -71,6 +71,12 @@ MUTATIONS = [
     ("fp8 exponent bias 8",
      "normal = (1.0 + mant / 8.0) * np.exp2(field - 7.0)",
      "normal = (1.0 + mant / 8.0) * np.exp2(field - 8.0)"),
+    ("bf16 rounding truncates",
+     "r = np.rint(a / step) * step", "r = np.trunc(a / step) * step"),
+    ("bf16 rounding ties away from zero",
+     "r = np.rint(a / step) * step", "r = np.copysign(np.floor(np.abs(a / step) + 0.5), a) * step"),
+    ("bf16 grid one bit too fine",
+     "step = np.ldexp(1.0, np.maximum(e - 8, -133))", "step = np.ldexp(1.0, np.maximum(e - 9, -133))"),
     ("fp8 encoding truncates",
      "r = np.round(a / step) * step", "r = np.floor(a / step) * step"),
     ("fp8 subnormal grid too fine",

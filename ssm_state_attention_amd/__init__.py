@@ -8,6 +8,7 @@ from .api import (  # noqa: F401
     dart_sma_decode,
     dart_sma_decode_workspace,
     dart_sma_fwd,
+    cache_overflowed,
     dart_state_pass,
     decode_dims,
     decode_step,

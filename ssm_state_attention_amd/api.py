@@ -447,9 +447,21 @@ def new_decode_state(batch, nheads, ngroups, dstate, headdim, chunk, max_chunks,
     }
 
 
-def decode_step(state, x, dt, A, Bm, C, Q, E, gate, y=None):
+def cache_overflowed(state):
+    """True once a decode step on ``state`` closed a chunk while its sequence's
+    cache was full: that chunk's memory was dropped (n_chunks stays at
+    max_chunks), so later tokens of the sequence attend an incomplete set of
+    memories.  Reads the flag the library keeps in the first int32 of the
+    workspace, which is a device-to-host copy and synchronises the stream."""
+    return bool(state["workspace"][:4].view(torch.int32).item())
+
+
+def decode_step(state, x, dt, A, Bm, C, Q, E, gate, y=None, check_overflow=False):
     """Advance ``state`` (from new_decode_state) by one token per sequence;
-    returns y [B,H,P]."""
+    returns y [B,H,P].  A full cache does not stop the step (see
+    :func:`cache_overflowed`); with ``check_overflow`` the step raises
+    RuntimeError once that has happened, at the price of a synchronisation
+    per call.  Without it, callers poll cache_overflowed themselves."""
     if y is None:
         y = torch.empty(x.shape, dtype=x.dtype, device=x.device)
     if "cache8" in state:
@@ -460,6 +472,9 @@ def decode_step(state, x, dt, A, Bm, C, Q, E, gate, y=None):
         dart_sma_decode(x, dt, A, Bm, C, Q, E, gate, state["cache"], state["h"],
                         state["dH_cur"], state["n_chunks"], state["pos"], y, state["workspace"],
                         state["chunk"])
+    if check_overflow and cache_overflowed(state):
+        raise RuntimeError("decode cache full: a finished chunk's memory could not be appended "
+                           "(allocate the state with a larger max_chunks)")
     return y
 
 

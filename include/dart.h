@@ -27,7 +27,8 @@
  * --------------------------
  * - Every tensor argument is a pointer to DEVICE memory owned by the caller,
  *   dense row-major in the layout given, 16-byte aligned.  The library never
- *   allocates, frees or keeps memory, and holds no global state.
+ *   allocates, frees or keeps memory, and holds no global state, apart from
+ *   the static device scratch of dart_sma_decode_noalloc.
  * - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *   enqueue work and return; results are ready once the stream reaches them.
  * - Dimensions and pointers are validated on the host before any HIP call; a
@@ -67,7 +68,9 @@ typedef enum dart_status {
   DART_ERR_DTYPE = 4,       /* io is not a dart_dtype value                 */
   DART_ERR_WORKSPACE = 5,   /* decode workspace missing or too small        */
   DART_ERR_HIP = 6,         /* a HIP launch reported an error               */
-  DART_ERR_ALIGN = 7        /* a pointer is not 16-byte aligned             */
+  DART_ERR_ALIGN = 7,       /* a pointer is not 16-byte aligned             */
+  DART_ERR_SCRATCH = 8      /* dims exceed the static scratch of the
+                               allocation-free decode entry point           */
 } dart_status;
 
 typedef enum dart_dtype { DART_F32 = 0, DART_BF16 = 1 } dart_dtype;
@@ -287,6 +290,33 @@ dart_status dart_sma_decode(const dart_decode_dims* dims, const void* x, const f
                             const void* E, float gate, void* cache, float* h,
                             float* dH_cur, int32_t* n_chunks, int32_t* pos, void* y,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free variant of dart_sma_decode, for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * steps and results as dart_sma_decode, except:
+ * - no workspace: the y_ssd rows and per-split partials live in a static
+ *   device array of DART_DECODE_SCRATCH_BYTES per GPU, which the library
+ *   holds from its first use on that GPU until the process ends.  Dims whose
+ *   dart_sma_decode_workspace() exceeds that size return DART_ERR_SCRATCH
+ *   (at N = 128, P = 64: beyond about 8,000 (sequence, head) pairs).  Nothing
+ *   in it needs clearing between calls (every call writes what it reads).
+ * - cache_full: a caller-owned device int32 (4-byte aligned), or NULL; set
+ *   to 1 (never cleared) when a chunk could not be appended because
+ *   n_chunks[b] had reached max_chunks (the workspace flag of
+ *   dart_sma_decode).  With NULL the condition is not reported.
+ * The function calls no allocator.  Its first call on a device looks up the
+ * array's address with that device current.  All calls on one GPU share the
+ * one array: calls that may overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller.
+ */
+#define DART_DECODE_SCRATCH_BYTES (4u << 20)
+dart_status dart_sma_decode_noalloc(const dart_decode_dims* dims, const void* x,
+                                    const float* dt, const float* A, const void* Bm,
+                                    const void* C, const void* Q, const void* E, float gate,
+                                    void* cache, float* h, float* dH_cur, int32_t* n_chunks,
+                                    int32_t* pos, void* y, int32_t* cache_full, void* stream);
 
 /*
  * fp8 chunk-memory cache.  Source: Pith review of DART, "Where Pith is

@@ -10,7 +10,12 @@ DART_F32, DART_BF16 = 0, 1
 STATUS_NAMES = {
     0: "DART_OK", 1: "DART_ERR_NULL_PTR", 2: "DART_ERR_BAD_DIMS", 3: "DART_ERR_UNSUPPORTED",
     4: "DART_ERR_DTYPE", 5: "DART_ERR_WORKSPACE", 6: "DART_ERR_HIP", 7: "DART_ERR_ALIGN",
+    8: "DART_ERR_SCRATCH",
 }
+
+# DART_DECODE_SCRATCH_BYTES of include/dart.h: the static scratch behind
+# dart_sma_decode_noalloc
+DECODE_SCRATCH_BYTES = 4 << 20
 
 
 class DartDims(ctypes.Structure):
@@ -49,6 +54,8 @@ _SIG = {
     "dart_sma_decode_workspace": [ctypes.POINTER(DartDecodeDims)],
     "dart_sma_decode": [ctypes.POINTER(DartDecodeDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F,
                         _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+    "dart_sma_decode_noalloc": [ctypes.POINTER(DartDecodeDims), _VP, _VP, _VP, _VP, _VP, _VP,
+                                _VP, _F, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "dart_sma_decode_fp8": [ctypes.POINTER(DartDecodeDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                             _F, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "dart_cache_fp8_store": [ctypes.POINTER(DartDecodeDims), _VP, ctypes.c_int64, ctypes.c_int64,

@@ -279,6 +279,32 @@ def dart_sma_decode(x, dt, A, Bm, C, Q, E, gate, cache, h, dH_cur, n_chunks, pos
                                 _stream()), "dart_sma_decode")
 
 
+def dart_sma_decode_noalloc(x, dt, A, Bm, C, Q, E, gate, cache, h, dH_cur, n_chunks, pos, y,
+                            chunk, cache_full=None):
+    """dart_sma_decode without a workspace (see include/dart.h): the library
+    keeps the step's partials in its static per-GPU scratch and allocates
+    nothing.  cache_full: an int32 device tensor of one element set to 1
+    when a chunk could not be appended (None: not reported).  Calls that may
+    overlap on one GPU race on the scratch."""
+    B, H, P = x.shape
+    G, N = Bm.shape[1], Bm.shape[2]
+    max_chunks = cache.shape[2]
+    io, dev = x.dtype, x.device
+    d = decode_dims(B, H, G, N, P, chunk, max_chunks, io)
+    args = [_ptr(x, "x", io, (B, H, P), dev), _ptr(dt, "dt", torch.float32, (B, H), dev),
+            _ptr(A, "A", torch.float32, (H,), dev), _ptr(Bm, "Bm", io, (B, G, N), dev),
+            _ptr(C, "C", io, (B, G, N), dev), _ptr(Q, "Q", io, (B, G, N), dev),
+            _ptr(E, "E", io, (B, H, P), dev)]
+    state = [_ptr(cache, "cache", io, (B, H, max_chunks, P, N), dev),
+             _ptr(h, "h", torch.float32, (B, H, P, N), dev),
+             _ptr(dH_cur, "dH_cur", torch.float32, (B, H, P, N), dev),
+             _ptr(n_chunks, "n_chunks", torch.int32, (B,), dev),
+             _ptr(pos, "pos", torch.int32, (B,), dev), _ptr(y, "y", io, (B, H, P), dev)]
+    flag = _ptr(cache_full, "cache_full", torch.int32, (1,), dev)
+    check(lib().dart_sma_decode_noalloc(d, *args, float(gate), *state, flag, _stream()),
+          "dart_sma_decode_noalloc")
+
+
 def dart_sma_decode_fp8(x, dt, A, Bm, C, Q, E, gate, cache8, scale, h, dH_cur, n_chunks, pos,
                         y, workspace, chunk):
     """dart_sma_decode over the fp8 cache: cache8 [B,H,max_chunks,P,N] uint8

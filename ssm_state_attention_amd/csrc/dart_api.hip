@@ -109,12 +109,13 @@ struct SmaDecodeFn {
   int *nc, *pos;
   void *y, *ws;
   hipStream_t st;
+  int* flag = nullptr;
   template <typename T, int N, int P>
   hipError_t run() {
     return dart::launch_sma_decode<T, N, P>(
         sh, static_cast<const T*>(x), dt, A, static_cast<const T*>(Bm), static_cast<const T*>(C),
         static_cast<const T*>(Q), static_cast<const T*>(E), gate, static_cast<T*>(cache), cache8,
-        cscale, h, dHc, nc, pos, static_cast<T*>(y), ws, st);
+        cscale, h, dHc, nc, pos, static_cast<T*>(y), ws, flag, st);
   }
 };
 
@@ -297,6 +298,25 @@ extern "C" dart_status dart_sma_decode(const dart_decode_dims* dims, const void*
   if (!aligned16(workspace)) return DART_ERR_ALIGN;
   SmaDecodeFn fn{decode_shape(dims), x, Bm, C, Q, E, dt, A, gate, cache, nullptr, nullptr, h,
                  dH_cur, n_chunks, pos, y, workspace, static_cast<hipStream_t>(stream)};
+  return dispatch(dims->io, dims->dstate, dims->headdim, fn);
+}
+
+extern "C" dart_status dart_sma_decode_noalloc(const dart_decode_dims* dims, const void* x,
+                                               const float* dt, const float* A, const void* Bm,
+                                               const void* C, const void* Q, const void* E,
+                                               float gate, void* cache, float* h, float* dH_cur,
+                                               int32_t* n_chunks, int32_t* pos, void* y,
+                                               int32_t* cache_full, void* stream) {
+  dart_status s = dart_validate_decode_dims(dims);
+  if (s != DART_OK) return s;
+  if ((s = check_ptrs(x, dt, A, Bm, C, Q, E, cache, h, dH_cur, n_chunks, pos, y)) != DART_OK)
+    return s;
+  if (cache_full && (reinterpret_cast<uintptr_t>(cache_full) & 3u) != 0) return DART_ERR_ALIGN;
+  if (dart::decode_workspace_bytes(*dims) > DART_DECODE_SCRATCH_BYTES) return DART_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (dart::decode_scratch(&ws) != hipSuccess) return DART_ERR_HIP;
+  SmaDecodeFn fn{decode_shape(dims), x, Bm, C, Q, E, dt, A, gate, cache, nullptr, nullptr, h,
+                 dH_cur, n_chunks, pos, y, ws, static_cast<hipStream_t>(stream), cache_full};
   return dispatch(dims->io, dims->dstate, dims->headdim, fn);
 }
 

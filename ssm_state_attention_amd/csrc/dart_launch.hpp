@@ -38,12 +38,19 @@ hipError_t launch_sma_fwd(const PrefillShape& s, const T* Q, const T* E, const T
                           const uint8_t* prior8, const float* pscale, hipStream_t st);
 
 // cache8 == nullptr: the cache is `cache` in the io type; otherwise it is
-// the fp8 code array cache8 with one scale per memory in cscale.
+// the fp8 code array cache8 with one scale per memory in cscale.  flag !=
+// nullptr: the cache-full flag goes there instead of the workspace's first
+// int32.
 template <typename T, int N, int P>
 hipError_t launch_sma_decode(const DecodeShape& s, const T* x, const float* dt, const float* A,
                              const T* Bm, const T* C, const T* Q, const T* E, float gate,
                              T* cache, uint8_t* cache8, float* cscale, float* h, float* dH_cur,
-                             int* n_chunks, int* pos, T* y, void* workspace, hipStream_t st);
+                             int* n_chunks, int* pos, T* y, void* workspace, int* flag,
+                             hipStream_t st);
+
+// Device address of this GPU's static decode scratch (DART_DECODE_SCRATCH_BYTES),
+// looked up on the first call made with the device current.
+hipError_t decode_scratch(void** ptr);
 
 // fp8 codes and scales of n_mem f32 memories per (batch, head), written to
 // cache slots first .. first + n_mem - 1 (T only selects the instantiation).

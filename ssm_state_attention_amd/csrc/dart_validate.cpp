@@ -13,6 +13,9 @@ extern "C" const char* dart_status_str(dart_status s) {
     case DART_ERR_WORKSPACE: return "DART_ERR_WORKSPACE: decode workspace missing or too small";
     case DART_ERR_HIP: return "DART_ERR_HIP: a HIP launch failed";
     case DART_ERR_ALIGN: return "DART_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case DART_ERR_SCRATCH:
+      return "DART_ERR_SCRATCH: the dims need more decode scratch than the allocation-free "
+             "entry point's static maximum (DART_DECODE_SCRATCH_BYTES)";
   }
   return "DART_ERR_UNKNOWN";
 }

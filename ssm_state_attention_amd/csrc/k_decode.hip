@@ -16,6 +16,9 @@
 // round-to-nearest-even encodings of dH[c]·2^-e, with e = max(E - 8, -126)
 // for the memory's largest magnitude f·2^E (0.5 <= f < 1), so every scaled
 // magnitude is below 256 and no code saturates.
+#include <mutex>
+
+#include "dart.h"
 #include "dart_launch.hpp"
 #include "dart_shapes.hpp"
 
@@ -543,6 +546,17 @@ __global__ __launch_bounds__(256) void k_fp8_store(const float* __restrict__ src
   if (tid == 0) cscale[slot] = pow2i(e);
 }
 
+// Device scratch of the allocation-free decode entry point
+// (dart_sma_decode_noalloc): the y_ssd rows and per-split partials that
+// dart_sma_decode keeps in its caller's workspace.  One copy per GPU, held
+// until the process ends.  Host code never names the array except to look
+// up its device address (decode_scratch below).
+static __device__ __align__(256) unsigned char scratch[DART_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
 struct DecodeWs {
   int* flag;
   float* yssd;
@@ -558,13 +572,31 @@ DecodeWs decode_ws(void* workspace, long pairs, int P) {
 
 }  // namespace
 
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 template <typename T, int N, int P>
 hipError_t launch_sma_decode(const DecodeShape& s, const T* x, const float* dt, const float* A,
                              const T* Bm, const T* C, const T* Q, const T* E, float gate,
                              T* cache, uint8_t* cache8, float* cscale, float* h, float* dH_cur,
-                             int* n_chunks, int* pos, T* y, void* workspace, hipStream_t st) {
+                             int* n_chunks, int* pos, T* y, void* workspace, int* flag,
+                             hipStream_t st) {
   const long pairs = (long)s.B * s.H;
-  const DecodeWs ws = decode_ws(workspace, pairs, P);
+  DecodeWs ws = decode_ws(workspace, pairs, P);
+  if (flag) ws.flag = flag;
   const int cps = (s.max_chunks + s.splits - 1) / s.splits;
   const float scale_log2 = kLog2e / sqrtf(static_cast<float>(N));
   const bool f8 = cache8 != nullptr;
@@ -609,7 +641,7 @@ hipError_t launch_fp8_store(int B, int H, int n_mem, int first, int max_chunks, 
 #define DART_INST_DECODE(T, N, P)                                                               \
   template hipError_t launch_sma_decode<T, N, P>(                                               \
       const DecodeShape&, const T*, const float*, const float*, const T*, const T*, const T*,   \
-      const T*, float, T*, uint8_t*, float*, float*, float*, int*, int*, T*, void*,             \
+      const T*, float, T*, uint8_t*, float*, float*, float*, int*, int*, T*, void*, int*,       \
       hipStream_t);                                                                             \
   template hipError_t launch_fp8_store<T, N, P>(int, int, int, int, int, const float*, uint8_t*, \
                                                 float*, hipStream_t);

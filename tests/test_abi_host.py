@@ -17,7 +17,7 @@ from ssm_state_attention_amd._lib import DartDecodeDims, DartDims
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dart.h")
 
-OK, NULLP, BAD, UNSUP, DTYPE, WS, HIP, ALIGN = range(8)
+OK, NULLP, BAD, UNSUP, DTYPE, WS, HIP, ALIGN, SCRATCH = range(9)
 F32, BF16 = 0, 1
 
 
@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function():
 
 def test_status_strings():
     lib = dart.lib()
-    for code in range(8):
+    for code in range(9):
         s = lib.dart_status_str(code).decode()
         assert s.startswith("DART_") and s == s.strip()
     assert lib.dart_status_str(99).decode() == "DART_ERR_UNKNOWN"
@@ -283,3 +283,31 @@ def test_validators_under_host_sanitizers(tmp_path):
                     "-g", "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0 and out.stdout.strip() == "OK", out.stdout + out.stderr
+
+
+def test_decode_noalloc_validates_on_host():
+    """The allocation-free decode entry point rejects bad arguments, and dims
+    whose scratch need exceeds DART_DECODE_SCRATCH_BYTES, before any HIP
+    call (so before its first look-up of the device scratch)."""
+    lib = dart.lib()
+    fn = lib.dart_sma_decode_noalloc
+    d = ddims()
+    # x, dt, A, Bm, C, Q, E, gate, cache, h, dH_cur, n_chunks, pos, y, cache_full
+    for i in range(13):
+        p = [A16] * 13
+        p[i] = None
+        assert fn(d, *p[:7], 0.5, *p[7:], None, None) == NULLP
+    p = [A16] * 13
+    p[8] = MIS
+    assert fn(d, *p[:7], 0.5, *p[7:], None, None) == ALIGN
+    assert fn(d, *p[:7], 0.5, *([A16] * 6), A16 + 2, None) == ALIGN   # cache_full not 4-aligned
+    assert fn(ddims(H=6, G=4), *([A16] * 7), 0.5, *([A16] * 6), None, None) == BAD
+    assert fn(ddims(N=96), *([A16] * 7), 0.5, *([A16] * 6), None, None) == UNSUP
+    # the scratch bound: the largest batch that fits is accepted by the size
+    # rule, one more sequence is rejected
+    cap = _lib.DECODE_SCRATCH_BYTES
+    fits = [B for B in range(200, 300) if api.dart_sma_decode_workspace(ddims(B=B)) <= cap]
+    big = max(fits) + 1
+    assert api.dart_sma_decode_workspace(ddims(B=big)) > cap
+    assert fn(ddims(B=big), *([A16] * 7), 0.5, *([A16] * 6), None, None) == SCRATCH
+    assert "DART_ERR_SCRATCH" in lib.dart_status_str(SCRATCH).decode()

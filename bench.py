@@ -8,7 +8,9 @@ accumulation.  `value` is prefill tokens/s (batch·L / step time).  The
 decode step over a 4 GiB chunk-memory cache (batch 64, 32 heads, 128
 cached chunks) is timed in the same run and reported under "decode", and
 the same step over the fp8 (E4M3) cache under "decode_fp8"; the backward of the
-prefill (SMA and scan) at the prefill shape is reported under "backward".
+prefill (SMA and scan) at the prefill shape is reported under "backward"; the
+same prefill step at L = 4096 (8 heads) and at L = 65536 (32 heads, 256
+memories per head) under "prefill_L4K" and "prefill_L64K".
 
 Prints one JSON line.  `python bench.py --steps K --warmup W`.
 """
@@ -20,6 +22,11 @@ import sys
 import time
 
 BASE = {"B": 4, "L": 8192, "H": 32, "G": 4, "N": 128, "P": 64, "S": 256, "gate": 0.5}
+# the L=4K prefill (8 heads, one B/C/Q group per head) and the long-context
+# prefill (one sequence of 65536 tokens, 256 chunk memories per head)
+PREFILL_L4K = {"B": 1, "L": 4096, "H": 8, "G": 8, "N": 128, "P": 64, "S": 256, "gate": 0.5}
+PREFILL_L64K = {"B": 1, "L": 65536, "H": 32, "G": 32, "N": 128, "P": 64, "S": 256, "gate": 0.5,
+                "seed": 3}
 DECODE = {"B": 64, "H": 32, "G": 32, "N": 128, "P": 64, "S": 256, "chunks": 128}
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
@@ -82,6 +89,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="skip the L=4K and L=64K prefill legs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
@@ -171,6 +180,54 @@ def bench_prefill(args, torch, api, synth):
         },
         "mfma_frac_whole_prefill": (flops_sma + flops_scan) / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
         "inputs": inp,
+    }
+
+
+def bench_prefill_extra(args, torch, api, synth, c, name, steps):
+    """Whole-prefill timing (same step as bench_prefill) at another
+    configuration: median and min over `steps` timed steps after 2 warm-up
+    steps, tokens/s and the fraction of the bf16 MFMA peak of the step's
+    algorithmic FLOPs and of the SMA launch's FLOPs."""
+    inp = synth.draw_prefill(c.get("seed", 0), c["B"], c["L"], c["H"], c["G"], c["N"], c["P"],
+                             io=torch.bfloat16)
+    d = {k: v.to("cuda:0") for k, v in inp.items()}
+    del inp
+    B, L, H, N, P, S = c["B"], c["L"], c["H"], c["N"], c["P"], c["S"]
+    M = L // S
+    f32 = dict(dtype=torch.float32, device="cuda:0")
+    bf = dict(dtype=torch.bfloat16, device="cuda:0")
+    out = {"acum": torch.empty(B, H, M, S, **f32), "dH": torch.empty(B, H, M, P, N, **bf),
+           "dH_f32": torch.empty(B, H, M, P, N, **f32), "H_in": torch.empty(B, H, M, P, N, **bf),
+           "h_final": torch.empty(B, H, P, N, **f32), "y_ssd": torch.empty(B, L, H, P, **bf),
+           "y": torch.empty(B, L, H, P, **bf)}
+
+    def step(ev):
+        ev[0].record()
+        api.dart_chunk_state(d["x"], d["dt"], d["A"], d["Bm"], out["acum"], out["dH"],
+                             out["dH_f32"], S)
+        api.dart_state_pass(d["x"], d["dt"], d["Bm"], d["C"], out["acum"], out["dH_f32"], None,
+                            out["H_in"], out["h_final"], out["y_ssd"], S)
+        ev[1].record()
+        api.dart_sma_fwd(d["Q"], d["E"], d["C"], out["dH"], out["y_ssd"], c["gate"], out["y"], S)
+        ev[2].record()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps + 2)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    evs = evs[2:]
+    tot = sorted(e[0].elapsed_time(e[2]) for e in evs)
+    sma = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    f_sma, f_scan = sma_flops(c), scan_flops(c)
+    med, sma_med = tot[len(tot) // 2], sma[len(sma) // 2]
+    return {
+        "workload": name, "batch": B, "seqlen": L, "heads": H, "groups": c["G"], "dstate": N,
+        "headdim": P, "chunk": S, "steps": steps,
+        "step_ms_median": med, "step_ms_min": tot[0], "sma_ms_median": sma_med,
+        "tokens_per_s": B * L / (med / 1e3),
+        "mfma_frac_whole_prefill": (f_sma + f_scan) / (med / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+        "sma_mfma_frac": f_sma / (sma_med / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+        "algorithmic_gflop_per_step": {"sma": f_sma / 1e9, "scan": f_scan / 1e9},
     }
 
 
@@ -373,11 +430,10 @@ def bench_decode_fp8(args, torch, api, synth):
     }
 
 
-def cpu_baseline(inp, seconds):
-    """The fp64 oracle, unmodified, on whole (batch, head) pairs of the same
-    workload until about `seconds` of CPU time; the full-layer rate follows
-    from the time per pair (every pair is the same amount of work)."""
-    import numpy as np
+def _oracle_pair_rate(inp, seconds, threads):
+    """Time the unmodified fp64 oracle on whole (batch, head) pairs of the
+    prefill workload for about `seconds`; returns (tokens/s of the full
+    layer, pairs done, seconds)."""
     from threadpoolctl import threadpool_limits
 
     import oracle
@@ -388,7 +444,7 @@ def cpu_baseline(inp, seconds):
     pairs = [(b, h) for b in range(c["B"]) for h in range(H)]
     pairs = pairs[::7] + [p for p in pairs if p not in pairs[::7]]
     done, t_total = 0, 0.0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         for b, h in pairs:
             g = h // (H // G)
             sl = {k: synth.as_f64(inp[k][b:b + 1, :, h:h + 1]) for k in ("x", "dt", "E")}
@@ -402,16 +458,64 @@ def cpu_baseline(inp, seconds):
             done += 1
             if t_total >= seconds:
                 break
-    per_pair = t_total / done
+    return L / (t_total / done * H), done, t_total
+
+
+def _oracle_decode_rate(seconds, threads):
+    """Time the unmodified fp64 oracle's decode step on single sequences of
+    the decode workload (32 heads, 128 cached memories each, drawn like the
+    benchmark's cache) for about `seconds`; returns chunk-memory bytes (bf16
+    cache) per second."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from ssm_state_attention_amd import synth
+
+    c = DECODE
+    H, N, P, S, k = c["H"], c["N"], c["P"], c["S"], c["chunks"]
+    done, t_total = 0, 0.0
+    with threadpool_limits(limits=threads):
+        while t_total < seconds and done < c["B"]:
+            cache = np.swapaxes(synth.as_f64(synth.draw_state(50 + done, (1, H, k, P, N), 0.01,
+                                                              torch.bfloat16)), -1, -2)
+            tok = {kk: synth.as_f64(v) for kk, v in
+                   synth.draw_decode_token(53 + done, 1, H, H, N, P).items()}
+            st = {"cache": cache, "h": np.zeros((1, H, N, P)), "dH_cur": np.zeros((1, H, N, P)),
+                  "n_chunks": np.array([k]), "pos": np.array([0])}
+            t0 = time.perf_counter()
+            oracle.decode_step(st, tok["x"], tok["dt"], tok["A"], tok["Bm"], tok["C"], tok["Q"],
+                               tok["E"], 0.5, S)
+            t_total += time.perf_counter() - t0
+            done += 1
+    return done * H * k * N * P * 2 / t_total, done, t_total
+
+
+def cpu_baseline(inp, seconds):
+    """The fp64 oracle, unmodified, on whole (batch, head) pairs of the same
+    workload until about `seconds` of wall time, once on one thread and once
+    with BLAS/OpenMP allowed every core this process may run on; the
+    full-layer rate follows from the time per pair (every pair is the same
+    amount of work).  The decode step is timed the same way on single
+    sequences of the decode workload."""
+    cores = len(os.sched_getaffinity(0))
+    v_all, n_all, t_all = _oracle_pair_rate(inp, seconds, cores)
+    v_one, n_one, t_one = _oracle_pair_rate(inp, seconds, 1)
+    dec_all, nd, td = _oracle_decode_rate(seconds / 3, cores)
     return {
-        "value": L / (per_pair * H),
+        "value": v_all,
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"{done} of {len(pairs)} (batch, head) pairs of the L=8192 layer, whole "
-                  f"sequence each, {t_total:.1f} s; full-layer tokens/s = L / (time per pair "
-                  f"x 32 heads); BLAS and numpy limited to 1 thread; host has "
-                  f"{os.cpu_count()} logical CPUs",
+        "sample": f"{n_all} of 128 (batch, head) pairs of the L=8192 layer, whole sequence "
+                  f"each, {t_all:.1f} s, numpy/BLAS allowed {cores} threads (the host CPUs this "
+                  f"process may use; os.cpu_count() = {os.cpu_count()}); full-layer tokens/s = "
+                  f"L / (time per pair x 32 heads)",
+        "one_thread": {"value": v_one, "unit": "tokens/s", "cores": 1,
+                       "sample": f"{n_one} pairs, {t_one:.1f} s"},
+        "decode": {"value": dec_all / 1e9, "unit": "GB/s of bf16 chunk memories", "cores": cores,
+                   "sample": f"{nd} sequences of 32 heads x 128 memories, {td:.1f} s"},
     }
 
 
@@ -490,6 +594,15 @@ def main():
                                                    "sma_ms_min")}
         result["mfma_frac_whole_prefill"] = pre["mfma_frac_whole_prefill"]
         result["algorithmic_gflop_per_step"] = {k: v / 1e9 for k, v in pre["flops"].items()}
+    if not args.no_extra_configs and pre is not None:
+        torch.cuda.empty_cache()
+        result["prefill_L4K"] = bench_prefill_extra(
+            args, torch, api, synth, PREFILL_L4K, "DART prefill, L=4096, 8 heads", args.steps)
+        torch.cuda.empty_cache()
+        result["prefill_L64K"] = bench_prefill_extra(
+            args, torch, api, synth, PREFILL_L64K,
+            "DART long-context prefill, L=65536, 32 heads (256 memories per head)",
+            max(3, min(args.steps, 5)))
     if not args.no_backward and pre is not None:
         torch.cuda.empty_cache()
         result["backward"] = bench_backward(args, torch, api, synth, pre["inputs"])

@@ -510,6 +510,324 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   }
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (lgkmcnt and expcnt left at their maxima).
+__host__ __device__ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Waits that order direct global-to-LDS loads with this wave's own LDS
+// accesses; the empty asm keeps the compiler from moving LDS accesses
+// across the wait.
+template <int IMM>
+__device__ __forceinline__ void wait_fence() {
+  __builtin_amdgcn_s_waitcnt(IMM);
+  asm volatile("" ::: "memory");
+}
+constexpr int kLgkm0 = 0xC07F;  // lgkmcnt(0)
+
+// Workgroup barrier for LDS hand-offs only: this wave's LDS reads and writes
+// are complete, then s_barrier.  Unlike __syncthreads it carries no release
+// fence, which would also wait for every direct global-to-LDS load in
+// flight (and with it for the memory fetched one step ahead).
+// The scheduling barriers keep every instruction (MFMAs included) on its
+// side of the workgroup barrier, as the ping-pong schedule requires.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  wait_fence<kLgkm0>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// LDS of k_sma_grp: two padded memory buffers, and per wave one E region
+// and one y_ssd region of its tokens
+template <int N, int P, int NTB, int WAVES>
+constexpr size_t sma_grp_lds_bytes() {
+  return (2ull * P * (N + 16) + 2ull * WAVES * 16 * NTB * P) * 2;
+}
+
+// Prefill SMA over the heads of one B/C/Q group.  One workgroup = WAVES
+// waves x 16·NTB tokens of ONE chunk k of one (batch, group); it runs the
+// heads of the group one after the other with k_sma_fwd's arithmetic and
+// ping-pong schedule (SmaMath16).  Q_t and C_t are shared by those heads,
+// so their fragments are loaded once, straight from HBM into the MFMA
+// B-operand registers, and stay resident for all of them; each head brings
+// only its E and y_ssd rows and its k memories.
+//
+// The memories of all heads form one sequence of hpg·k steps (head-major)
+// that the staging pipeline runs through without a break (buffer parity
+// follows the flat step index).  Each wave finishes a head for its own
+// tokens once the softmax of its last memory is done: y = y_ssd + gate·o
+// through its private y_ssd rows in LDS, whole-row stores, then the next
+// head's E values and a fresh softmax state.  It does so in the MFMA half
+// of the next head's first step, behind that step's products, so the work
+// overlaps the matrix core instead of holding the other waves at a
+// barrier; that step is peeled out of the inner loops, which match
+// k_sma_fwd's.  E and y_ssd rows of a wave's tokens reach its private LDS
+// regions by direct global-to-LDS loads one head ahead, so neither barriers
+// nor staging registers are involved and a head change costs no HBM round
+// trip.
+//
+// Grid mapping: blockIdx % 8 selects the XCD; an XCD takes every 8th (batch,
+// group), one after the other, each one's chunks heaviest first: its
+// running workgroups share one group's memories in L2, and a CU that drew
+// chunk k draws about M - 1 - k next.
+template <int N, int P, int NTB, int WAVES, bool STATS>
+__global__ __launch_bounds__(64 * WAVES) void k_sma_grp(
+    const bf16* __restrict__ Q, const bf16* __restrict__ E, const bf16* __restrict__ C,
+    const bf16* __restrict__ dH, const bf16* __restrict__ y_ssd, float gate,
+    bf16* __restrict__ y, int L, int H, int G, int S, int BG, int nbx, float scale_log2,
+    float* __restrict__ o_out, float* __restrict__ lse_out) {
+  typedef bf16 T;
+  typedef bf16x8 vec_t;
+  using TM = SmaMath16<T, N, P, NTB>;
+  constexpr int VE = 8;
+  constexpr int LDN = N + 2 * VE;  // memory rows [p][n] (see k_sma_fwd)
+  constexpr int TW = 16 * NTB, TWG = TW * WAVES;
+  constexpr int NVEC = P * N / VE;  // 16-byte vectors per memory
+  constexpr int NTHR = 64 * WAVES;
+  constexpr int VPT = (NVEC + NTHR - 1) / NTHR;
+  // a wave's E / y_ssd rows: RV 16-byte vectors per row, RPI rows per
+  // 64-lane direct load, NI loads per region.  Inside a row, vector v sits
+  // in slot v ^ (row % SW): the lanes' 8-byte accesses at one p-offset of
+  // 16 consecutive rows then fall into distinct banks (2-way at most)
+  constexpr int RV = P / VE, RPI = 64 / RV, NI = TW / RPI, SW = RV < 8 ? RV : 8;
+  constexpr int NPB = P / 16;
+  static_assert(64 % RV == 0 && TW % RPI == 0, "k_sma_grp row split");
+  static_assert(WAVES >= 2 && WAVES % 2 == 0, "k_sma_grp ping-pong halves");
+  __shared__ __align__(16) T sh_mem[2 * P * LDN];
+  __shared__ __align__(16) T sh_e[WAVES][TW * P];  // E rows of the next head to load
+  __shared__ __align__(16) T sh_y[WAVES][TW * P];  // y_ssd rows of the current head
+  static_assert(sizeof(sh_mem) + sizeof(sh_e) + sizeof(sh_y) ==
+                    sma_grp_lds_bytes<N, P, NTB, WAVES>(), "k_sma_grp LDS plan");
+
+  const int M = L / S, tpc = S / TWG, hpg = H / G;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int per_bg = M * tpc;
+  const int jb = slot / per_bg, rem = slot % per_bg;
+  const int kr = rem / tpc, sub = rem % tpc;
+  const int bg = jb * 8 + xcd;
+  if (bg >= BG || jb >= nbx) return;  // uniform over the workgroup
+  const int k = M - 1 - kr;
+  const int b = bg / G, g = bg % G, h0 = g * hpg;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long row0 = (long)b * L + (long)k * S + sub * TWG;  // first token of the tile
+  const long wrow0 = row0 + w * TW;                         // first token of this wave
+  const long HP = (long)H * P;
+
+  if (k == 0) {  // no memory is visible: y = y_ssd for every head, o = 0, lse = 0
+    const int rowv = hpg * RV;  // the group's heads are adjacent in a token row
+    for (int i = tid; i < TWG * rowv; i += NTHR) {
+      const int t = i / rowv, v = i % rowv;
+      const long o = (row0 + t) * HP + (long)h0 * P + v * VE;
+      *reinterpret_cast<vec_t*>(y + o) = load16(y_ssd + o);
+    }
+    if constexpr (STATS) {
+      for (int i = tid; i < TWG * hpg * (P / 4); i += NTHR) {
+        const int t = i / (hpg * (P / 4)), q = i % (hpg * (P / 4));
+        *reinterpret_cast<floatx4*>(o_out + (row0 + t) * HP + (long)h0 * P + 4 * q) =
+            floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+      for (int i = tid; i < TWG * hpg; i += NTHR) {
+        const int hh = i / TWG, t = i % TWG;
+        lse_out[((long)b * H + h0 + hh) * L + (long)k * S + sub * TWG + t] = 0.f;
+      }
+    }
+    return;
+  }
+
+  // the lane index, opaque: the swizzled LDS offsets derived from it are
+  // computed where they are used (once per head) instead of being kept
+  // in registers across the loops
+  auto lane_now = [&]() __attribute__((always_inline)) {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return l;
+  };
+  // direct global -> LDS copy of this wave's TW token rows of head hh into
+  // its swizzled [t][p] region: lane l of load q fills slot l % RV of row
+  // q·RPI + l / RV, i.e. vector (l % RV) ^ (row % SW) of that token row.
+  // The lane's element offset is made opaque so that its address arithmetic
+  // stays here instead of occupying registers across the loops.
+  auto dma_rows = [&](const T* src, T* region, int hh) __attribute__((always_inline)) {
+    const int l = lane_now(), r = l / RV;
+    const int off = r * (int)HP + ((l % RV) ^ (r % SW)) * VE;
+    const T* base = src + wrow0 * HP + (long)(h0 + hh) * P;
+#pragma unroll
+    for (int q = 0; q < NI; ++q)
+      __builtin_amdgcn_global_load_lds(
+          base + (long)q * RPI * HP + off,
+          (__attribute__((address_space(3))) void*)(region + q * RPI * P), 16, 0, 0);
+  };
+  // element (row, p) of a swizzled region
+  auto swz = [&](int row, int p) __attribute__((always_inline)) {
+    return row * P + (((p / VE) ^ (row % SW)) * VE) + p % VE;
+  };
+
+  const int nsteps = hpg * k;
+  // the memories are fetched in flat order (head-major): gh, gc are the
+  // head and chunk of the next one; after the last, the last is fetched
+  // again (a duplicate nobody reads)
+  int gh = 0, gc = 0;
+  vec_t stg0[VPT], stg[VPT];
+  auto gload_next = [&](vec_t (&dst)[VPT]) __attribute__((always_inline)) {
+    const T* m = dH + ((long)(b * H + h0 + gh) * M + gc) * (P * N);
+    if (++gc == k) {
+      gc = 0;
+      if (gh + 1 < hpg) ++gh; else gc = k - 1;
+    }
+    const vec_t* src = reinterpret_cast<const vec_t*>(m);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      const int vi = tid + v * NTHR;
+      if (NVEC % NTHR == 0 || vi < NVEC) dst[v] = src[vi];
+    }
+  };
+  auto swrite = [&](int buf, const vec_t (&src)[VPT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      const int vi = tid + v * NTHR;
+      if (NVEC % NTHR == 0 || vi < NVEC) {
+        const int p = vi / (N / VE), nv = vi % (N / VE);
+        *reinterpret_cast<vec_t*>(&sh_mem[buf * (P * LDN) + p * LDN + nv * VE]) = src[v];
+      }
+    }
+  };
+
+  TM tm;
+  tm.init(w, lane);
+  // this lane's E values (p = pb·16 + 4·grp .. +3 of its token rows)
+  auto load_e = [&]() __attribute__((always_inline)) {
+    const int l = lane_now(), col = l & 15, grp = l >> 4;
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb)
+        tm.ev[tb][pb] =
+            *reinterpret_cast<const bf16x4*>(&sh_e[w][swz(tb * 16 + col, pb * 16 + 4 * grp)]);
+  };
+  // ---- prologue: E and y_ssd rows of the first head, the Q/C fragments
+  // (resident for every head), the first two memories ----
+  dma_rows(E, sh_e[w], 0);
+  tm.load_q(Q + (row0 * G + g) * N, G * N);
+  tm.load_c(C + (row0 * G + g) * N, G * N);
+  dma_rows(y_ssd, sh_y[w], 0);
+  gload_next(stg0);
+  gload_next(stg);
+  wait_fence<vmcnt_imm(0)>();
+  load_e();
+  swrite(0, stg0);
+  wait_fence<kLgkm0>();  // the E reads are done before the region is refilled
+  if (hpg > 1) dma_rows(E, sh_e[w], 1);
+  __syncthreads();
+
+  // Head hh is complete (the softmax of its last memory is done): y rows of
+  // head hh for this wave's tokens, then the softmax state of head hh + 1.
+  // Run in the MFMA half of head hh + 1's first step, after that step's
+  // products are issued, so it overlaps the matrix core instead of holding
+  // up the other waves at a barrier.  The direct loads of head hh's y_ssd
+  // and head hh + 1's E are older than the newest memory fetch, which alone
+  // may stay in flight.
+  auto finish_head = [&](int hh) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);  // not interleaved with the products
+    wait_fence<vmcnt_imm(VPT)>();
+    const int h = h0 + hh;
+    if constexpr (STATS)
+      tm.stats(o_out + (row0 * H + h) * P, HP,
+               lse_out + ((long)b * H + h) * L + (long)k * S + sub * TWG, true);
+    // y = y_ssd + gate·o in the lane's own places of the y_ssd rows
+    const int l = lane_now(), col = l & 15, grp = l >> 4;
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+      const float f = gate / tm.ls[tb];
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb) {
+        T* q = &sh_y[w][swz(tb * 16 + col, pb * 16 + 4 * grp)];
+        store4(q, load4_f32(q) + f * tm.acc[tb][pb]);
+      }
+    }
+    {
+      // whole rows out (the slot a lane reads holds vector (l % RV) ^ (row % SW))
+      const int r = l / RV;
+      const int off = r * (int)HP + ((l % RV) ^ (r % SW)) * VE;
+      T* dst = y + wrow0 * HP + (long)h * P;
+#pragma unroll
+      for (int q = 0; q < NI; ++q)
+        *reinterpret_cast<vec_t*>(dst + (long)q * RPI * HP + off) =
+            *reinterpret_cast<const vec_t*>(&sh_y[w][(q * RPI + r) * P + (l % RV) * VE]);
+    }
+    // the next head's E (after the last head: stale values, never used) and
+    // a fresh softmax state: with the reference max at -inf the next
+    // memory's rescale factor is 0, which clears ls and acc on its own
+    load_e();
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) tm.mx[tb] = -INFINITY;
+    wait_fence<kLgkm0>();  // this wave's y_ssd and E reads are done
+    if (hh + 1 < hpg) dma_rows(y_ssd, sh_y[w], hh + 1);
+    if (hh + 2 < hpg) dma_rows(E, sh_e[w], hh + 2);
+  };
+
+  // ping-pong (k_sma_fwd's schedule) over the flat steps i = 0 .. nsteps:
+  // memory i sits in buffer i&1 during both halves of step i; each wave
+  // stages its share of memory i+1 into the other buffer in its softmax
+  // half and fetches memory i+2.  Lead waves multiply memory i in the
+  // first half and fold it into the softmax in the second; the others fold
+  // in memory i-1 in the first half and multiply memory i in the second.
+  // The first step of each head is peeled: it carries the previous head's
+  // finish in its MFMA half.
+  auto stage_next = [&](int i) __attribute__((always_inline)) {
+    swrite((i + 1) & 1, stg);
+    gload_next(stg);
+  };
+  auto mma = [&](int i) __attribute__((always_inline)) {
+    tm.mma(&sh_mem[(i & 1) * (P * LDN)], LDN);
+  };
+  auto softmax = [&]() __attribute__((always_inline)) { tm.template softmax<false>(scale_log2); };
+  int i = 0;
+  if (w < WAVES / 2) {
+    for (int hh = 0; hh < hpg; ++hh) {
+      mma(i);
+      if (hh > 0) finish_head(hh - 1);
+      lds_barrier();
+      softmax();
+      stage_next(i);
+      lds_barrier();
+      ++i;
+      for (int c = 1; c < k; ++c, ++i) {
+        mma(i);
+        lds_barrier();
+        softmax();
+        stage_next(i);
+        lds_barrier();
+      }
+    }
+    finish_head(hpg - 1);  // step nsteps: the other waves fold in the last memory
+    lds_barrier();
+    lds_barrier();
+  } else {
+    for (int hh = 0; hh < hpg; ++hh) {
+      if (hh > 0) softmax();  // the previous head's last memory
+      stage_next(i);
+      lds_barrier();
+      mma(i);
+      if (hh > 0) finish_head(hh - 1);
+      lds_barrier();
+      ++i;
+      for (int c = 1; c < k; ++c, ++i) {
+        softmax();
+        stage_next(i);
+        lds_barrier();
+        mma(i);
+        lds_barrier();
+      }
+    }
+    softmax();  // step nsteps: the last head's last memory
+    finish_head(hpg - 1);
+    lds_barrier();
+    lds_barrier();
+  }
+}
+
 template <typename T, int N, int P, int NTB, int WAVES>
 hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T* C, const T* dH,
                          const T* y_ssd, const float* acum, float gate, T* y, const T* prior,
@@ -534,6 +852,24 @@ hipError_t sma_fwd_waves(const PrefillShape& s, const T* Q, const T* E, const T*
     }
   } else if (prior8) {
     return hipErrorNotSupported;
+  }
+  if constexpr (std::is_same<T, bf16>::value && WAVES >= 2 && P % 32 == 0 &&
+                sma_grp_lds_bytes<N, P, NTB, WAVES>() <= 160 * 1024) {
+    // heads sharing a group: one workgroup per (batch, group, tile), the
+    // group's heads in turn (plain and training forward)
+    if (hpg > 1 && !acum && k0 == 0) {
+      const int BG = s.B * s.G, nbx = (BG + 7) / 8;
+      const long gblocks = 8L * nbx * M * tpc;
+      if (o)
+        hipLaunchKernelGGL((k_sma_grp<N, P, NTB, WAVES, true>), dim3(gblocks), dim3(64 * WAVES),
+                           0, st, Q, E, C, dH, y_ssd, gate, y, s.L, s.H, s.G, s.S, BG, nbx,
+                           scale_log2, o, lse);
+      else
+        hipLaunchKernelGGL((k_sma_grp<N, P, NTB, WAVES, false>), dim3(gblocks), dim3(64 * WAVES),
+                           0, st, Q, E, C, dH, y_ssd, gate, y, s.L, s.H, s.G, s.S, BG, nbx,
+                           scale_log2, nullptr, nullptr);
+      return hipGetLastError();
+    }
   }
   if (acum)
     hipLaunchKernelGGL((k_sma_fwd<T, N, P, NTB, WAVES, true>), dim3(blocks), dim3(64 * WAVES), 0,

@@ -726,11 +726,16 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_grp(
   // Run in the MFMA half of head hh + 1's first step, after that step's
   // products are issued, so it overlaps the matrix core instead of holding
   // up the other waves at a barrier.  The direct loads of head hh's y_ssd
-  // and head hh + 1's E are older than the newest memory fetch, which alone
-  // may stay in flight.
-  auto finish_head = [&](int hh) __attribute__((always_inline)) {
+  // and head hh + 1's E were issued at the previous head change; inside the
+  // loops at least one memory fetch was issued after them, and only the
+  // newest fetch may stay in flight.  After the loops (`last`) no fetch may
+  // follow them (one memory per head), so everything is waited for.
+  auto finish_head = [&](int hh, auto last) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);  // not interleaved with the products
-    wait_fence<vmcnt_imm(VPT)>();
+    if constexpr (decltype(last)::value)
+      wait_fence<vmcnt_imm(0)>();
+    else
+      wait_fence<vmcnt_imm(VPT)>();
     const int h = h0 + hh;
     if constexpr (STATS)
       tm.stats(o_out + (row0 * H + h) * P, HP,
@@ -787,7 +792,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_grp(
   if (w < WAVES / 2) {
     for (int hh = 0; hh < hpg; ++hh) {
       mma(i);
-      if (hh > 0) finish_head(hh - 1);
+      if (hh > 0) finish_head(hh - 1, IC<0>{});
       lds_barrier();
       softmax();
       stage_next(i);
@@ -801,7 +806,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_grp(
         lds_barrier();
       }
     }
-    finish_head(hpg - 1);  // step nsteps: the other waves fold in the last memory
+    finish_head(hpg - 1, IC<1>{});  // step nsteps: the other waves fold in the last memory
     lds_barrier();
     lds_barrier();
   } else {
@@ -810,7 +815,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_grp(
       stage_next(i);
       lds_barrier();
       mma(i);
-      if (hh > 0) finish_head(hh - 1);
+      if (hh > 0) finish_head(hh - 1, IC<0>{});
       lds_barrier();
       ++i;
       for (int c = 1; c < k; ++c, ++i) {
@@ -822,7 +827,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_grp(
       }
     }
     softmax();  // step nsteps: the last head's last memory
-    finish_head(hpg - 1);
+    finish_head(hpg - 1, IC<1>{});
     lds_barrier();
     lds_barrier();
   }

@@ -504,3 +504,47 @@ def test_config3_long_context_sampled_tokens(qscale):
         else:
             o_gpu = synth.as_f64(out["y"][0, tokens, h]) - synth.as_f64(out["y_ssd"][0, tokens, h])
             assert_parity(o_gpu, o[0, tokens, 0], io, f"c3 o (sharpened, sampled) h{h}")
+
+
+def _sma_launches(d, out, gate, S, reps):
+    """reps launches of dart_sma_fwd into fresh outputs (after one prefill)."""
+    ys = []
+    for _ in range(reps):
+        y = torch.full_like(out["y"], float("nan"))
+        api.dart_sma_fwd(d["Q"], d["E"], d["C"], out["dH"], out["y_ssd"], gate, y, S)
+        ys.append(y)
+    torch.cuda.synchronize()
+    return ys
+
+
+def test_grouped_sma_one_memory_tiles_repeated():
+    """Heads sharing a group, two chunks: every tile of chunk 1 sees one
+    memory, so o_t = C_tᵀ·dH[0] (the softmax weight is 1) and each head of
+    a group is finished after a single step, the case where the direct
+    loads of a head's y_ssd rows are newest.  o = y - y_ssd against the
+    oracle on every token, and 20 launches bit-identical."""
+    _need_gpu()
+    B, L, H, G, N, P, S, gate = 4, 512, 32, 4, 128, 64, 256, 1.0
+    inp = synth.draw_prefill(31, B, L, H, G, N, P, io=torch.bfloat16, qscale=10.0)
+    d = _to_dev(inp)
+    out = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate, S)
+    ys = _sma_launches(d, out, gate, S, 20)
+    n = _np(inp)
+    dH = oracle.chunk_states(n["x"], n["dt"], n["A"], n["Bm"], S)
+    o_ref = oracle.sma(n["Q"], n["E"], n["C"], dH, S)
+    for r, y in enumerate(ys):
+        assert torch.equal(y, ys[0]), f"launch {r} differs from launch 0"
+    o_gpu = synth.as_f64(ys[0]) - synth.as_f64(out["y_ssd"])
+    assert_parity(o_gpu, o_ref, torch.bfloat16, "o (one memory per tile)")
+
+
+def test_sma_repeated_launches_bit_identical():
+    """The L=8K ~370M-layer shape: ten SMA launches over the same inputs give
+    bit-identical outputs (no launch-to-launch variation from LDS staging)."""
+    _need_gpu()
+    B, L, H, G, N, P, S, gate = 4, 8192, 32, 4, 128, 64, 256, 0.5
+    d = _to_dev(synth.draw_prefill(0, B, L, H, G, N, P, io=torch.bfloat16))
+    out = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate, S)
+    ys = _sma_launches(d, out, gate, S, 10)
+    for r, y in enumerate(ys):
+        assert torch.equal(y, ys[0]), f"launch {r} differs from launch 0"

@@ -558,11 +558,10 @@ constexpr size_t sma_grp_lds_bytes() {
 // follows the flat step index).  Each wave finishes a head for its own
 // tokens once the softmax of its last memory is done: y = y_ssd + gate·o
 // through its private y_ssd rows in LDS, whole-row stores, then the next
-// head's E values and a fresh softmax state.  It does so in the MFMA half
-// of the next head's first step, behind that step's products, so the work
-// overlaps the matrix core instead of holding the other waves at a
-// barrier; that step is peeled out of the inner loops, which match
-// k_sma_fwd's.  E and y_ssd rows of a wave's tokens reach its private LDS
+// head's E values and a fresh softmax state.  All waves do so in the first
+// half of the next head's first step (the lead waves behind that step's
+// products), so the finishes of the two halves overlap; that step is
+// peeled out of the inner loops, which match k_sma_fwd's.  E and y_ssd rows of a wave's tokens reach its private LDS
 // regions by direct global-to-LDS loads one head ahead, so neither barriers
 // nor staging registers are involved and a head change costs no HBM round
 // trip.
@@ -723,9 +722,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_grp(
 
   // Head hh is complete (the softmax of its last memory is done): y rows of
   // head hh for this wave's tokens, then the softmax state of head hh + 1.
-  // Run in the MFMA half of head hh + 1's first step, after that step's
-  // products are issued, so it overlaps the matrix core instead of holding
-  // up the other waves at a barrier.  The direct loads of head hh's y_ssd
+  // Both halves of the waves run it in the first half of head hh + 1's
+  // first step (the lead waves behind that step's products, the others
+  // behind the softmax of head hh's last memory), so the two overlap
+  // instead of each holding up the other at a barrier.  The direct loads
+  // of head hh's y_ssd
   // and head hh + 1's E were issued at the previous head change; inside the
   // loops at least one memory fetch was issued after them, and only the
   // newest fetch may stay in flight.  After the loops (`last`) no fetch may
@@ -811,11 +812,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_grp(
     lds_barrier();
   } else {
     for (int hh = 0; hh < hpg; ++hh) {
-      if (hh > 0) softmax();  // the previous head's last memory
+      if (hh > 0) {  // the previous head's last memory, and its finish in
+        softmax();   // the same half as the lead waves' finish
+        finish_head(hh - 1, IC<0>{});
+      }
       stage_next(i);
       lds_barrier();
       mma(i);
-      if (hh > 0) finish_head(hh - 1, IC<0>{});
       lds_barrier();
       ++i;
       for (int c = 1; c < k; ++c, ++i) {

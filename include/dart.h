@@ -283,7 +283,7 @@ size_t dart_sma_decode_workspace(const dart_decode_dims* dims);
  *         bytes; its first int32 is set to 1 (never cleared by the library)
  *         when a chunk could not be appended because n_chunks[b] had reached
  *         max_chunks (the cache is never written out of bounds; n_chunks
- *         then stays at max_chunks).
+ *         then stays at max_chunks).  One workspace serves one call at a time.
  */
 dart_status dart_sma_decode(const dart_decode_dims* dims, const void* x, const float* dt,
                             const float* A, const void* Bm, const void* C, const void* Q,

@@ -44,8 +44,9 @@ int decode_splits(const dart_decode_dims& d) {
 size_t decode_workspace_bytes(const dart_decode_dims& d) {
   const int splits = decode_splits(d);
   const size_t pairs = static_cast<size_t>(d.batch * d.nheads);
-  size_t bytes = 256;                                            // status flag
-  bytes += ((pairs * d.headdim * sizeof(float) + 255) / 256) * 256;  // y_ssd
+  size_t bytes = 256;                                                   // status flag
+  bytes += ((static_cast<size_t>(d.batch) * sizeof(int32_t) + 255) / 256) * 256;  // n_chunks copy
+  bytes += ((pairs * d.headdim * sizeof(float) + 255) / 256) * 256;     // y_ssd
   bytes += ((pairs * splits * (d.headdim + 2) * sizeof(float) + 255) / 256) * 256;
   return bytes;
 }

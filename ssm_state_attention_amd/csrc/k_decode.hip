@@ -54,42 +54,26 @@ __device__ __forceinline__ float block_max256(float m, float* sh) {
   return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
 }
 
-// Decode, step 1: one workgroup per (head, batch) advances the SSM state,
-// forms y_ssd = C·h into the workspace and, when the token closes its chunk,
-// appends the finished memory to the cache (at index n_chunks[b], which the
-// streaming kernel never reads): rounded to the io type, or (F8) encoded
-// with the scale taken from the memory's largest magnitude, which the
-// workgroup finds from the registers it already holds.  A launch of its
-// own: done by the first of the streaming workgroups it held every stream
-// back behind a latency-bound read-modify-write of 128 KB of state.
+// The state step of one (batch, head), run by a 256-thread workgroup: advances
+// the SSM state, forms y_ssd = C·h into sh_y and, when the token closes its
+// chunk, appends the finished memory to the cache (at index kc = n_chunks[b],
+// which the streaming loops never read): rounded to the io type, or (F8)
+// encoded with the scale taken from the memory's largest magnitude, which the
+// workgroup finds from the registers it already holds.  sh_c, sh_b, sh_x
+// (C, B, x of the token) must be in LDS; sh_y is complete on return.
 template <typename T, int N, int P, bool F8>
-__global__ __launch_bounds__(256) void k_decode_state(
-    const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
-    const T* __restrict__ Bm, const T* __restrict__ C, T* __restrict__ cache,
-    uint8_t* __restrict__ cache8, float* __restrict__ cscale, float* __restrict__ hst,
-    float* __restrict__ dHc, const int* __restrict__ n_chunks, const int* __restrict__ pos,
-    int* __restrict__ ws_flag, float* __restrict__ ws_yssd, int H, int G, int S,
-    int max_chunks) {
+__device__ __forceinline__ void state_step(float dtv, float Ah, T* __restrict__ cache,
+                                           uint8_t* __restrict__ cache8,
+                                           float* __restrict__ cscale, float* __restrict__ hst,
+                                           float* __restrict__ dHc, long pair, int kc, int ps,
+                                           int S, int max_chunks, int* ws_flag,
+                                           const float* sh_c, const float* sh_b,
+                                           const float* sh_x, float* sh_y, float* sh_m) {
   constexpr int Q4 = N / 4;
   static_assert((P * N / 4) % 64 == 0 && 64 % Q4 == 0, "decode state mapping");
-  __shared__ float sh_c[N], sh_b[N], sh_x[P], sh_y[P], sh_m[4];
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int g = h / (H / G);
-  const long pair = (long)b * H + h;
   const int tid = threadIdx.x;
-  int kc = n_chunks[b];
-  kc = kc < 0 ? 0 : (kc > max_chunks ? max_chunks : kc);
-  const int ps = pos[b];
-  for (int i = tid; i < N; i += 256) {
-    const long o = ((long)b * G + g) * N + i;
-    sh_c[i] = to_f32(C[o]);
-    sh_b[i] = to_f32(Bm[o]);
-  }
-  for (int i = tid; i < P; i += 256) sh_x[i] = to_f32(x[pair * P + i]);
-  __syncthreads();
   {
-    const float dtv = dt[pair];
-    const float a = exp_neg(dtv * A[h]);
+    const float a = exp_neg(dtv * Ah);
     const bool close = ps == S - 1;
     const bool append = close && kc < max_chunks;  // uniform over the workgroup
     floatx4* hp = reinterpret_cast<floatx4*>(hst + pair * (P * N));
@@ -167,17 +151,71 @@ __global__ __launch_bounds__(256) void k_decode_state(
     }
     if (close && !append && tid == 0) atomicOr(ws_flag, 1);
     __syncthreads();
-    for (int p = tid; p < P; p += 256) ws_yssd[pair * P + p] = sh_y[p];
   }
 }
 
-// Merge of the per-wave online-softmax states of one workgroup into the
-// split's (max, denominator, numerator[P]) partial.  acc: this lane's value
-// sums for rows it·RP + pr, already reduced over the lanes of a row.
-template <int P, int NW, int NPASS, int RP>
-__device__ __forceinline__ void write_split_partial(const float (&acc)[NPASS], float mx, float ls,
-                                                    bool row_lead, int pr, float* ws_part,
-                                                    long pair, int splits, int split) {
+// Decode, step 1: one workgroup per (head, batch) runs the state step and
+// leaves y_ssd and the cache length n_chunks[b] in the workspace.  A launch of its own: run by the streaming
+// workgroups (before or after their stream), its 128 KB of state reads and
+// writes per head interleave with the cache stream and cost more HBM time
+// than a separate launch does.
+template <typename T, int N, int P, bool F8>
+__global__ __launch_bounds__(256) void k_decode_state(
+    const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
+    const T* __restrict__ Bm, const T* __restrict__ C, T* __restrict__ cache,
+    uint8_t* __restrict__ cache8, float* __restrict__ cscale, float* __restrict__ hst,
+    float* __restrict__ dHc, const int* __restrict__ n_chunks, const int* __restrict__ pos,
+    int* __restrict__ ws_flag, int* __restrict__ ws_kc, float* __restrict__ ws_yssd, int H,
+    int G, int S, int max_chunks) {
+  __shared__ float sh_c[N], sh_b[N], sh_x[P], sh_y[P], sh_m[4];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (H / G);
+  const long pair = (long)b * H + h;
+  const int tid = threadIdx.x;
+  int kc = n_chunks[b];
+  kc = kc < 0 ? 0 : (kc > max_chunks ? max_chunks : kc);
+  const int ps = pos[b];
+  // the streaming kernel reads this copy, so that its workgroups may advance
+  // n_chunks and pos while others still stream
+  if (h == 0 && tid == 0) ws_kc[b] = kc;
+  for (int i = tid; i < N; i += 256) {
+    const long o = ((long)b * G + g) * N + i;
+    sh_c[i] = to_f32(C[o]);
+    sh_b[i] = to_f32(Bm[o]);
+  }
+  for (int i = tid; i < P; i += 256) sh_x[i] = to_f32(x[pair * P + i]);
+  __syncthreads();
+  state_step<T, N, P, F8>(dt[pair], A[h], cache, cache8, cscale, hst, dHc, pair, kc, ps, S,
+                          max_chunks, ws_flag, sh_c, sh_b, sh_x, sh_y, sh_m);
+  for (int p = tid; p < P; p += 256) ws_yssd[pair * P + p] = sh_y[p];
+}
+
+// Arguments of one decode call, as the streaming kernels see them.  From the
+// workspace: kc (n_chunks[b] at the start of the call, clamped), yssd (the
+// state kernel's y_ssd rows) and part (per-split partials).
+template <typename T>
+struct DecodeArgs {
+  const T *x, *Bm, *C, *Q, *E;
+  const float *dt, *A;
+  T* cache;
+  uint8_t* cache8;
+  float* cscale;
+  float *h, *dHc;
+  int *n_chunks, *pos;
+  int* kc;
+  float *yssd, *part;
+  T* y;
+  float gate, scale_log2;
+  int B, H, G, S, max_chunks, splits, cps;
+};
+
+// Merge of the per-wave online-softmax states of one workgroup: emit(p, num,
+// m, den) receives, for each row p, the (max, denominator, numerator) of the
+// workgroup's memories.  acc: this lane's value sums for rows it·RP + pr,
+// already reduced over the lanes of a row.
+template <int P, int NW, int NPASS, int RP, typename Emit>
+__device__ __forceinline__ void merge_waves(const float (&acc)[NPASS], float mx, float ls,
+                                            bool row_lead, int pr, Emit emit) {
   __shared__ float sh_wm[NW], sh_wl[NW];
   __shared__ float sh_wacc[NW][P];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -203,12 +241,66 @@ __device__ __forceinline__ void write_split_partial(const float (&acc)[NPASS], f
         den += f * sh_wl[ww];
       }
     }
-    float* part = ws_part + (pair * splits + split) * (P + 2);
-    part[2 + p] = num;
-    if (p == 0) {
-      part[0] = mall;
-      part[1] = den;
-    }
+    emit(p, num, mall, den);
+  }
+}
+
+// Token operands the streaming workgroup of (b, h) stages in LDS: Q and C of
+// the group and E of the head.
+template <typename T, int N, int P>
+__device__ __forceinline__ void stage_token(const DecodeArgs<T>& a, int b, int g, long pair,
+                                            float* sh_q, float* sh_c, float* sh_e) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < N; i += 256) {
+    const long o = ((long)b * a.G + g) * N + i;
+    sh_q[i] = to_f32(a.Q[o]);
+    sh_c[i] = to_f32(a.C[o]);
+  }
+  for (int i = tid; i < P; i += 256) sh_e[i] = to_f32(a.E[pair * P + i]);
+  __syncthreads();
+}
+
+// Advance sequence b's position after its token: n_chunks (clamped value kc
+// from the start of the call) grows by one when the token closed a chunk.
+__device__ __forceinline__ void advance_position(int* n_chunks, int* pos, int b, int kc, int S,
+                                                 int max_chunks) {
+  if (pos[b] == S - 1) {
+    n_chunks[b] = kc < max_chunks ? kc + 1 : max_chunks;
+    pos[b] = 0;
+  } else {
+    pos[b] += 1;
+  }
+}
+
+// End of a streaming workgroup.  Several splits per (b, h): the split's
+// (max, denominator, numerator[P]) partial goes to the workspace for
+// k_decode_combine.  One split (SINGLE): the workgroup holds all of the
+// head's memories, so it writes y = y_ssd + gate·o itself (y_ssd from the
+// state kernel, which ran before), and the workgroup of head 0 advances its
+// sequence's position (no other workgroup of the launch reads it).
+template <typename T, int P, bool SINGLE, int NW, int NPASS, int RP>
+__device__ __forceinline__ void stream_tail(const float (&acc)[NPASS], float mx, float ls,
+                                            bool row_lead, int pr, const DecodeArgs<T>& a,
+                                            long pair, int b, int h, int kc, int split) {
+  if constexpr (!SINGLE) {
+    float* part = a.part + (pair * a.splits + split) * (P + 2);
+    merge_waves<P, NW, NPASS, RP>(acc, mx, ls, row_lead, pr,
+                                  [&](int p, float num, float m, float den) {
+                                    part[2 + p] = num;
+                                    if (p == 0) {
+                                      part[0] = m;
+                                      part[1] = den;
+                                    }
+                                  });
+  } else {
+    const float* ys = a.yssd + pair * P;
+    T* yp = a.y + pair * P;
+    merge_waves<P, NW, NPASS, RP>(acc, mx, ls, row_lead, pr,
+                                  [&](int p, float num, float m, float den) {
+                                    const float o = den > 0.f ? num / den : 0.f;
+                                    yp[p] = from_f32<T>(ys[p] + a.gate * o);
+                                  });
+    if (h == 0 && threadIdx.x == 0) advance_position(a.n_chunks, a.pos, b, kc, a.S, a.max_chunks);
   }
 }
 
@@ -218,14 +310,9 @@ __device__ __forceinline__ void write_split_partial(const float (&acc)[NPASS], f
 // loads): lane (nv, pr) holds key entries n in [nv·VE, nv·VE + VE) of rows
 // p = it·RP + pr, forms partial Q·dH[c] and C·dH[c] over its n-range,
 // reduces the score across the wave and keeps an online softmax whose value
-// accumulator stays partial over n until the end.  The (max, denominator,
-// numerator[P]) partial of the split goes to the workspace; k_decode_combine
-// merges the splits and adds y_ssd.
-template <typename T, int N, int P>
-__global__ __launch_bounds__(256) void k_sma_decode(
-    const T* __restrict__ C, const T* __restrict__ Q, const T* __restrict__ E,
-    const T* __restrict__ cache, const int* __restrict__ n_chunks, float* __restrict__ ws_part,
-    int H, int G, int max_chunks, int splits, int cps, float scale_log2) {
+// accumulator stays partial over n until the end (stream_tail).
+template <typename T, int N, int P, bool SINGLE>
+__global__ __launch_bounds__(256) void k_sma_decode(const DecodeArgs<T> a) {
   constexpr int VE = Vec16<T>::n;
   constexpr int NV = N / VE;   // 16-byte vectors per memory row
   constexpr int RP = 64 / NV;  // rows per wave pass
@@ -236,22 +323,14 @@ __global__ __launch_bounds__(256) void k_sma_decode(
   __shared__ float sh_q[N], sh_c[N], sh_e[P];
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int g = h / (H / G);
-  const long pair = (long)b * H + h;
+  const int g = h / (a.H / a.G);
+  const long pair = (long)b * a.H + h;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int kc = n_chunks[b];
-  kc = kc < 0 ? 0 : (kc > max_chunks ? max_chunks : kc);
+  const int kc = a.kc[b];
+  stage_token<T, N, P>(a, b, g, pair, sh_q, sh_c, sh_e);
 
-  for (int i = tid; i < N; i += 256) {
-    const long o = ((long)b * G + g) * N + i;
-    sh_q[i] = to_f32(Q[o]);
-    sh_c[i] = to_f32(C[o]);
-  }
-  for (int i = tid; i < P; i += 256) sh_e[i] = to_f32(E[pair * P + i]);
-  __syncthreads();
-
-  const int c_begin = split * cps;
-  const int c_end = min(kc, c_begin + cps);
+  const int c_begin = split * a.cps;
+  const int c_end = min(kc, c_begin + a.cps);
   const int nv = lane % NV, pr = lane / NV;
   constexpr bool kDot2 = std::is_same<T, bf16>::value;
   float qv[VE], cv[VE], ev[NPASS], acc[NPASS];
@@ -276,7 +355,7 @@ __global__ __launch_bounds__(256) void k_sma_decode(
     acc[it] = 0.f;
   }
   float mx = -INFINITY, ls = 0.f;
-  const T* base = cache + pair * (long)max_chunks * (P * N);
+  const T* base = a.cache + pair * (long)a.max_chunks * (P * N);
   for (int c = c_begin + w; c < c_end; c += NW) {
     const T* src = base + (long)c * (P * N);
     vec_t raw[NPASS];
@@ -304,7 +383,7 @@ __global__ __launch_bounds__(256) void k_sma_decode(
       zc[it] = z2;
       s += ev[it] * zq;
     }
-    s = wave_sum_dpp(s) * scale_log2;
+    s = wave_sum_dpp(s) * a.scale_log2;
     // lazy rescale, as in the prefill kernel (s is uniform over the wave)
     if (s > mx + kLazyLog2) {
       const float al = exp2_fast(mx - s);  // 0 for the first memory
@@ -322,7 +401,8 @@ __global__ __launch_bounds__(256) void k_sma_decode(
   for (int it = 0; it < NPASS; ++it)
 #pragma unroll
     for (int off = 1; off < NV; off <<= 1) acc[it] += __shfl_xor(acc[it], off);
-  write_split_partial<P, NW, NPASS, RP>(acc, mx, ls, nv == 0, pr, ws_part, pair, splits, split);
+  stream_tail<T, P, SINGLE, NW, NPASS, RP>(acc, mx, ls, nv == 0, pr, a, pair, b, h, kc,
+                                           split);
 }
 
 // Bytes of one fp8 cache row that a lane loads at a time: the widest of 16,
@@ -357,12 +437,8 @@ __device__ __forceinline__ unsigned word(typename Words<W>::v r, int j) {
 // every E4M3 value is a bfloat16 value) and contracts it with dot2; fp32 io
 // decodes into fp32.  The products are those of the codes, so the memory's
 // scale multiplies the reduced score and the softmax weight of its value.
-template <typename T, int N, int P>
-__global__ __launch_bounds__(256) void k_sma_decode_f8(
-    const T* __restrict__ C, const T* __restrict__ Q, const T* __restrict__ E,
-    const uint8_t* __restrict__ cache8, const float* __restrict__ cscale,
-    const int* __restrict__ n_chunks, float* __restrict__ ws_part, int H, int G, int max_chunks,
-    int splits, int cps, float scale_log2) {
+template <typename T, int N, int P, bool SINGLE>
+__global__ __launch_bounds__(256) void k_sma_decode_f8(const DecodeArgs<T> a) {
   constexpr int LB = F8Load<N, P>::LB, W = F8Load<N, P>::W;
   constexpr int NV = N / LB;   // loads per memory row
   constexpr int RP = 64 / NV;  // rows per wave pass
@@ -373,23 +449,15 @@ __global__ __launch_bounds__(256) void k_sma_decode_f8(
   __shared__ float sh_q[N], sh_c[N], sh_e[P];
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int g = h / (H / G);
-  const long pair = (long)b * H + h;
+  const int g = h / (a.H / a.G);
+  const long pair = (long)b * a.H + h;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int kc = n_chunks[b];
-  kc = kc < 0 ? 0 : (kc > max_chunks ? max_chunks : kc);
+  const int kc = a.kc[b];
+  stage_token<T, N, P>(a, b, g, pair, sh_q, sh_c, sh_e);
 
-  for (int i = tid; i < N; i += 256) {
-    const long o = ((long)b * G + g) * N + i;
-    sh_q[i] = to_f32(Q[o]);
-    sh_c[i] = to_f32(C[o]);
-  }
-  for (int i = tid; i < P; i += 256) sh_e[i] = to_f32(E[pair * P + i]);
-  __syncthreads();
-
-  const int c_begin = split * cps;
-  const int c_end = min(kc, c_begin + cps);
+  const int c_begin = split * a.cps;
+  const int c_end = min(kc, c_begin + a.cps);
   const int nv = lane % NV, pr = lane / NV;
   constexpr bool kDot2 = std::is_same<T, bf16>::value;
   float qv[LB], cv[LB], ev[NPASS], acc[NPASS];
@@ -412,8 +480,8 @@ __global__ __launch_bounds__(256) void k_sma_decode_f8(
     acc[it] = 0.f;
   }
   float mx = -INFINITY, ls = 0.f;
-  const uint8_t* base = cache8 + pair * (long)max_chunks * (P * N);
-  const float* sbase = cscale + pair * (long)max_chunks;
+  const uint8_t* base = a.cache8 + pair * (long)a.max_chunks * (P * N);
+  const float* sbase = a.cscale + pair * (long)a.max_chunks;
   for (int c = c_begin + w; c < c_end; c += NW) {
     const uint8_t* src = base + (long)c * (P * N);
     load_t raw[NPASS];
@@ -448,7 +516,7 @@ __global__ __launch_bounds__(256) void k_sma_decode_f8(
       zc[it] = z2;
       s += ev[it] * zq;
     }
-    s = wave_sum_dpp(s) * (sc * scale_log2);
+    s = wave_sum_dpp(s) * (sc * a.scale_log2);
     if (s > mx + kLazyLog2) {
       const float al = exp2_fast(mx - s);  // 0 for the first memory
       ls *= al;
@@ -466,16 +534,21 @@ __global__ __launch_bounds__(256) void k_sma_decode_f8(
   for (int it = 0; it < NPASS; ++it)
 #pragma unroll
     for (int off = 1; off < NV; off <<= 1) acc[it] += __shfl_xor(acc[it], off);
-  write_split_partial<P, NW, NPASS, RP>(acc, mx, ls, nv == 0, pr, ws_part, pair, splits, split);
+  stream_tail<T, P, SINGLE, NW, NPASS, RP>(acc, mx, ls, nv == 0, pr, a, pair, b, h, kc,
+                                           split);
 }
 
 // Merge the per-split (max, denominator, numerator[P]) partials of one
-// (batch, head) and apply the gate.
+// (batch, head) and apply the gate; the workgroup of head 0 advances its
+// sequence's position (the launch reads no other position).
 template <typename T>
 __global__ __launch_bounds__(128) void k_decode_combine(const float* __restrict__ ws_yssd,
                                                         const float* __restrict__ ws_part,
-                                                        float gate, T* __restrict__ y, int P,
-                                                        int splits) {
+                                                        const int* __restrict__ ws_kc,
+                                                        float gate, T* __restrict__ y,
+                                                        int* __restrict__ n_chunks,
+                                                        int* __restrict__ pos, int H, int P,
+                                                        int splits, int S, int max_chunks) {
   const long pair = blockIdx.x;
   const float* part = ws_part + pair * splits * (P + 2);
   float mall = -INFINITY;
@@ -493,19 +566,9 @@ __global__ __launch_bounds__(128) void k_decode_combine(const float* __restrict_
     const float o = den > 0.f ? num / den : 0.f;
     y[pair * P + p] = from_f32<T>(ws_yssd[pair * P + p] + gate * o);
   }
-}
-
-// Advance the per-sequence position after every head has read it.
-__global__ void k_decode_advance(int* __restrict__ n_chunks, int* __restrict__ pos, int B, int S,
-                                 int max_chunks) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= B) return;
-  if (pos[b] == S - 1) {
-    const int k = n_chunks[b];
-    n_chunks[b] = k < max_chunks ? k + 1 : max_chunks;
-    pos[b] = 0;
-  } else {
-    pos[b] += 1;
+  if (pair % H == 0 && threadIdx.x == 0) {
+    const int b = static_cast<int>(pair / H);
+    advance_position(n_chunks, pos, b, ws_kc[b], S, max_chunks);
   }
 }
 
@@ -559,15 +622,20 @@ void* g_scratch_ptr[kMaxScratchDevices] = {};
 
 struct DecodeWs {
   int* flag;
+  int* kc;
   float* yssd;
   float* part;
 };
-// Workspace layout: status flag (256 bytes), y_ssd [B·H, P] f32, then the
-// per-split partials [B·H, splits, P + 2] f32, each 256-byte aligned.
-DecodeWs decode_ws(void* workspace, long pairs, int P) {
+constexpr long round256(long bytes) { return (bytes + 255) / 256 * 256; }
+// Workspace layout, each part 256-byte aligned: the cache-full flag (256
+// bytes), kc [B] int32, y_ssd [B·H, P] f32, the per-split partials
+// [B·H, splits, P + 2] f32.  Every call writes what it reads, except the
+// flag, which the library only ever sets.
+DecodeWs decode_ws(void* workspace, int B, long pairs, int P) {
   char* ws = static_cast<char*>(workspace);
-  return {reinterpret_cast<int*>(ws), reinterpret_cast<float*>(ws + 256),
-          reinterpret_cast<float*>(ws + 256 + ((pairs * P * sizeof(float) + 255) / 256) * 256)};
+  const long o_kc = 256, o_y = o_kc + round256(B * 4L), o_part = o_y + round256(pairs * P * 4L);
+  return {reinterpret_cast<int*>(ws), reinterpret_cast<int*>(ws + o_kc),
+          reinterpret_cast<float*>(ws + o_y), reinterpret_cast<float*>(ws + o_part)};
 }
 
 }  // namespace
@@ -595,37 +663,42 @@ hipError_t launch_sma_decode(const DecodeShape& s, const T* x, const float* dt, 
                              int* n_chunks, int* pos, T* y, void* workspace, int* flag,
                              hipStream_t st) {
   const long pairs = (long)s.B * s.H;
-  DecodeWs ws = decode_ws(workspace, pairs, P);
+  DecodeWs ws = decode_ws(workspace, s.B, pairs, P);
   if (flag) ws.flag = flag;
   const int cps = (s.max_chunks + s.splits - 1) / s.splits;
   const float scale_log2 = kLog2e / sqrtf(static_cast<float>(N));
   const bool f8 = cache8 != nullptr;
+  const DecodeArgs<T> a{x,     Bm,      C,       Q,      E,      dt,       A,
+                        cache, cache8,  cscale,  h,      dH_cur, n_chunks, pos,
+                        ws.kc, ws.yssd, ws.part, y,      gate,   scale_log2,
+                        s.B,   s.H,     s.G,     s.S,    s.max_chunks, s.splits, cps};
   if (f8)
     hipLaunchKernelGGL((k_decode_state<T, N, P, true>), dim3(1, s.H, s.B), dim3(256), 0, st, x,
                        dt, A, Bm, C, nullptr, cache8, cscale, h, dH_cur, n_chunks, pos, ws.flag,
-                       ws.yssd, s.H, s.G, s.S, s.max_chunks);
+                       ws.kc, ws.yssd, s.H, s.G, s.S, s.max_chunks);
   else
     hipLaunchKernelGGL((k_decode_state<T, N, P, false>), dim3(1, s.H, s.B), dim3(256), 0, st, x,
                        dt, A, Bm, C, cache, nullptr, nullptr, h, dH_cur, n_chunks, pos, ws.flag,
-                       ws.yssd, s.H, s.G, s.S, s.max_chunks);
+                       ws.kc, ws.yssd, s.H, s.G, s.S, s.max_chunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const dim3 grid(s.splits, s.H, s.B);
+  if (s.splits == 1) {
+    // the streaming workgroups also write y and advance the positions
+    if (f8)
+      hipLaunchKernelGGL((k_sma_decode_f8<T, N, P, true>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_sma_decode<T, N, P, true>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   if (f8)
-    hipLaunchKernelGGL((k_sma_decode_f8<T, N, P>), dim3(s.splits, s.H, s.B), dim3(256), 0, st, C,
-                       Q, E, cache8, cscale, n_chunks, ws.part, s.H, s.G, s.max_chunks, s.splits,
-                       cps, scale_log2);
+    hipLaunchKernelGGL((k_sma_decode_f8<T, N, P, false>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((k_sma_decode<T, N, P>), dim3(s.splits, s.H, s.B), dim3(256), 0, st, C, Q,
-                       E, cache, n_chunks, ws.part, s.H, s.G, s.max_chunks, s.splits, cps,
-                       scale_log2);
+    hipLaunchKernelGGL((k_sma_decode<T, N, P, false>), grid, dim3(256), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_decode_combine<T>), dim3(pairs), dim3(128), 0, st, ws.yssd, ws.part, gate,
-                     y, P, s.splits);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_decode_advance, dim3((s.B + 255) / 256), dim3(256), 0, st, n_chunks, pos,
-                     s.B, s.S, s.max_chunks);
+  hipLaunchKernelGGL((k_decode_combine<T>), dim3(pairs), dim3(128), 0, st, ws.yssd, ws.part,
+                     ws.kc, gate, y, n_chunks, pos, s.H, P, s.splits, s.S, s.max_chunks);
   return hipGetLastError();
 }
 

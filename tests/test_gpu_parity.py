@@ -289,11 +289,16 @@ def test_decode_cache_full_sets_flag():
     assert st["n_chunks"].tolist() == [mx] * B and st["pos"].tolist() == [0] * B
 
 
-@pytest.mark.parametrize("io,N,P,S", [(torch.bfloat16, 128, 64, 64), (torch.float32, 16, 16, 32)])
-def test_decode_continues_prefill(io, N, P, S):
+@pytest.mark.parametrize("io,N,P,S,cap", [(torch.bfloat16, 128, 64, 64, 3),
+                                           (torch.bfloat16, 128, 64, 64, 16),
+                                           (torch.float32, 16, 16, 32, 3)])
+def test_decode_continues_prefill(io, N, P, S, cap):
     """Prefill k chunks, then decode the next chunk token by token: decode
     outputs match the prefill of the longer sequence, and the appended
-    memory matches the prefill's memory (GPU against GPU and oracle)."""
+    memory matches the prefill's memory (GPU against GPU and oracle).  A
+    cache of 3 slots is streamed by one workgroup per (sequence, head), whose
+    last one advances the positions; 16 slots split each stream over several
+    workgroups with separate combine and advance launches."""
     _need_gpu()
     B, H, G, k0, M = 2, 4, 2, 2, 3
     L = S * M
@@ -305,7 +310,7 @@ def test_decode_continues_prefill(io, N, P, S):
     pre = {k: v[:, :k0 * S].contiguous() if k != "A" else v for k, v in d.items()}
     head = api.prefill(pre["x"], pre["dt"], pre["A"], pre["Bm"], pre["C"], pre["Q"], pre["E"],
                        gate, S)
-    st = api.new_decode_state(B, H, G, N, P, S, M, io, DEV)
+    st = api.new_decode_state(B, H, G, N, P, S, cap, io, DEV)
     st["cache"][:, :, :k0].copy_(head["dH"])
     st["h"].copy_(head["h_final"])
     st["n_chunks"].fill_(k0)

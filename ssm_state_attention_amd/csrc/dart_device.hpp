@@ -150,4 +150,57 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return sum_lane_groups(v);
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (lgkmcnt and expcnt left at their maxima).
+__host__ __device__ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Waits that order direct global-to-LDS loads with this wave's own LDS
+// accesses; the empty asm keeps the compiler from moving LDS accesses
+// across the wait.
+template <int IMM>
+__device__ __forceinline__ void wait_fence() {
+  __builtin_amdgcn_s_waitcnt(IMM);
+  asm volatile("" ::: "memory");
+}
+constexpr int kLgkm0 = 0xC07F;  // lgkmcnt(0)
+
+// Workgroup barrier for LDS hand-offs only: this wave's LDS reads and writes
+// are complete, then s_barrier.  Unlike __syncthreads it carries no release
+// fence, which would also wait for every direct global-to-LDS load in
+// flight (and with it for the memory fetched one step ahead).
+// The scheduling barriers keep every instruction (MFMAs included) on its
+// side of the workgroup barrier, as schedules that hand work between waves
+// at the barrier require.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  wait_fence<kLgkm0>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Direct global-to-LDS copies (this lane's 16 or 4 bytes at gptr go to LDS
+// byte address lds + 16·lane, resp. lds + 4·lane; lds is wave-uniform),
+// issued through inline assembly so that the compiler does not track them:
+// it would otherwise wait for every copy in flight before LDS reads it
+// cannot tell apart from the copies' targets.  The caller orders them with
+// explicit waits (wait_fence<vmcnt_imm(n)>, counting these copies among the
+// wave's vector-memory operations) and barriers.  No register receives data.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return static_cast<unsigned>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+__device__ __forceinline__ void lds_copy16(const void* gptr, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4(const void* gptr, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(gptr), "s"(lds)
+               : "memory", "m0");
+}
+
 }  // namespace dart

@@ -874,6 +874,258 @@ __global__ __launch_bounds__(kOutThreads) void k_chunk_out_tr(
   }
 }
 
+// LDS plan of k_chunk_out_dma (chunks of kMaxChunk tokens): the log-decay
+// factors of the head being computed (first, so that their addresses fit
+// the 16-bit offsets of LDS instructions), then three head slots, each
+// holding x [s][p] and H_in[k] [p][n] as XOR-swizzled 16-byte chunks without
+// padding (direct global-to-LDS copies fill whole 1 KB runs) and the head's
+// raw acum and dt.  Phase 1's padded B rows share the bytes of slots 0 and 1.
+template <int N, int P>
+struct ChunkOutDma {
+  static constexpr int S = kMaxChunk;
+  static constexpr int LDC = N + 16;
+  static constexpr int XB = S * P * 2, HB = P * N * 2;
+  static constexpr int SLOT = XB + HB + 2 * S * 4;
+  static constexpr int FAC = 3 * S * 4;  // A_s, v_s, log2 dt_s
+  static constexpr size_t bytes = 3ull * SLOT + FAC;
+  static constexpr bool fits = P == 64 && N % 64 == 0 && bytes <= 160 * 1024 &&
+                               size_t(S) * LDC * 2 <= 2ull * SLOT;
+};
+
+// Native chunk output, 16-bit io, S = kMaxChunk and P = 64: the arithmetic
+// of k_chunk_out_tr (same tiles, weights and k-slot pairing), with each
+// head's x, H_in[k], acum and dt fetched by direct global-to-LDS copies two
+// heads ahead into a ring of three slots, so that one workgroup per CU keeps
+// two heads of input in flight while it computes a third.  The C operand is
+// read from HBM straight into fragments and y leaves from the accumulators.
+// Per head: wait for this wave's copies of the head, barrier (every wave's
+// copies have landed and every wave is done with the previous head, whose
+// slot now receives head + 2), log-decay factors, barrier, compute.
+template <int N, int P>
+__global__ __launch_bounds__(kOutThreads) void k_chunk_out_dma(
+    const bf16* __restrict__ x, const float* __restrict__ dt, const bf16* __restrict__ Bm,
+    const bf16* __restrict__ C, const float* __restrict__ acum, const bf16* __restrict__ H_in,
+    bf16* __restrict__ y_ssd, int L, int H, int G) {
+  using MM = Mma<bf16>;
+  using Lds = ChunkOutDma<N, P>;
+  typedef bf16x8 vec_t;
+  constexpr int S = kMaxChunk;
+  constexpr int VE = 8, K = MM::K, KL = MM::KL;
+  constexpr int LDC = Lds::LDC;
+  constexpr int NKK = N / K, NPB = P / 16;
+  constexpr int NSLOT = kMaxBlk + 2;
+  constexpr int RV = S * (N / VE) / kOutThreads;     // B vectors per thread (phase 1)
+  constexpr int HCH = N / VE;                         // 16-byte chunks per H row
+  constexpr int RPH = 64 / HCH;                       // H rows per 1 KB copy
+  constexpr int XI = S * P * 2 / 1024 / kOutWaves;    // x copies per wave and head
+  constexpr int HI = P * N * 2 / 1024 / kOutWaves;    // H_in copies per wave and head
+  constexpr int NDMA = XI + HI + 1;                   // + acum (waves 0-3) or dt (4-7)
+  static_assert(Lds::fits && P / VE == 8 && XI >= 1 && HI >= 1 &&
+                    XI * kOutWaves * 1024 == S * P * 2 && HI * kOutWaves * 1024 == P * N * 2 &&
+                    kOutWaves == 8 && RV * kOutThreads == S * (N / VE),
+                "k_chunk_out_dma mapping");
+  static_assert(kOutWaves * 2 == kMaxBlk, "two token blocks per wave");
+  __shared__ __align__(16) unsigned char sh_raw[Lds::bytes];
+  float* sh_at = reinterpret_cast<float*>(sh_raw);  // A_s = acum_s·log2(e)
+  float* sh_v = sh_at + S;                           // v_j
+  float* sh_ld = sh_v + S;                           // log2 dt_j
+  unsigned char* sh_slots = sh_raw + Lds::FAC;
+  bf16* sh_b = reinterpret_cast<bf16*>(sh_slots);
+
+  const int k = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int M = L / S, hpg = H / G;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const long tok0 = (long)b * L + (long)k * S;
+  const int tb0 = w, tb1 = 2 * kOutWaves - 1 - w;
+  const int n0 = 2 * (tb0 / 2 + 1);  // slots of tb0 (pairs of key blocks)
+
+  // head hh lives in slot (hh + 2) % 3: head 0 in slot 2, clear of phase 1.
+  // The slot offset is opaque, so that addresses within the slot are formed
+  // from it with immediate offsets instead of precomputed per slot.
+  auto slot = [&](int hh) __attribute__((always_inline)) {
+    int off = ((hh + 2) % 3) * Lds::SLOT;
+    asm volatile("" : "+s"(off));
+    return sh_slots + off;
+  };
+  // the lane index, opaque, so that the copy addresses are formed where the
+  // copies are issued instead of being held in registers across the loop
+  auto lane_now = [&]() __attribute__((always_inline)) {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return l;
+  };
+  // x row r keeps its logical 16-byte chunk c at c ^ 2·(r % 4); H_in row r
+  // keeps chunk c at c ^ (r % HCH).  Copy I of x is rows 8I .. 8I+7, copy I
+  // of H_in rows RPH·I ..; lane l writes the l-th 16 bytes of the copy.
+  auto dma_head = [&](int hh) __attribute__((always_inline)) {
+    const int h = g * hpg + hh;
+    const long pair = (long)b * H + h;
+    unsigned char* sl = slot(hh);
+    bf16* sx = reinterpret_cast<bf16*>(sl);
+    bf16* sh = reinterpret_cast<bf16*>(sl + Lds::XB);
+    float* sa = reinterpret_cast<float*>(sl + Lds::XB + Lds::HB);
+    const int l = lane_now();
+#pragma unroll
+    for (int q = 0; q < XI; ++q) {
+      const int I = w * XI + q, r = 8 * I + l / 8, c = (l % 8) ^ (2 * (r % 4));
+      lds_copy16(x + ((tok0 + r) * H + h) * P + c * VE, lds_addr(sx + I * 512));
+    }
+    const bf16* hsrc = H_in + (pair * M + k) * (long)(P * N);
+#pragma unroll
+    for (int q = 0; q < HI; ++q) {
+      const int I = w * HI + q, r = RPH * I + l / HCH, c = (l % HCH) ^ (r % HCH);
+      lds_copy16(hsrc + r * N + c * VE, lds_addr(sh + I * 512));
+    }
+    if (w < 4)
+      lds_copy4(acum + (pair * M + k) * S + w * 64 + l, lds_addr(sa + w * 64));
+    else
+      lds_copy4(dt + (tok0 + (w - 4) * 64 + l) * H + h, lds_addr(sa + S + (w - 4) * 64));
+  };
+
+  dma_head(0);
+
+  // ---- phase 1: B rows -> LDS, C fragments from HBM; C·Bᵀ tiles ----
+  typename MM::frag cf0[NKK], cf1[NKK];
+  {
+    vec_t br[RV];
+#pragma unroll
+    for (int v = 0; v < RV; ++v) {
+      const int i = tid + v * kOutThreads, s = i / (N / VE), nv = i % (N / VE);
+      br[v] = load16(Bm + ((tok0 + s) * G + g) * N + nv * VE);
+    }
+    // B operand fragments: column t, k-slots n of C row t
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      cf0[kk] = load16(C + ((tok0 + tb0 * 16 + col) * G + g) * N + kk * K + grp * KL);
+      cf1[kk] = load16(C + ((tok0 + tb1 * 16 + col) * G + g) * N + kk * K + grp * KL);
+    }
+#pragma unroll
+    for (int v = 0; v < RV; ++v) {
+      const int i = tid + v * kOutThreads, s = i / (N / VE), nv = i % (N / VE);
+      *reinterpret_cast<vec_t*>(&sh_b[s * LDC + nv * VE]) = br[v];
+    }
+  }
+  lds_barrier();
+  floatx4 gs[NSLOT];
+#pragma unroll
+  for (int sl = 0; sl < NSLOT; ++sl) {
+    gs[sl] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const bool is0 = sl < n0;
+    const int jb = is0 ? sl : NSLOT - 1 - sl;
+    const bool live = is0 ? sl <= tb0 : jb <= tb1;
+    if (live) {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        gs[sl] = MM::mma(MM::load(&sh_b[(jb * 16 + col) * LDC + kk * K + grp * KL]),
+                         is0 ? cf0[kk] : cf1[kk], gs[sl]);
+      if (jb == (is0 ? tb0 : tb1)) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) gs[sl][i4] = 4 * grp + i4 <= col ? gs[sl][i4] : 0.f;
+      }
+    }
+  }
+  lds_barrier();  // B is dead: slots 0 and 1 are free
+  if (hpg > 1) dma_head(1);
+
+  // ---- phase 2: the heads of the group ----
+  for (int hh = 0; hh < hpg; ++hh) {
+    const int h = g * hpg + hh;
+    // this wave's copies of head hh are done (head hh+1's, if issued, are
+    // the only loads after them)
+    if (hh + 1 < hpg)
+      wait_fence<vmcnt_imm(NDMA)>();
+    else
+      wait_fence<vmcnt_imm(0)>();
+    lds_barrier();  // every wave: head hh landed, head hh-1 done (its slot is free)
+    if (hh + 2 < hpg) dma_head(hh + 2);
+    const unsigned char* sl = slot(hh);
+    const bf16* sx = reinterpret_cast<const bf16*>(sl);
+    const bf16* shh = reinterpret_cast<const bf16*>(sl + Lds::XB);
+    if (tid < S) {
+      const float* sa = reinterpret_cast<const float*>(sl + Lds::XB + Lds::HB);
+      const float a2 = sa[tid] * kLog2e;
+      // A at the end of this thread's 16-token block, from lane tid|15
+      const float e2 = __shfl(a2, lane | 15);
+      const float ld = __builtin_amdgcn_logf(sa[S + tid]);
+      sh_at[tid] = a2;
+      sh_ld[tid] = ld;
+      sh_v[tid] = exp2_fast(e2 - a2 + ld);
+    }
+    lds_barrier();
+
+    auto block_out = [&](int tb, const typename MM::frag (&cf)[NKK], auto pick)
+        __attribute__((always_inline)) {
+      const int t = tb * 16 + col;
+      const float at_t = sh_at[t];
+      floatx4 yin[NPB], yia[NPB];
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb) {
+        yin[pb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        yia[pb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        const int row = pb * 16 + col;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+          yin[pb] = MM::mma(
+              MM::load(&shh[row * N + (((kk * K + grp * KL) / VE) ^ (row % HCH)) * VE]), cf[kk],
+              yin[pb]);
+      }
+      // weights of tile jb: as in k_chunk_out_tr
+      auto weights = [&](int jb, floatx4 tile) __attribute__((always_inline)) {
+        floatx4 wv = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (jb < tb) {
+          const float u = exp2_fast(at_t - sh_at[jb * 16 + 15]);
+          const floatx4 vj = *reinterpret_cast<const floatx4*>(&sh_v[jb * 16 + 4 * grp]);
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) wv[i4] = (tile[i4] * u) * vj[i4];
+        } else if (jb == tb) {
+          const floatx4 aj = *reinterpret_cast<const floatx4*>(&sh_at[jb * 16 + 4 * grp]);
+          const floatx4 lj = *reinterpret_cast<const floatx4*>(&sh_ld[jb * 16 + 4 * grp]);
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4)
+            wv[i4] = 4 * grp + i4 <= col ? tile[i4] * exp2_fast((at_t - aj[i4]) + lj[i4]) : 0.f;
+        }
+        return wv;
+      };
+#pragma unroll
+      for (int jb0 = 0; jb0 < kMaxBlk; jb0 += 2) {
+        if (jb0 <= tb) {
+          floatx4 t0, t1;
+          pick(jb0, t0, t1);
+          const floatx4 w0 = weights(jb0, t0), w1 = weights(jb0 + 1, t1);
+          const bf16x8 bfr = {from_f32<bf16>(w0[0]), from_f32<bf16>(w0[1]),
+                              from_f32<bf16>(w0[2]), from_f32<bf16>(w0[3]),
+                              from_f32<bf16>(w1[0]), from_f32<bf16>(w1[1]),
+                              from_f32<bf16>(w1[2]), from_f32<bf16>(w1[3])};
+          // xᵀ operand by transpose reads of the swizzled x rows
+          const int r0 = jb0 * 16 + 4 * grp + (col >> 2);
+          const int sw = 2 * (r0 % 4);  // r0 + 16 has the same swizzle
+#pragma unroll
+          for (int pb = 0; pb < NPB; ++pb) {
+            const int c = ((2 * pb + ((col & 3) >> 1)) ^ sw) * VE + (col & 1) * 4;
+            const bf16x4 lo = lds_read_tr4(&sx[r0 * P + c]);
+            const bf16x4 hi = lds_read_tr4(&sx[(r0 + 16) * P + c]);
+            const bf16x8 afr = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            yia[pb] = MM::mma(afr, bfr, yia[pb]);
+          }
+        }
+      }
+      const float dec_t = exp2_fast(at_t);
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb)
+        store4(y_ssd + ((tok0 + t) * H + h) * P + pb * 16 + 4 * grp, yia[pb] + dec_t * yin[pb]);
+    };
+    block_out(tb0, cf0, [&](int jb0, floatx4& t0, floatx4& t1) __attribute__((always_inline)) {
+      t0 = gs[jb0];
+      t1 = gs[jb0 + 1];
+    });
+    block_out(tb1, cf1, [&](int jb0, floatx4& t0, floatx4& t1) __attribute__((always_inline)) {
+      t0 = gs[NSLOT - 1 - jb0];
+      t1 = gs[NSLOT - 2 - jb0];
+    });
+  }
+}
+
 }  // namespace
 
 template <typename T, int N, int P>
@@ -900,6 +1152,13 @@ hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt,
                      dim3(kThreads), 0, st, acum, dH_f32, h0, H_in, h_final, s.H, M, s.S, PN);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if constexpr (std::is_same<T, bf16>::value && ChunkOutDma<N, P>::fits) {
+    if (s.S == kMaxChunk) {
+      hipLaunchKernelGGL((k_chunk_out_dma<N, P>), dim3(M, s.G, s.B), dim3(kOutThreads), 0, st, x,
+                         dt, Bm, C, acum, H_in, y_ssd, s.L, s.H, s.G);
+      return hipGetLastError();
+    }
+  }
   if constexpr (std::is_same<T, bf16>::value)
     hipLaunchKernelGGL((k_chunk_out_tr<N, P>), dim3(M, s.G, s.B), dim3(kOutThreads), 0, st, x, dt,
                        Bm, C, acum, H_in, y_ssd, s.L, s.H, s.G, s.S);

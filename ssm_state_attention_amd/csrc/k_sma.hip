@@ -510,34 +510,6 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_fwd(
   }
 }
 
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wave are outstanding (lgkmcnt and expcnt left at their maxima).
-__host__ __device__ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
-
-// Waits that order direct global-to-LDS loads with this wave's own LDS
-// accesses; the empty asm keeps the compiler from moving LDS accesses
-// across the wait.
-template <int IMM>
-__device__ __forceinline__ void wait_fence() {
-  __builtin_amdgcn_s_waitcnt(IMM);
-  asm volatile("" ::: "memory");
-}
-constexpr int kLgkm0 = 0xC07F;  // lgkmcnt(0)
-
-// Workgroup barrier for LDS hand-offs only: this wave's LDS reads and writes
-// are complete, then s_barrier.  Unlike __syncthreads it carries no release
-// fence, which would also wait for every direct global-to-LDS load in
-// flight (and with it for the memory fetched one step ahead).
-// The scheduling barriers keep every instruction (MFMAs included) on its
-// side of the workgroup barrier, as the ping-pong schedule requires.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  wait_fence<kLgkm0>();
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // LDS of k_sma_grp: two padded memory buffers, and per wave one E region
 // and one y_ssd region of its tokens
 template <int N, int P, int NTB, int WAVES>

@@ -37,17 +37,19 @@ METRIC = "SMA+scan prefill tokens/s & MFMA% at L=8K; decode chunk-memory HBM GB/
 # only for the kernel source it was measured on (SHA-1 of that file).
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "ssm_state_attention_amd", "csrc")
 PROFILED_TRAFFIC = {
-    "k_sma_fwd": ("k_sma.hip", "f6f9434729a4e2da041c040785b1ddc12d04969a",
-                  (541.44 + 134.22) * 1e6),
-    # the four launches of one decode call (state, stream, combine, advance)
-    "dart_sma_decode": ("k_decode.hip", "1edf2954b0ac30901f6e19755b249602c54386d1",
-                        (135.75 + 134.74 + 4296.37 + 0.59 + 1.57 + 0.26) * 1e6),
-    "dart_sma_decode_fp8": ("k_decode.hip", "1edf2954b0ac30901f6e19755b249602c54386d1",
-                            (135.75 + 134.74 + 2150.97 + 0.59 + 1.57 + 0.26) * 1e6),
+    # dart_sma_fwd at the L=8K shape: the grouped kernel k_sma_grp
+    "k_sma_grp": ("k_sma.hip", "dc9720b752190e628d3a8d436d50ca99f1838525",
+                  (432.61 + 131.07) * 1e6),
+    # the two launches of one decode call with one split per head (state
+    # update, then the cache stream that also writes y and advances pos)
+    "dart_sma_decode": ("k_decode.hip", "96907b8151c470e13fe0da044f3303debd896370",
+                        (132.57 + 131.58 + 4196.18 + 0.26) * 1e6),
+    "dart_sma_decode_fp8": ("k_decode.hip", "96907b8151c470e13fe0da044f3303debd896370",
+                            (132.56 + 131.58 + 2101.07 + 0.26) * 1e6),
     # the launches of one SMA backward call (dy·o pass, gate sum, token- and
     # memory-major kernels)
     "dart_sma_bwd": ("k_sma_bwd.hip", "06886dd2840539233c3b3aa764f7abb9a7d1c8a6",
-                     (402.77 + 8.85 + 0.04 + 501.35 + 532.68 + 1789.51 + 135.51) * 1e6),
+                     (393.33 + 8.67 + 0.04 + 489.80 + 520.19 + 1754.37 + 132.41) * 1e6),
 }
 
 
@@ -170,13 +172,13 @@ def bench_prefill(args, torch, api, synth):
                       "sma_fwd": sma_ms},
         "flops": {"sma": flops_sma, "scan": flops_scan},
         "roofline": {
-            "kernel": "k_sma_fwd",
+            "kernel": "k_sma_grp",
             "bound": "mfma",
             "achieved": flops_sma / (sma_ms / 1e3) / 1e12,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": flops_sma / (sma_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
-            "traffic": profiled_traffic("k_sma_fwd"),
+            "traffic": profiled_traffic("k_sma_grp"),
         },
         "mfma_frac_whole_prefill": (flops_sma + flops_scan) / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
         "inputs": inp,
@@ -371,8 +373,9 @@ def bench_decode(args, torch, api, synth):
         "config": {"workload": "DART decode over the chunk-memory cache", "batch": B,
                    "heads": H, "dstate": N, "headdim": P, "chunk": S, "cached_chunks": k,
                    "io": "bf16"},
-        # the whole decode call (state update, cache stream, combine,
-        # position advance): its algorithmic bytes over its time
+        # the whole decode call (state update, then the cache stream that
+        # also forms y and advances the positions): its algorithmic bytes
+        # over its time
         "roofline": {"kernel": "dart_sma_decode", "bound": "hbm", "achieved": tot,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": tot / PEAK_HBM_GBS,
                      "traffic": profiled_traffic("dart_sma_decode")},

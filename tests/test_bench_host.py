@@ -34,12 +34,12 @@ def test_algorithmic_flops_of_the_layer_shape():
 
 
 def test_profiled_traffic_follows_the_source(tmp_path, monkeypatch):
-    src, sha1, nbytes = bench.PROFILED_TRAFFIC["k_sma_fwd"]
+    src, sha1, nbytes = bench.PROFILED_TRAFFIC["k_sma_grp"]
     path = os.path.join(bench.CSRC, src)
     with open(path, "rb") as f:
         live = hashlib.sha1(f.read()).hexdigest()
-    assert bench.profiled_traffic("k_sma_fwd") == (nbytes if live == sha1 else None)
+    assert bench.profiled_traffic("k_sma_grp") == (nbytes if live == sha1 else None)
     # a different source text: no figure
     (tmp_path / src).write_text("// changed\n")
     monkeypatch.setattr(bench, "CSRC", str(tmp_path))
-    assert bench.profiled_traffic("k_sma_fwd") is None
+    assert bench.profiled_traffic("k_sma_grp") is None

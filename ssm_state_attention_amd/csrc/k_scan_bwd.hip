@@ -194,6 +194,31 @@ __global__ __launch_bounds__(256) void k_ssd_bwd_pass(
   *reinterpret_cast<floatx4*>(dh0 + pair * PN + e4 * 4) = G;
 }
 
+// Workgroup order of the block kernels: workgroups go to the 8 XCDs
+// round-robin by linear index, and the nblk blocks of one (chunk, group,
+// batch) unit read each other's token rows.  Units are taken eight at a
+// time; block blk of unit 8q + r gets linear index 8·(nblk·q + blk) + r, so
+// a unit's blocks share an XCD (and its L2) and follow each other there.
+// Units past the last whole group of eight keep a plain order.
+__device__ __forceinline__ void unit_block(int nblk, int M, int G, int B, int& c, int& blk,
+                                           int& g, int& b) {
+  const int lin = blockIdx.x, units = M * G * B;
+  const int full = (units / 8) * 8 * nblk;
+  int unit;
+  if (lin < full) {
+    const int q = lin / (8 * nblk), r = lin % (8 * nblk);
+    blk = r / 8;
+    unit = 8 * q + r % 8;
+  } else {
+    const int r = lin - full;
+    unit = (units / 8) * 8 + r / nblk;
+    blk = r % nblk;
+  }
+  c = unit % M;
+  g = (unit / M) % G;
+  b = unit / (M * G);
+}
+
 // Key-block backward: one workgroup (4 waves) per (64-token block j of
 // chunk c, head group, batch); it walks the heads of the group (B, and so
 // dB, is shared by them) and wave w owns key columns 16w .. 16w+15.  Per
@@ -210,14 +235,15 @@ __global__ __launch_bounds__(256, 2) void k_ssd_bwd_j(
     const bf16* __restrict__ C, const bf16* __restrict__ dy, const float* __restrict__ acum,
     const bf16* __restrict__ dmem, float* __restrict__ dx, float* __restrict__ dB,
     float* __restrict__ ddtd, float* __restrict__ duj, float* __restrict__ gwj, int L, int H,
-    int G, int S) {
+    int G, int S, int nB) {
   constexpr int LDN = N + 16, LDP = P + 16, NKK = N / 32, NK2 = P / 32, NNB = N / 16,
                 NPB = P / 16;
   __shared__ __align__(16) bf16 sX[kT * LDP], sB[kT * LDN], sC[kT * LDN], sDy[kT * LDP],
       sD[P * LDN];
   __shared__ __align__(16) float su[kT];
-  const int nblk = S / kT, c = blockIdx.x / nblk, jb = blockIdx.x % nblk;
-  const int g = blockIdx.y, b = blockIdx.z, hpg = H / G, M = L / S;
+  const int nblk = S / kT, hpg = H / G, M = L / S;
+  int c, jb, g, b;
+  unit_block(nblk, M, G, nB, c, jb, g, b);
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int jw = 16 * w + col;  // key within the block
@@ -379,14 +405,15 @@ __global__ __launch_bounds__(256, 2) void k_ssd_bwd_t(
     const bf16* __restrict__ x, const float* __restrict__ dt, const bf16* __restrict__ Bm,
     const bf16* __restrict__ C, const bf16* __restrict__ dy, const float* __restrict__ acum,
     const bf16* __restrict__ H_in, const float* dC_in, float* dC, float* __restrict__ dut, int L,
-    int H, int G, int S) {
+    int H, int G, int S, int nB) {
   constexpr int LDN = N + 16, LDP = P + 16, NKK = N / 32, NK2 = P / 32, NNB = N / 16,
                 NPB = P / 16;
   __shared__ __align__(16) bf16 sC[kT * LDN], sDy[kT * LDP], sX[kT * LDP], sB[kT * LDN],
       sH[P * LDN];
   __shared__ __align__(16) float su[kT], sdt[kT];
-  const int nblk = S / kT, c = blockIdx.x / nblk, tb = blockIdx.x % nblk;
-  const int g = blockIdx.y, b = blockIdx.z, hpg = H / G, M = L / S;
+  const int nblk = S / kT, hpg = H / G, M = L / S;
+  int c, tb, g, b;
+  unit_block(nblk, M, G, nB, c, tb, g, b);
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tw = 16 * w + col;
@@ -624,11 +651,12 @@ hipError_t launch_scan_bwd(const PrefillShape& s, const T* x, const float* dt, c
     hipLaunchKernelGGL(k_ssd_bwd_pass, dim3(ntile, s.H, s.B), dim3(256), 0, st, acum, H_in,
                        ws.Yc, ddH, dh_final, ws.dmem, ws.dus, dh0, s.H, M, s.S, PN);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_ssd_bwd_j<N, P>), dim3(M * nblk, s.G, s.B), dim3(256), 0, st, x, dt, Bm,
-                       C, dy, acum, ws.dmem, dx, dB, ws.ddtd, ws.duj, ws.gwj, s.L, s.H, s.G, s.S);
+    const dim3 blocks(M * nblk * s.G * s.B);
+    hipLaunchKernelGGL((k_ssd_bwd_j<N, P>), blocks, dim3(256), 0, st, x, dt, Bm, C, dy, acum,
+                       ws.dmem, dx, dB, ws.ddtd, ws.duj, ws.gwj, s.L, s.H, s.G, s.S, s.B);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_ssd_bwd_t<N, P>), dim3(M * nblk, s.G, s.B), dim3(256), 0, st, x, dt, Bm,
-                       C, dy, acum, H_in, dC_sma, dC, ws.dut, s.L, s.H, s.G, s.S);
+    hipLaunchKernelGGL((k_ssd_bwd_t<N, P>), blocks, dim3(256), 0, st, x, dt, Bm, C, dy, acum,
+                       H_in, dC_sma, dC, ws.dut, s.L, s.H, s.G, s.S, s.B);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_ssd_bwd_fin, dim3(M, s.H, s.B), dim3(256), 0, st, dt, A, ws.duj, ws.dut,
                        ws.gwj, ws.dus, ws.ddtd, ddt, ws.dApart, s.L, s.H, s.S, ntile);

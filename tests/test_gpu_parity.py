@@ -97,6 +97,8 @@ def test_config1_bf16_prefill():
     (2, 288, 3, 3, 32, 32, 96, torch.float32),        # S not a power of two, M = 3
     (1, 384, 2, 2, 64, 64, 96, torch.bfloat16),       # S = 96 (three 1-wave tiles), M = 4
     (1, 320, 2, 1, 16, 16, 32, torch.float32),
+    (1, 768, 6, 2, 128, 64, 256, torch.bfloat16),     # 3 heads per group: the chunk output's
+    (1, 768, 10, 2, 64, 64, 256, torch.bfloat16),     # ring of 3 head slots wraps (5 heads, N=64)
 ])
 def test_prefill_shapes(B, L, H, G, N, P, S, io):
     run_prefill_case(B, L, H, G, N, P, S, io, seed=B * 100 + L + H)

@@ -304,6 +304,37 @@ __device__ __forceinline__ void stream_tail(const float (&acc)[NPASS], float mx,
   }
 }
 
+// The memory loop of a streaming wave: memories c0, c0 + step, ... < c_end
+// (c0 uniform over the wave).  PIPE: the loads of the next memory are issued
+// into a second register set before the current one is consumed, so every
+// wave keeps a memory in flight while it computes (used where the two sets
+// leave enough registers: 64 per set for the 16-bit cache, 32 for fp8, whose
+// decoding needs more temporaries).
+template <bool PIPE, typename Raw, typename Load, typename Consume>
+__device__ __forceinline__ void stream_memories(Load load, Consume consume, int c0, int c_end,
+                                                int step) {
+  Raw ra, rb;
+  if constexpr (PIPE) {
+    int c = c0;
+    if (c < c_end) load(ra, c);
+    while (c < c_end) {
+      if (c + step < c_end) load(rb, c + step);
+      consume(ra);
+      c += step;
+      if (c >= c_end) break;
+      if (c + step < c_end) load(ra, c + step);
+      consume(rb);
+      c += step;
+    }
+  } else {
+    (void)rb;
+    for (int c = c0; c < c_end; c += step) {
+      load(ra, c);
+      consume(ra);
+    }
+  }
+}
+
 // Decode, step 2: one workgroup (4 waves) per (split, head, batch) streams
 // the cached memories of its split once from HBM.  Each wave takes whole
 // memories c = first + wave, first + wave + 4, ... (non-temporal 16-byte
@@ -356,11 +387,13 @@ __global__ __launch_bounds__(256) void k_sma_decode(const DecodeArgs<T> a) {
   }
   float mx = -INFINITY, ls = 0.f;
   const T* base = a.cache + pair * (long)a.max_chunks * (P * N);
-  for (int c = c_begin + w; c < c_end; c += NW) {
+  // the wave's memories c_begin + w, + NW, ... (stream_memories)
+  auto load = [&](vec_t (&raw)[NPASS], int c) __attribute__((always_inline)) {
     const T* src = base + (long)c * (P * N);
-    vec_t raw[NPASS];
 #pragma unroll
     for (int it = 0; it < NPASS; ++it) raw[it] = load16_nt(src + ((it * RP + pr) * NV + nv) * VE);
+  };
+  auto consume = [&](const vec_t (&raw)[NPASS]) __attribute__((always_inline)) {
     float s = 0.f, zc[NPASS];
 #pragma unroll
     for (int it = 0; it < NPASS; ++it) {
@@ -396,7 +429,9 @@ __global__ __launch_bounds__(256) void k_sma_decode(const DecodeArgs<T> a) {
     ls += pw;
 #pragma unroll
     for (int it = 0; it < NPASS; ++it) acc[it] += pw * zc[it];
-  }
+  };
+  stream_memories<NPASS * sizeof(vec_t) <= 256, vec_t[NPASS]>(load, consume, c_begin + w, c_end,
+                                                              NW);
 #pragma unroll
   for (int it = 0; it < NPASS; ++it)
 #pragma unroll
@@ -482,21 +517,27 @@ __global__ __launch_bounds__(256) void k_sma_decode_f8(const DecodeArgs<T> a) {
   float mx = -INFINITY, ls = 0.f;
   const uint8_t* base = a.cache8 + pair * (long)a.max_chunks * (P * N);
   const float* sbase = a.cscale + pair * (long)a.max_chunks;
-  for (int c = c_begin + w; c < c_end; c += NW) {
-    const uint8_t* src = base + (long)c * (P * N);
+  // codes and scale of memory c, consumed after the next memory's are issued
+  struct Mem {
     load_t raw[NPASS];
+    float sc;
+  };
+  auto load = [&](Mem& m, int c) __attribute__((always_inline)) {
+    const uint8_t* src = base + (long)c * (P * N);
 #pragma unroll
     for (int it = 0; it < NPASS; ++it)
-      raw[it] = __builtin_nontemporal_load(
+      m.raw[it] = __builtin_nontemporal_load(
           reinterpret_cast<const load_t*>(src + (it * RP + pr) * N + nv * LB));
-    const float sc = sbase[c];
+    m.sc = sbase[c];
+  };
+  auto consume = [&](const Mem& m) __attribute__((always_inline)) {
     float s = 0.f, zc[NPASS];
 #pragma unroll
     for (int it = 0; it < NPASS; ++it) {
       float zq = 0.f, z2 = 0.f;
 #pragma unroll
       for (int j = 0; j < W; ++j) {
-        const unsigned wd = word<W>(raw[it], j);
+        const unsigned wd = word<W>(m.raw[it], j);
         if constexpr (kDot2) {
           const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd, 1.0f, false);
           const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd, 1.0f, true);
@@ -516,7 +557,7 @@ __global__ __launch_bounds__(256) void k_sma_decode_f8(const DecodeArgs<T> a) {
       zc[it] = z2;
       s += ev[it] * zq;
     }
-    s = wave_sum_dpp(s) * (sc * a.scale_log2);
+    s = wave_sum_dpp(s) * (m.sc * a.scale_log2);
     if (s > mx + kLazyLog2) {
       const float al = exp2_fast(mx - s);  // 0 for the first memory
       ls *= al;
@@ -526,10 +567,11 @@ __global__ __launch_bounds__(256) void k_sma_decode_f8(const DecodeArgs<T> a) {
     }
     const float pw = exp2_fast(s - mx);
     ls += pw;
-    const float pv = pw * sc;
+    const float pv = pw * m.sc;
 #pragma unroll
     for (int it = 0; it < NPASS; ++it) acc[it] += pv * zc[it];
-  }
+  };
+  stream_memories<NPASS * sizeof(load_t) <= 128, Mem>(load, consume, c_begin + w, c_end, NW);
 #pragma unroll
   for (int it = 0; it < NPASS; ++it)
 #pragma unroll

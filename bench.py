@@ -39,17 +39,17 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "ssm_state_atten
 PROFILED_TRAFFIC = {
     # dart_sma_fwd at the L=8K shape: the grouped kernel k_sma_grp
     "k_sma_grp": ("k_sma.hip", "dc9720b752190e628d3a8d436d50ca99f1838525",
-                  (432.61 + 131.07) * 1e6),
+                  (432.48 + 131.07) * 1e6),
     # the two launches of one decode call with one split per head (state
     # update, then the cache stream that also writes y and advances pos)
-    "dart_sma_decode": ("k_decode.hip", "96907b8151c470e13fe0da044f3303debd896370",
-                        (132.57 + 131.58 + 4196.18 + 0.26) * 1e6),
-    "dart_sma_decode_fp8": ("k_decode.hip", "96907b8151c470e13fe0da044f3303debd896370",
-                            (132.56 + 131.58 + 2101.07 + 0.26) * 1e6),
+    "dart_sma_decode": ("k_decode.hip", "5161f28fb5c89b1dff36f1c14942a25bb2ad9145",
+                        (132.57 + 131.58 + 4196.22 + 0.26) * 1e6),
+    "dart_sma_decode_fp8": ("k_decode.hip", "5161f28fb5c89b1dff36f1c14942a25bb2ad9145",
+                            (132.58 + 131.58 + 2101.10 + 0.26) * 1e6),
     # the launches of one SMA backward call (dy·o pass, gate sum, token- and
     # memory-major kernels)
     "dart_sma_bwd": ("k_sma_bwd.hip", "06886dd2840539233c3b3aa764f7abb9a7d1c8a6",
-                     (393.33 + 8.67 + 0.04 + 489.80 + 520.19 + 1754.37 + 132.41) * 1e6),
+                     (393.33 + 8.66 + 0.04 + 490.04 + 520.19 + 1749.04 + 132.52) * 1e6),
 }
 
 

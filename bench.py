@@ -112,22 +112,24 @@ def bench_prefill(args, torch, api, synth):
     out = {
         "acum": torch.empty(B, H, M, S, **f32),
         "dH": torch.empty(B, H, M, P, N, dtype=torch.bfloat16, device="cuda:0"),
-        "dH_f32": torch.empty(B, H, M, P, N, **f32),
         "H_in": torch.empty(B, H, M, P, N, dtype=torch.bfloat16, device="cuda:0"),
         "h_final": torch.empty(B, H, P, N, **f32),
         "y_ssd": torch.empty(B, L, H, P, dtype=torch.bfloat16, device="cuda:0"),
         "y": torch.empty(B, L, H, P, dtype=torch.bfloat16, device="cuda:0"),
     }
+    ws = torch.empty(api.dart_chunk_scan_workspace(api.prefill_dims(d["x"], d["Bm"], S)),
+                     dtype=torch.uint8, device="cuda:0")
 
+    # the prefill path of api.prefill: one-pass chunk scan, chunk output, SMA
     def step(ev=None):
         if ev:
             ev[0].record()
-        api.dart_chunk_state(d["x"], d["dt"], d["A"], d["Bm"], out["acum"], out["dH"],
-                             out["dH_f32"], S)
+        api.dart_chunk_scan(d["x"], d["dt"], d["A"], d["Bm"], None, out["acum"], out["dH"], None,
+                            out["H_in"], out["h_final"], ws, S)
         if ev:
             ev[1].record()
-        api.dart_state_pass(d["x"], d["dt"], d["Bm"], d["C"], out["acum"], out["dH_f32"], None,
-                            out["H_in"], out["h_final"], out["y_ssd"], S)
+        api.dart_chunk_out(d["x"], d["dt"], d["Bm"], d["C"], out["acum"], out["H_in"],
+                           out["y_ssd"], S)
         if ev:
             ev[2].record()
         api.dart_sma_fwd(d["Q"], d["E"], d["C"], out["dH"], out["y_ssd"], c["gate"], out["y"], S)
@@ -168,7 +170,7 @@ def bench_prefill(args, torch, api, synth):
         "sma_ms_median": per_sma[len(per_sma) // 2],
         "sma_ms_min": per_sma[0],
         "tokens_per_s": B * L / (ms / 1e3),
-        "kernel_ms": {"chunk_state": split[0], "state_pass+chunk_out": split[1],
+        "kernel_ms": {"chunk_scan": split[0], "chunk_out": split[1],
                       "sma_fwd": sma_ms},
         "flops": {"sma": flops_sma, "scan": flops_scan},
         "roofline": {
@@ -199,16 +201,17 @@ def bench_prefill_extra(args, torch, api, synth, c, name, steps):
     f32 = dict(dtype=torch.float32, device="cuda:0")
     bf = dict(dtype=torch.bfloat16, device="cuda:0")
     out = {"acum": torch.empty(B, H, M, S, **f32), "dH": torch.empty(B, H, M, P, N, **bf),
-           "dH_f32": torch.empty(B, H, M, P, N, **f32), "H_in": torch.empty(B, H, M, P, N, **bf),
-           "h_final": torch.empty(B, H, P, N, **f32), "y_ssd": torch.empty(B, L, H, P, **bf),
-           "y": torch.empty(B, L, H, P, **bf)}
+           "H_in": torch.empty(B, H, M, P, N, **bf), "h_final": torch.empty(B, H, P, N, **f32),
+           "y_ssd": torch.empty(B, L, H, P, **bf), "y": torch.empty(B, L, H, P, **bf)}
+    ws = torch.empty(api.dart_chunk_scan_workspace(api.prefill_dims(d["x"], d["Bm"], S)),
+                     dtype=torch.uint8, device="cuda:0")
 
     def step(ev):
         ev[0].record()
-        api.dart_chunk_state(d["x"], d["dt"], d["A"], d["Bm"], out["acum"], out["dH"],
-                             out["dH_f32"], S)
-        api.dart_state_pass(d["x"], d["dt"], d["Bm"], d["C"], out["acum"], out["dH_f32"], None,
-                            out["H_in"], out["h_final"], out["y_ssd"], S)
+        api.dart_chunk_scan(d["x"], d["dt"], d["A"], d["Bm"], None, out["acum"], out["dH"], None,
+                            out["H_in"], out["h_final"], ws, S)
+        api.dart_chunk_out(d["x"], d["dt"], d["Bm"], d["C"], out["acum"], out["H_in"],
+                           out["y_ssd"], S)
         ev[1].record()
         api.dart_sma_fwd(d["Q"], d["E"], d["C"], out["dH"], out["y_ssd"], c["gate"], out["y"], S)
         ev[2].record()

@@ -11,7 +11,9 @@
  * comment 3 (paper §3 Eq. 8) and minor comment 1 (paper §4 Eq. 14).
  *
  * Prefill is three calls on one stream, in this order:
- *   dart_chunk_state -> dart_state_pass -> dart_sma_fwd
+ *   dart_chunk_scan -> dart_chunk_out -> dart_sma_fwd
+ * (or, with the f32 memories kept as an output and the state recurrence as a
+ * pass of its own: dart_chunk_state -> dart_state_pass -> dart_sma_fwd).
  * Decode is one call per generated token: dart_sma_decode.
  * Extensions of the same path:
  *   training: dart_sma_fwd_train in place of dart_sma_fwd, then the backward
@@ -28,7 +30,8 @@
  * - Every tensor argument is a pointer to DEVICE memory owned by the caller,
  *   dense row-major in the layout given, 16-byte aligned.  The library never
  *   allocates, frees or keeps memory, and holds no global state, apart from
- *   the static device scratch of dart_sma_decode_noalloc.
+ *   the static device scratch of dart_sma_decode_noalloc and a call counter
+ *   that tags dart_chunk_scan's workspace flags.
  * - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *   enqueue work and return; results are ready once the stream reaches them.
  * - Dimensions and pointers are validated on the host before any HIP call; a
@@ -130,6 +133,64 @@ dart_status dart_state_pass(const dart_dims* dims, const void* x, const float* d
                             const void* Bm, const void* C, const float* acum,
                             const float* dH_f32, const float* h0, void* H_in,
                             float* h_final, void* y_ssd, void* stream);
+
+/*
+ * Chunk memories and the inter-chunk state recurrence in one pass: the
+ * outputs of dart_chunk_state and the state half of dart_state_pass
+ * without the f32 memories round trip through memory.
+ * Source: as dart_chunk_state and dart_state_pass (Pith review of DART, axiom
+ * ledger: the chunked scan's chunk contributions and inter-chunk state
+ * passing; "What carries the argument": dH[c] is chunk c's contribution to
+ * the chunk-boundary state).
+ *
+ *   acum, dH            as dart_chunk_state
+ *   H[0] = h0 (zero when h0 == NULL)
+ *   H[c+1] = exp(acum[c, S-1])·H[c] + dH_f32[c]     (f32, in chunk order)
+ *   H_in[c] = io(H[c]) for c < M;  h_final = H[M]
+ * The results are bit-identical to dart_chunk_state followed by
+ * dart_state_pass.
+ *
+ * in:  x [B,L,H,P] io; dt [B,L,H] f32; A [H] f32; Bm [B,L,G,N] io;
+ *      h0 [B,H,P,N] f32 or NULL
+ * out: acum [B,H,M,S] f32; dH [B,H,M,P,N] io; dH_f32 [B,H,M,P,N] f32 when
+ *      not NULL (the unrounded memories; NULL skips them); H_in [B,H,M,P,N]
+ *      io; h_final [B,H,P,N] f32
+ * workspace: device memory of at least dart_chunk_scan_workspace(dims) bytes
+ *      (workspace_bytes gives its size; smaller returns DART_ERR_WORKSPACE).
+ *      Any initial contents.  For 16-bit io it holds one f32 state slot pair
+ *      and one flag per (batch, head), through which the workgroup of each
+ *      group of chunks hands its outgoing state to the next; each call tags
+ *      its flags with a per-call number, so a flag left by an earlier call
+ *      never passes for this one.  Every wait is bounded: a wait that gives
+ *      up (which a correct launch never does) adds one to the workspace's
+ *      first int32 and leaves that call's outputs undefined; callers that
+ *      check it zero that int32 beforehand.  Calls that share a workspace
+ *      must not overlap (the same stream, or ordered streams).  For f32 io
+ *      the workspace holds the f32 memories of a two-pass recurrence.
+ */
+size_t dart_chunk_scan_workspace(const dart_dims* dims);
+dart_status dart_chunk_scan(const dart_dims* dims, const void* x, const float* dt,
+                            const float* A, const void* Bm, const float* h0, float* acum,
+                            void* dH, float* dH_f32, void* H_in, float* h_final,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The native Mamba-2 chunk output alone (the y_ssd half of dart_state_pass),
+ * from H_in as dart_chunk_scan or dart_state_pass wrote it.
+ * Source: Pith review of DART, axiom ledger (SSD as structured causal
+ * attention, paper Eq. 4; intra- and inter-chunk terms of the chunked scan)
+ * and "Core claim" (Mamba-2 reads values from its state as C_t·H_t).
+ *
+ *   y_ssd[t] = sum_{j in k, j<=t} (C_t·B_j)·exp(acum_t - acum_j)·dt_j·x_j
+ *            + exp(acum_t)·C_tᵀ·H_in[k]
+ *
+ * in:  x, dt, Bm as dart_chunk_state; C [B,L,G,N] io; acum [B,H,M,S] f32;
+ *      H_in [B,H,M,P,N] io
+ * out: y_ssd [B,L,H,P] io (bit-identical to dart_state_pass's)
+ */
+dart_status dart_chunk_out(const dart_dims* dims, const void* x, const float* dt,
+                           const void* Bm, const void* C, const float* acum, const void* H_in,
+                           void* y_ssd, void* stream);
 
 /*
  * State-memory attention over completed chunks plus the gated add.

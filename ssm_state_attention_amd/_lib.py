@@ -44,6 +44,10 @@ _SIG = {
     "dart_chunk_state": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "dart_state_pass": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                         _VP, _VP],
+    "dart_chunk_scan_workspace": [ctypes.POINTER(DartDims)],
+    "dart_chunk_scan": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                        _VP, _VP, ctypes.c_size_t, _VP],
+    "dart_chunk_out": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "dart_sma_fwd": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _F, _VP, _VP],
     "dart_sma_fwd_decayed": [ctypes.POINTER(DartDims), _VP, _VP, _VP, _VP, _VP, _VP, _F, _VP,
                              _VP],
@@ -72,7 +76,7 @@ _SIG = {
     "dart_validate_decode_dims": [ctypes.POINTER(DartDecodeDims)],
     "dart_status_str": [ctypes.c_int],
 }
-_RES = {"dart_sma_decode_workspace": ctypes.c_size_t, "dart_sma_bwd_workspace": ctypes.c_size_t,
+_RES = {"dart_sma_decode_workspace": ctypes.c_size_t, "dart_chunk_scan_workspace": ctypes.c_size_t, "dart_sma_bwd_workspace": ctypes.c_size_t,
         "dart_scan_bwd_workspace": ctypes.c_size_t,
         "dart_status_str": ctypes.c_char_p}
 

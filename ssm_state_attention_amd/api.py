@@ -84,6 +84,56 @@ def dart_state_pass(x, dt, Bm, C, acum, dH_f32, h0, H_in, h_final, y_ssd, chunk)
     check(lib().dart_state_pass(d, *args, _stream()), "dart_state_pass")
 
 
+def dart_chunk_scan_workspace(dims):
+    """Bytes of device workspace dart_chunk_scan needs for these dims."""
+    return int(lib().dart_chunk_scan_workspace(dims))
+
+
+def dart_chunk_scan(x, dt, A, Bm, h0, acum, dH, dH_f32, H_in, h_final, workspace, chunk):
+    """Chunk memories and the state recurrence in one pass: acum, dH (io),
+    dH_f32 (f32, or None to skip), H_in (io) and h_final (f32), the outputs
+    of dart_chunk_state and of dart_state_pass's recurrence; h0 [B,H,P,N]
+    f32 or None (zero); workspace a uint8 device tensor of at least
+    dart_chunk_scan_workspace bytes."""
+    d = prefill_dims(x, Bm, chunk)
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    M, io, dev = L // chunk, x.dtype, x.device
+    args = [_ptr(x, "x", io, (B, L, H, P), dev), _ptr(dt, "dt", torch.float32, (B, L, H), dev),
+            _ptr(A, "A", torch.float32, (H,), dev), _ptr(Bm, "Bm", io, (B, L, G, N), dev),
+            _ptr(h0, "h0", torch.float32, (B, H, P, N), dev),
+            _ptr(acum, "acum", torch.float32, (B, H, M, chunk), dev),
+            _ptr(dH, "dH", io, (B, H, M, P, N), dev),
+            _ptr(dH_f32, "dH_f32", torch.float32, (B, H, M, P, N), dev),
+            _ptr(H_in, "H_in", io, (B, H, M, P, N), dev),
+            _ptr(h_final, "h_final", torch.float32, (B, H, P, N), dev)]
+    wsp = _ptr(workspace, "workspace", torch.uint8, None, dev)
+    check(lib().dart_chunk_scan(d, *args, wsp, workspace.numel(), _stream()), "dart_chunk_scan")
+
+
+def dart_chunk_out(x, dt, Bm, C, acum, H_in, y_ssd, chunk):
+    """Native chunk output y_ssd [B,L,H,P] io from H_in [B,H,M,P,N] io."""
+    d = prefill_dims(x, Bm, chunk)
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    M, io, dev = L // chunk, x.dtype, x.device
+    args = [_ptr(x, "x", io, (B, L, H, P), dev), _ptr(dt, "dt", torch.float32, (B, L, H), dev),
+            _ptr(Bm, "Bm", io, (B, L, G, N), dev), _ptr(C, "C", io, (B, L, G, N), dev),
+            _ptr(acum, "acum", torch.float32, (B, H, M, chunk), dev),
+            _ptr(H_in, "H_in", io, (B, H, M, P, N), dev),
+            _ptr(y_ssd, "y_ssd", io, (B, L, H, P), dev)]
+    check(lib().dart_chunk_out(d, *args, _stream()), "dart_chunk_out")
+
+
+def _scan(out, x, dt, A, Bm, C, chunk, h0, keep_f32):
+    """dart_chunk_scan then dart_chunk_out into the tensors of ``out``."""
+    ws = torch.empty(dart_chunk_scan_workspace(prefill_dims(x, Bm, chunk)), dtype=torch.uint8,
+                     device=x.device)
+    dart_chunk_scan(x, dt, A, Bm, h0, out["acum"], out["dH"], out["dH_f32"] if keep_f32 else None,
+                    out["H_in"], out["h_final"], ws, chunk)
+    dart_chunk_out(x, dt, Bm, C, out["acum"], out["H_in"], out["y_ssd"], chunk)
+
+
 def dart_sma_fwd(Q, E, C, dH, y_ssd, gate, y, chunk):
     """State-memory attention + gated add: y [B,L,H,P] io."""
     B, L, H, P = E.shape
@@ -344,11 +394,11 @@ def dart_cache_fp8_store(dH_f32, first, cache8, scale, ngroups, chunk, io):
 
 
 # ----------------------------------------------------------------- helpers
-def prefill(x, dt, A, Bm, C, Q, E, gate, chunk, h0=None, decayed=False):
+def prefill(x, dt, A, Bm, C, Q, E, gate, chunk, h0=None, decayed=False, keep_f32=False):
     """Whole prefill path; returns a dict of device tensors: y, y_ssd, dH
-    ([B,H,M,P,N] io), dH_f32, H_in ([B,H,M,P,N] io, the state entering each
-    chunk), h_final ([B,H,P,N] f32, the state after the last chunk) and
-    acum."""
+    ([B,H,M,P,N] io), H_in ([B,H,M,P,N] io, the state entering each chunk),
+    h_final ([B,H,P,N] f32, the state after the last chunk), acum and, with
+    keep_f32, dH_f32 (the unrounded memories)."""
     B, L, H, P = x.shape
     N = Bm.shape[3]
     M, dev = L // chunk, x.device
@@ -356,15 +406,14 @@ def prefill(x, dt, A, Bm, C, Q, E, gate, chunk, h0=None, decayed=False):
     out = {
         "acum": torch.empty(B, H, M, chunk, **f32),
         "dH": torch.empty(B, H, M, P, N, dtype=x.dtype, device=dev),
-        "dH_f32": torch.empty(B, H, M, P, N, **f32),
         "H_in": torch.empty(B, H, M, P, N, dtype=x.dtype, device=dev),
         "h_final": torch.empty(B, H, P, N, **f32),
         "y_ssd": torch.empty(B, L, H, P, dtype=x.dtype, device=x.device),
         "y": torch.empty(B, L, H, P, dtype=x.dtype, device=dev),
     }
-    dart_chunk_state(x, dt, A, Bm, out["acum"], out["dH"], out["dH_f32"], chunk)
-    dart_state_pass(x, dt, Bm, C, out["acum"], out["dH_f32"], h0, out["H_in"], out["h_final"],
-                    out["y_ssd"], chunk)
+    if keep_f32:
+        out["dH_f32"] = torch.empty(B, H, M, P, N, **f32)
+    _scan(out, x, dt, A, Bm, C, chunk, h0, keep_f32)
     if decayed:
         dart_sma_fwd_decayed(Q, E, C, out["dH"], out["acum"], out["y_ssd"], gate, out["y"], chunk)
     else:
@@ -382,7 +431,6 @@ def prefill_train(x, dt, A, Bm, C, Q, E, gate, chunk, h0=None):
     out = {
         "acum": torch.empty(B, H, M, chunk, **f32),
         "dH": torch.empty(B, H, M, P, N, dtype=x.dtype, device=dev),
-        "dH_f32": torch.empty(B, H, M, P, N, **f32),
         "H_in": torch.empty(B, H, M, P, N, dtype=x.dtype, device=dev),
         "h_final": torch.empty(B, H, P, N, **f32),
         "y_ssd": torch.empty(B, L, H, P, dtype=x.dtype, device=dev),
@@ -390,9 +438,7 @@ def prefill_train(x, dt, A, Bm, C, Q, E, gate, chunk, h0=None):
         "o": torch.empty(B, L, H, P, **f32),
         "lse": torch.empty(B, H, L, **f32),
     }
-    dart_chunk_state(x, dt, A, Bm, out["acum"], out["dH"], out["dH_f32"], chunk)
-    dart_state_pass(x, dt, Bm, C, out["acum"], out["dH_f32"], h0, out["H_in"], out["h_final"],
-                    out["y_ssd"], chunk)
+    _scan(out, x, dt, A, Bm, C, chunk, h0, False)
     dart_sma_fwd_train(Q, E, C, out["dH"], out["y_ssd"], gate, out["y"], out["o"], out["lse"],
                        chunk)
     return out

@@ -2,6 +2,9 @@
 // element type and (N, P) to the compiled kernel set.
 #include <stdint.h>
 
+#include <atomic>
+#include <chrono>
+
 #include "dart.h"
 #include "dart_launch.hpp"
 #include "dart_shapes.hpp"
@@ -72,6 +75,55 @@ struct StatePassFn {
                                             static_cast<T*>(y_ssd), st);
   }
 };
+
+struct ChunkScanFn {
+  dart::PrefillShape sh;
+  const void *x, *Bm;
+  const float *dt, *A, *h0;
+  float* acum;
+  void* dH;
+  float* dHf;
+  void* H_in;
+  float* h_final;
+  void* ws;
+  unsigned tag;
+  hipStream_t st;
+  template <typename T, int N, int P>
+  hipError_t run() {
+    return dart::launch_chunk_scan<T, N, P>(sh, static_cast<const T*>(x), dt, A,
+                                            static_cast<const T*>(Bm), h0, acum,
+                                            static_cast<T*>(dH), dHf, static_cast<T*>(H_in),
+                                            h_final, ws, tag, st);
+  }
+};
+
+struct ChunkOutFn {
+  dart::PrefillShape sh;
+  const void *x, *Bm, *C;
+  const float *dt, *acum;
+  const void* H_in;
+  void* y_ssd;
+  hipStream_t st;
+  template <typename T, int N, int P>
+  hipError_t run() {
+    return dart::launch_chunk_out<T, N, P>(sh, static_cast<const T*>(x), dt,
+                                           static_cast<const T*>(Bm), static_cast<const T*>(C),
+                                           acum, static_cast<const T*>(H_in),
+                                           static_cast<T*>(y_ssd), st);
+  }
+};
+
+// Tags of dart_chunk_scan calls: distinct per call within the process, and
+// started from the clock so that a flag value left in reused device memory
+// by an earlier process is unlikely to match.
+unsigned next_scan_tag() {
+  static std::atomic<unsigned> counter{static_cast<unsigned>(
+      std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761ull)};
+  unsigned t;
+  do t = counter.fetch_add(1, std::memory_order_relaxed);
+  while (t == 0);
+  return t;
+}
 
 struct SmaFwdFn {
   dart::PrefillShape sh;
@@ -202,6 +254,40 @@ extern "C" dart_status dart_state_pass(const dart_dims* dims, const void* x, con
   if (h0 && !aligned16(h0)) return DART_ERR_ALIGN;
   StatePassFn fn{prefill_shape(dims), x, Bm, C, dt, acum, dH_f32, h0, H_in, h_final, y_ssd,
        static_cast<hipStream_t>(stream)};
+  return dispatch(dims->io, dims->dstate, dims->headdim, fn);
+}
+
+extern "C" size_t dart_chunk_scan_workspace(const dart_dims* dims) {
+  if (dart_validate_dims(dims) != DART_OK) return 0;
+  return (dart::chunk_scan_workspace_bytes(dims->io, dims->batch, dims->seqlen, dims->nheads,
+                                           dims->dstate, dims->headdim, dims->chunk) +
+          255) / 256 * 256;
+}
+
+extern "C" dart_status dart_chunk_scan(const dart_dims* dims, const void* x, const float* dt,
+                                       const float* A, const void* Bm, const float* h0,
+                                       float* acum, void* dH, float* dH_f32, void* H_in,
+                                       float* h_final, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  dart_status s = dart_validate_dims(dims);
+  if (s != DART_OK) return s;
+  if ((s = check_ptrs(x, dt, A, Bm, acum, dH, H_in, h_final)) != DART_OK) return s;
+  if ((h0 && !aligned16(h0)) || (dH_f32 && !aligned16(dH_f32))) return DART_ERR_ALIGN;
+  if (!workspace || workspace_bytes < dart_chunk_scan_workspace(dims)) return DART_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DART_ERR_ALIGN;
+  ChunkScanFn fn{prefill_shape(dims), x, Bm, dt, A, h0, acum, dH, dH_f32, H_in, h_final,
+                 workspace, next_scan_tag(), static_cast<hipStream_t>(stream)};
+  return dispatch(dims->io, dims->dstate, dims->headdim, fn);
+}
+
+extern "C" dart_status dart_chunk_out(const dart_dims* dims, const void* x, const float* dt,
+                                      const void* Bm, const void* C, const float* acum,
+                                      const void* H_in, void* y_ssd, void* stream) {
+  dart_status s = dart_validate_dims(dims);
+  if (s != DART_OK) return s;
+  if ((s = check_ptrs(x, dt, Bm, C, acum, H_in, y_ssd)) != DART_OK) return s;
+  ChunkOutFn fn{prefill_shape(dims), x, Bm, C, dt, acum, H_in, y_ssd,
+                static_cast<hipStream_t>(stream)};
   return dispatch(dims->io, dims->dstate, dims->headdim, fn);
 }
 

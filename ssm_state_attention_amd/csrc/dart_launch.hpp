@@ -25,6 +25,25 @@ hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt,
                              const float* h0, T* H_in, float* h_final, T* y_ssd,
                              hipStream_t st);
 
+// Native chunk output y_ssd from H_in (the second half of launch_state_pass).
+template <typename T, int N, int P>
+hipError_t launch_chunk_out(const PrefillShape& s, const T* x, const float* dt, const T* Bm,
+                            const T* C, const float* acum, const T* H_in, T* y_ssd,
+                            hipStream_t st);
+
+// Chunk memories and the state recurrence in one pass (16-bit io: one
+// kernel handing the f32 state from chunk to chunk through the workspace;
+// f32 io: launch_chunk_state and the recurrence kernel, the f32 memories in
+// dH_f32 or, when that is null, in the workspace).  tag must differ from
+// the tags of earlier calls that used the same workspace.
+template <typename T, int N, int P>
+hipError_t launch_chunk_scan(const PrefillShape& s, const T* x, const float* dt, const float* A,
+                             const T* Bm, const float* h0, float* acum, T* dH, float* dH_f32,
+                             T* H_in, float* h_final, void* workspace, unsigned tag,
+                             hipStream_t st);
+size_t chunk_scan_workspace_bytes(int io, int64_t B, int64_t L, int64_t H, int64_t N, int64_t P,
+                                  int64_t S);
+
 // acum == nullptr: the SMA of the pages; otherwise the decay-included variant.
 // k0 > 0: the tokens continue sequences whose first k0 memories are in prior
 // (pstride memories per (batch, head)), or, with prior8 != nullptr, in the fp8

@@ -136,23 +136,51 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
 
 constexpr int kStKB = 64;  // tokens per K-block of k_chunk_state_tr
 
-// Chunk state memories, 16-bit io: the arithmetic of k_chunk_state with
-// every HBM access in whole token rows.  B and w∘x K-blocks sit row-major in
-// LDS ([s][n], [s][p]) and both MFMA operands are read with LDS transpose
-// reads, so the token axis becomes each lane's k-run without a transposing
-// store.  Lane group grp takes the k-slots s = ks + 4·grp + 0..3 and
-// ks + 16 + 4·grp + 0..3 of a 32-token step in both operands (each read
-// covers 16 consecutive rows: no LDS bank conflicts at either row stride).
-// The loads of K-block i+1 are in flight while block i multiplies.
+// LDS of one chunk's memory product: the K-block tiles during the product,
+// afterwards the finished memory as f32 rows [p][n] (a 16-byte pad keeps the
+// fragment writes conflict-free), the chunk's decay weights and the
+// log-decay at its last token.
 template <int N, int P>
-__global__ __launch_bounds__(kThreads) void k_chunk_state_tr(
-    const bf16* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
-    const bf16* __restrict__ Bm, float* __restrict__ acum, bf16* __restrict__ dH,
-    float* __restrict__ dHf, int L, int H, int G, int S) {
+struct alignas(16) ChunkMemLds {
+  static constexpr int LDB = N + 16, LDX = P + 16;  // K-block row strides (elements)
+  static constexpr int LDO = N + 4;                 // f32 memory row stride
+  static constexpr int KB_BYTES = kStKB * (LDB + LDX) * 2;
+  static constexpr int OUT_BYTES = P * LDO * 4;
+  static constexpr int RAW = KB_BYTES > OUT_BYTES ? KB_BYTES : OUT_BYTES;
+  unsigned char raw[RAW];
+  float w[kMaxChunk];
+  float part[4];
+  float aend;
+  __device__ float* mem() { return reinterpret_cast<float*>(raw); }
+};
+
+// Chunk state memory c of (batch b, head h), 16-bit io, computed by the 256
+// threads tid = 0..255 of one part of the workgroup: the arithmetic of
+// k_chunk_state with every HBM access in whole token rows.  B and w∘x
+// K-blocks sit row-major in LDS ([s][n], [s][p]) and both MFMA operands are
+// read with LDS transpose reads, so the token axis becomes each lane's k-run
+// without a transposing store.  Lane group grp takes the k-slots
+// s = ks + 4·grp + 0..3 and ks + 16 + 4·grp + 0..3 of a 32-token step in
+// both operands (each read covers 16 consecutive rows: no LDS bank conflicts
+// at either row stride).  The loads of K-block i+1 are in flight while
+// block i multiplies.
+// Writes acum of the chunk and leaves the f32 memory as rows [p][n] in
+// sm.mem() and acum at the last token in sm.aend, both visible to the whole
+// workgroup on return.  Contains workgroup barriers: every part of the
+// workgroup calls it once, with the same S.
+template <int N, int P>
+__device__ __forceinline__ void chunk_memory_tr(const bf16* __restrict__ x,
+                                                const float* __restrict__ dt,
+                                                const float* __restrict__ A,
+                                                const bf16* __restrict__ Bm,
+                                                float* __restrict__ acum, int L, int H, int G,
+                                                int S, int c, int h, int b, int tid,
+                                                ChunkMemLds<N, P>& sm) {
   using MM = Mma<bf16>;
+  using Lds = ChunkMemLds<N, P>;
   typedef bf16x8 vec_t;
   constexpr int VE = 8, K = MM::K;
-  constexpr int LDB = N + 16, LDX = P + 16;  // row strides (elements)
+  constexpr int LDB = Lds::LDB, LDX = Lds::LDX, LDO = Lds::LDO;
   constexpr int NB = N / 16;
   constexpr int NPB = P / 16;
   constexpr int NT = NB * NPB;        // 16x16 output tiles
@@ -165,24 +193,13 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state_tr(
   constexpr int XV = kStKB * (P / VE) / kThreads;  // vectors per thread per K-block
   constexpr int BV = kStKB * (N / VE) / kThreads;
   static_assert(XV * kThreads == kStKB * (P / VE) && BV * kThreads == kStKB * (N / VE),
-                "k_chunk_state_tr staging split");
-  // K-block tiles during the product; afterwards the finished memory as fp32
-  // rows [p][n] (a 16-byte pad keeps the fragment writes conflict-free), so
-  // both outputs leave as whole contiguous rows
-  constexpr int LDO = N + 4;
-  constexpr int KB_ELEMS = kStKB * (LDB + LDX);
-  constexpr int OUT_BYTES = P * LDO * 4;
-  constexpr int RAW = KB_ELEMS * 2 > OUT_BYTES ? KB_ELEMS * 2 : OUT_BYTES;
-  __shared__ __align__(16) unsigned char sh_raw[RAW];
-  bf16* sh_b = reinterpret_cast<bf16*>(sh_raw);
+                "chunk_memory_tr staging split");
+  bf16* sh_b = reinterpret_cast<bf16*>(sm.raw);
   bf16* sh_x = sh_b + kStKB * LDB;
-  float* sh_o = reinterpret_cast<float*>(sh_raw);
-  __shared__ float sh_w[kMaxChunk];
-  __shared__ float sh_part[4];
+  float* sh_o = sm.mem();
 
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int M = L / S, g = h / (H / G);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const long tok0 = (long)b * L + (long)c * S;
   const long pair = (long)b * H + h;
@@ -209,14 +226,15 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state_tr(
     const float u = __shfl_up(v, off);
     if (lane >= off) v += u;
   }
-  if (lane == 63) sh_part[w] = v;
+  if (lane == 63) sm.part[w] = v;
   __syncthreads();
-  for (int i = 0; i < w; ++i) v += sh_part[i];
-  const float total = sh_part[0] + sh_part[1] + sh_part[2] + sh_part[3];
+  for (int i = 0; i < w; ++i) v += sm.part[i];
+  const float total = sm.part[0] + sm.part[1] + sm.part[2] + sm.part[3];
   if (tid < S) {
     acum[(pair * M + c) * S + tid] = v;
-    sh_w[tid] = exp_neg(total - v) * dtv;
+    sm.w[tid] = exp_neg(total - v) * dtv;
   }
+  if (tid == S - 1) sm.aend = v;
   __syncthreads();
 
   // 2. dH[n][p] = sum_s B[s][n]·w_s·x[s][p] over K-blocks of kStKB tokens
@@ -232,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state_tr(
 #pragma unroll
     for (int v2 = 0; v2 < XV; ++v2) {
       const int i = tid + v2 * kThreads, s = i / (P / VE), pv = i % (P / VE);
-      const float wv = s0 + s < S ? sh_w[s0 + s] : 0.f;
+      const float wv = s0 + s < S ? sm.w[s0 + s] : 0.f;
       vec_t o;
 #pragma unroll
       for (int e = 0; e < VE; ++e) o[e] = from_f32<bf16>(to_f32(xr[v2][e]) * wv);
@@ -244,9 +262,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state_tr(
     for (int ks = 0; ks < kStKB; ks += K) {
       const int r0 = ks + 4 * grp + (col >> 2), c0 = 4 * (col & 3);
       // k-slots r0 .. (4 rows) and r0 + 16 .. of column c + col
-      auto frag = [&](const bf16* tile, int ld, int c) __attribute__((always_inline)) {
-        const bf16x4 lo = lds_read_tr4(&tile[r0 * ld + c + c0]);
-        const bf16x4 hi = lds_read_tr4(&tile[(r0 + 16) * ld + c + c0]);
+      auto frag = [&](const bf16* tile, int ld, int cc) __attribute__((always_inline)) {
+        const bf16x4 lo = lds_read_tr4(&tile[r0 * ld + cc + c0]);
+        const bf16x4 hi = lds_read_tr4(&tile[(r0 + 16) * ld + cc + c0]);
         return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       };
       if constexpr (kGrid) {
@@ -274,8 +292,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state_tr(
   }
 
   // 3. memory c value-axis-major ([p][n]): lane holds n = nb*16 + 4*grp + i,
-  //    p = pb*16 + col; through LDS, then whole rows to both outputs (the
-  //    loop's last barrier has released the K-block tiles)
+  //    p = pb*16 + col (the loop's last barrier has released the K-block
+  //    tiles)
 #pragma unroll
   for (int j = 0; j < TPW; ++j) {
     const int tt = w + 4 * j;
@@ -285,15 +303,25 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state_tr(
     }
   }
   __syncthreads();
-  const long base = (pair * M + c) * (long)(P * N);
+}
+
+// Whole rows of memory c from sm.mem() to dH (io, rounded to nearest even)
+// and, when dHf is not null, to dHf (f32), by the 256 threads tid.
+template <int N, int P>
+__device__ __forceinline__ void store_memory_rows(ChunkMemLds<N, P>& sm, bf16* __restrict__ dH,
+                                                  float* __restrict__ dHf, long base, int tid) {
+  constexpr int LDO = ChunkMemLds<N, P>::LDO;
+  const float* sh_o = sm.mem();
   constexpr int F4 = P * N / 4;  // float4s of one memory
+  if (dHf) {
 #pragma unroll
-  for (int v = 0; v < (F4 + kThreads - 1) / kThreads; ++v) {
-    const int i = tid + v * kThreads;
-    if (F4 % kThreads != 0 && i >= F4) break;
-    const int p = i / (N / 4), n = (i % (N / 4)) * 4;
-    *reinterpret_cast<floatx4*>(dHf + base + (long)i * 4) =
-        *reinterpret_cast<const floatx4*>(&sh_o[p * LDO + n]);
+    for (int v = 0; v < (F4 + kThreads - 1) / kThreads; ++v) {
+      const int i = tid + v * kThreads;
+      if (F4 % kThreads != 0 && i >= F4) break;
+      const int p = i / (N / 4), n = (i % (N / 4)) * 4;
+      *reinterpret_cast<floatx4*>(dHf + base + (long)i * 4) =
+          *reinterpret_cast<const floatx4*>(&sh_o[p * LDO + n]);
+    }
   }
 #pragma unroll
   for (int v = 0; v < (F4 / 2 + kThreads - 1) / kThreads; ++v) {
@@ -306,6 +334,176 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state_tr(
         bf16x8{from_f32<bf16>(lo[0]), from_f32<bf16>(lo[1]), from_f32<bf16>(lo[2]),
                from_f32<bf16>(lo[3]), from_f32<bf16>(hi[0]), from_f32<bf16>(hi[1]),
                from_f32<bf16>(hi[2]), from_f32<bf16>(hi[3])};
+  }
+}
+
+// One workgroup per (chunk c, head h, batch b): memory c as io and f32 rows.
+template <int N, int P>
+__global__ __launch_bounds__(kThreads) void k_chunk_state_tr(
+    const bf16* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
+    const bf16* __restrict__ Bm, float* __restrict__ acum, bf16* __restrict__ dH,
+    float* __restrict__ dHf, int L, int H, int G, int S) {
+  __shared__ ChunkMemLds<N, P> sm;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  chunk_memory_tr<N, P>(x, dt, A, Bm, acum, L, H, G, S, c, h, b, threadIdx.x, sm);
+  const long pair = (long)b * H + h;
+  store_memory_rows<N, P>(sm, dH, dHf, (pair * (L / S) + c) * (long)(P * N), threadIdx.x);
+}
+
+// Chunk memories and the inter-chunk state recurrence in one pass, 16-bit io.
+// A workgroup of CPW parts (256 threads each) takes CPW consecutive chunks
+// j·CPW .. j·CPW + CPW - 1 of one (batch, head): each part computes its
+// chunk's memory (chunk_memory_tr) and writes it as io rows; then the
+// workgroup waits for the f32 state entering chunk j·CPW from the workgroup
+// of link j - 1 (h0 or zero for j = 0), advances it through its chunks,
+//   H[c+1] = exp(acum[c, S-1])·H[c] + dH[c]          (f32, in chunk order)
+// hands H[(j+1)·CPW] to link j + 1 (or writes it as h_final), and writes
+// H_in[c] = io(H[c]) for its chunks.  The hand-over goes through a
+// two-slot f32 ring per (batch, head) (link j writes slot j % 2 after reading
+// slot (j - 1) % 2, so a slot is rewritten only after its reader has
+// published) and a 64-bit flag per (batch, head) holding (tag << 32) | links
+// done.  Ring values and flag are relaxed agent-scope atomics, each access
+// coherent across the XCDs' L2s by itself; the flag is stored only after
+// every wave's ring stores are performed (vmcnt(0), then a barrier), and the
+// ring is read only after the flag was seen (a barrier after the poll).  A
+// release/acquire pair would add an L2-wide write-back per hand-over.  tag is
+// distinct per call, so a flag left by an earlier call never matches.
+// Link j waits only for link j - 1, whose block index is lower: blocks start
+// in index order, so every awaited workgroup is already resident.  The wait
+// is bounded all the same: after kScanSpinLimit polls (or once another
+// wait of this call has given up) it counts a failure in err[0], records
+// the tag in err[1] and continues, so the kernel always ends.
+// Block order: with xcd_major, block i runs on XCD i % 8 and holds the
+// (batch, group) pairs bg ≡ i % 8 (mod 8), chunk-major within the XCD, so
+// a (batch, head)'s chain and a group's shared B rows stay in one L2.
+constexpr int kScanSpinLimit = 1 << 20;
+constexpr size_t kLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
+
+template <int N, int P, int CPW>
+__global__ __launch_bounds__(kThreads * CPW) void k_chunk_scan(
+    const bf16* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
+    const bf16* __restrict__ Bm, const float* __restrict__ h0, float* __restrict__ acum,
+    bf16* __restrict__ dH, float* __restrict__ dHf, bf16* __restrict__ H_in,
+    float* __restrict__ h_final, float* __restrict__ ring, unsigned long long* flags, int* err,
+    unsigned tag, int L, int H, int G, int S, int BH, int xcd_major) {
+  constexpr int PN = P * N;
+  constexpr int LDO = ChunkMemLds<N, P>::LDO;
+  constexpr int TT = kThreads * CPW;
+  constexpr int F4 = PN / 4;
+  constexpr int V = (F4 + TT - 1) / TT;  // state float4s per thread
+  __shared__ ChunkMemLds<N, P> sm[CPW];
+
+  const int M = L / S, NJ = M / CPW;
+  const int i = blockIdx.x;
+  int pair, j;
+  if (xcd_major) {
+    const int per = BH >> 3, hpg = H / G;  // pairs per XCD, heads per group
+    const int jj = i >> 3;
+    j = jj / per;
+    const int lp = jj - j * per;
+    pair = ((i & 7) + 8 * (lp / hpg)) * hpg + lp % hpg;
+  } else {
+    j = i / BH;
+    pair = i - j * BH;
+  }
+  const int b = pair / H, h = pair - b * H;
+  const int part = threadIdx.x >> 8, tid = threadIdx.x & (kThreads - 1);
+  const int c0 = j * CPW;
+
+  chunk_memory_tr<N, P>(x, dt, A, Bm, acum, L, H, G, S, c0 + part, h, b, tid, sm[part]);
+  store_memory_rows<N, P>(sm[part], dH, dHf, ((long)pair * M + c0 + part) * (long)PN, tid);
+
+  // the state entering chunk c0
+  floatx4 st[V];
+  if (j == 0) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e4 = threadIdx.x + v * TT;
+      st[v] = h0 && e4 < F4 ? reinterpret_cast<const floatx4*>(h0 + (long)pair * PN)[e4]
+                            : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  } else {
+    if (threadIdx.x == 0) {
+      const unsigned long long want = ((unsigned long long)tag << 32) | (unsigned)j;
+      for (int it = 0;; ++it) {
+        if (__hip_atomic_load(&flags[pair], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want)
+          break;
+        if (it >= kScanSpinLimit ||
+            ((it & 63) == 63 &&
+             __hip_atomic_load(&err[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (int)tag)) {
+          __hip_atomic_fetch_add(&err[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&err[1], (int)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    __syncthreads();  // no thread reads the slot before the flag was seen
+    const float* src = ring + ((long)pair * 2 + ((j + 1) & 1)) * PN;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e4 = threadIdx.x + v * TT;
+      if (e4 < F4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          st[v][q] = __hip_atomic_load(&src[e4 * 4 + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        st[v] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+
+  // advance through the workgroup's chunks, keeping the entering states
+  floatx4 hin[CPW][V];
+#pragma unroll
+  for (int k = 0; k < CPW; ++k) {
+    const float dec = exp_neg(sm[k].aend);
+    const float* mem = sm[k].mem();
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e4 = threadIdx.x + v * TT;
+      hin[k][v] = st[v];
+      if (e4 < F4) {
+        const int p = e4 / (N / 4), n = (e4 % (N / 4)) * 4;
+        st[v] = dec * st[v] + *reinterpret_cast<const floatx4*>(&mem[p * LDO + n]);
+      }
+    }
+  }
+
+  // hand the state to the next link, or write it as h_final
+  if (j + 1 < NJ) {
+    float* dst = ring + ((long)pair * 2 + (j & 1)) * PN;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e4 = threadIdx.x + v * TT;
+      if (e4 < F4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          __hip_atomic_store(&dst[e4 * 4 + q], st[v][q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    wait_fence<vmcnt_imm(0)>();  // this wave's slot stores are performed at agent scope
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&flags[pair], ((unsigned long long)tag << 32) | (unsigned)(j + 1),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e4 = threadIdx.x + v * TT;
+      if (e4 < F4) reinterpret_cast<floatx4*>(h_final + (long)pair * PN)[e4] = st[v];
+    }
+  }
+
+  // H_in rows of the workgroup's chunks
+#pragma unroll
+  for (int k = 0; k < CPW; ++k) {
+    bf16* dst = H_in + ((long)pair * M + c0 + k) * PN;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e4 = threadIdx.x + v * TT;
+      if (e4 < F4) store4(dst + e4 * 4, hin[k][v]);
+    }
   }
 }
 
@@ -1142,16 +1340,10 @@ hipError_t launch_chunk_state(const PrefillShape& s, const T* x, const float* dt
 }
 
 template <typename T, int N, int P>
-hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt, const T* Bm,
-                             const T* C, const float* acum, const float* dH_f32,
-                             const float* h0, T* H_in, float* h_final, T* y_ssd,
-                             hipStream_t st) {
+hipError_t launch_chunk_out(const PrefillShape& s, const T* x, const float* dt, const T* Bm,
+                            const T* C, const float* acum, const T* H_in, T* y_ssd,
+                            hipStream_t st) {
   const int M = s.L / s.S;
-  constexpr int PN = P * N;
-  hipLaunchKernelGGL(k_state_pass<T>, dim3((PN / 4 + kThreads - 1) / kThreads, s.H, s.B),
-                     dim3(kThreads), 0, st, acum, dH_f32, h0, H_in, h_final, s.H, M, s.S, PN);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   if constexpr (std::is_same<T, bf16>::value && ChunkOutDma<N, P>::fits) {
     if (s.S == kMaxChunk) {
       hipLaunchKernelGGL((k_chunk_out_dma<N, P>), dim3(M, s.G, s.B), dim3(kOutThreads), 0, st, x,
@@ -1168,6 +1360,79 @@ hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt,
   return hipGetLastError();
 }
 
+template <typename T>
+static hipError_t launch_state_recurrence(const PrefillShape& s, int PN, const float* acum,
+                                          const float* dH_f32, const float* h0, T* H_in,
+                                          float* h_final, hipStream_t st) {
+  const int M = s.L / s.S;
+  hipLaunchKernelGGL(k_state_pass<T>, dim3((PN / 4 + kThreads - 1) / kThreads, s.H, s.B),
+                     dim3(kThreads), 0, st, acum, dH_f32, h0, H_in, h_final, s.H, M, s.S, PN);
+  return hipGetLastError();
+}
+
+template <typename T, int N, int P>
+hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt, const T* Bm,
+                             const T* C, const float* acum, const float* dH_f32,
+                             const float* h0, T* H_in, float* h_final, T* y_ssd,
+                             hipStream_t st) {
+  hipError_t e = launch_state_recurrence<T>(s, P * N, acum, dH_f32, h0, H_in, h_final, st);
+  if (e != hipSuccess) return e;
+  return launch_chunk_out<T, N, P>(s, x, dt, Bm, C, acum, H_in, y_ssd, st);
+}
+
+size_t chunk_scan_workspace_bytes(int io, int64_t B, int64_t L, int64_t H, int64_t N, int64_t P,
+                                  int64_t S) {
+  const size_t pairs = static_cast<size_t>(B * H), PN = static_cast<size_t>(N * P);
+  if (io == DART_F32)  // the f32 memories of the two-kernel path
+    return pairs * static_cast<size_t>(L / S) * PN * sizeof(float);
+  // failure words, one flag per (batch, head), two ring slots per (batch, head)
+  return 256 + ((pairs * 8 + 255) / 256) * 256 + pairs * 2 * PN * sizeof(float);
+}
+
+template <typename T, int N, int P>
+hipError_t launch_chunk_scan(const PrefillShape& s, const T* x, const float* dt, const float* A,
+                             const T* Bm, const float* h0, float* acum, T* dH, float* dH_f32,
+                             T* H_in, float* h_final, void* workspace, unsigned tag,
+                             hipStream_t st) {
+  const int M = s.L / s.S, BH = s.B * s.H;
+  if constexpr (std::is_same<T, bf16>::value) {
+    char* w = static_cast<char*>(workspace);
+    int* err = reinterpret_cast<int*>(w);
+    auto* flags = reinterpret_cast<unsigned long long*>(w + 256);
+    float* ring = reinterpret_cast<float*>(w + 256 + ((size_t(BH) * 8 + 255) / 256) * 256);
+    const int xcd = (s.B * s.G) % 8 == 0 ? 1 : 0;
+    // chunks per workgroup: 4, else 2, else 1, as M and the LDS allow
+    constexpr size_t lds1 = sizeof(ChunkMemLds<N, P>);
+    if constexpr (4 * lds1 <= kLdsBytes) {
+      if (M % 4 == 0) {
+        hipLaunchKernelGGL((k_chunk_scan<N, P, 4>), dim3(M / 4 * BH), dim3(kThreads * 4), 0, st,
+                           x, dt, A, Bm, h0, acum, dH, dH_f32, H_in, h_final, ring, flags, err,
+                           tag, s.L, s.H, s.G, s.S, BH, xcd);
+        return hipGetLastError();
+      }
+    }
+    if constexpr (2 * lds1 <= kLdsBytes) {
+      if (M % 2 == 0) {
+        hipLaunchKernelGGL((k_chunk_scan<N, P, 2>), dim3(M / 2 * BH), dim3(kThreads * 2), 0, st,
+                           x, dt, A, Bm, h0, acum, dH, dH_f32, H_in, h_final, ring, flags, err,
+                           tag, s.L, s.H, s.G, s.S, BH, xcd);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((k_chunk_scan<N, P, 1>), dim3(M * BH), dim3(kThreads), 0, st, x, dt, A,
+                       Bm, h0, acum, dH, dH_f32, H_in, h_final, ring, flags, err, tag, s.L, s.H,
+                       s.G, s.S, BH, xcd);
+    return hipGetLastError();
+  } else {
+    (void)tag;
+    float* f = dH_f32 ? dH_f32 : static_cast<float*>(workspace);
+    hipError_t e = launch_chunk_state<T, N, P>(s, x, dt, A, Bm, acum, dH, f, st);
+    if (e != hipSuccess) return e;
+    return launch_state_recurrence<T>(s, P * N, acum, f, h0, H_in, h_final, st);
+  }
+  (void)M;
+}
+
 #define DART_INST_SCAN(T, N, P)                                                              \
   template hipError_t launch_chunk_state<T, N, P>(const PrefillShape&, const T*, const float*, \
                                                   const float*, const T*, float*, T*, float*,  \
@@ -1175,6 +1440,13 @@ hipError_t launch_state_pass(const PrefillShape& s, const T* x, const float* dt,
   template hipError_t launch_state_pass<T, N, P>(const PrefillShape&, const T*, const float*,  \
                                                  const T*, const T*, const float*,             \
                                                  const float*, const float*, T*, float*, T*,   \
+                                                 hipStream_t);                                 \
+  template hipError_t launch_chunk_out<T, N, P>(const PrefillShape&, const T*, const float*,   \
+                                                const T*, const T*, const float*, const T*, T*, \
+                                                hipStream_t);                                  \
+  template hipError_t launch_chunk_scan<T, N, P>(const PrefillShape&, const T*, const float*,  \
+                                                 const float*, const T*, const float*, float*, \
+                                                 T*, float*, T*, float*, void*, unsigned,      \
                                                  hipStream_t);
 DART_FOR_EACH_SHAPE(DART_INST_SCAN)
 

@@ -311,3 +311,43 @@ def test_decode_noalloc_validates_on_host():
     assert api.dart_sma_decode_workspace(ddims(B=big)) > cap
     assert fn(ddims(B=big), *([A16] * 7), 0.5, *([A16] * 6), None, None) == SCRATCH
     assert "DART_ERR_SCRATCH" in lib.dart_status_str(SCRATCH).decode()
+
+
+def test_chunk_scan_workspace_sizes():
+    """16-bit io: 256 bytes of failure words, an 8-byte flag per (batch, head)
+    rounded to 256 bytes, two f32 state slots per (batch, head); f32 io: the
+    f32 memories of every chunk."""
+    B, L, H, G, N, P, S = 4, 8192, 32, 4, 128, 64, 256
+    got = api.dart_chunk_scan_workspace(dims(B, L, H, G, N, P, S, BF16))
+    assert got == 256 + 1024 + B * H * 2 * N * P * 4
+    got = api.dart_chunk_scan_workspace(dims(1, 1024, 2, 1, 16, 16, 64, F32))
+    assert got == 2 * 16 * 16 * 16 * 4
+    assert api.dart_chunk_scan_workspace(dims(L=1000)) == 0
+
+
+def test_chunk_scan_and_chunk_out_reject_bad_arguments():
+    lib = dart.lib()
+    d = dims(1, 1024, 2, 1, 128, 64, 256, BF16)
+    need = api.dart_chunk_scan_workspace(d)
+    # x, dt, A, Bm, h0 (may be NULL), acum, dH, dH_f32 (may be NULL), H_in, h_final
+    for i in (0, 1, 2, 3, 5, 6, 8, 9):
+        q = [A16] * 10
+        q[4] = q[7] = None
+        q[i] = None
+        assert lib.dart_chunk_scan(d, *q, A16, need, None) == NULLP
+    q = [A16] * 10
+    assert lib.dart_chunk_scan(d, *q, None, need, None) == WS
+    assert lib.dart_chunk_scan(d, *q, A16, need - 256, None) == WS
+    assert lib.dart_chunk_scan(d, *q, MIS, need, None) == ALIGN
+    q[4] = MIS
+    assert lib.dart_chunk_scan(d, *q, A16, need, None) == ALIGN
+    q[4], q[7] = A16, MIS
+    assert lib.dart_chunk_scan(d, *q, A16, need, None) == ALIGN
+    assert lib.dart_chunk_scan(dims(N=16, P=32), *([A16] * 10), A16, need, None) == UNSUP
+    for i in range(7):
+        q = [A16] * 7
+        q[i] = None
+        assert lib.dart_chunk_out(d, *q, None) == NULLP
+    q = [A16] * 7
+    q[5] = MIS
+    assert lib.dart_chunk_out(d, *q, None) == ALIGN

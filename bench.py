@@ -112,24 +112,22 @@ def bench_prefill(args, torch, api, synth):
     out = {
         "acum": torch.empty(B, H, M, S, **f32),
         "dH": torch.empty(B, H, M, P, N, dtype=torch.bfloat16, device="cuda:0"),
+        "dH_f32": torch.empty(B, H, M, P, N, **f32),
         "H_in": torch.empty(B, H, M, P, N, dtype=torch.bfloat16, device="cuda:0"),
         "h_final": torch.empty(B, H, P, N, **f32),
         "y_ssd": torch.empty(B, L, H, P, dtype=torch.bfloat16, device="cuda:0"),
         "y": torch.empty(B, L, H, P, dtype=torch.bfloat16, device="cuda:0"),
     }
-    ws = torch.empty(api.dart_chunk_scan_workspace(api.prefill_dims(d["x"], d["Bm"], S)),
-                     dtype=torch.uint8, device="cuda:0")
 
-    # the prefill path of api.prefill: one-pass chunk scan, chunk output, SMA
     def step(ev=None):
         if ev:
             ev[0].record()
-        api.dart_chunk_scan(d["x"], d["dt"], d["A"], d["Bm"], None, out["acum"], out["dH"], None,
-                            out["H_in"], out["h_final"], ws, S)
+        api.dart_chunk_state(d["x"], d["dt"], d["A"], d["Bm"], out["acum"], out["dH"],
+                             out["dH_f32"], S)
         if ev:
             ev[1].record()
-        api.dart_chunk_out(d["x"], d["dt"], d["Bm"], d["C"], out["acum"], out["H_in"],
-                           out["y_ssd"], S)
+        api.dart_state_pass(d["x"], d["dt"], d["Bm"], d["C"], out["acum"], out["dH_f32"], None,
+                            out["H_in"], out["h_final"], out["y_ssd"], S)
         if ev:
             ev[2].record()
         api.dart_sma_fwd(d["Q"], d["E"], d["C"], out["dH"], out["y_ssd"], c["gate"], out["y"], S)
@@ -170,7 +168,7 @@ def bench_prefill(args, torch, api, synth):
         "sma_ms_median": per_sma[len(per_sma) // 2],
         "sma_ms_min": per_sma[0],
         "tokens_per_s": B * L / (ms / 1e3),
-        "kernel_ms": {"chunk_scan": split[0], "chunk_out": split[1],
+        "kernel_ms": {"chunk_state": split[0], "state_pass+chunk_out": split[1],
                       "sma_fwd": sma_ms},
         "flops": {"sma": flops_sma, "scan": flops_scan},
         "roofline": {
@@ -201,17 +199,16 @@ def bench_prefill_extra(args, torch, api, synth, c, name, steps):
     f32 = dict(dtype=torch.float32, device="cuda:0")
     bf = dict(dtype=torch.bfloat16, device="cuda:0")
     out = {"acum": torch.empty(B, H, M, S, **f32), "dH": torch.empty(B, H, M, P, N, **bf),
-           "H_in": torch.empty(B, H, M, P, N, **bf), "h_final": torch.empty(B, H, P, N, **f32),
-           "y_ssd": torch.empty(B, L, H, P, **bf), "y": torch.empty(B, L, H, P, **bf)}
-    ws = torch.empty(api.dart_chunk_scan_workspace(api.prefill_dims(d["x"], d["Bm"], S)),
-                     dtype=torch.uint8, device="cuda:0")
+           "dH_f32": torch.empty(B, H, M, P, N, **f32), "H_in": torch.empty(B, H, M, P, N, **bf),
+           "h_final": torch.empty(B, H, P, N, **f32), "y_ssd": torch.empty(B, L, H, P, **bf),
+           "y": torch.empty(B, L, H, P, **bf)}
 
     def step(ev):
         ev[0].record()
-        api.dart_chunk_scan(d["x"], d["dt"], d["A"], d["Bm"], None, out["acum"], out["dH"], None,
-                            out["H_in"], out["h_final"], ws, S)
-        api.dart_chunk_out(d["x"], d["dt"], d["Bm"], d["C"], out["acum"], out["H_in"],
-                           out["y_ssd"], S)
+        api.dart_chunk_state(d["x"], d["dt"], d["A"], d["Bm"], out["acum"], out["dH"],
+                             out["dH_f32"], S)
+        api.dart_state_pass(d["x"], d["dt"], d["Bm"], d["C"], out["acum"], out["dH_f32"], None,
+                            out["H_in"], out["h_final"], out["y_ssd"], S)
         ev[1].record()
         api.dart_sma_fwd(d["Q"], d["E"], d["C"], out["dH"], out["y_ssd"], c["gate"], out["y"], S)
         ev[2].record()
@@ -557,6 +554,12 @@ def environment(torch):
             "hbm_bytes": prop.total_memory, "sclk": shader_clock_levels()}
 
 
+def progress(msg):
+    """One line per finished leg on stderr (the JSON result stays the only
+    stdout line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -600,6 +603,7 @@ def main():
                                                    "sma_ms_min")}
         result["mfma_frac_whole_prefill"] = pre["mfma_frac_whole_prefill"]
         result["algorithmic_gflop_per_step"] = {k: v / 1e9 for k, v in pre["flops"].items()}
+        progress(f"prefill L=8K {pre['ms_per_step']:.3f} ms per step")
     if not args.no_extra_configs and pre is not None:
         torch.cuda.empty_cache()
         result["prefill_L4K"] = bench_prefill_extra(
@@ -609,15 +613,19 @@ def main():
             args, torch, api, synth, PREFILL_L64K,
             "DART long-context prefill, L=65536, 32 heads (256 memories per head)",
             max(3, min(args.steps, 5)))
+        progress("prefill L=4K and L=64K done")
     if not args.no_backward and pre is not None:
         torch.cuda.empty_cache()
         result["backward"] = bench_backward(args, torch, api, synth, pre["inputs"])
+        progress("backward done")
     if not args.no_decode:
         torch.cuda.empty_cache()
         result["decode"] = bench_decode(args, torch, api, synth)
         torch.cuda.empty_cache()
         result["decode_fp8"] = bench_decode_fp8(args, torch, api, synth)
+        progress("decode done")
     if not args.no_cpu_baseline and pre is not None:
+        progress("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(pre["inputs"], args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

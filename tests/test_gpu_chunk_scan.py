@@ -133,3 +133,29 @@ def test_one_pass_benchmark_shape_against_oracle_and_two_pass():
             bound = 2e-2 * float(np.max(np.abs(rv)))
             print(f"(b{b}, h{h}) {name}: max err {err:.3e} bound {bound:.3e}", flush=True)
             assert err <= bound
+
+
+@pytest.mark.parametrize("decayed", [False, True])
+def test_prefill_one_pass_equals_default(decayed):
+    """api.prefill(one_pass=True) gives the default path's outputs bit for
+    bit (y through the SMA and gated add included), and prefill_train the
+    same for what the backward reads."""
+    _need_gpu()
+    B, L, H, G, N, P, S = 2, 2048, 8, 2, 128, 64, 256
+    print(f"prefill one_pass decayed={decayed}", flush=True)
+    d = {k: v.to(DEV) for k, v in synth.draw_prefill(97, B, L, H, G, N, P, io=torch.bfloat16,
+                                                      qscale=30.0).items()}
+    h0 = synth.draw_state(98, (B, H, P, N), 0.3, torch.float32).to(DEV)
+    args = (d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], 0.5, S)
+    a = api.prefill(*args, h0=h0, decayed=decayed)
+    b = api.prefill(*args, h0=h0, decayed=decayed, one_pass=True)
+    torch.cuda.synchronize()
+    assert "dH_f32" not in b
+    for k, v in b.items():
+        assert torch.equal(v, a[k]), f"{k} differs"
+    if not decayed:
+        ta = api.prefill_train(*args, h0=h0)
+        tb = api.prefill_train(*args, h0=h0, one_pass=True)
+        torch.cuda.synchronize()
+        for k, v in tb.items():
+            assert torch.equal(v, ta[k]), f"prefill_train {k} differs"

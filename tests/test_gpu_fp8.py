@@ -210,7 +210,7 @@ def test_decode_fp8_continues_prefill():
     d = {k: v.to(DEV) for k, v in inp.items()}
     pre = {k: v[:, :k0 * S].contiguous() if k != "A" else v for k, v in d.items()}
     head = api.prefill(pre["x"], pre["dt"], pre["A"], pre["Bm"], pre["C"], pre["Q"], pre["E"],
-                       gate, S, keep_f32=True)
+                       gate, S)
     st = api.new_decode_state(B, H, G, N, P, S, M, io, DEV, fp8_cache=True)
     api.store_memories(st, head["dH_f32"])
     st["h"].copy_(head["h_final"])
@@ -359,7 +359,7 @@ def test_prefill_continuation_fp8_cache():
     part = lambda lo, hi: {k: (v if k == "A" else v[:, lo:hi].contiguous()) for k, v in d.items()}
     pre, tail = part(0, k0 * S), part(k0 * S, L)
     head = api.prefill(pre["x"], pre["dt"], pre["A"], pre["Bm"], pre["C"], pre["Q"], pre["E"],
-                       gate, S, keep_f32=True)
+                       gate, S)
     st = api.new_decode_state(B, H, G, N, P, S, k0 + M, io, DEV, fp8_cache=True)
     api.store_memories(st, head["dH_f32"])
     cont = api.prefill_continue(tail["x"], tail["dt"], tail["A"], tail["Bm"], tail["C"],

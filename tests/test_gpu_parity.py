@@ -59,7 +59,7 @@ def run_prefill_case(B, L, H, G, N, P, S, io, seed=0, gate=0.5, qscale=1.0, h0_s
         h0 = synth.draw_state(seed + 1, (B, H, P, N), h0_std, torch.float32)
     d = _to_dev(inp)
     out = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate, S,
-                      h0=None if h0 is None else h0.to(DEV), decayed=decayed, keep_f32=True)
+                      h0=None if h0 is None else h0.to(DEV), decayed=decayed)
     torch.cuda.synchronize()
     n = _np(inp)
     ref = oracle.prefill(n["x"], n["dt"], n["A"], n["Bm"], n["C"], n["Q"], n["E"], gate, S,
@@ -142,8 +142,7 @@ def test_prefill_large_decay(io, N, P, S):
     inp["A"] = torch.full((H,), -16.0, dtype=torch.float32)
     d = _to_dev(inp)
     gate = 0.5
-    out = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate, S,
-                      keep_f32=True)
+    out = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate, S)
     torch.cuda.synchronize()
     n = _np(inp)
     ref = oracle.prefill(n["x"], n["dt"], n["A"], n["Bm"], n["C"], n["Q"], n["E"], gate, S)
@@ -203,7 +202,7 @@ def test_memories_rounded_from_f32():
     _need_gpu()
     inp = _to_dev(synth.draw_prefill(12, 1, 512, 2, 2, 128, 64, io=torch.bfloat16))
     out = api.prefill(inp["x"], inp["dt"], inp["A"], inp["Bm"], inp["C"], inp["Q"], inp["E"],
-                      0.5, 256, keep_f32=True)
+                      0.5, 256)
     torch.cuda.synchronize()
     assert torch.equal(out["dH"], out["dH_f32"].to(torch.bfloat16))
 

@@ -33,23 +33,26 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "SMA+scan prefill tokens/s & MFMA% at L=8K; decode chunk-memory HBM GB/s"
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this
-# benchmark, calibrated against a 1 GiB copy (profiles/); each figure is valid
-# only for the kernel source it was measured on (SHA-1 of that file).
+# benchmark (bytes read = FETCH_SIZE KiB x 2 x 1024, written = WRITE_SIZE KiB x
+# 1024, as calibrated by device copies of known size; profiles/); each figure
+# is valid only for the kernel source it was measured on (SHA-1 of that file).
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "ssm_state_attention_amd", "csrc")
+_KIB = 1024
 PROFILED_TRAFFIC = {
     # dart_sma_fwd at the L=8K shape: the grouped kernel k_sma_grp
     "k_sma_grp": ("k_sma.hip", "dc9720b752190e628d3a8d436d50ca99f1838525",
-                  (432.48 + 131.07) * 1e6),
+                  (216334 * 2 + 131072) * _KIB),
     # the two launches of one decode call with one split per head (state
     # update, then the cache stream that also writes y and advances pos)
     "dart_sma_decode": ("k_decode.hip", "5161f28fb5c89b1dff36f1c14942a25bb2ad9145",
-                        (132.57 + 131.58 + 4196.22 + 0.26) * 1e6),
+                        (66288 * 2 + 131584 + 2098108 * 2 + 256) * _KIB),
     "dart_sma_decode_fp8": ("k_decode.hip", "5161f28fb5c89b1dff36f1c14942a25bb2ad9145",
-                            (132.58 + 131.58 + 2101.10 + 0.26) * 1e6),
+                            (66287 * 2 + 131584 + 1050550 * 2 + 256) * _KIB),
     # the launches of one SMA backward call (dy·o pass, gate sum, token- and
     # memory-major kernels)
     "dart_sma_bwd": ("k_sma_bwd.hip", "06886dd2840539233c3b3aa764f7abb9a7d1c8a6",
-                     (393.33 + 8.66 + 0.04 + 490.04 + 520.19 + 1749.04 + 132.52) * 1e6),
+                     (196666 * 2 + 8669 + 22 * 2 + 1 + 244703 * 2 + 520192 + 868713 * 2
+                      + 132419) * _KIB),
 }
 
 

@@ -278,8 +278,10 @@ dart_status dart_sma_fwd_train(const dart_dims* dims, const void* Q, const void*
  * workspace: device memory of at least dart_sma_bwd_workspace(dims) bytes:
  *      about 4·B·H·L bytes plus 8 bytes per visible (token, memory) pair,
  *      B·H·L·(M-1)/2 of them (~130 MB at B=4, H=32, L=8192, S=256).
- * Compiled for bf16 io with P <= 64 and chunks that are multiples of 64;
- * other dims return DART_ERR_UNSUPPORTED.
+ * Compiled for bf16 io with P <= 64 and chunks that are multiples of 64
+ * (MFMA kernels), and for every f32 io shape and chunk size (plain f32
+ * kernels, the f32 correctness shapes); other dims return
+ * DART_ERR_UNSUPPORTED.
  */
 size_t dart_sma_bwd_workspace(const dart_dims* dims);
 dart_status dart_sma_bwd(const dart_dims* dims, const void* Q, const void* E, const void* C,
@@ -306,8 +308,9 @@ dart_status dart_sma_bwd(const dart_dims* dims, const void* Q, const void* E, co
  * out: dx [B,L,H,P], ddt [B,L,H], dA [H], dB, dC [B,L,G,N], dh0 [B,H,P,N],
  *      all f32 (dB and dC summed over the heads of each group)
  * workspace: at least dart_scan_bwd_workspace(dims) bytes of device memory.
- * Compiled for bf16 io with P <= 64 and chunks that are multiples of 64;
- * other dims return DART_ERR_UNSUPPORTED.
+ * Compiled for bf16 io with P <= 64 and chunks that are multiples of 64
+ * (MFMA kernels), and for every f32 io shape and chunk size (plain f32
+ * kernels); other dims return DART_ERR_UNSUPPORTED.
  */
 size_t dart_scan_bwd_workspace(const dart_dims* dims);
 dart_status dart_scan_bwd(const dart_dims* dims, const void* x, const float* dt, const float* A,

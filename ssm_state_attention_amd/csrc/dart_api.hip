@@ -221,6 +221,8 @@ struct ScanBwdFn {
 // The backward is compiled for 16-bit io with P <= 64 and chunks of whole
 // 64-token tiles.
 bool bwd_supported(const dart_dims* d) {
+  // f32 io: the plain f32 kernels, every compiled shape and chunk size
+  if (d->io == DART_F32) return true;
   // the dy·o pass launches one workgroup per four (batch, token) rows
   return d->io == DART_BF16 && d->headdim <= 64 && d->chunk % 64 == 0 &&
          d->batch * d->seqlen / 4 < (int64_t(1) << 31);
@@ -442,6 +444,9 @@ extern "C" dart_status dart_cache_fp8_store(const dart_decode_dims* dims, const 
 
 extern "C" size_t dart_sma_bwd_workspace(const dart_dims* dims) {
   if (dart_validate_dims(dims) != DART_OK || !bwd_supported(dims)) return 0;
+  if (dims->io == DART_F32)
+    return (dart::sma_bwd_f32_workspace_bytes(dims->batch, dims->seqlen, dims->nheads,
+                                              dims->ngroups, dims->chunk) + 255) / 256 * 256;
   return (dart::sma_bwd_workspace_bytes(dims->batch, dims->seqlen, dims->nheads,
                                         dims->chunk) + 255) / 256 *
          256;
@@ -465,6 +470,9 @@ extern "C" dart_status dart_sma_bwd(const dart_dims* dims, const void* Q, const 
 
 extern "C" size_t dart_scan_bwd_workspace(const dart_dims* dims) {
   if (dart_validate_dims(dims) != DART_OK || !bwd_supported(dims)) return 0;
+  if (dims->io == DART_F32)
+    return dart::scan_bwd_f32_workspace_bytes(dims->batch, dims->seqlen, dims->nheads,
+                                              dims->dstate, dims->headdim, dims->chunk);
   return dart::scan_bwd_workspace_bytes(dims->batch, dims->seqlen, dims->nheads, dims->dstate,
                                         dims->headdim, dims->chunk);
 }

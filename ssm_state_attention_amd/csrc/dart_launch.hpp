@@ -87,6 +87,25 @@ hipError_t launch_sma_bwd(const PrefillShape& s, const T* Q, const T* E, const T
                           void* workspace, hipStream_t st);
 size_t sma_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t S);
 
+// Backward for f32 io (N = P = 16 or 32), plain f32 kernels: the same
+// arguments and results as launch_sma_bwd / launch_scan_bwd, with their own
+// workspaces.
+template <int N, int P>
+hipError_t launch_sma_bwd_f32(const PrefillShape& s, const float* Q, const float* E,
+                              const float* C, const float* dH, const float* o, const float* lse,
+                              const float* dy, float gate, float* dQ, float* dE, float* dC,
+                              float* ddH, float* dgate, void* workspace, hipStream_t st);
+template <int N, int P>
+hipError_t launch_scan_bwd_f32(const PrefillShape& s, const float* x, const float* dt,
+                               const float* A, const float* Bm, const float* C,
+                               const float* acum, const float* H_in, const float* dy,
+                               const float* ddH, const float* dh_final, const float* dC_sma,
+                               float* dx, float* ddt, float* dA, float* dB, float* dC,
+                               float* dh0, void* workspace, hipStream_t st);
+size_t sma_bwd_f32_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t G, int64_t S);
+size_t scan_bwd_f32_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t N, int64_t P,
+                                    int64_t S);
+
 // Scan backward (16-bit io, P <= 64, S a multiple of 64): dx, ddt, dA, dB,
 // dC (+ dC_sma), dh0 (all f32) from dy, ddH and dh_final (both may be null).
 template <typename T, int N, int P>

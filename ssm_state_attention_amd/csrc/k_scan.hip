@@ -338,8 +338,12 @@ __device__ __forceinline__ void store_memory_rows(ChunkMemLds<N, P>& sm, bf16* _
 }
 
 // One workgroup per (chunk c, head h, batch b): memory c as io and f32 rows.
+// At most 128 VGPRs (four waves per SIMD): at N = 128, P = 64 the kernel
+// fits without spills and four workgroups share a CU instead of three
+// (3.5% faster at the ~370M layer shape, same code otherwise).
 template <int N, int P>
-__global__ __launch_bounds__(kThreads) void k_chunk_state_tr(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void
+k_chunk_state_tr(
     const bf16* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
     const bf16* __restrict__ Bm, float* __restrict__ acum, bf16* __restrict__ dH,
     float* __restrict__ dHf, int L, int H, int G, int S) {

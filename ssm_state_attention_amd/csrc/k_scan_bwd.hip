@@ -639,7 +639,10 @@ hipError_t launch_scan_bwd(const PrefillShape& s, const T* x, const float* dt, c
                            const float* ddH, const float* dh_final, const float* dC_sma,
                            float* dx, float* ddt, float* dA, float* dB, float* dC, float* dh0,
                            void* workspace, hipStream_t st) {
-  if constexpr (!std::is_same<T, bf16>::value || P > 64) {
+  if constexpr (std::is_same<T, float>::value) {
+    return launch_scan_bwd_f32<N, P>(s, x, dt, A, Bm, C, acum, H_in, dy, ddH, dh_final, dC_sma,
+                                     dx, ddt, dA, dB, dC, dh0, workspace, st);
+  } else if constexpr (!std::is_same<T, bf16>::value || P > 64) {
     return hipErrorNotSupported;
   } else {
     const int M = s.L / s.S, PN = P * N, ntile = PN / 1024, nblk = s.S / kT;

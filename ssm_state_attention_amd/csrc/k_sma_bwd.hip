@@ -504,7 +504,10 @@ hipError_t launch_sma_bwd(const PrefillShape& s, const T* Q, const T* E, const T
                           const T* dH, const float* o, const float* lse, const T* dy,
                           float gate, float* dQ, float* dE, float* dC, float* ddH,
                           float* dgate, void* workspace, hipStream_t st) {
-  if constexpr (!std::is_same<T, bf16>::value || P > 64) {
+  if constexpr (std::is_same<T, float>::value) {
+    return launch_sma_bwd_f32<N, P>(s, Q, E, C, dH, o, lse, dy, gate, dQ, dE, dC, ddH, dgate,
+                                    workspace, st);
+  } else if constexpr (!std::is_same<T, bf16>::value || P > 64) {
     return hipErrorNotSupported;
   } else {
     const int M = s.L / s.S;

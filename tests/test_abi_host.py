@@ -207,9 +207,14 @@ def test_backward_entry_points_validate_on_host():
     d = dims(2, 512, 4, 2, 128, 64, 128, BF16)
     ws_sma, ws_scan = lib.dart_sma_bwd_workspace(d), lib.dart_scan_bwd_workspace(d)
     assert ws_sma > 0 and ws_sma % 256 == 0 and ws_scan > 0
-    # unsupported: fp32 io, P = 128, 32-token chunks
-    for bad in (dims(1, 1024, 1, 1, 16, 16, 64, F32), dims(1, 512, 2, 2, 128, 128, 256, BF16),
-                dims(1, 1024, 2, 2, 128, 64, 32, BF16)):
+    # f32 io: the plain f32 kernels' workspaces (dgate partials and the
+    # factor pairs; du, the two state-gradient arrays and the dA partials)
+    f = dims(1, 1024, 1, 1, 16, 16, 64, F32)
+    M = 16
+    assert lib.dart_sma_bwd_workspace(f) == 256 + 1 * 64 * M * (M - 1) // 2 * 8
+    assert lib.dart_scan_bwd_workspace(f) == 4096 + 2 * (M * 256 * 4) + 256
+    # unsupported: P = 128, 32-token chunks (bf16)
+    for bad in (dims(1, 512, 2, 2, 128, 128, 256, BF16), dims(1, 1024, 2, 2, 128, 64, 32, BF16)):
         assert lib.dart_sma_bwd_workspace(bad) == 0 and lib.dart_scan_bwd_workspace(bad) == 0
         assert lib.dart_sma_bwd(bad, *([A16] * 7), 0.5, *([A16] * 5), A16, 1 << 30,
                                 None) == UNSUP

@@ -270,3 +270,115 @@ def test_backward_single_chunk():
     for k in ("dx", "ddt", "dA", "dB", "dC"):
         assert_parity(gr[k], ref[k], f"single chunk {k}")
     assert_parity(_pn_to_np(gr["dh0"]), ref["dh0"], "single chunk dh0")
+
+
+# ------------------------------------------------------------ f32 io
+# The f32 backward runs plain f32 kernels (every compiled f32 shape, any chunk
+# size).  Bar: max|gpu - ref| <= 1e-4 · max(1, max|ref|) per tensor: the fp32
+# bar of 1e-4 absolute, relative to the tensor's scale where gradients that
+# sum many products exceed 1.
+F32 = torch.float32
+
+
+def assert_parity_f32(gpu, ref, what):
+    g = gpu if isinstance(gpu, np.ndarray) else synth.as_f64(gpu)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert g.shape == ref.shape, f"{what}: shape {g.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = float(np.max(np.abs(g - ref))) if g.size else 0.0
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    bound = 1e-4 * max(1.0, scale)
+    print(f"{what}: max err {err:.3e} bound {bound:.3e} (max|ref| {scale:.3e})", flush=True)
+    assert err <= bound, f"{what}: max err {err:.3e} > bound {bound:.3e}"
+
+
+@pytest.mark.parametrize("B,L,H,G,N,P,S,qscale,mem_std", [
+    (1, 1024, 1, 1, 16, 16, 64, 1.0, 0.05),     # the tiny fp32 layer's shape (16 chunks)
+    (2, 288, 3, 3, 32, 32, 96, 30.0, 0.05),     # S = 96, sharpened
+    (1, 256, 4, 2, 32, 32, 32, 100.0, 0.05),    # 32-token chunks, heads sharing a group
+])
+def test_sma_backward_f32(B, L, H, G, N, P, S, qscale, mem_std):
+    _need_gpu()
+    print(f"f32 sma backward case B{B} L{L} H{H} G{G} N{N} P{P} S{S} qscale{qscale}", flush=True)
+    gate = 0.7
+    inp = synth.draw_prefill(14, B, L, H, G, N, P, io=F32, qscale=qscale)
+    inp["dH"] = synth.draw_state(15, (B, H, L // S, P, N), mem_std, F32)
+    inp["dy"] = synth.draw_state(16, (B, L, H, P), 1.0, F32)
+    inp["y_ssd"] = synth.draw_state(17, (B, L, H, P), 1.0, F32)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    y = torch.empty(B, L, H, P, dtype=F32, device=DEV)
+    o = torch.empty(B, L, H, P, dtype=F32, device=DEV)
+    lse = torch.empty(B, H, L, dtype=F32, device=DEV)
+    api.dart_sma_fwd_train(d["Q"], d["E"], d["C"], d["dH"], d["y_ssd"], gate, y, o, lse, S)
+    gr = api.dart_sma_bwd(d["Q"], d["E"], d["C"], d["dH"], o, lse, d["dy"], gate, S)
+    torch.cuda.synchronize()
+    n = {k: synth.as_f64(v) for k, v in inp.items()}
+    dHo = np.swapaxes(n["dH"], -1, -2)
+    o_ref = oracle.sma(n["Q"], n["E"], n["C"], dHo, S)
+    assert_parity_f32(o, o_ref, "o")
+    _, do, dg = oracle.gated_backward(n["dy"], o_ref, gate)
+    dQ, dE, dC, ddH = oracle.sma_backward(n["Q"], n["E"], n["C"], dHo, S, do)
+    assert_parity_f32(gr["dQ"], dQ, "dQ")
+    assert_parity_f32(gr["dE"], dE, "dE")
+    assert_parity_f32(gr["dC"], dC, "dC")
+    assert_parity_f32(_pn_to_np(gr["ddH"]), ddH, "ddH")
+    dg_gpu = float(gr["dgate"].item())
+    print(f"dgate {dg_gpu:.6e} ref {dg:.6e}", flush=True)
+    assert abs(dg_gpu - dg) <= 1e-4 * max(1.0, abs(dg))
+
+
+@pytest.mark.parametrize("B,L,H,G,N,P,S,with_extra", [
+    (1, 1024, 1, 1, 16, 16, 64, True),     # the tiny fp32 layer's shape
+    (2, 288, 3, 3, 32, 32, 96, True),      # S = 96
+    (1, 256, 4, 2, 32, 32, 32, False),     # 32-token chunks, shared B/C; dy only
+    (1, 512, 2, 1, 16, 16, 256, True),     # 256-token chunks
+])
+def test_scan_backward_f32(B, L, H, G, N, P, S, with_extra):
+    _need_gpu()
+    print(f"f32 scan backward case B{B} L{L} H{H} G{G} N{N} P{P} S{S} extra{with_extra}",
+          flush=True)
+    inp = synth.draw_prefill(22, B, L, H, G, N, P, io=F32)
+    M = L // S
+    extra = {"dy": synth.draw_state(23, (B, L, H, P), 1.0, F32),
+             "ddH": synth.draw_state(24, (B, H, M, P, N), 1.0, F32),
+             "dhf": synth.draw_state(25, (B, H, P, N), 1.0, F32),
+             "dCs": synth.draw_state(26, (B, L, G, N), 1.0, F32)}
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    e = {k: v.to(DEV) for k, v in extra.items()}
+    fwd = api.prefill(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], 0.5, S)
+    gr = api.dart_scan_bwd(d["x"], d["dt"], d["A"], d["Bm"], d["C"], fwd["acum"], fwd["H_in"],
+                           e["dy"], S, ddH=e["ddH"] if with_extra else None,
+                           dh_final=e["dhf"] if with_extra else None,
+                           dC_sma=e["dCs"] if with_extra else None)
+    torch.cuda.synchronize()
+    ref = _oracle_scan(inp, extra, S, with_extra)
+    for k in ("dx", "ddt", "dA", "dB", "dC"):
+        assert_parity_f32(gr[k], ref[k], f"f32 scan {k}")
+    assert_parity_f32(_pn_to_np(gr["dh0"]), ref["dh0"], "f32 scan dh0")
+
+
+def test_prefill_backward_end_to_end_f32():
+    """The tiny fp32 layer (batch 1, 1 head, L=1024, S=64, N=P=16): the
+    whole prefill backward (SMA feeding the scan) against the oracle's
+    chain."""
+    _need_gpu()
+    B, L, H, G, N, P, S, gate = 1, 1024, 1, 1, 16, 16, 64, 0.5
+    inp = synth.draw_prefill(0, B, L, H, G, N, P, io=F32)
+    dy = synth.draw_state(33, (B, L, H, P), 1.0, F32)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    fwd = api.prefill_train(d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"], gate, S)
+    gr = api.prefill_backward(fwd, d["x"], d["dt"], d["A"], d["Bm"], d["C"], d["Q"], d["E"],
+                              gate, S, dy.to(DEV))
+    torch.cuda.synchronize()
+    n = {k: synth.as_f64(v) for k, v in inp.items()}
+    dH = oracle.chunk_states(n["x"], n["dt"], n["A"], n["Bm"], S)
+    o = oracle.sma(n["Q"], n["E"], n["C"], dH, S)
+    _, do, dg = oracle.gated_backward(synth.as_f64(dy), o, gate)
+    dQ, dE, dC_s, ddH = oracle.sma_backward(n["Q"], n["E"], n["C"], dH, S, do)
+    ref = oracle.ssd_backward(n["x"], n["dt"], n["A"], n["Bm"], n["C"], S, synth.as_f64(dy), ddH)
+    ref["dC"] = ref["dC"] + dC_s
+    for k in ("dx", "ddt", "dA", "dB", "dC"):
+        assert_parity_f32(gr[k], ref[k], f"f32 end-to-end {k}")
+    assert_parity_f32(gr["dQ"], dQ, "f32 end-to-end dQ")
+    assert_parity_f32(gr["dE"], dE, "f32 end-to-end dE")
+    assert abs(float(gr["dgate"].item()) - dg) <= 1e-4 * max(1.0, abs(dg))

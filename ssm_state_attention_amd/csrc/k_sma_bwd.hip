@@ -18,7 +18,7 @@
 // k_sma_bwd_tok:  token-major (as the forward): dQ, dC, dE; it also leaves
 //                 ds/sqrt(N) and g·α of every visible (token, memory) pair
 //                 in the workspace.
-// k_sma_bwd_mem:  memory-major: ddH[c] from every later token, from those
+// k_sma_bwd_mem4: memory-major: ddH[c] from every later token, from those
 //                 factors (no recomputation).
 // The token kernel recomputes Zq and Zc with the forward's MFMA tiles; the
 // products with dH[c] taken along P (dQ, dC) and the token sums (ddH) read
@@ -312,38 +312,37 @@ __global__ __launch_bounds__(64 * WAVES) void k_sma_bwd_tok(
   }
 }
 
-// Memory-major backward: one workgroup (8 waves) per (batch, head) and pair
-// of memories c0 = 2j, c1 = 2j+1, summing ddH[c] = Σ_t (Q_t·ds/sqrt(N)) E_tᵀ +
-// (C_t·g·α) dy_tᵀ over the 64-token tiles of chunks M-1 down to c0+1 (the
-// tiles of chunk c1 count for c0 only).  The factors ds/sqrt(N) and g·α come
-// from the token-major kernel, so a tile needs no recomputation: its Q and
-// C rows are staged in LDS once for both memories, its E and dy rows once
-// per memory, already scaled by that memory's factors (double-buffered, one
-// barrier per tile; the next tile and its factors are fetched into
-// registers while the current one is multiplied), and the sums are MFMAs
-// whose K axis is the token, both operands read as token columns by
-// transpose reads straight into the MFMAs.
-// Waves 4m .. 4m+3 take memory c0 + m; among them wave w takes tokens
-// 32·(w/2 % 2) .. +31 of each tile and the rows n of half w%2 of ddH[c]
-// (each E/dy column is read by two waves of a memory, each Q/C column by
-// one); the two token halves are added once at the end.  The workgroups of
-// one (batch, head) start on the same tiles and share them through L2.
+// Memory-major backward: ddH[c] = Σ_t (Q_t·ds/sqrt(N)) E_tᵀ + (C_t·g·α) dy_tᵀ
+// over the 64-token tiles of the chunks after c, one workgroup (8 waves) per
+// (batch, head) and four memories c0 = 4j .. 4j+3.  The factors ds/sqrt(N)
+// and g·α come from the token-major kernel, so a tile needs no
+// recomputation, and the sums are MFMAs whose K axis is the token, both
+// operands read as token columns by transpose reads.  The kernel's time
+// goes to fetching the tiles (every later tile of the sequence, for every
+// group of memories), so each staged tile serves four memories.  Q, C, E and dy rows are staged once per tile with the
+// four memories' factor pairs (ds/sqrt(N), g·α) of its tokens
+// (double-buffered, one barrier per tile, the next tile fetched into
+// registers while the current one is multiplied); each wave scales its E
+// and dy operands by its memory's factors after the transpose reads (the
+// same f32 product and rounding as scaling them at staging).
+// Waves 2m, 2m+1 take memory c0 + m, rows n of half w%2 of ddH[c], every
+// token of the tile (two 32-token K-steps).
 template <int N, int P>
-__global__ __launch_bounds__(512) void k_sma_bwd_mem(
+__global__ __launch_bounds__(512) void k_sma_bwd_mem4(
     const bf16* __restrict__ Q, const bf16* __restrict__ E, const bf16* __restrict__ C,
     const bf16* __restrict__ dy, const float2* __restrict__ dsga, float* __restrict__ ddH,
     int B, int L, int H, int G, int S) {
   constexpr int NPB = P / 16, NNB = N / 16;
   constexpr int NBW = NNB / 2;  // n blocks per wave
-  constexpr int LDN = N + 16, LDP = P + 16, T = 64, NT = 512;
+  constexpr int LDN = N + 16, LDP = P + 16, T = 64, NT = 512, MEMS = 4;
   constexpr int QN = T * N / 8, EN = T * P / 8;  // 16-byte vectors of a Q (C) and an E (dy) tile
   constexpr int QV = (QN + NT - 1) / NT, EV = (EN + NT - 1) / NT;
-  constexpr int TILE = 2 * T * LDN + 4 * T * LDP;  // bf16: Q, C, then E·ds, dy·gα per memory
-  constexpr int RED = 2 * NBW * NPB * 64 * 4;       // floats of one memory's final exchange
-  constexpr int SH = 2 * TILE > RED * 4 ? 2 * TILE : RED * 4;  // RED * 4 bf16 = 2·RED floats
-  __shared__ __align__(16) bf16 sh[SH];
+  constexpr int TILE = 2 * T * LDN + 2 * T * LDP;  // bf16: Q, C, E, dy rows
+  constexpr int BUF = TILE + MEMS * T * 4;         // then float2 factors [memory][token]
+  static_assert((TILE * 2) % 16 == 0 && MEMS * T <= NT, "k_sma_bwd_mem4 layout");
+  __shared__ __align__(16) bf16 sh[2 * BUF];
 
-  const int M = L / S, BH = B * H, hpg = H / G;
+  const int M = L / S, BH = B * H, hpg = H / G, NJ = (M + MEMS - 1) / MEMS;
   int pair, j;
   if ((B * G) % 8 == 0) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per = BH / 8;
@@ -354,12 +353,13 @@ __global__ __launch_bounds__(512) void k_sma_bwd_mem(
     pair = blockIdx.x % BH;
     j = blockIdx.x / BH;
   }
+  (void)NJ;
   const int b = pair / H, h = pair % H, g = h / hpg;
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int mw = w >> 2, tg = (w >> 1) & 1, nh = w & 1;
-  const int c0 = 2 * j, c = c0 + mw;
-  const bool live = c < M;  // c1 = M when M is odd: no memory
+  const int mw = w >> 1, nh = w & 1;
+  const int c0 = MEMS * j, c = c0 + mw;
+  const bool live = c < M;
 
   floatx4 acc[NBW][NPB];
 #pragma unroll
@@ -368,16 +368,16 @@ __global__ __launch_bounds__(512) void k_sma_bwd_mem(
     for (int pb = 0; pb < NPB; ++pb) acc[i][pb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int ntile = (M - 1 - c0) * (S / T);
-  // tile i covers tokens tok0(i) .. +63 of chunk kc(i), chunks from the last one down
   auto kc = [&](int i) __attribute__((always_inline)) { return M - 1 - i / (S / T); };
   auto tok0 = [&](int i) __attribute__((always_inline)) {
     return kc(i) * S + (i % (S / T)) * T;
   };
+  // this thread's factor slot: memory fm, token ft of the tile
+  const int fm = tid / T, ft = tid % T;
+  const bool fslot = tid < MEMS * T && c0 + fm < M;
+  const long fbase = fslot ? dsga_offset(pair, c0 + fm, M, S) - (long)(c0 + fm + 1) * S : 0;
   bf16x8 rq[QV], rc[QV], re[EV], rd[EV];
-  float2 rf[2][EV];  // factors (ds/sqrt(N), g·α) of the token of re[v], per memory
-  const bool live1 = c0 + 1 < M;
-  const long f0 = dsga_offset(pair, c0, M, S) - (long)(c0 + 1) * S;
-  const long f1 = live1 ? dsga_offset(pair, c0 + 1, M, S) - (long)(c0 + 2) * S : 0;
+  float2 rf;
   auto fetch = [&](int i) __attribute__((always_inline)) {
     const int t0 = tok0(i);
     const long r0 = (long)b * L + t0;
@@ -395,17 +395,17 @@ __global__ __launch_bounds__(512) void k_sma_bwd_mem(
       if (EN % NT == 0 || vi < EN) {
         re[v] = *reinterpret_cast<const bf16x8*>(E + ((r0 + t) * H + h) * P + pv * 8);
         rd[v] = *reinterpret_cast<const bf16x8*>(dy + ((r0 + t) * H + h) * P + pv * 8);
-        rf[0][v] = dsga[f0 + t0 + t];
-        // memory c1 takes no part in the tiles of its own chunk
-        rf[1][v] = live1 && kc(i) > c0 + 1 ? dsga[f1 + t0 + t] : float2{0.f, 0.f};
       }
     }
+    // memory c0 + fm takes part in the tiles of later chunks only
+    rf = fslot && kc(i) > c0 + fm ? dsga[fbase + t0 + ft] : float2{0.f, 0.f};
   };
   auto stage = [&](int buf) __attribute__((always_inline)) {
-    bf16* sQ = sh + buf * TILE;
+    bf16* sQ = sh + buf * BUF;
     bf16* sC = sQ + T * LDN;
-    bf16* sE = sC + T * LDN;  // [memory][t][p], then sD likewise
-    bf16* sD = sE + 2 * T * LDP;
+    bf16* sE = sC + T * LDN;
+    bf16* sD = sE + T * LDP;
+    float2* sF = reinterpret_cast<float2*>(sQ + TILE);
 #pragma unroll
     for (int v = 0; v < QV; ++v) {
       const int vi = tid + v * NT, t = vi / (N / 8), nv = vi % (N / 8);
@@ -418,43 +418,53 @@ __global__ __launch_bounds__(512) void k_sma_bwd_mem(
     for (int v = 0; v < EV; ++v) {
       const int vi = tid + v * NT, t = vi / (P / 8), pv = vi % (P / 8);
       if (EN % NT == 0 || vi < EN) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          float ve[8], vd[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            ve[e] = to_f32(re[v][e]) * rf[m][v].x;
-            vd[e] = to_f32(rd[v][e]) * rf[m][v].y;
-          }
-          *reinterpret_cast<bf16x8*>(&sE[(m * T + t) * LDP + pv * 8]) = pack8(ve);
-          *reinterpret_cast<bf16x8*>(&sD[(m * T + t) * LDP + pv * 8]) = pack8(vd);
-        }
+        *reinterpret_cast<bf16x8*>(&sE[t * LDP + pv * 8]) = re[v];
+        *reinterpret_cast<bf16x8*>(&sD[t * LDP + pv * 8]) = rd[v];
       }
     }
+    if (tid < MEMS * T) sF[tid] = rf;
   };
   auto multiply = [&](int buf) __attribute__((always_inline)) {
-    const bf16* sQ = sh + buf * TILE;
+    const bf16* sQ = sh + buf * BUF;
     const bf16* sC = sQ + T * LDN;
-    const bf16* sE = sC + T * LDN + mw * T * LDP;  // this wave's memory
-    const bf16* sD = sE + 2 * T * LDP;
-    const int r0 = tg * 32 + 4 * grp;  // this lane's token runs r0.., r0+16..
-    bf16x8 be[NPB], bd[NPB];
+    const bf16* sE = sC + T * LDN;
+    const bf16* sD = sE + T * LDP;
+    const float2* sF = reinterpret_cast<const float2*>(sQ + TILE) + mw * T;
 #pragma unroll
-    for (int pb = 0; pb < NPB; ++pb) {
-      const int o = (r0 + col / 4) * LDP + pb * 16 + 4 * (col % 4);
-      be[pb] = cat8(lds_read_tr4(&sE[o]), lds_read_tr4(&sE[o + 16 * LDP]));
-      bd[pb] = cat8(lds_read_tr4(&sD[o]), lds_read_tr4(&sD[o + 16 * LDP]));
-    }
+    for (int ks = 0; ks < 2; ++ks) {
+      const int r0 = ks * 32 + 4 * grp;  // this lane's tokens r0 .. r0+3, r0+16 .. r0+19
+      float2 f[8];
 #pragma unroll
-    for (int i2 = 0; i2 < NBW; ++i2) {
-      const int nb = nh * NBW + i2;
-      const int o = (r0 + col / 4) * LDN + nb * 16 + 4 * (col % 4);
-      const bf16x8 aq = cat8(lds_read_tr4(&sQ[o]), lds_read_tr4(&sQ[o + 16 * LDN]));
-      const bf16x8 ac = cat8(lds_read_tr4(&sC[o]), lds_read_tr4(&sC[o + 16 * LDN]));
+      for (int e = 0; e < 4; ++e) {
+        f[e] = sF[r0 + e];
+        f[4 + e] = sF[r0 + 16 + e];
+      }
+      bf16x8 be[NPB], bd[NPB];
 #pragma unroll
       for (int pb = 0; pb < NPB; ++pb) {
-        acc[i2][pb] = Mma<bf16>::mma(aq, be[pb], acc[i2][pb]);
-        acc[i2][pb] = Mma<bf16>::mma(ac, bd[pb], acc[i2][pb]);
+        const int o = (r0 + col / 4) * LDP + pb * 16 + 4 * (col % 4);
+        const bf16x8 xe = cat8(lds_read_tr4(&sE[o]), lds_read_tr4(&sE[o + 16 * LDP]));
+        const bf16x8 xd = cat8(lds_read_tr4(&sD[o]), lds_read_tr4(&sD[o + 16 * LDP]));
+        float ve[8], vd[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ve[e] = to_f32(xe[e]) * f[e].x;
+          vd[e] = to_f32(xd[e]) * f[e].y;
+        }
+        be[pb] = pack8(ve);
+        bd[pb] = pack8(vd);
+      }
+#pragma unroll
+      for (int i2 = 0; i2 < NBW; ++i2) {
+        const int nb = nh * NBW + i2;
+        const int o = (r0 + col / 4) * LDN + nb * 16 + 4 * (col % 4);
+        const bf16x8 aq = cat8(lds_read_tr4(&sQ[o]), lds_read_tr4(&sQ[o + 16 * LDN]));
+        const bf16x8 ac = cat8(lds_read_tr4(&sC[o]), lds_read_tr4(&sC[o + 16 * LDN]));
+#pragma unroll
+        for (int pb = 0; pb < NPB; ++pb) {
+          acc[i2][pb] = Mma<bf16>::mma(aq, be[pb], acc[i2][pb]);
+          acc[i2][pb] = Mma<bf16>::mma(ac, bd[pb], acc[i2][pb]);
+        }
       }
     }
   };
@@ -471,19 +481,8 @@ __global__ __launch_bounds__(512) void k_sma_bwd_mem(
     if (i + 1 < ntile) stage((i + 1) & 1);
     __syncthreads();
   }
-  // the second token half of each memory hands its sums to the first
-  float* red = reinterpret_cast<float*>(sh) + mw * RED;
-  if (tg == 1) {
-#pragma unroll
-    for (int i2 = 0; i2 < NBW; ++i2)
-#pragma unroll
-      for (int pb = 0; pb < NPB; ++pb)
-        *reinterpret_cast<floatx4*>(&red[(((nh * NBW + i2) * NPB + pb) * 64 + lane) * 4]) =
-            acc[i2][pb];
-  }
-  __syncthreads();
   // ddH[c] rows [p][n]: lane holds n = nb·16 + 4·grp .. +3 of column p = pb·16 + col
-  if (tg == 0 && live) {
+  if (live) {
     float* out = ddH + ((long)pair * M + c) * (P * N);
 #pragma unroll
     for (int i2 = 0; i2 < NBW; ++i2)
@@ -491,8 +490,7 @@ __global__ __launch_bounds__(512) void k_sma_bwd_mem(
       for (int pb = 0; pb < NPB; ++pb) {
         const int nb = nh * NBW + i2;
         *reinterpret_cast<floatx4*>(out + (pb * 16 + col) * N + nb * 16 + 4 * grp) =
-            acc[i2][pb] +
-            *reinterpret_cast<const floatx4*>(&red[((nb * NPB + pb) * 64 + lane) * 4]);
+            acc[i2][pb];
       }
   }
 }
@@ -535,7 +533,7 @@ hipError_t launch_sma_bwd(const PrefillShape& s, const T* Q, const T* E, const T
                          dy, lse, dyo, gate, dQ, dE, dC, dsga, s.B, s.L, s.H, s.G, s.S,
                          scale_log2, rsn);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_sma_bwd_mem<N, P>), dim3((long)s.B * s.H * ((M + 1) / 2)), dim3(512),
+    hipLaunchKernelGGL((k_sma_bwd_mem4<N, P>), dim3((long)s.B * s.H * ((M + 3) / 4)), dim3(512),
                        0, st, Q, E, C, dy, dsga, ddH, s.B, s.L, s.H, s.G, s.S);
     return hipGetLastError();
   }

@@ -50,9 +50,9 @@ PROFILED_TRAFFIC = {
                             (66287 * 2 + 131584 + 1050550 * 2 + 256) * _KIB),
     # the launches of one SMA backward call (dy·o pass, gate sum, token- and
     # memory-major kernels)
-    "dart_sma_bwd": ("k_sma_bwd.hip", "06886dd2840539233c3b3aa764f7abb9a7d1c8a6",
-                     (196666 * 2 + 8669 + 22 * 2 + 1 + 244703 * 2 + 520192 + 868713 * 2
-                      + 132419) * _KIB),
+    "dart_sma_bwd": ("k_sma_bwd.hip", "31d2af3059dbc1e78eba8955c260928519cbc45c",
+                     (196665 * 2 + 8656 + 18 * 2 + 0 + 244766 * 2 + 520192 + 565978 * 2
+                      + 133251) * _KIB),
 }
 
 

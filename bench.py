@@ -50,7 +50,7 @@ PROFILED_TRAFFIC = {
                             (66287 * 2 + 131584 + 1050550 * 2 + 256) * _KIB),
     # the launches of one SMA backward call (dy·o pass, gate sum, token- and
     # memory-major kernels)
-    "dart_sma_bwd": ("k_sma_bwd.hip", "31d2af3059dbc1e78eba8955c260928519cbc45c",
+    "dart_sma_bwd": ("k_sma_bwd.hip", "39e45d840efc609e8323aa62695f69393d652841",
                      (196665 * 2 + 8656 + 18 * 2 + 0 + 244766 * 2 + 520192 + 565978 * 2
                       + 133251) * _KIB),
 }

@@ -1398,8 +1398,8 @@ hipError_t launch_chunk_scan(const PrefillShape& s, const T* x, const float* dt,
                              const T* Bm, const float* h0, float* acum, T* dH, float* dH_f32,
                              T* H_in, float* h_final, void* workspace, unsigned tag,
                              hipStream_t st) {
-  const int M = s.L / s.S, BH = s.B * s.H;
   if constexpr (std::is_same<T, bf16>::value) {
+    const int M = s.L / s.S, BH = s.B * s.H;
     char* w = static_cast<char*>(workspace);
     int* err = reinterpret_cast<int*>(w);
     auto* flags = reinterpret_cast<unsigned long long*>(w + 256);
@@ -1434,7 +1434,6 @@ hipError_t launch_chunk_scan(const PrefillShape& s, const T* x, const float* dt,
     if (e != hipSuccess) return e;
     return launch_state_recurrence<T>(s, P * N, acum, f, h0, H_in, h_final, st);
   }
-  (void)M;
 }
 
 #define DART_INST_SCAN(T, N, P)                                                              \

@@ -342,7 +342,7 @@ __global__ __launch_bounds__(512) void k_sma_bwd_mem4(
   static_assert((TILE * 2) % 16 == 0 && MEMS * T <= NT, "k_sma_bwd_mem4 layout");
   __shared__ __align__(16) bf16 sh[2 * BUF];
 
-  const int M = L / S, BH = B * H, hpg = H / G, NJ = (M + MEMS - 1) / MEMS;
+  const int M = L / S, BH = B * H, hpg = H / G;
   int pair, j;
   if ((B * G) % 8 == 0) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per = BH / 8;
@@ -353,7 +353,6 @@ __global__ __launch_bounds__(512) void k_sma_bwd_mem4(
     pair = blockIdx.x % BH;
     j = blockIdx.x / BH;
   }
-  (void)NJ;
   const int b = pair / H, h = pair % H, g = h / hpg;
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -54,3 +54,47 @@ def test_noalloc_decode_matches_workspace_decode():
     # call 3: the benchmark decode shape's element types at many pairs (one split)
     _both(100, 64, 32, 32, 128, 64, 256, 8, torch.bfloat16, list(range(8)) * 8,
           [255, 0, 3, 128] * 16, 1.0)
+
+
+def test_noalloc_decode_replayed_from_a_captured_graph():
+    """Callers under HIP graph capture are among those the allocation-free
+    entry point serves: one decode step captured once and replayed five
+    times (new token values copied into the captured inputs before each
+    replay, eager work between the replays) matches dart_sma_decode run
+    eagerly on a twin state, bit for bit, at every replay; sequence 0
+    closes its chunk during the replays."""
+    B, H, G, N, P, S, mx, io = 4, 8, 4, 128, 64, 64, 8, torch.bfloat16
+    n_chunks, pos = [2, 5, 0, 7], [60, 3, 63, 10]
+    print("noalloc graph replay case", flush=True)
+    ref = _state(110, B, H, G, N, P, S, mx, io, n_chunks, pos)
+    cap = _state(110, B, H, G, N, P, S, mx, io, n_chunks, pos)
+    warm = _state(110, B, H, G, N, P, S, mx, io, n_chunks, pos)
+    names = ("x", "dt", "A", "Bm", "C", "Q", "E")
+    inp = {k: v.to(DEV) for k, v in synth.draw_decode_token(113, B, H, G, N, P, io=io).items()}
+    args = tuple(inp[k] for k in names) + (0.75,)
+    y_cap = torch.empty(B, H, P, dtype=io, device=DEV)
+    # the first call on a device looks the scratch address up: not under capture
+    api.dart_sma_decode_noalloc(*args, warm["cache"], warm["h"], warm["dH_cur"],
+                                warm["n_chunks"], warm["pos"], torch.empty_like(y_cap), S)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        api.dart_sma_decode_noalloc(*args, cap["cache"], cap["h"], cap["dH_cur"],
+                                    cap["n_chunks"], cap["pos"], y_cap, S)
+    torch.cuda.synchronize()
+    for rep in range(5):
+        tok = synth.draw_decode_token(120 + rep, B, H, G, N, P, io=io)
+        for k in names:
+            inp[k].copy_(tok[k].to(DEV))
+        graph.replay()
+        y_ref = torch.empty(B, H, P, dtype=io, device=DEV)
+        api.dart_sma_decode(*args, ref["cache"], ref["h"], ref["dH_cur"], ref["n_chunks"],
+                            ref["pos"], y_ref, ref["workspace"], S)
+        float(torch.randn(1 << 20, device=DEV).square().sum())  # eager work in between
+        torch.cuda.synchronize()
+        assert torch.equal(y_cap, y_ref), f"replay {rep}: y"
+        for k in ("cache", "h", "dH_cur", "n_chunks", "pos"):
+            assert torch.equal(cap[k], ref[k]), f"replay {rep}: {k}"
+    assert int(cap["n_chunks"][0].item()) == 3  # sequence 0 closed its chunk

@@ -296,6 +296,7 @@ def assert_parity_f32(gpu, ref, what):
     (1, 1024, 1, 1, 16, 16, 64, 1.0, 0.05),     # the tiny fp32 layer's shape (16 chunks)
     (2, 288, 3, 3, 32, 32, 96, 30.0, 0.05),     # S = 96, sharpened
     (1, 256, 4, 2, 32, 32, 32, 100.0, 0.05),    # 32-token chunks, heads sharing a group
+    (2, 64, 2, 1, 16, 16, 64, 1.0, 0.05),       # one chunk: no memory visible, zero gradients
 ])
 def test_sma_backward_f32(B, L, H, G, N, P, S, qscale, mem_std):
     _need_gpu()
@@ -332,6 +333,7 @@ def test_sma_backward_f32(B, L, H, G, N, P, S, qscale, mem_std):
     (2, 288, 3, 3, 32, 32, 96, True),      # S = 96
     (1, 256, 4, 2, 32, 32, 32, False),     # 32-token chunks, shared B/C; dy only
     (1, 512, 2, 1, 16, 16, 256, True),     # 256-token chunks
+    (2, 64, 2, 2, 32, 32, 64, True),       # one chunk
 ])
 def test_scan_backward_f32(B, L, H, G, N, P, S, with_extra):
     _need_gpu()

@@ -76,6 +76,7 @@ CASES = [
     (2, 2048, 8, 4, 128, 128, 128, torch.bfloat16, 0.0),   # P=128, M=16: 2/wg, XCD-major
     (1, 448, 2, 2, 32, 32, 64, torch.bfloat16, 0.0),       # M=7, small state
     (2, 256, 2, 1, 32, 32, 32, torch.bfloat16, 0.2),       # S=32 (shorter than a K-block), M=8
+    (1, 65536, 32, 32, 128, 64, 256, torch.bfloat16, 0.0),  # long context: 64 links per chain
     (1, 1024, 2, 1, 16, 16, 64, torch.float32, 0.5),       # f32 io, two-kernel recurrence
     (1, 1024, 2, 1, 32, 32, 32, torch.float32, 0.0),       # f32 io, S=32
 ]

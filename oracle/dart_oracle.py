@@ -34,7 +34,7 @@ Sources (cited by page and section; the pages print no code):
   (editorial extensions): since SMA reads the scan's own ΔH, the memory cache
   could be combined with cache quantisation.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
 * Mamba-2 recurrence h_t = exp(dt_t·A)·h_{t-1} + dt_t·B_t x_tᵀ, y_t = C_tᵀ h_t
   (zero-order-hold discretisation; D skip, gating and norm are absent).
 * A token in chunk k attends over the completed chunks c < k only; tokens of
